@@ -1,0 +1,407 @@
+/*
+ * moe_ref.c: the oracle of one Stable-LatentMoE layer with MXFP4 experts.
+ *
+ * TEST INFRASTRUCTURE ONLY (see moe_ref.h): plain loops, one thread, every
+ * sum in fp64, rounded once at the points the layer defines.  Built with
+ * -ffp-contract=off so no multiply-add is fused behind the reader's back.
+ */
+#include "moe_ref.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------ sizes */
+
+/* kimi-k3-in-c post, "experts that are already 4-bit MXFP4": 0.5 B per weight
+ * plus 1/32 B of shared scale, times 3 matrices of d_latent * d_ffn weights. */
+size_t moe_ref_expert_bytes(int32_t d_latent, int32_t d_ffn) {
+  size_t w = (size_t)3 * (size_t)d_latent * (size_t)d_ffn;
+  return w / 2 + w / 32;
+}
+
+/* ------------------------------------------------------------- MXFP4 value */
+
+/* E2M1 (OCP MX v1.0): sign bit 3, exponent bits 2..1 (bias 1), mantissa bit 0.
+ * Exponent field 0 is subnormal: 0 or 0.5.  Read off the format definition:
+ *   magnitude code 0..7 -> 0, 0.5, 1, 1.5, 2, 3, 4, 6. */
+float moe_ref_e2m1(int32_t code) {
+  int mag = code & 7;
+  int ex = mag >> 1;
+  int man = mag & 1;
+  float v;
+  if (ex == 0)
+    v = 0.5f * (float)man;                           /* subnormal: man * 2^-1 */
+  else
+    v = ldexpf(1.0f + 0.5f * (float)man, ex - 1);    /* (1 + man/2) * 2^(ex-1) */
+  return (code & 8) ? -v : v;
+}
+
+/* kimi-k3-mlx digest, quantisation tiers (e8m0 scale) and kimi-k3-in-c post,
+ * MXFP4 section (one 8-bit exponent per 32 weights): weight = E2M1 * 2^(s-127).
+ * e8m0 255 encodes NaN (OCP MX v1.0).  ldexpf is exact here except overflow,
+ * which gives +-inf as fp32 rounding would. */
+float moe_ref_mxfp4_value(int32_t code, int32_t scale) {
+  if (scale == 255) return nanf("");
+  return ldexpf(moe_ref_e2m1(code), scale - 127);
+}
+
+/* Low-nibble-first (kimi-k3-mlx digest, quantisation tiers): element 2j of a
+ * row is the low nibble of byte j, element 2j+1 the high nibble.  The scale of
+ * element c of row r is scales[r][c/32].  One row is dequantised at a time; the
+ * block's 2^(s-127) is formed once and applied as an fp32 multiply, which is
+ * exact (or overflows to inf) exactly as moe_ref_mxfp4_value. */
+static void mx_row(const uint8_t* codes, const uint8_t* scales, int64_t cols, int64_t r, float* out) {
+  float lut[16];
+  for (int c = 0; c < 16; ++c) lut[c] = moe_ref_e2m1(c);
+  const uint8_t* cr = codes + r * (cols / 2);
+  const uint8_t* sr = scales + r * (cols / 32);
+  for (int64_t b = 0; b < cols / 32; ++b) {
+    float sc = sr[b] == 255 ? nanf("") : ldexpf(1.0f, (int)sr[b] - 127);
+    for (int64_t i = 0; i < 32; ++i) {
+      int64_t c = b * 32 + i;
+      uint8_t byte = cr[c / 2];
+      int code = (c & 1) ? (byte >> 4) : (byte & 15);
+      out[c] = lut[code] * sc;
+    }
+  }
+}
+
+int moe_ref_dequant_matrix(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                           float* out) {
+  if (!codes || !scales || !out || rows < 0 || cols <= 0 || cols % 32) return MOE_REF_ERR_ARG;
+  for (int64_t r = 0; r < rows; ++r) mx_row(codes, scales, cols, r, out + r * cols);
+  return MOE_REF_OK;
+}
+
+/* --------------------------------------------------------------- rounding */
+
+/* bf16 keeps 8 significant bits, exponent range of fp32 (normals from 2^-126,
+ * subnormal spacing 2^-133).  Round v to that grid, ties to even. */
+uint16_t moe_ref_bf16_from_f64(double v) {
+  if (isnan(v)) return 0x7FC0;
+  if (isinf(v)) return v > 0 ? 0x7F80 : 0xFF80;
+  if (v == 0.0) return signbit(v) ? 0x8000 : 0x0000;
+  int e;
+  frexp(v, &e);                  /* |v| = m * 2^e, 0.5 <= m < 1 */
+  int qexp = e - 8;              /* spacing of 8-bit significands at this binade */
+  if (qexp < -133) qexp = -133;  /* bf16 subnormal spacing */
+  double q = ldexp(1.0, qexp);
+  double r = nearbyint(v / q) * q; /* v/q and the product are exact; nearbyint ties to even */
+  if (fabs(r) >= ldexp(1.0, 128)) return r > 0 ? 0x7F80 : 0xFF80;
+  float f = (float)r;             /* exact: r has <= 8 significant bits */
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  return (uint16_t)(u >> 16);
+}
+
+static inline double bf16_to_f64(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+/* ------------------------------------------------ exact router dot product */
+
+/*
+ * The router logit is defined as the correctly rounded fp32 value of the exact
+ * sum of products of bf16 numbers.  A bf16 number is m * 2^q with m an integer
+ * below 2^8 (q = be - 134 for a normal biased exponent be, q = -133 for a
+ * subnormal).  A product is M * 2^Q with M < 2^16 and Q >= -266.  The sum is
+ * accumulated exactly in a fixed-point integer whose least significant bit is
+ * 2^-266: KW signed 64-bit "digits" of 32 bits each, carries resolved at the end.
+ */
+#define KW 20
+#define KLSB 266
+
+typedef struct {
+  int64_t acc[KW];
+  int nan, pinf, ninf;
+} kulisch;
+
+static void k_add_product(kulisch* K, uint16_t a, uint16_t b) {
+  int sa = a >> 15, sb = b >> 15;
+  int ea = (a >> 7) & 0xFF, eb = (b >> 7) & 0xFF;
+  int fa = a & 0x7F, fb = b & 0x7F;
+  int a_inf = (ea == 255 && fa == 0), b_inf = (eb == 255 && fb == 0);
+  int a_nan = (ea == 255 && fa != 0), b_nan = (eb == 255 && fb != 0);
+  int a_zero = (ea == 0 && fa == 0), b_zero = (eb == 0 && fb == 0);
+  if (a_nan || b_nan || (a_inf && b_zero) || (b_inf && a_zero)) {
+    K->nan = 1;
+    return;
+  }
+  if (a_inf || b_inf) {
+    if (sa ^ sb) K->ninf = 1; else K->pinf = 1;
+    return;
+  }
+  if (a_zero || b_zero) return;
+  int64_t ma = ea ? (128 + fa) : fa, mb = eb ? (128 + fb) : fb;
+  int qa = ea ? ea - 134 : -133, qb = eb ? eb - 134 : -133;
+  uint64_t M = (uint64_t)(ma * mb);
+  int o = qa + qb + KLSB; /* >= 0 */
+  int wi = o >> 5, sh = o & 31;
+  uint64_t v = M << sh; /* < 2^47 */
+  int64_t lo = (int64_t)(v & 0xFFFFFFFFull), hi = (int64_t)(v >> 32);
+  if (sa ^ sb) {
+    K->acc[wi] -= lo;
+    K->acc[wi + 1] -= hi;
+  } else {
+    K->acc[wi] += lo;
+    K->acc[wi + 1] += hi;
+  }
+}
+
+static int get_bit(const uint32_t* dig, int i) { return (dig[i >> 5] >> (i & 31)) & 1; }
+
+static float k_round(const kulisch* K) {
+  if (K->nan || (K->pinf && K->ninf)) return nanf("");
+  if (K->pinf) return INFINITY;
+  if (K->ninf) return -INFINITY;
+  uint32_t dig[KW];
+  int64_t carry = 0;
+  for (int w = 0; w < KW; ++w) {
+    int64_t v = K->acc[w] + carry;
+    dig[w] = (uint32_t)v;
+    carry = (v - (int64_t)dig[w]) / 4294967296LL; /* exact: numerator is a multiple of 2^32 */
+  }
+  int neg = carry < 0;
+  if (neg) { /* two's complement negate the KW-digit number */
+    uint64_t c = 1;
+    for (int w = 0; w < KW; ++w) {
+      uint64_t v = (uint64_t)(uint32_t)~dig[w] + c;
+      dig[w] = (uint32_t)v;
+      c = v >> 32;
+    }
+  }
+  int P = -1;
+  for (int i = KW * 32 - 1; i >= 0; --i)
+    if (get_bit(dig, i)) { P = i; break; }
+  if (P < 0) return 0.0f;
+  /* fp32: 24 significant bits; least significant bit no lower than 2^-149 */
+  int lsb = P - 23;
+  if (lsb < KLSB - 149) lsb = KLSB - 149;
+  uint32_t mant = 0;
+  for (int i = P; i >= lsb; --i) mant = (mant << 1) | (uint32_t)get_bit(dig, i);
+  int rbit = get_bit(dig, lsb - 1);
+  int sticky = 0;
+  for (int i = lsb - 2; i >= 0 && !sticky; --i) sticky = get_bit(dig, i);
+  if (rbit && (sticky || (mant & 1))) mant += 1;
+  float r = ldexpf((float)mant, lsb - KLSB); /* exact, or overflow to inf */
+  return neg ? -r : r;
+}
+
+float moe_ref_dot_bf16_exact(const uint16_t* a, const uint16_t* b, int64_t n) {
+  kulisch K;
+  memset(&K, 0, sizeof K);
+  for (int64_t i = 0; i < n; ++i) k_add_product(&K, a[i], b[i]);
+  return k_round(&K);
+}
+
+/* ----------------------------------------------------------------- router */
+
+/* kimi-k3-mlx digest, architecture table (896 routed experts, router picks 16
+ * per token); the router reads the 7168-wide token.  Bias is optional. */
+int moe_ref_router_logits(const uint16_t* x, const uint16_t* router_w, const float* bias,
+                          int64_t bias_stride, int64_t T, int32_t d, int32_t E, float* logits) {
+  if (!x || !router_w || !logits || T < 0 || d <= 0 || E <= 0) return MOE_REF_ERR_ARG;
+  for (int64_t t = 0; t < T; ++t)
+    for (int32_t e = 0; e < E; ++e) {
+      float l = moe_ref_dot_bf16_exact(x + t * d, router_w + (int64_t)e * d, d);
+      if (bias) {
+        volatile float s = l + bias[t * bias_stride + e]; /* one fp32 rounding */
+        l = s;
+      }
+      logits[t * E + e] = l;
+    }
+  return MOE_REF_OK;
+}
+
+/* Order for selection: larger logit first; equal logits (+0 and -0 are equal)
+ * go to the lower expert index; NaN ranks below every number. */
+static int ranks_before(float va, int ia, float vb, int ib) {
+  int na = isnan(va), nb = isnan(vb);
+  if (na != nb) return nb;          /* the non-NaN one is first */
+  if (!na && va != vb) return va > vb;
+  return ia < ib;
+}
+
+static int cmp_int(const void* a, const void* b) {
+  int x = *(const int*)a, y = *(const int*)b;
+  return (x > y) - (x < y);
+}
+
+/* kimi-k3-mlx digest, REAP section: router weights are probabilities that are
+ * renormalised over the surviving experts; here over the k selected ones. */
+int moe_ref_select(const float* logits, int64_t T, int32_t E, int32_t k, int32_t renormalize,
+                   int32_t* idx, float* w) {
+  if (!logits || !idx || T < 0 || E <= 0 || k < 1 || k > E) return MOE_REF_ERR_ARG;
+  char* taken = (char*)malloc((size_t)E);
+  if (!taken) return MOE_REF_ERR_ARG;
+  for (int64_t t = 0; t < T; ++t) {
+    const float* l = logits + t * E;
+    int32_t* it = idx + t * k;
+    memset(taken, 0, (size_t)E);
+    for (int32_t j = 0; j < k; ++j) { /* k passes of "take the first not yet taken" */
+      int best = -1;
+      for (int32_t e = 0; e < E; ++e)
+        if (!taken[e] && (best < 0 || ranks_before(l[e], e, l[best], best))) best = e;
+      taken[best] = 1;
+      it[j] = best;
+    }
+    qsort(it, (size_t)k, sizeof(int32_t), cmp_int);
+    if (w) {
+      double m = -INFINITY;
+      for (int32_t j = 0; j < k; ++j)
+        if (l[it[j]] > m) m = l[it[j]];
+      double den = 0.0;
+      if (renormalize) {
+        for (int32_t j = 0; j < k; ++j) den += exp((double)l[it[j]] - m);
+      } else {
+        for (int32_t e = 0; e < E; ++e)
+          if ((double)l[e] > m) m = l[e];
+        for (int32_t e = 0; e < E; ++e) den += exp((double)l[e] - m);
+      }
+      for (int32_t j = 0; j < k; ++j) w[t * k + j] = (float)(exp((double)l[it[j]] - m) / den);
+    }
+  }
+  free(taken);
+  return MOE_REF_OK;
+}
+
+/* ------------------------------------------------------------ permutation */
+
+/* Group the T*k (token, slot) rows by expert, tokens ascending inside a group:
+ * a counting sort that walks the rows in (t, j) order. */
+int moe_ref_permute(const int32_t* idx, int64_t T, int32_t k, int32_t E, int32_t* counts,
+                    int32_t* offsets, int32_t* perm) {
+  if (!idx || !counts || !offsets || !perm || T < 0 || k < 1 || E < 1) return MOE_REF_ERR_ARG;
+  for (int32_t e = 0; e < E; ++e) counts[e] = 0;
+  for (int64_t r = 0; r < T * k; ++r) {
+    if (idx[r] < 0 || idx[r] >= E) return MOE_REF_ERR_ARG;
+    counts[idx[r]] += 1;
+  }
+  offsets[0] = 0;
+  for (int32_t e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+  int32_t* cur = (int32_t*)malloc(sizeof(int32_t) * (size_t)E);
+  if (!cur) return MOE_REF_ERR_ARG;
+  for (int32_t e = 0; e < E; ++e) cur[e] = offsets[e];
+  for (int64_t r = 0; r < T * k; ++r) perm[cur[idx[r]]++] = (int32_t)r;
+  free(cur);
+  return MOE_REF_OK;
+}
+
+/* ------------------------------------------------------------ dense parts */
+
+/* kimi-k3-mlx digest, architecture: the latent projections 7168 -> 3584 and
+ * back are bf16 matrices; sum in fp64, round once to bf16. */
+int moe_ref_linear_bf16(const uint16_t* in, const uint16_t* W, int64_t T, int32_t n_in, int32_t n_out,
+                        uint16_t* out) {
+  if (!in || !W || !out || T < 0 || n_in <= 0 || n_out <= 0) return MOE_REF_ERR_ARG;
+  for (int64_t t = 0; t < T; ++t)
+    for (int32_t o = 0; o < n_out; ++o) {
+      double s = 0.0;
+      for (int32_t i = 0; i < n_in; ++i)
+        s += bf16_to_f64(in[t * n_in + i]) * bf16_to_f64(W[(int64_t)o * n_in + i]);
+      out[t * n_out + o] = moe_ref_bf16_from_f64(s);
+    }
+  return MOE_REF_OK;
+}
+
+/* ---------------------------------------------------------------- experts */
+
+double moe_ref_silu(double g) { return g / (1.0 + exp(-g)); }
+
+/* One routed expert, GLU form implied by 3 matrices of 3584 x 3072 per expert
+ * (kimi-k3-in-c post, MXFP4 section: 33,030,144 = 3 * 3584 * 3072), with the
+ * activation in fp32 or better (kimi-k3-mlx digest, SiTU-GLU bullet):
+ *   g = RN32(W_g h), u = RN32(W_u h), a = bf16(act(g) * u), y = RN32(W_dn a). */
+int moe_ref_expert(const uint16_t* h, const uint8_t* record, int32_t L, int32_t F, int32_t act,
+                   uint16_t* a_out, float* y) {
+  if (!h || !record || !y || L <= 0 || F <= 0 || L % 32 || F % 32) return MOE_REF_ERR_ARG;
+  if (act != MOE_REF_ACT_SILU) return MOE_REF_ERR_UNSUPPORTED;
+  const int64_t ncode = (int64_t)F * L / 2, mat = ncode + (int64_t)F * L / 32;
+  const uint8_t* gate = record;
+  const uint8_t* up = record + mat;
+  const uint8_t* down = record + 2 * mat;
+  const int32_t wmax = L > F ? L : F;
+  uint16_t* a = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)F);
+  float* wg = (float*)malloc(sizeof(float) * (size_t)wmax);
+  float* wu = (float*)malloc(sizeof(float) * (size_t)wmax);
+  if (!a || !wg || !wu) { free(a); free(wg); free(wu); return MOE_REF_ERR_ARG; }
+  for (int32_t f = 0; f < F; ++f) {
+    mx_row(gate, gate + ncode, L, f, wg);
+    mx_row(up, up + ncode, L, f, wu);
+    double sg = 0.0, su = 0.0;
+    for (int32_t l = 0; l < L; ++l) {
+      double hl = bf16_to_f64(h[l]);
+      sg += hl * (double)wg[l];
+      su += hl * (double)wu[l];
+    }
+    float g = (float)sg, u = (float)su;
+    a[f] = moe_ref_bf16_from_f64(moe_ref_silu((double)g) * (double)u);
+  }
+  for (int32_t l = 0; l < L; ++l) {
+    mx_row(down, down + ncode, F, l, wg);
+    double s = 0.0;
+    for (int32_t f = 0; f < F; ++f) s += bf16_to_f64(a[f]) * (double)wg[f];
+    y[l] = (float)s;
+  }
+  if (a_out) memcpy(a_out, a, sizeof(uint16_t) * (size_t)F);
+  free(a); free(wg); free(wu);
+  return MOE_REF_OK;
+}
+
+/* weighted combine of the k expert outputs of each token, in latent space */
+int moe_ref_combine(const float* y, const float* w, int64_t T, int32_t k, int32_t L, uint16_t* z) {
+  if (!y || !w || !z || T < 0 || k < 1 || L <= 0) return MOE_REF_ERR_ARG;
+  for (int64_t t = 0; t < T; ++t)
+    for (int32_t l = 0; l < L; ++l) {
+      double s = 0.0;
+      for (int32_t j = 0; j < k; ++j) s += (double)w[t * k + j] * (double)y[(t * k + j) * L + l];
+      z[t * L + l] = moe_ref_bf16_from_f64(s);
+    }
+  return MOE_REF_OK;
+}
+
+/* ------------------------------------------------------------ whole layer */
+
+int moe_ref_layer_forward(int32_t d, int32_t L, int32_t F, int32_t E, int32_t k, int32_t act,
+                          int32_t renormalize, const uint16_t* x, const uint16_t* router_w,
+                          const float* bias, int64_t bias_stride, const uint16_t* latent_down,
+                          const uint16_t* latent_up, const uint8_t* blob, const int32_t* tokens,
+                          int64_t n_tokens, uint16_t* out, int32_t* idx, float* w, float* logits,
+                          uint16_t* h_out, uint16_t* z_out) {
+  if (!x || !router_w || !latent_down || !latent_up || !blob || !out || d <= 0 || L <= 0 ||
+      F <= 0 || E <= 0 || k < 1 || k > E || n_tokens < 0 || L % 32 || F % 32)
+    return MOE_REF_ERR_ARG;
+  if (act != MOE_REF_ACT_SILU) return MOE_REF_ERR_UNSUPPORTED;
+  const size_t rec = moe_ref_expert_bytes(L, F);
+  float* lg = (float*)malloc(sizeof(float) * (size_t)E);
+  int32_t* id = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
+  float* wt = (float*)malloc(sizeof(float) * (size_t)k);
+  uint16_t* h = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)L);
+  float* y = (float*)malloc(sizeof(float) * (size_t)k * (size_t)L);
+  uint16_t* z = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)L);
+  int rc = MOE_REF_OK;
+  if (!lg || !id || !wt || !h || !y || !z) rc = MOE_REF_ERR_ARG;
+  for (int64_t i = 0; i < n_tokens && rc == MOE_REF_OK; ++i) {
+    int64_t t = tokens ? tokens[i] : i;
+    const uint16_t* xt = x + t * d;
+    const float* bt = bias ? bias + t * bias_stride : NULL;
+    moe_ref_router_logits(xt, router_w, bt, 0, 1, d, E, lg);
+    moe_ref_select(lg, 1, E, k, renormalize, id, wt);
+    moe_ref_linear_bf16(xt, latent_down, 1, d, L, h);
+    for (int32_t j = 0; j < k && rc == MOE_REF_OK; ++j)
+      rc = moe_ref_expert(h, blob + (size_t)id[j] * rec, L, F, act, NULL, y + (size_t)j * L);
+    moe_ref_combine(y, wt, 1, k, L, z);
+    moe_ref_linear_bf16(z, latent_up, 1, L, d, out + i * d);
+    if (idx) memcpy(idx + i * k, id, sizeof(int32_t) * (size_t)k);
+    if (w) memcpy(w + i * k, wt, sizeof(float) * (size_t)k);
+    if (logits) memcpy(logits + i * E, lg, sizeof(float) * (size_t)E);
+    if (h_out) memcpy(h_out + i * L, h, sizeof(uint16_t) * (size_t)L);
+    if (z_out) memcpy(z_out + i * L, z, sizeof(uint16_t) * (size_t)L);
+  }
+  free(lg); free(id); free(wt); free(h); free(y); free(z);
+  return rc;
+}
