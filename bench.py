@@ -1,0 +1,233 @@
+#!/usr/bin/env python3
+"""Throughput of one Kimi-K3-shaped Stable-LatentMoE layer with MXFP4 experts on one MI355X.
+
+One step = one pass of the whole layer (router, latent down projection, top-k,
+permutation, MXFP4 gate/up with the fp32 GLU, MXFP4 down, combine, latent up)
+over one batch of synthetic tokens, through the C ABI (moe_layer_forward).
+
+Inputs are resident in HBM before the timed region.  So that a step does not find
+the previous step's weights in the 256 MB Infinity Cache, step i takes token
+batch i (distinct tokens route to distinct experts) and dense-weight copy
+i mod --dense-copies.
+
+Prints one JSON line (rank 0).  The roofline object covers the dominant kernel
+(the MXFP4 gate/up GEMV for decode): algorithmic bytes per launch over its mean
+duration, measured with HIP events recorded around it on the layer's stream
+inside the timed region.  cpu_baseline times the C oracle on the host.
+"""
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s on 1 MI355X; HBM GB/s (decode), FP4 MFMA util (prefill)"
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """hipEventCreate / hipEventElapsedTime through the HIP runtime."""
+
+    def __init__(self):
+        self.rt = ctypes.CDLL("libamdhip64.so")
+        self.rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        evs = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.rt.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            evs.append(e.value)
+        return evs
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        if self.rt.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.rt.hipEventDestroy(e)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="decode1", choices=["decode1", "decode64", "prefill4k", "prefill32k", "tiny"])
+    ap.add_argument("--dense-copies", type=int, default=3)
+    ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0, help="0 skips the oracle baseline")
+    ap.add_argument("--breakdown", action="store_true", help="also time every stage (extra untimed pass)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs the layer on one GPU only: this build has no multi-GPU path "
+              "(expert-parallel sharding is a design note, not code). Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import mxfp4_expert_gemm_amd as moe
+    import synth
+
+    c = synth.CONFIGS[args.config]
+    K, W = args.steps, args.warmup
+    nbatch = K + W
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def up(a):
+        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+
+    t0 = time.time()
+    dense = synth.make_dense(c)
+    log(f"[bench] config {c.name}: T={c.T} d={c.d} L={c.L} F={c.F} E={c.E} k={c.k}; generating inputs")
+    blob_host = synth.make_blob(c)
+    blob = up(blob_host)
+    copies = [dict(router_w=up(dense["router_w"]), latent_down=up(dense["latent_down"]),
+                   latent_up=up(dense["latent_up"])) for _ in range(max(1, args.dense_copies))]
+    x_host = synth.make_tokens(c, T=c.T * nbatch).reshape(nbatch, c.T, c.d)
+    xs = up(x_host)
+    bias_host = synth.make_bias(c)
+    bias = None if bias_host is None else up(bias_host)
+    log(f"[bench] inputs resident in HBM ({time.time() - t0:.1f}s)")
+
+    cfg = moe.make_config(c.T, c.d, c.L, c.F, c.E, bias=bias)
+    ws = moe.alloc_workspace(cfg, c.k, dev)
+    out = torch.empty((c.T, c.d), dtype=torch.int16, device=dev)
+    counts = torch.zeros((nbatch, c.E), dtype=torch.int32, device=dev)
+    hip = HipEvents()
+    ev_start, ev_stop = hip.create(2)
+    dom = moe.STAGES.index("gate_up")
+    kev = hip.create(2 * nbatch)
+
+    def step(i, events=None):
+        cp = copies[i % len(copies)]
+        routing = {"expert_counts": counts[i]}
+        if events is None:
+            moe.layer_forward(xs[i], cp["router_w"], cp["latent_down"], cp["latent_up"], blob, c.k, d_ffn=c.F,
+                              bias=bias, out=out, workspace=ws, routing=routing)
+        else:
+            moe.layer_forward_profiled(xs[i], cp["router_w"], cp["latent_down"], cp["latent_up"], blob, c.k,
+                                       events, d_ffn=c.F, bias=bias, out=out, workspace=ws, routing=routing)
+
+    def dom_events(i):
+        ev = moe.StageEvents()
+        ev.begin[dom] = kev[2 * i]
+        ev.end[dom] = kev[2 * i + 1]
+        return ev
+
+    for i in range(W):
+        step(i, dom_events(i))
+    torch.cuda.synchronize()
+
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    hip.rt.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    torch.cuda.synchronize()
+    hip.rt.hipEventRecord(ev_start, stream)
+    for i in range(W, W + K):
+        step(i, dom_events(i))
+    hip.rt.hipEventRecord(ev_stop, stream)
+    torch.cuda.synchronize()
+    total_ms = hip.elapsed_ms(ev_start, ev_stop)
+    ms_per_step = total_ms / K
+    dom_ms = [hip.elapsed_ms(kev[2 * i], kev[2 * i + 1]) for i in range(W, W + K)]
+
+    # algorithmic bytes of the dominant kernel per launch: gate and up codes+scales of every
+    # active expert, the latent rows it reads and the GLU rows it writes
+    cnt = counts.cpu().numpy()[W:W + K]
+    mat_bytes = c.F * c.L // 2 + c.F * c.L // 32
+    active = (cnt > 0).sum(1)
+    dom_bytes = active * 2 * mat_bytes + c.T * c.L * 2 + c.T * c.k * c.F * 2
+    dom_gbs = float(np.mean(dom_bytes / (np.array(dom_ms) * 1e-3)) / 1e9)
+    # whole-layer algorithmic bytes: weights read (dense + active experts) + x + out + bias
+    dense_bytes = (c.E * c.d + 2 * c.L * c.d) * 2
+    layer_bytes = dense_bytes + active * 3 * mat_bytes + 2 * c.T * c.d * 2
+    if bias_host is not None:
+        layer_bytes = layer_bytes + bias_host.nbytes
+    layer_gbs = float(np.mean(layer_bytes) / (ms_per_step * 1e-3) / 1e9)
+
+    stages = None
+    if args.breakdown:
+        evs = hip.create(2 * moe.NUM_STAGES)
+        sums = np.zeros(moe.NUM_STAGES)
+        n = min(K, 10)
+        for i in range(W, W + n):
+            ev = moe.StageEvents()
+            for s in range(moe.NUM_STAGES):
+                ev.begin[s] = evs[2 * s]
+                ev.end[s] = evs[2 * s + 1]
+            step(i, ev)
+            torch.cuda.synchronize()
+            sums += [hip.elapsed_ms(evs[2 * s], evs[2 * s + 1]) for s in range(moe.NUM_STAGES)]
+        stages = {name: round(1e3 * v / n, 2) for name, v in zip(moe.STAGES, sums)}
+        hip.destroy(evs)
+
+    cpu = None
+    if args.cpu_baseline_seconds > 0:
+        import oracle
+
+        budget = args.cpu_baseline_seconds
+        t1 = time.time()
+        n = 0
+        xb = np.ascontiguousarray(x_host.reshape(nbatch * c.T, c.d)[: c.T])  # the first batch
+        while True:
+            oracle.layer_forward(xb, dense["router_w"], dense["latent_down"], dense["latent_up"], blob_host, c.k, c.L,
+                                 c.F, bias=bias_host, tokens=[n % c.T])
+            n += 1
+            if time.time() - t1 >= budget:
+                break
+        dt = time.time() - t1
+        cpu = {"value": round(n / dt, 4), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": f"{n} tokens of the {c.name} workload, whole layer one token at a time "
+                         f"(single-threaded C oracle, fp64 sums, exact router), {dt:.1f} s"}
+
+    tokens_per_s = c.T * K / (total_ms * 1e-3)
+    result = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{c.name}: {c.description}", "tokens": c.T, "d_model": c.d, "d_latent": c.L,
+                   "d_ffn": c.F, "experts": c.E, "top_k": c.k, "expert_weights": "mxfp4 (e2m1 + e8m0 per 32)",
+                   "activations": "bf16, fp32 accumulation, fp32 GLU", "parallelism": "single GPU",
+                   "dense_weight_copies": len(copies), "mean_active_experts": float(np.mean(active))},
+        "roofline": {"bound": "hbm", "kernel": "gate_up (MXFP4 gate/up GEMV + fp32 GLU)",
+                     "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel_us": round(1e3 * float(np.mean(dom_ms)), 2),
+                     "bytes_per_launch": int(np.mean(dom_bytes))},
+        "layer_hbm": {"achieved_GBs": round(layer_gbs, 1), "frac": round(layer_gbs / HBM_PEAK_GBS, 4),
+                      "bytes_per_step": int(np.mean(layer_bytes))},
+        "cpu_baseline": cpu,
+    }
+    if stages is not None:
+        result["stages_us"] = stages
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,212 @@
+/*
+ * moe_layer.h: C ABI of an MI355X (gfx950) implementation of one
+ * Stable-LatentMoE layer whose routed experts stay in MXFP4.
+ *
+ * The layer (cited by page title and section):
+ *  - router: per token, the top-k (k = 16 in Kimi K3) of E = 896 routed
+ *    experts by router logit (kimi-k3-mlx digest, architecture table; the
+ *    kimi-k3-in-c post's introduction: 16 of 896 experts wake per token);
+ *    router weights are probabilities, renormalised over the experts kept
+ *    (kimi-k3-mlx digest, REAP pruning section);
+ *  - Stable LatentMoE: routed experts work in a 3584-wide latent space under
+ *    the 7168-wide residual (kimi-k3-mlx digest, architecture table and the
+ *    LatentMoE bullet), so the token is projected down (bf16 7168 -> 3584),
+ *    the experts run in the latent space, their weighted sum is projected
+ *    back up (bf16 3584 -> 7168);
+ *  - each routed expert is a GLU FFN (gate, up, down; 3 x 3584 x 3072 weights)
+ *    stored in MXFP4: 4-bit E2M1 codes, low nibble first, one e8m0 exponent
+ *    per 32 consecutive weights, 17,547,264 bytes per expert (kimi-k3-in-c
+ *    post, "experts that are already 4-bit MXFP4"; kimi-k3-mlx digest,
+ *    quantisation tiers); the GLU activation runs in fp32 (kimi-k3-mlx
+ *    digest, SiTU-GLU bullet).
+ *
+ * Readings fixed by this library where the pages are silent:
+ *  - logits are fp32; the selection is that of the correctly rounded fp32
+ *    value of the exact bf16 dot product, then + bias in one fp32 add; order is
+ *    (logit descending, expert index ascending); +0 == -0; NaN ranks last.
+ *    Selected ids are written in ascending order.  Weights: softmax over the
+ *    k selected logits (renormalize = 1) or over all E (renormalize = 0).
+ *  - expert record e sits at byte e * moe_expert_bytes(L, F) of the blob and
+ *    holds gate [F][L], up [F][L], down [L][F]; each matrix is its code bytes
+ *    (rows x cols/2, element 2j in the low nibble of byte j) followed by its
+ *    scale bytes (rows x cols/32; scale s means 2^(s-127), 255 is NaN).
+ *  - rounding points: h = bf16(x W_d^T); g, u fp32; a = bf16(act(g) * u);
+ *    y fp32; z = bf16(sum_j w_j y_j); out = bf16(z W_u^T); round to nearest
+ *    even.  act = SiLU; the SiTU formula is not on the pages, so
+ *    MOE_ACT_SITU returns MOE_ERR_UNSUPPORTED.
+ *
+ * Conventions for every entry point:
+ *  - bf16 tensors are passed as raw 16-bit patterns (void* / uint16_t*),
+ *    row-major, contiguous.
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *    allocates no device memory and keeps no pointer after the enqueued work
+ *    completes.  Scratch space comes from the caller's workspace, sized by
+ *    moe_workspace_size().
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL is the default stream)
+ *    and the call returns without waiting.  Argument errors are detected
+ *    before anything is enqueued and return synchronously; a failed launch
+ *    returns MOE_ERR_DEVICE.
+ *  - num_tokens == 0 is a no-op returning MOE_OK.
+ *  - Calls on distinct workspaces are independent; the library has no global
+ *    mutable state.
+ */
+#ifndef MOE_LAYER_H
+#define MOE_LAYER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* A hipStream_t (HIP declares hipStream_t as struct ihipStream_t*). */
+typedef struct ihipStream_t* moe_stream_t;
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1,  /* NULL, bad size, misalignment, aliasing */
+  MOE_ERR_UNSUPPORTED = -2,  /* a valid but unimplemented option (e.g. MOE_ACT_SITU) */
+  MOE_ERR_WORKSPACE = -3,    /* workspace NULL or smaller than moe_workspace_size() */
+  MOE_ERR_DEVICE = -4        /* a HIP launch or runtime call failed */
+} moe_status;
+
+typedef enum { MOE_ACT_SILU = 0, MOE_ACT_SITU = 1 } moe_act;
+
+/* Route flags (moe_route only). */
+enum {
+  /* recompute every logit exactly instead of only the ones near the top-k
+   * boundary (for tests of the exact path) */
+  MOE_ROUTE_EXACT_ALL = 1
+};
+
+typedef struct {
+  int64_t num_tokens;   /* T >= 0 */
+  int32_t d_model;      /* d, multiple of 32 */
+  int32_t d_latent;     /* L, multiple of 32 */
+  int32_t d_ffn;        /* F, multiple of 32 */
+  int32_t num_experts;  /* E >= 1 */
+  int32_t act;          /* moe_act */
+  int32_t renormalize;  /* 1: softmax over the k selected logits; 0: over all E */
+  int64_t bias_row_stride; /* router bias: 0 -> one fp32 [E] row for all tokens; E -> fp32 [T][E] */
+} moe_config;
+
+/* Optional routing outputs of moe_layer_forward / inputs+outputs of the stage
+ * calls.  Every member may be NULL in moe_layer_forward. */
+typedef struct {
+  int32_t* topk_idx;       /* [T][k] expert ids, ascending within a row */
+  float* topk_w;           /* [T][k] routing weights */
+  float* logits;           /* [T][E] fp32 logits incl. bias; entries recomputed
+                              exactly near the top-k boundary are exact, the rest
+                              are within the certified error bound */
+  int32_t* expert_counts;  /* [E] rows routed to each expert */
+  int32_t* expert_offsets; /* [E+1] exclusive prefix of expert_counts */
+  int32_t* perm;           /* [T*k] row t*k+j of each routed (token, slot), grouped by
+                              expert, tokens ascending inside a group */
+} moe_routing_out;
+
+/* Bytes of one expert record: 3 * L * F weights at 0.53125 B (kimi-k3-in-c
+ * post, MXFP4 section).  0 if L or F is not a positive multiple of 32. */
+size_t moe_expert_bytes(int32_t d_latent, int32_t d_ffn);
+
+/* Human-readable name of a status. */
+const char* moe_status_string(moe_status s);
+
+/* Workspace bytes needed by moe_layer_forward and by every stage call for this
+ * config and k.  Writes *bytes; MOE_ERR_INVALID_ARG for a bad config. */
+moe_status moe_workspace_size(const moe_config* cfg, int32_t k, size_t* bytes);
+
+/*
+ * The whole layer: out[T][d] (bf16) for x[T][d] (bf16).
+ *   router_w     bf16 [E][d]
+ *   latent_down  bf16 [L][d]     (h = x W_d^T)
+ *   latent_up    bf16 [d][L]     (out = z W_u^T)
+ *   expert_blob  E records of moe_expert_bytes(L, F), 16-byte aligned
+ *   k            experts per token, 1 <= k <= min(E, 64)
+ *   router_bias  nullable fp32, shape per cfg->bias_row_stride
+ *   routing      nullable; non-NULL members receive the routing
+ * x, out and workspace must not overlap; every pointer 16-byte aligned.
+ */
+moe_status moe_layer_forward(const void* x, const void* router_w, const void* latent_down,
+                             const void* latent_up, const uint8_t* expert_blob, int32_t k,
+                             const moe_config* cfg, const float* router_bias, void* out,
+                             moe_routing_out* routing, void* workspace, size_t workspace_bytes,
+                             moe_stream_t stream);
+
+/* Stages of moe_layer_forward, in launch order. */
+typedef enum {
+  MOE_STAGE_ROUTER_DOWN = 0, /* router logits and latent down projection (one launch) */
+  MOE_STAGE_ROUTE = 1,       /* certified top-k, weights */
+  MOE_STAGE_PERMUTE = 2,     /* grouping of routed rows by expert */
+  MOE_STAGE_GATE_UP = 3,     /* MXFP4 gate/up GEMMs with the fp32 GLU */
+  MOE_STAGE_DOWN = 4,        /* MXFP4 down GEMMs */
+  MOE_STAGE_COMBINE = 5,     /* weighted combine */
+  MOE_STAGE_UP = 6,          /* latent up projection */
+  MOE_NUM_STAGES = 7
+} moe_stage;
+
+/* A hipEvent_t (HIP declares it as struct ihipEvent_t*). */
+typedef struct ihipEvent_t* moe_event_t;
+
+/* Caller-created events recorded on the stream right before (begin) and right
+ * after (end) the kernels of each stage; NULL entries are skipped. */
+typedef struct {
+  moe_event_t begin[MOE_NUM_STAGES];
+  moe_event_t end[MOE_NUM_STAGES];
+} moe_stage_events;
+
+/* moe_layer_forward with hipEventRecord calls around its stages, for timing
+ * individual kernels on the stream they run on.  Same arguments, same result. */
+moe_status moe_layer_forward_profiled(const void* x, const void* router_w, const void* latent_down,
+                                      const void* latent_up, const uint8_t* expert_blob, int32_t k,
+                                      const moe_config* cfg, const float* router_bias, void* out,
+                                      moe_routing_out* routing, void* workspace, size_t workspace_bytes,
+                                      const moe_stage_events* events, moe_stream_t stream);
+
+/* ---- stage entry points (the same kernels moe_layer_forward runs) ---- */
+
+/* Dequantise one [rows][cols] MXFP4 matrix (codes then scales as above) to
+ * fp32, bit-exact: E2M1(code) * 2^(s-127), inf past the fp32 range, NaN for
+ * s = 255.  cols multiple of 32.  No workspace. */
+moe_status moe_dequant_mxfp4(const uint8_t* codes, const uint8_t* scales, int64_t rows, int32_t cols,
+                             float* out, moe_stream_t stream);
+
+/* Router logits and exact top-k selection: fills routing->logits, topk_idx,
+ * topk_w (all three required).  flags: MOE_ROUTE_*.  Uses the workspace. */
+moe_status moe_route(const void* x, const void* router_w, const float* router_bias,
+                     const moe_config* cfg, int32_t k, int32_t flags, moe_routing_out* routing,
+                     void* workspace, size_t workspace_bytes, moe_stream_t stream);
+
+/* Selection alone on caller-given fp32 logits [T][E] (no certification: the
+ * given logits are taken as exact).  Writes idx [T][k] and w [T][k]. */
+moe_status moe_topk(const float* logits, int64_t num_tokens, int32_t num_experts, int32_t k,
+                    int32_t renormalize, int32_t* topk_idx, float* topk_w, moe_stream_t stream);
+
+/* Grouping of routed rows by expert: from idx [T][k] fill counts [E],
+ * offsets [E+1], perm [T*k] (bit-exact, deterministic).  Uses the workspace
+ * (size it with a cfg of the same T, E). */
+moe_status moe_permute(const int32_t* topk_idx, int64_t num_tokens, int32_t k, int32_t num_experts,
+                       int32_t* expert_counts, int32_t* expert_offsets, int32_t* perm,
+                       void* workspace, size_t workspace_bytes, moe_stream_t stream);
+
+/* Routed experts on latent rows: h bf16 [T][L] -> y fp32 [T*k][L] with row
+ * t*k+j the output of expert topk_idx[t][j] on h[t]; a_out (nullable) bf16
+ * [T*k][F] receives the GLU output in the same row order.  routing must hold
+ * topk_idx, expert_counts, expert_offsets and perm (from moe_permute). */
+moe_status moe_expert_ffn(const void* h, const uint8_t* expert_blob, int32_t k, const moe_config* cfg,
+                          const moe_routing_out* routing, float* y, void* a_out, void* workspace,
+                          size_t workspace_bytes, moe_stream_t stream);
+
+/* Weighted combine: z[t][l] = bf16(sum_j w[t][j] y[t*k+j][l]). */
+moe_status moe_combine(const float* y, const float* topk_w, int64_t num_tokens, int32_t k,
+                       int32_t d_latent, void* z, moe_stream_t stream);
+
+/* Dense bf16 projection: out[t][o] = bf16(sum_i in[t][i] W[o][i]), fp32
+ * accumulation (the latent down/up projections).  n_in multiple of 32. */
+moe_status moe_linear_bf16(const void* in, const void* W, int64_t num_tokens, int32_t n_in,
+                           int32_t n_out, void* out, moe_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_LAYER_H */

@@ -1,0 +1,176 @@
+// Dense bf16 GEMV for few tokens: router logits and the latent projections.
+//
+// out[t][r] = sum_i x[t][i] * W[r][i] over rows of W[rows][K] (kimi-k3-mlx digest,
+// architecture table: the router scores 896 experts from the 7168-wide token;
+// Stable LatentMoE projects 7168 -> 3584 and back with bf16 matrices).
+//
+// Memory-bound: every weight byte is read once per token group.  One wave owns one
+// row; lane l reads 16 bytes (8 bf16) at column 8*(64c + l) for chunk c, so each
+// load instruction covers 1 KiB of the row contiguously and the token values the
+// lane needs stay in registers for the whole row.  Products of bf16 pairs are exact
+// in fp32 (v_dot2_f32_bf16).
+//
+// Router rows fold each 8-element chunk partial into an fp64 accumulator.  Error
+// bound: a chunk partial is 4 dot2 steps from zero, at most 8 fp32 roundings of
+// partial sums bounded by the chunk's sum of |products| (2^-23 each, covering
+// round-toward-zero too); the fp64 folds and the 6-step wave tree add at most
+// (NCH + 6) * 2^-53 relative to the sum of |products|.  With S = sum |x_i w_i|
+// <= |x| |w|, the error of the fp64 logit is below 8.0001 * 2^-23 * |x||w|;
+// GEMV_ROUTER_GAMMA = 16 * 2^-23 leaves a factor of two for the fp32 norm sums.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+struct DenseParams {
+  const uint16_t* x;
+  int64_t T;
+  int32_t K;
+  int32_t nseg;
+  DenseSeg seg[2];
+};
+
+template <int NCH, int G>
+__global__ void __launch_bounds__(256) dense_gemv_kernel(DenseParams p) {
+  const int lane = lane_id();
+  const int wave = threadIdx.x / WAVE;
+  int64_t row = (int64_t)blockIdx.x * 4 + wave;
+  int si = 0;
+  if (row >= p.seg[0].rows) {
+    row -= p.seg[0].rows;
+    si = 1;
+    if (si >= p.nseg || row >= p.seg[1].rows) return;
+  }
+  const DenseSeg& s = p.seg[si];
+  const int32_t K = p.K;
+  const int64_t t0 = (int64_t)blockIdx.y * G;
+
+  uint4 xr[G][NCH];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      int col = 8 * (64 * c + lane);
+      if (col < K && t0 + g < p.T)
+        xr[g][c] = *reinterpret_cast<const uint4*>(p.x + (t0 + g) * K + col);
+      else
+        xr[g][c] = make_uint4(0, 0, 0, 0);
+    }
+
+  uint4 wr[NCH];
+  const uint16_t* wrow = s.W + row * K;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    int col = 8 * (64 * c + lane);
+    wr[c] = col < K ? load_nt16(wrow + col)
+                    : make_uint4(0, 0, 0, 0);
+  }
+
+  if (!s.router) {
+    float acc[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) acc[g] = 0.f;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        acc[g] = dot2(xr[g][c].x, wr[c].x, acc[g]);
+        acc[g] = dot2(xr[g][c].y, wr[c].y, acc[g]);
+        acc[g] = dot2(xr[g][c].z, wr[c].z, acc[g]);
+        acc[g] = dot2(xr[g][c].w, wr[c].w, acc[g]);
+      }
+    uint16_t* out = reinterpret_cast<uint16_t*>(s.out);
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float v = wave_sum(acc[g]);
+      if (lane == 0 && t0 + g < p.T) out[(t0 + g) * s.rows + row] = f32_to_bf16(v);
+    }
+    return;
+  }
+
+  // router row: fp32 chunk partials folded into fp64
+  double acc[G];
+  float wn = 0.f;
+#pragma unroll
+  for (int g = 0; g < G; ++g) acc[g] = 0.0;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    wn = dot2(wr[c].x, wr[c].x, wn);
+    wn = dot2(wr[c].y, wr[c].y, wn);
+    wn = dot2(wr[c].z, wr[c].z, wn);
+    wn = dot2(wr[c].w, wr[c].w, wn);
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float pc = dot2(xr[g][c].x, wr[c].x, 0.f);
+      pc = dot2(xr[g][c].y, wr[c].y, pc);
+      pc = dot2(xr[g][c].z, wr[c].z, pc);
+      pc = dot2(xr[g][c].w, wr[c].w, pc);
+      acc[g] += (double)pc;
+    }
+  }
+  float* out = reinterpret_cast<float*>(s.out);
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    double v = wave_sum(acc[g]);
+    if (lane == 0 && t0 + g < p.T) out[(t0 + g) * s.rows + row] = (float)v;
+  }
+  wn = wave_sum(wn);
+  if (lane == 0 && blockIdx.y == 0) s.wnorm2[row] = wn;
+  if (row == 0) {  // one wave per token group writes the token norms
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float xn = 0.f;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        xn = dot2(xr[g][c].x, xr[g][c].x, xn);
+        xn = dot2(xr[g][c].y, xr[g][c].y, xn);
+        xn = dot2(xr[g][c].z, xr[g][c].z, xn);
+        xn = dot2(xr[g][c].w, xr[g][c].w, xn);
+      }
+      xn = wave_sum(xn);
+      if (lane == 0 && t0 + g < p.T) s.xnorm2[t0 + g] = xn;
+    }
+  }
+}
+
+template <int NCH, int G>
+static hipError_t launch_nch_g(const DenseParams& p, hipStream_t st) {
+  int64_t rows = p.seg[0].rows + (p.nseg > 1 ? p.seg[1].rows : 0);
+  if (ceil_div(p.T, G) > 65535 || ceil_div(rows, 4) > 0x7FFFFFFF) return hipErrorInvalidValue;
+  dim3 grid((unsigned)ceil_div(rows, 4), (unsigned)ceil_div(p.T, G));
+  hipLaunchKernelGGL((dense_gemv_kernel<NCH, G>), grid, dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+template <int NCH>
+static hipError_t launch_nch(const DenseParams& p, hipStream_t st) {
+  // keep the token registers (G * NCH * 4 VGPRs) near 64
+  if (NCH <= 4 && p.T >= 4) return launch_nch_g<NCH, 4>(p, st);
+  if (NCH <= 8 && p.T >= 2) return launch_nch_g<NCH, 2>(p, st);
+  return launch_nch_g<NCH, 1>(p, st);
+}
+
+hipError_t launch_dense_gemv(const uint16_t* x, int64_t T, int32_t K, const DenseSeg* segs, int nseg,
+                             hipStream_t st) {
+  DenseParams p;
+  p.x = x;
+  p.T = T;
+  p.K = K;
+  p.nseg = nseg;
+  p.seg[0] = segs[0];
+  p.seg[1] = nseg > 1 ? segs[1] : segs[0];
+  if (T == 0) return hipSuccess;
+  int nch = (int)ceil_div(K, 512);
+  switch (nch) {
+    case 1: return launch_nch<1>(p, st);
+    case 2: return launch_nch<2>(p, st);
+    case 3: case 4: return launch_nch<4>(p, st);
+    case 5: case 6: case 7: return launch_nch<7>(p, st);
+    case 8: return launch_nch<8>(p, st);
+    case 9: case 10: case 11: case 12: case 13: case 14: return launch_nch<14>(p, st);
+    case 15: case 16: return launch_nch<16>(p, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace moe

@@ -1,0 +1,112 @@
+"""The C-ABI library loads, exports every entry point the header declares, and rejects
+bad arguments before touching a device (so this runs without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mxfp4_expert_gemm_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_layer.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(moe.LIB_PATH), reason="libmoe_layer.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 11
+    lib = moe.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(moe.EXPORTS) == names
+
+
+def test_expert_bytes_and_status_strings():
+    assert moe.expert_bytes(3584, 3072) == 17_547_264
+    assert moe.expert_bytes(128, 128) == 26_112
+    assert moe.expert_bytes(100, 128) == 0
+    for s, name in moe.STATUS.items():
+        assert moe.lib().moe_status_string(s).decode() == name
+
+
+FAKE = 0x7F0000000000  # a 16-byte aligned address; never dereferenced on these paths
+
+
+def k3(T=1, **kw):
+    c = dict(num_tokens=T, d_model=7168, d_latent=3584, d_ffn=3072, num_experts=896)
+    c.update(kw)
+    return moe.MoEConfig(c["num_tokens"], c["d_model"], c["d_latent"], c["d_ffn"], c["num_experts"],
+                         kw.get("act", 0), kw.get("renormalize", 1), kw.get("bias_row_stride", 0))
+
+
+def ws_status(cfg, k):
+    n = ctypes.c_size_t(0)
+    return moe.lib().moe_workspace_size(ctypes.byref(cfg), k, ctypes.byref(n)), n.value
+
+
+def test_workspace_size_valid_and_invalid():
+    st, n = ws_status(k3(T=4096), 16)
+    assert st == 0 and n > 4096 * 16 * 3072 * 2
+    assert ws_status(k3(), 0)[0] == -1            # k < 1
+    assert ws_status(k3(), 65)[0] == -1           # k > 64
+    assert ws_status(k3(num_experts=8), 9)[0] == -1  # k > E
+    assert ws_status(k3(d_latent=100), 16)[0] == -1  # not a multiple of 32
+    assert ws_status(k3(d_latent=3616), 16)[0] == -2  # multiple of 32, not of 128: unsupported here
+    assert ws_status(k3(act=1), 16)[0] == -2      # SiTU not defined on the pages
+    assert ws_status(k3(act=7), 16)[0] == -1
+    assert ws_status(k3(renormalize=2), 16)[0] == -1
+    assert ws_status(k3(bias_row_stride=5), 16)[0] == -1
+    assert ws_status(k3(num_experts=2048), 16)[0] == -2
+    assert ws_status(k3(T=-1), 16)[0] == -1
+    assert moe.lib().moe_workspace_size(None, 16, ctypes.byref(ctypes.c_size_t())) == -1
+
+
+def fwd(cfg, k=16, x=FAKE, out=FAKE + (1 << 30), ws=FAKE + (2 << 30), ws_bytes=1 << 40, **ptrs):
+    p = dict(router_w=FAKE + (3 << 30), latent_down=FAKE + (4 << 30), latent_up=FAKE + (5 << 30),
+             blob=FAKE + (6 << 30), bias=None)
+    p.update(ptrs)
+    return moe.lib().moe_layer_forward(x, p["router_w"], p["latent_down"], p["latent_up"], p["blob"], k,
+                                       ctypes.byref(cfg), p["bias"], out, None, ws, ws_bytes, None)
+
+
+def test_forward_argument_errors_return_before_any_launch():
+    assert fwd(k3(T=0)) == 0                                  # T = 0 is a no-op
+    assert fwd(k3(), x=None) == -1
+    assert fwd(k3(), out=None) == -1
+    assert fwd(k3(), blob=None) == -1
+    assert fwd(k3(), x=FAKE + 8) == -1                         # misaligned
+    assert fwd(k3(), out=FAKE) == -1                           # out aliases x
+    assert fwd(k3(), k=0) == -1
+    assert fwd(k3(act=1)) == -2
+    assert fwd(k3(), ws=None) == -3
+    assert fwd(k3(), ws_bytes=1024) == -3
+    assert fwd(k3(), ws=FAKE + (2 << 30) + 8) == -1            # misaligned workspace
+    assert fwd(k3(), bias=FAKE + 2) == -1                      # misaligned bias
+
+
+def test_stage_argument_errors():
+    L = moe.lib()
+    assert L.moe_dequant_mxfp4(None, FAKE, 4, 64, FAKE, None) == -1
+    assert L.moe_dequant_mxfp4(FAKE, FAKE, 4, 48, FAKE, None) == -1
+    assert L.moe_dequant_mxfp4(FAKE, FAKE, 0, 64, FAKE, None) == 0  # empty launch
+    assert L.moe_topk(FAKE, 4, 8, 9, 1, FAKE, FAKE, None) == -1
+    assert L.moe_topk(FAKE, 0, 8, 2, 1, FAKE, FAKE, None) == 0
+    assert L.moe_topk(FAKE, 4, 2048, 2, 1, FAKE, FAKE, None) == -2
+    assert L.moe_permute(FAKE, 4, 2, 8, FAKE, FAKE, FAKE, None, 0, None) == -3
+    assert L.moe_permute(FAKE, 0, 2, 8, FAKE, FAKE, FAKE, None, 0, None) == 0
+    assert L.moe_combine(FAKE, FAKE, 4, 2, 100, FAKE, None) == -1
+    assert L.moe_linear_bf16(FAKE, FAKE, 4, 100, 8, FAKE, None) == -1
+    assert L.moe_linear_bf16(FAKE, FAKE, 0, 64, 8, FAKE, None) == 0
+    r = moe.RoutingOut(None, None, None, None, None, None)
+    assert L.moe_route(FAKE, FAKE, None, ctypes.byref(k3()), 16, 0, ctypes.byref(r), FAKE, 1 << 40, None) == -1
+    r = moe.RoutingOut(FAKE, FAKE, FAKE, None, None, None)
+    assert L.moe_route(FAKE, FAKE, None, ctypes.byref(k3()), 16, 8, ctypes.byref(r), FAKE, 1 << 40, None) == -1
+    assert L.moe_expert_ffn(FAKE, FAKE, 16, ctypes.byref(k3()), None, FAKE, None, FAKE, 1 << 40, None) == -1

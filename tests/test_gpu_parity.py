@@ -1,0 +1,271 @@
+"""Parity of the HIP library (through its C ABI) with the CPU oracle.
+
+Bit-exact: MXFP4 dequantisation, top-k selection on shared logits, the exact
+routing of every token, and the permutation.  Floating-point layer outputs:
+relative L2 error <= 2e-3 (fp32 accumulation, bf16 in/out).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import mxfp4_expert_gemm_amd as moe
+import oracle
+import synth
+from _util import bf16_bits_to_f64, f64_to_bf16_bits, rel_l2
+from gpu_common import dev_weights, from_dev, host_layer, log, to_dev
+
+pytestmark = pytest.mark.gpu
+
+TOL_OUT = 2e-3
+
+
+def _same_f32(a, b):
+    a = np.asarray(a, np.float32)
+    b = np.asarray(b, np.float32)
+    return ((a.view(np.uint32) == b.view(np.uint32)) | (np.isnan(a) & np.isnan(b))).all()
+
+
+# ----------------------------------------------------------------- dequant
+
+def test_dequant_every_code_and_scale():
+    """256 rows, one per e8m0 value; each row holds every byte value once (all 16x16 code pairs)."""
+    codes = np.tile(np.arange(256, dtype=np.uint8), 256)
+    scales = np.repeat(np.arange(256, dtype=np.uint8), 16)
+    got = from_dev(moe.dequant_mxfp4(to_dev(codes), to_dev(scales), 256, 512))
+    want = oracle.dequant_matrix(codes, scales, 256, 512)
+    assert _same_f32(got, want)
+
+
+def test_dequant_k3_records_bit_exact():
+    h = host_layer("decode1")
+    blob = h["blob"]
+    dblob = dev_weights("decode1")["blob"]
+    L, F = 3584, 3072
+    rec = synth.expert_record_bytes(L, F)
+    nc, mat = F * L // 2, F * L // 2 + F * L // 32
+    for e in (0, 447, 895):
+        for m, (rows, cols) in enumerate([(F, L), (F, L), (L, F)]):
+            base = e * rec + m * mat
+            got = from_dev(moe.dequant_mxfp4(dblob[base:base + nc], dblob[base + nc:base + mat], rows, cols))
+            want = oracle.dequant_matrix(blob[base:base + nc], blob[base + nc:base + mat], rows, cols)
+            assert _same_f32(got, want), (e, m)
+
+
+# ------------------------------------------------------------------- top-k
+
+@pytest.mark.parametrize("E,k", [(8, 1), (8, 2), (8, 8), (100, 7), (896, 16), (1024, 64)])
+def test_topk_on_shared_logits_bit_exact(E, k):
+    rng = np.random.default_rng(E * 100 + k)
+    T = 300
+    pool = np.array([-1.0, 0.0, -0.0, 1.0, 2.0, np.nan, -np.inf, np.inf, 0.5], dtype=np.float32)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    logits[: T // 2] = pool[rng.integers(0, pool.size, (T // 2, E))]
+    idx, w = moe.topk(to_dev(logits), k)
+    want_idx, want_w = oracle.select(logits, k)
+    assert np.array_equal(from_dev(idx), want_idx)
+    gw = from_dev(w)
+    fin = np.isfinite(want_w)
+    assert np.allclose(gw[fin], want_w[fin], rtol=2e-6, atol=1e-7)
+
+
+# ----------------------------------------------------------------- routing
+
+def test_route_tiny_every_logit_exact():
+    h = host_layer("tiny")
+    dw = dev_weights("tiny")
+    c = h["cfg"]
+    logits, idx, w = moe.route(to_dev(h["x"]), dw["router_w"], c.k, flags=moe.ROUTE_EXACT_ALL)
+    want = oracle.router_logits(h["x"], h["router_w"])
+    assert _same_f32(from_dev(logits), want)
+    want_idx, want_w = oracle.select(want, c.k)
+    assert np.array_equal(from_dev(idx), want_idx)
+    assert np.allclose(from_dev(w), want_w, rtol=2e-6, atol=0)
+
+
+def _bf(v):
+    return int(np.array([v], np.float32).view(np.uint32)[0] >> 16)
+
+
+def test_route_exact_path_decides_midpoints():
+    """Rows whose exact logits sit on or next to an fp32 rounding midpoint: only the
+    fixed-point accumulator can round them; the oracle's exact dot must agree."""
+    d, E = 64, 8
+    x = np.zeros((4, d), np.uint16)
+    W = np.zeros((E, d), np.uint16)
+    one, tiny, far = _bf(1.0), _bf(2.0 ** -12), _bf(2.0 ** -60)
+    x[:, 0], x[:, 1] = one, tiny
+    x[1, 2] = far
+    x[2, 2] = _bf(-(2.0 ** -60))
+    x[3, 3] = _bf(3.0)
+    for e in range(E):
+        W[e, 0], W[e, 1] = one, tiny
+        W[e, 2] = far
+        W[e, 3] = _bf(2.0 ** (-70 - e))
+    logits, idx, w = moe.route(to_dev(x), to_dev(W), 3, flags=moe.ROUTE_EXACT_ALL)
+    want = oracle.router_logits(x, W)
+    assert _same_f32(from_dev(logits), want)
+    assert np.array_equal(from_dev(idx), oracle.select(want, 3)[0])
+
+
+@pytest.mark.parametrize("name,T", [("tiny", None), ("decode1", None), ("decode64", None), ("prefill4k", 256),
+                                    ("prefill32k", 256)])
+def test_route_indices_bit_exact(name, T):
+    h = host_layer(name, T)
+    c = h["cfg"]
+    dw = dev_weights(name)
+    bias = None if h["bias"] is None else to_dev(h["bias"])
+    log(f"route {name} T={h['x'].shape[0]}")
+    logits, idx, w = moe.route(to_dev(h["x"]), dw["router_w"], c.k, bias=bias)
+    want_l = oracle.router_logits(h["x"], h["router_w"], h["bias"])
+    want_idx, want_w = oracle.select(want_l, c.k)
+    assert np.array_equal(from_dev(idx), want_idx)
+    gl = from_dev(logits).astype(np.float64)
+    dev_max = np.max(np.abs(gl - want_l))
+    log(f"  max |logit - exact| = {dev_max:.3g}")
+    assert dev_max < 1e-3
+    assert np.allclose(from_dev(w), want_w, rtol=1e-4, atol=1e-6)
+
+
+# ------------------------------------------------------------- permutation
+
+@pytest.mark.parametrize("T,k,E", [(1, 16, 896), (16, 2, 8), (64, 16, 896), (3, 5, 100), (4096, 16, 896),
+                                   (32768, 16, 896)])
+def test_permute_bit_exact(T, k, E):
+    rng = np.random.default_rng(T + k + E)
+    p = rng.random(E) ** 3
+    p /= p.sum()
+    idx = np.stack([np.sort(rng.choice(E, k, replace=False, p=p)) for _ in range(T)]).astype(np.int32)
+    counts, offsets, perm = moe.permute(to_dev(idx), E)
+    wc, wo, wp = oracle.permute(idx, E)
+    assert np.array_equal(from_dev(counts), wc)
+    assert np.array_equal(from_dev(offsets), wo)
+    assert np.array_equal(from_dev(perm), wp)
+
+
+# --------------------------------------------------------- dense + experts
+
+@pytest.mark.parametrize("T,n_in,n_out", [(1, 7168, 3584), (3, 3584, 7168), (16, 256, 128), (5, 128, 96)])
+def test_linear_bf16(T, n_in, n_out):
+    a = synth.normal_bf16(5, 1, 1.0, (T, n_in))
+    W = synth.normal_bf16(5, 2, 0.02, (n_out, n_in))
+    got = from_dev(moe.linear_bf16(to_dev(a), to_dev(W)))
+    want = oracle.linear_bf16(a, W)
+    assert rel_l2(bf16_bits_to_f64(got), bf16_bits_to_f64(want)) < 1e-4
+    assert np.mean(got == want) > 0.99
+
+
+@pytest.mark.parametrize("name,T", [("tiny", None), ("decode1", None), ("decode64", 8)])
+def test_expert_ffn(name, T):
+    h = host_layer(name, T)
+    c = h["cfg"]
+    dw = dev_weights(name)
+    Tn = h["x"].shape[0]
+    hl = oracle.linear_bf16(h["x"], h["latent_down"])
+    lg = oracle.router_logits(h["x"], h["router_w"], h["bias"])
+    idx, w = oracle.select(lg, c.k)
+    y, a = moe.expert_ffn(to_dev(hl), dw["blob"], to_dev(idx), d_model=c.d, d_ffn=c.F, num_experts=c.E,
+                          want_a=True)
+    y, a = from_dev(y), from_dev(a)
+    rec = c.record_bytes
+    for t in range(Tn):
+        for j in range(c.k):
+            e = int(idx[t, j])
+            wa, wy = oracle.expert(hl[t], h["blob"][e * rec:(e + 1) * rec], c.L, c.F)
+            r = t * c.k + j
+            assert rel_l2(y[r], wy) < 1e-4, (t, j, rel_l2(y[r], wy))
+            assert np.mean(a[r] == wa) > 0.98
+
+
+def test_combine():
+    rng = np.random.default_rng(1)
+    T, k, L = 33, 16, 3584
+    y = rng.standard_normal((T * k, L)).astype(np.float32) * 1e3
+    _, w = oracle.select(rng.standard_normal((T, 896)).astype(np.float32), k)
+    got = from_dev(moe.combine(to_dev(y), to_dev(w), dtype=torch.int16))
+    want = oracle.combine(y, w)
+    # fp32 accumulation of k terms vs fp64: per element the difference stays within one bf16
+    # rounding of the result plus k fp32 roundings of partial sums bounded by sum_j |w_j y_j|
+    g, r = bf16_bits_to_f64(got), bf16_bits_to_f64(want)
+    mag = np.einsum("tj,tjl->tl", np.abs(w).astype(np.float64), np.abs(y.reshape(T, k, L)).astype(np.float64))
+    # |RN(a) - RN(b)| <= |a - b| + one ulp (each rounding moves by at most half an ulp <= 2^-8 |value|)
+    assert (np.abs(g - r) <= 2.0 ** -7 * np.maximum(np.abs(g), np.abs(r)) + k * 2.0 ** -23 * mag).all()
+    assert np.mean(got == want) > 0.999
+
+
+# ------------------------------------------------------------- whole layer
+
+def _layer_case(name, T=None, sample=None):
+    h = host_layer(name, T)
+    c = h["cfg"]
+    dw = dev_weights(name)
+    Tn = h["x"].shape[0]
+    x = to_dev(h["x"])
+    bias = None if h["bias"] is None else to_dev(h["bias"])
+    routing = dict(topk_idx=torch.empty((Tn, c.k), dtype=torch.int32, device="cuda"),
+                   topk_w=torch.empty((Tn, c.k), dtype=torch.float32, device="cuda"),
+                   logits=torch.empty((Tn, c.E), dtype=torch.float32, device="cuda"),
+                   expert_counts=torch.empty(c.E, dtype=torch.int32, device="cuda"),
+                   expert_offsets=torch.empty(c.E + 1, dtype=torch.int32, device="cuda"),
+                   perm=torch.empty(Tn * c.k, dtype=torch.int32, device="cuda"))
+    log(f"layer {name} T={Tn}")
+    out = moe.layer_forward(x, dw["router_w"], dw["latent_down"], dw["latent_up"], dw["blob"], c.k, d_ffn=c.F,
+                            bias=bias, routing=routing)
+    torch.cuda.synchronize()
+    out = from_dev(out)
+    gidx = from_dev(routing["topk_idx"])
+    tokens = list(range(Tn)) if sample is None else sorted(set(sample))
+    ref = oracle.layer_forward(h["x"], h["router_w"], h["latent_down"], h["latent_up"], h["blob"], c.k, c.L, c.F,
+                               bias=h["bias"], tokens=tokens)
+    assert np.array_equal(gidx[tokens], ref["idx"])
+    err = rel_l2(bf16_bits_to_f64(out[tokens]), bf16_bits_to_f64(ref["out"]))
+    log(f"  rel-L2 = {err:.3g}")
+    assert err <= TOL_OUT
+    # the permutation of the GPU's own routing equals the oracle's grouping of it
+    wc, wo, wp = oracle.permute(gidx, c.E)
+    assert np.array_equal(from_dev(routing["expert_counts"]), wc)
+    assert np.array_equal(from_dev(routing["expert_offsets"]), wo)
+    assert np.array_equal(from_dev(routing["perm"]), wp)
+    assert (wc.sum() == Tn * c.k) and all(len(set(r)) == c.k for r in gidx.tolist())
+    return out
+
+
+def test_layer_tiny():
+    _layer_case("tiny")
+
+
+def test_layer_decode1():
+    _layer_case("decode1")
+
+
+def test_layer_decode64_sampled():
+    _layer_case("decode64", sample=[0, 17, 33, 63])
+
+
+def test_layer_deterministic():
+    a = _layer_case("tiny")
+    b = _layer_case("tiny")
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("T,d,L,F,E,k", [(3, 256, 128, 256, 100, 5), (1, 128, 128, 128, 8, 8), (7, 64, 256, 128, 2, 1)])
+def test_layer_ragged_shapes(T, d, L, F, E, k):
+    s = 0x5EED + T
+    x = synth.normal_bf16(s, 1, 1.0, (T, d))
+    Wr = synth.normal_bf16(s, 2, 0.02, (E, d))
+    Wd = synth.normal_bf16(s, 3, 0.02, (L, d))
+    Wu = synth.normal_bf16(s, 4, 0.02, (d, L))
+    blob = synth.expert_blob(s, L, F, E)
+    out = moe.layer_forward(to_dev(x), to_dev(Wr), to_dev(Wd), to_dev(Wu), to_dev(blob), k, d_ffn=F)
+    ref = oracle.layer_forward(x, Wr, Wd, Wu, blob, k, L, F)
+    assert rel_l2(bf16_bits_to_f64(from_dev(out)), bf16_bits_to_f64(ref["out"])) <= TOL_OUT
+
+
+def test_layer_zero_tokens_is_a_noop():
+    dw = dev_weights("tiny")
+    c = synth.CONFIGS["tiny"]
+    x = torch.empty((0, c.d), dtype=torch.int16, device="cuda")
+    out = moe.layer_forward(x, dw["router_w"], dw["latent_down"], dw["latent_up"], dw["blob"], c.k, d_ffn=c.F,
+                            workspace=torch.empty(256, dtype=torch.uint8, device="cuda"))
+    assert out.shape == (0, c.d)
