@@ -73,6 +73,8 @@ def main():
     ap.add_argument("--dense-copies", type=int, default=3)
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0, help="0 skips the oracle baseline")
     ap.add_argument("--breakdown", action="store_true", help="also time every stage (extra untimed pass)")
+    ap.add_argument("--layout", default="packed", choices=["packed", "record"],
+                    help="expert weights as packed once by moe_pack_experts (default) or as checkpoint records")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -99,6 +101,11 @@ def main():
     log(f"[bench] config {c.name}: T={c.T} d={c.d} L={c.L} F={c.F} E={c.E} k={c.k}; generating inputs")
     blob_host = synth.make_blob(c)
     blob = up(blob_host)
+    packed = args.layout == "packed"
+    if packed:  # a one-time reordering at load, outside the timed region
+        blob = moe.pack_experts(blob, c.E, c.L, c.F)
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
     copies = [dict(router_w=up(dense["router_w"]), latent_down=up(dense["latent_down"]),
                    latent_up=up(dense["latent_up"])) for _ in range(max(1, args.dense_copies))]
     x_host = synth.make_tokens(c, T=c.T * nbatch).reshape(nbatch, c.T, c.d)
@@ -107,7 +114,7 @@ def main():
     bias = None if bias_host is None else up(bias_host)
     log(f"[bench] inputs resident in HBM ({time.time() - t0:.1f}s)")
 
-    cfg = moe.make_config(c.T, c.d, c.L, c.F, c.E, bias=bias)
+    cfg = moe.make_config(c.T, c.d, c.L, c.F, c.E, bias=bias, packed=packed)
     ws = moe.alloc_workspace(cfg, c.k, dev)
     out = torch.empty((c.T, c.d), dtype=torch.int16, device=dev)
     counts = torch.zeros((nbatch, c.E), dtype=torch.int32, device=dev)
@@ -121,10 +128,11 @@ def main():
         routing = {"expert_counts": counts[i]}
         if events is None:
             moe.layer_forward(xs[i], cp["router_w"], cp["latent_down"], cp["latent_up"], blob, c.k, d_ffn=c.F,
-                              bias=bias, out=out, workspace=ws, routing=routing)
+                              bias=bias, out=out, workspace=ws, routing=routing, packed=packed)
         else:
             moe.layer_forward_profiled(xs[i], cp["router_w"], cp["latent_down"], cp["latent_up"], blob, c.k,
-                                       events, d_ffn=c.F, bias=bias, out=out, workspace=ws, routing=routing)
+                                       events, d_ffn=c.F, bias=bias, out=out, workspace=ws, routing=routing,
+                                       packed=packed)
 
     def dom_events(i):
         ev = moe.StageEvents()
@@ -151,7 +159,8 @@ def main():
     # algorithmic bytes of the dominant kernel per launch: gate and up codes+scales of every
     # active expert, the latent rows it reads and the GLU rows it writes
     cnt = counts.cpu().numpy()[W:W + K]
-    mat_bytes = c.F * c.L // 2 + c.F * c.L // 32
+    # bytes of one gate (or up) matrix in the layout streamed (the same for the K3 shapes)
+    mat_bytes = (moe.packed_expert_bytes(c.L, c.F) if packed else moe.expert_bytes(c.L, c.F)) // 3
     active = (cnt > 0).sum(1)
     dom_bytes = active * 2 * mat_bytes + c.T * c.L * 2 + c.T * c.k * c.F * 2
     dom_gbs = float(np.mean(dom_bytes / (np.array(dom_ms) * 1e-3)) / 1e9)
@@ -214,7 +223,8 @@ def main():
         "config": {"workload": f"{c.name}: {c.description}", "tokens": c.T, "d_model": c.d, "d_latent": c.L,
                    "d_ffn": c.F, "experts": c.E, "top_k": c.k, "expert_weights": "mxfp4 (e2m1 + e8m0 per 32)",
                    "activations": "bf16, fp32 accumulation, fp32 GLU", "parallelism": "single GPU",
-                   "dense_weight_copies": len(copies), "mean_active_experts": float(np.mean(active))},
+                   "dense_weight_copies": len(copies), "mean_active_experts": float(np.mean(active)),
+                   "expert_layout": "packed by moe_pack_experts at load" if packed else "checkpoint records"},
         "roofline": {"bound": "hbm", "kernel": "gate_up (MXFP4 gate/up GEMV + fp32 GLU)",
                      "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": None,

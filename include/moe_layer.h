@@ -73,6 +73,21 @@ typedef enum {
 
 typedef enum { MOE_ACT_SILU = 0, MOE_ACT_SITU = 1 } moe_act;
 
+/* Expert weight layouts (moe_config.expert_layout).
+ *  MOE_LAYOUT_RECORD: E records of moe_expert_bytes(L, F) in the checkpoint order of
+ *    the kimi-k3-in-c post, MXFP4 section: gate [F][L], up [F][L], down [L][F], each
+ *    matrix its E2M1 codes row-major (two per byte, low nibble first) followed by its
+ *    e8m0 scales row-major (one per 32 consecutive weights of a row).
+ *  MOE_LAYOUT_PACKED: the same codes and scales, reordered by moe_pack_experts so that
+ *    the kernels stream every load as one contiguous run: E records of
+ *    moe_packed_expert_bytes(L, F); in a record gate, up, down; a matrix of R rows and
+ *    K columns is R/16 groups of 16 rows, a group K/128 code tiles of 1024 bytes (tile
+ *    s, bytes 16l..16l+15: row l%16 of the group, its weights 128s+32(l/16) ..
+ *    128s+32(l/16)+31) then ceil(K/512) scale tiles of 256 bytes (tile c, byte 4l+j:
+ *    the scale of those 32 weights for s = 4c+j, 127 where s >= K/128).  Same size as
+ *    the record when L and F are multiples of 512. */
+typedef enum { MOE_LAYOUT_RECORD = 0, MOE_LAYOUT_PACKED = 1 } moe_expert_layout;
+
 /* Route flags (moe_route only). */
 enum {
   /* recompute every logit exactly instead of only the ones near the top-k
@@ -82,13 +97,14 @@ enum {
 
 typedef struct {
   int64_t num_tokens;   /* T >= 0 */
-  int32_t d_model;      /* d, multiple of 32 */
-  int32_t d_latent;     /* L, multiple of 32 */
-  int32_t d_ffn;        /* F, multiple of 32 */
-  int32_t num_experts;  /* E >= 1 */
+  int32_t d_model;      /* d, multiple of 32, at most 8192 */
+  int32_t d_latent;     /* L, multiple of 32; the layer call needs a multiple of 128, at most 7168 */
+  int32_t d_ffn;        /* F, likewise */
+  int32_t num_experts;  /* E >= 1, at most 1024 */
   int32_t act;          /* moe_act */
   int32_t renormalize;  /* 1: softmax over the k selected logits; 0: over all E */
   int64_t bias_row_stride; /* router bias: 0 -> one fp32 [E] row for all tokens; E -> fp32 [T][E] */
+  int32_t expert_layout;   /* moe_expert_layout of expert_blob */
 } moe_config;
 
 /* Optional routing outputs of moe_layer_forward / inputs+outputs of the stage
@@ -109,6 +125,17 @@ typedef struct {
  * post, MXFP4 section).  0 if L or F is not a positive multiple of 32. */
 size_t moe_expert_bytes(int32_t d_latent, int32_t d_ffn);
 
+/* Bytes of one expert in MOE_LAYOUT_PACKED; 0 if L or F is not a positive
+ * multiple of 128. */
+size_t moe_packed_expert_bytes(int32_t d_latent, int32_t d_ffn);
+
+/* Reorders num_experts checkpoint records (MOE_LAYOUT_RECORD, 16-byte aligned) into
+ * MOE_LAYOUT_PACKED at packed (num_experts * moe_packed_expert_bytes, 16-byte
+ * aligned, not overlapping blob).  A pure byte permutation, run once when the
+ * weights are loaded.  L and F multiples of 128. */
+moe_status moe_pack_experts(const uint8_t* blob, int32_t num_experts, int32_t d_latent, int32_t d_ffn,
+                            uint8_t* packed, moe_stream_t stream);
+
 /* Human-readable name of a status. */
 const char* moe_status_string(moe_status s);
 
@@ -121,7 +148,7 @@ moe_status moe_workspace_size(const moe_config* cfg, int32_t k, size_t* bytes);
  *   router_w     bf16 [E][d]
  *   latent_down  bf16 [L][d]     (h = x W_d^T)
  *   latent_up    bf16 [d][L]     (out = z W_u^T)
- *   expert_blob  E records of moe_expert_bytes(L, F), 16-byte aligned
+ *   expert_blob  E experts in cfg->expert_layout, 16-byte aligned
  *   k            experts per token, 1 <= k <= min(E, 64)
  *   router_bias  nullable fp32, shape per cfg->bias_row_stride
  *   routing      nullable; non-NULL members receive the routing

@@ -21,9 +21,11 @@ LIB_PATH = os.path.join(_HERE, "libmoe_layer.so")
 
 ACT_SILU, ACT_SITU = 0, 1
 ROUTE_EXACT_ALL = 1
+LAYOUT_RECORD, LAYOUT_PACKED = 0, 1
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED", -3: "MOE_ERR_WORKSPACE",
           -4: "MOE_ERR_DEVICE"}
-EXPORTS = ["moe_expert_bytes", "moe_status_string", "moe_workspace_size", "moe_layer_forward",
+EXPORTS = ["moe_expert_bytes", "moe_packed_expert_bytes", "moe_pack_experts", "moe_status_string",
+           "moe_workspace_size", "moe_layer_forward",
            "moe_layer_forward_profiled",
            "moe_dequant_mxfp4", "moe_route", "moe_topk", "moe_permute", "moe_expert_ffn", "moe_combine",
            "moe_linear_bf16"]
@@ -38,7 +40,8 @@ class MoEError(RuntimeError):
 class MoEConfig(ctypes.Structure):
     _fields_ = [("num_tokens", ctypes.c_int64), ("d_model", ctypes.c_int32), ("d_latent", ctypes.c_int32),
                 ("d_ffn", ctypes.c_int32), ("num_experts", ctypes.c_int32), ("act", ctypes.c_int32),
-                ("renormalize", ctypes.c_int32), ("bias_row_stride", ctypes.c_int64)]
+                ("renormalize", ctypes.c_int32), ("bias_row_stride", ctypes.c_int64),
+                ("expert_layout", ctypes.c_int32)]
 
 
 NUM_STAGES = 7
@@ -68,6 +71,8 @@ def lib():
         cfgp, rp = ctypes.POINTER(MoEConfig), ctypes.POINTER(RoutingOut)
         sig = {
             "moe_expert_bytes": (sz, [i32, i32]),
+            "moe_packed_expert_bytes": (sz, [i32, i32]),
+            "moe_pack_experts": (ctypes.c_int, [vp, i32, i32, i32, vp, vp]),
             "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
             "moe_workspace_size": (ctypes.c_int, [cfgp, i32, ctypes.POINTER(sz)]),
             "moe_layer_forward": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, cfgp, vp, vp, rp, vp, sz, vp]),
@@ -110,13 +115,28 @@ def _stream(stream=None):
 
 
 def make_config(num_tokens: int, d_model: int, d_latent: int, d_ffn: int, num_experts: int, *,
-                act: int = ACT_SILU, renormalize: bool = True, bias: Optional[torch.Tensor] = None) -> MoEConfig:
+                act: int = ACT_SILU, renormalize: bool = True, bias: Optional[torch.Tensor] = None,
+                packed: bool = False) -> MoEConfig:
     stride = 0 if bias is None or bias.dim() == 1 else num_experts
-    return MoEConfig(num_tokens, d_model, d_latent, d_ffn, num_experts, act, int(renormalize), stride)
+    return MoEConfig(num_tokens, d_model, d_latent, d_ffn, num_experts, act, int(renormalize), stride,
+                     LAYOUT_PACKED if packed else LAYOUT_RECORD)
 
 
 def expert_bytes(d_latent: int, d_ffn: int) -> int:
     return int(lib().moe_expert_bytes(d_latent, d_ffn))
+
+
+def packed_expert_bytes(d_latent: int, d_ffn: int) -> int:
+    return int(lib().moe_packed_expert_bytes(d_latent, d_ffn))
+
+
+def pack_experts(blob: torch.Tensor, num_experts: int, d_latent: int, d_ffn: int,
+                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The experts of a checkpoint blob in the packed layout (see moe_pack_experts)."""
+    if out is None:
+        out = torch.empty(num_experts * packed_expert_bytes(d_latent, d_ffn), dtype=torch.uint8, device=blob.device)
+    _check(lib().moe_pack_experts(_p(blob), num_experts, d_latent, d_ffn, _p(out), _stream()), "moe_pack_experts")
+    return out
 
 
 def workspace_size(cfg: MoEConfig, k: int) -> int:
@@ -139,12 +159,12 @@ def _routing(r: Optional[dict]) -> Optional[RoutingOut]:
 def layer_forward(x, router_w, latent_down, latent_up, expert_blob, k: int, *, d_ffn: int,
                   bias: Optional[torch.Tensor] = None, renormalize: bool = True, act: int = ACT_SILU,
                   out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                  routing: Optional[dict] = None, stream=None) -> torch.Tensor:
+                  routing: Optional[dict] = None, stream=None, packed: bool = False) -> torch.Tensor:
     """out = layer(x); routing (dict of preallocated tensors) receives the routing if given."""
     T, d = x.shape
     E = router_w.shape[0]
     L = latent_down.shape[0]
-    cfg = make_config(T, d, L, d_ffn, E, act=act, renormalize=renormalize, bias=bias)
+    cfg = make_config(T, d, L, d_ffn, E, act=act, renormalize=renormalize, bias=bias, packed=packed)
     if out is None:
         out = torch.empty((T, d), dtype=x.dtype, device=x.device)
     if workspace is None:
@@ -159,10 +179,11 @@ def layer_forward(x, router_w, latent_down, latent_up, expert_blob, k: int, *, d
 def layer_forward_profiled(x, router_w, latent_down, latent_up, expert_blob, k: int, events: "StageEvents", *,
                            d_ffn: int, bias: Optional[torch.Tensor] = None, renormalize: bool = True,
                            out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                           routing: Optional[dict] = None, stream=None) -> torch.Tensor:
+                           routing: Optional[dict] = None, stream=None, packed: bool = False) -> torch.Tensor:
     """layer_forward that records the caller's HIP events around each stage (see StageEvents)."""
     T, d = x.shape
-    cfg = make_config(T, d, latent_down.shape[0], d_ffn, router_w.shape[0], renormalize=renormalize, bias=bias)
+    cfg = make_config(T, d, latent_down.shape[0], d_ffn, router_w.shape[0], renormalize=renormalize, bias=bias,
+                      packed=packed)
     if out is None:
         out = torch.empty((T, d), dtype=x.dtype, device=x.device)
     if workspace is None:
@@ -213,19 +234,21 @@ def permute(idx: torch.Tensor, num_experts: int):
     counts = torch.empty(num_experts, dtype=torch.int32, device=idx.device)
     offsets = torch.empty(num_experts + 1, dtype=torch.int32, device=idx.device)
     perm = torch.empty(T * k, dtype=torch.int32, device=idx.device)
-    ws = torch.empty(((T * k + 2047) // 2048) * num_experts * 4 + num_experts * 4 + 1024, dtype=torch.uint8,
-                     device=idx.device)
+    align = lambda n: (n + 255) // 256 * 256
+    ws = torch.empty(align(((T * k + 2047) // 2048) * num_experts * 4) + align(num_experts * 4) +
+                     align(num_experts * 16) + 256,
+                     dtype=torch.uint8, device=idx.device)
     _check(lib().moe_permute(_p(idx), T, k, num_experts, _p(counts), _p(offsets), _p(perm), _p(ws), ws.numel(),
                              _stream()), "moe_permute")
     return counts, offsets, perm
 
 
 def expert_ffn(h: torch.Tensor, expert_blob: torch.Tensor, idx: torch.Tensor, *, d_model: int, d_ffn: int,
-               num_experts: int, want_a: bool = False, workspace=None):
+               num_experts: int, want_a: bool = False, workspace=None, packed: bool = False):
     """Routed experts on latent rows h [T, L]: returns y fp32 [T*k, L] (and a bf16 [T*k, F])."""
     T, L = h.shape
     k = idx.shape[1]
-    cfg = make_config(T, d_model, L, d_ffn, num_experts)
+    cfg = make_config(T, d_model, L, d_ffn, num_experts, packed=packed)
     y = torch.empty((T * k, L), dtype=torch.float32, device=h.device)
     a = torch.empty((T * k, d_ffn), dtype=h.dtype, device=h.device) if want_a else None
     if workspace is None:
@@ -252,6 +275,7 @@ def linear_bf16(inp: torch.Tensor, W: torch.Tensor) -> torch.Tensor:
     return out
 
 
-__all__ = ["lib", "MoEConfig", "RoutingOut", "MoEError", "make_config", "expert_bytes", "workspace_size",
+__all__ = ["lib", "MoEConfig", "RoutingOut", "MoEError", "make_config", "expert_bytes", "packed_expert_bytes",
+           "pack_experts", "LAYOUT_RECORD", "LAYOUT_PACKED", "workspace_size",
            "alloc_workspace", "layer_forward", "layer_forward_profiled", "StageEvents", "STAGES", "dequant_mxfp4", "route", "topk", "permute", "expert_ffn", "combine",
            "linear_bf16", "ACT_SILU", "ACT_SITU", "ROUTE_EXACT_ALL", "EXPORTS", "LIB_PATH"]

@@ -13,9 +13,11 @@ namespace {
 constexpr int MAX_K = 64;
 constexpr int MAX_E = 1024;    // experts held in registers by the routing wave
 constexpr int MAX_DIM = 8192;  // columns a GEMV wave holds in registers
+constexpr int MAX_EXPERT_DIM = 7168;  // latent / FFN width whose staged activation rows fit LDS
 
 struct Layout {
-  size_t logits_fast, xnorm2, wnorm2, idx, w, counts, offsets, perm, active, nact, stats, permws, h, a, y, z;
+  size_t logits_fast, xnorm2, wnorm2, idx, w, counts, offsets, perm, tiles, nact, permws, h, y, z;
+  size_t hq_hi, hq_lo, hq_shi, hq_slo, aq_hi, aq_lo, aq_shi, aq_slo;
   size_t total;
 };
 
@@ -37,12 +39,18 @@ Layout layout(const moe_config& c, int k) {
   l.counts = take(E * 4);
   l.offsets = take((E + 1) * 4);
   l.perm = take(T * K * 4);
-  l.active = take(E * 4);
+  l.tiles = take(E * 16);
   l.nact = take(4);
-  l.stats = take(16);
   l.permws = take(permute_ws_bytes((int64_t)(T * K), (int32_t)E));
   l.h = take(T * L * 2);
-  l.a = take(T * K * F * 2);
+  l.hq_hi = take(T * L);
+  l.hq_lo = take(T * L);
+  l.hq_shi = take(T * L / 32);
+  l.hq_slo = take(T * L / 32);
+  l.aq_hi = take(T * K * F);
+  l.aq_lo = take(T * K * F);
+  l.aq_shi = take(T * K * F / 32);
+  l.aq_slo = take(T * K * F / 32);
   l.y = take(T * K * L * 4);
   l.z = take(T * L * 2);
   l.total = off;
@@ -70,14 +78,17 @@ moe_status check_config(const moe_config* c, int32_t k) {
   if (c->act != MOE_ACT_SILU && c->act != MOE_ACT_SITU) return MOE_ERR_INVALID_ARG;
   if (c->renormalize != 0 && c->renormalize != 1) return MOE_ERR_INVALID_ARG;
   if (c->bias_row_stride != 0 && c->bias_row_stride != c->num_experts) return MOE_ERR_INVALID_ARG;
+  if (c->expert_layout != MOE_LAYOUT_RECORD && c->expert_layout != MOE_LAYOUT_PACKED) return MOE_ERR_INVALID_ARG;
   if (c->act == MOE_ACT_SITU) return MOE_ERR_UNSUPPORTED;  // formula not defined on the pages
   // sizes this build's kernels hold in registers; the expert GEMV also needs 128-column multiples
-  if (c->num_experts > MAX_E || c->d_model > MAX_DIM || c->d_latent > MAX_DIM || c->d_ffn > MAX_DIM ||
+  if (c->num_experts > MAX_E || c->d_model > MAX_DIM || c->d_latent > MAX_EXPERT_DIM || c->d_ffn > MAX_EXPERT_DIM ||
       c->d_latent % 128 || c->d_ffn % 128)
     return MOE_ERR_UNSUPPORTED;
   if (c->num_tokens > (int64_t)1 << 24 || c->num_tokens * k > (int64_t)INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
+
+int32_t max_tiles(int64_t rows, int32_t E) { return (int32_t)(rows < E ? rows : E); }
 
 moe_status dev(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_DEVICE; }
 
@@ -120,9 +131,8 @@ moe_status run_router_and_down(const moe_config& c, const void* x, const void* r
   return dev(launch_dense_gemv(static_cast<const uint16_t*>(x), c.num_tokens, c.d_model, segs, nseg, st));
 }
 
-moe_status run_route(const moe_config& c, int k, int flags, const void* x, const void* router_w,
-                     const float* bias, int32_t* idx, float* w, float* logits_out, void* ws, const Layout& l,
-                     hipStream_t st) {
+RouteArgs route_args(const moe_config& c, int k, int flags, const void* x, const void* router_w, const float* bias,
+                     int32_t* idx, float* w, float* logits_out, void* ws, const Layout& l) {
   RouteArgs a;
   a.logits_fast = at<float>(ws, l.logits_fast);
   a.xnorm2 = at<float>(ws, l.xnorm2);
@@ -142,30 +152,37 @@ moe_status run_route(const moe_config& c, int k, int flags, const void* x, const
   a.idx = idx;
   a.w = w;
   a.logits_out = logits_out;
-  a.stats = at<int32_t>(ws, l.stats);
-  MOE_TRY(zero_i32(a.stats, 4, st));
-  return dev(launch_route(a, st));
+  a.stats = nullptr;
+  a.h = nullptr;
+  a.L = c.d_latent;
+  a.hq = QRows{nullptr, nullptr, nullptr, nullptr};
+  return a;
 }
 
-ExpertArgs expert_args(const moe_config& c, int k, const void* h, const uint8_t* blob, void* ws, const Layout& l,
-                       const int32_t* counts, const int32_t* offsets, const int32_t* perm, float* y) {
-  ExpertArgs e;
-  e.h = static_cast<const uint16_t*>(h);
-  e.blob = blob;
-  e.L = c.d_latent;
-  e.F = c.d_ffn;
-  e.k = k;
-  e.T = c.num_tokens;
-  e.counts = counts;
-  e.offsets = offsets;
-  e.perm = perm;
-  e.active = at<int32_t>(ws, l.active);
-  e.n_active = at<int32_t>(ws, l.nact);
-  int64_t rows = c.num_tokens * k;
-  e.max_active = (int32_t)(rows < c.num_experts ? rows : c.num_experts);
-  e.a = at<uint16_t>(ws, l.a);
-  e.y = y;
-  return e;
+QRows hq_rows(void* ws, const Layout& l) {
+  return QRows{at<uint8_t>(ws, l.hq_hi), at<uint8_t>(ws, l.hq_lo), at<uint8_t>(ws, l.hq_shi), at<uint8_t>(ws, l.hq_slo)};
+}
+QRows aq_rows(void* ws, const Layout& l) {
+  return QRows{at<uint8_t>(ws, l.aq_hi), at<uint8_t>(ws, l.aq_lo), at<uint8_t>(ws, l.aq_shi), at<uint8_t>(ws, l.aq_slo)};
+}
+
+MxArgs mx_args(const moe_config& c, int k, const uint8_t* blob, void* ws, const Layout& l, const int32_t* perm,
+               float* y) {
+  MxArgs m;
+  m.blob = blob;
+  m.packed = c.expert_layout == MOE_LAYOUT_PACKED;
+  m.L = c.d_latent;
+  m.F = c.d_ffn;
+  m.k = k;
+  m.T = c.num_tokens;
+  m.tiles = at<int4>(ws, l.tiles);
+  m.max_active = max_tiles(c.num_tokens * k, c.num_experts);
+  m.perm = perm;
+  m.hq = hq_rows(ws, l);
+  m.aq = aq_rows(ws, l);
+  m.a_bf16 = nullptr;
+  m.y = y;
+  return m;
 }
 
 }  // namespace
@@ -176,6 +193,23 @@ size_t moe_expert_bytes(int32_t d_latent, int32_t d_ffn) {
   if (d_latent <= 0 || d_ffn <= 0 || d_latent % 32 || d_ffn % 32) return 0;
   size_t wts = (size_t)3 * (size_t)d_latent * (size_t)d_ffn;
   return wts / 2 + wts / 32;
+}
+
+size_t moe_packed_expert_bytes(int32_t d_latent, int32_t d_ffn) {
+  if (d_latent <= 0 || d_ffn <= 0 || d_latent % 128 || d_ffn % 128) return 0;
+  return (size_t)packed_expert_bytes(d_latent, d_ffn);
+}
+
+moe_status moe_pack_experts(const uint8_t* blob, int32_t num_experts, int32_t d_latent, int32_t d_ffn,
+                            uint8_t* packed, moe_stream_t stream) {
+  if (num_experts < 0 || d_latent <= 0 || d_ffn <= 0 || d_latent % 128 || d_ffn % 128) return MOE_ERR_INVALID_ARG;
+  if (num_experts == 0) return MOE_OK;
+  if (!blob || !packed || !aligned16(blob) || !aligned16(packed)) return MOE_ERR_INVALID_ARG;
+  const size_t in = (size_t)num_experts * moe_expert_bytes(d_latent, d_ffn);
+  const size_t outb = (size_t)num_experts * moe_packed_expert_bytes(d_latent, d_ffn);
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(blob), b0 = reinterpret_cast<uintptr_t>(packed);
+  if (a0 < b0 + outb && b0 < a0 + in) return MOE_ERR_INVALID_ARG;  // overlap
+  return dev(launch_pack_experts(blob, packed, num_experts, d_latent, d_ffn, reinterpret_cast<hipStream_t>(stream)));
 }
 
 const char* moe_status_string(moe_status s) {
@@ -232,24 +266,46 @@ static moe_status forward_impl(const void* x, const void* router_w, const void* 
   MOE_TRY(mark(MOE_STAGE_ROUTER_DOWN, true));
   MOE_TRY(run_router_and_down(c, x, router_w, latent_down, ws, l, st));
   MOE_TRY(mark(MOE_STAGE_ROUTER_DOWN, false));
+  RouteArgs ra = route_args(c, k, 0, x, router_w, router_bias, idx, w, logits_out, ws, l);
+  ra.h = at<uint16_t>(ws, l.h);
+  ra.hq = hq_rows(ws, l);
+  PermOut po{counts, offsets, perm, at<int4>(ws, l.tiles), at<int32_t>(ws, l.nact),
+             max_tiles(c.num_tokens * k, c.num_experts)};
   MOE_TRY(mark(MOE_STAGE_ROUTE, true));
-  MOE_TRY(run_route(c, k, 0, x, router_w, router_bias, idx, w, logits_out, ws, l, st));
-  MOE_TRY(mark(MOE_STAGE_ROUTE, false));
-  MOE_TRY(mark(MOE_STAGE_PERMUTE, true));
-  MOE_TRY(dev(launch_permute(idx, c.num_tokens * k, c.num_experts, counts, offsets, perm, at<int32_t>(ws, l.active),
-                             at<int32_t>(ws, l.nact), at<void>(ws, l.permws), st)));
+  if (c.num_tokens <= ROUTE_FUSED_TOKENS) {
+    MOE_TRY(dev(launch_route_permute_small(ra, po, st)));
+    MOE_TRY(mark(MOE_STAGE_ROUTE, false));
+    MOE_TRY(mark(MOE_STAGE_PERMUTE, true));
+  } else if (c.num_tokens <= ROUTE_PLACE_TOKENS && c.num_tokens * k <= ROUTE_SMALL_ROWS) {
+    MOE_TRY(dev(launch_route(ra, st)));
+    MOE_TRY(mark(MOE_STAGE_ROUTE, false));
+    MOE_TRY(mark(MOE_STAGE_PERMUTE, true));
+    MOE_TRY(dev(launch_place_rows(idx, c.num_tokens, k, c.num_experts, po, st)));
+  } else {
+    MOE_TRY(dev(launch_route(ra, st)));
+    MOE_TRY(mark(MOE_STAGE_ROUTE, false));
+    MOE_TRY(mark(MOE_STAGE_PERMUTE, true));
+    MOE_TRY(dev(launch_permute(idx, c.num_tokens * k, c.num_experts, po, at<void>(ws, l.permws), st)));
+  }
   MOE_TRY(mark(MOE_STAGE_PERMUTE, false));
-  ExpertArgs ea = expert_args(c, k, at<uint16_t>(ws, l.h), expert_blob, ws, l, counts, offsets, perm,
-                              at<float>(ws, l.y));
+  const MxArgs mx = mx_args(c, k, expert_blob, ws, l, perm, at<float>(ws, l.y));
   MOE_TRY(mark(MOE_STAGE_GATE_UP, true));
-  MOE_TRY(dev(launch_expert_gateup(ea, st)));
+  MOE_TRY(dev(launch_gateup_mx(mx, st)));
   MOE_TRY(mark(MOE_STAGE_GATE_UP, false));
-  MOE_TRY(mark(MOE_STAGE_DOWN, true));
-  MOE_TRY(dev(launch_expert_down(ea, st)));
-  MOE_TRY(mark(MOE_STAGE_DOWN, false));
-  MOE_TRY(mark(MOE_STAGE_COMBINE, true));
-  MOE_TRY(dev(launch_combine(at<float>(ws, l.y), w, c.num_tokens, k, c.d_latent, at<uint16_t>(ws, l.z), st)));
-  MOE_TRY(mark(MOE_STAGE_COMBINE, false));
+  if (down_combine_fits(c.num_tokens, k)) {
+    MOE_TRY(mark(MOE_STAGE_DOWN, true));
+    MOE_TRY(dev(launch_down_combine_mx(mx, idx, w, at<uint16_t>(ws, l.z), st)));
+    MOE_TRY(mark(MOE_STAGE_DOWN, false));
+    MOE_TRY(mark(MOE_STAGE_COMBINE, true));
+    MOE_TRY(mark(MOE_STAGE_COMBINE, false));
+  } else {
+    MOE_TRY(mark(MOE_STAGE_DOWN, true));
+    MOE_TRY(dev(launch_down_mx(mx, st)));
+    MOE_TRY(mark(MOE_STAGE_DOWN, false));
+    MOE_TRY(mark(MOE_STAGE_COMBINE, true));
+    MOE_TRY(dev(launch_combine(at<float>(ws, l.y), w, c.num_tokens, k, c.d_latent, at<uint16_t>(ws, l.z), st)));
+    MOE_TRY(mark(MOE_STAGE_COMBINE, false));
+  }
   DenseSeg up;
   up.W = static_cast<const uint16_t*>(latent_up);
   up.rows = c.d_model;
@@ -300,8 +356,9 @@ moe_status moe_route(const void* x, const void* router_w, const float* router_bi
   if (!workspace || workspace_bytes < l.total) return MOE_ERR_WORKSPACE;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   MOE_TRY(run_router_and_down(c, x, router_w, nullptr, workspace, l, st));
-  return run_route(c, k, flags, x, router_w, router_bias, routing->topk_idx, routing->topk_w, routing->logits,
-                   workspace, l, st);
+  const RouteArgs ra = route_args(c, k, flags, x, router_w, router_bias, routing->topk_idx, routing->topk_w,
+                                  routing->logits, workspace, l);
+  return dev(launch_route(ra, st));
 }
 
 moe_status moe_topk(const float* logits, int64_t num_tokens, int32_t num_experts, int32_t k, int32_t renormalize,
@@ -332,14 +389,12 @@ moe_status moe_permute(const int32_t* topk_idx, int64_t num_tokens, int32_t k, i
   if (num_experts > MAX_E) return MOE_ERR_UNSUPPORTED;
   const int64_t rows = num_tokens * k;
   if (rows == 0) return MOE_OK;
-  const size_t need = align_up(permute_ws_bytes(rows, num_experts), 256) + align_up((size_t)num_experts * 4, 256) + 256;
+  const size_t pws = align_up(permute_ws_bytes(rows, num_experts), 256);
+  const size_t need = pws + align_up((size_t)num_experts * 16, 256) + 256;
   if (!workspace || workspace_bytes < need) return MOE_ERR_WORKSPACE;
-  void* pws = workspace;
-  int32_t* active = at<int32_t>(workspace, align_up(permute_ws_bytes(rows, num_experts), 256));
-  int32_t* nact = at<int32_t>(workspace, align_up(permute_ws_bytes(rows, num_experts), 256) +
-                                             align_up((size_t)num_experts * 4, 256));
-  return dev(launch_permute(topk_idx, rows, num_experts, expert_counts, expert_offsets, perm, active, nact, pws,
-                            reinterpret_cast<hipStream_t>(stream)));
+  PermOut po{expert_counts, expert_offsets, perm, at<int4>(workspace, pws),
+             at<int32_t>(workspace, pws + align_up((size_t)num_experts * 16, 256)), max_tiles(rows, num_experts)};
+  return dev(launch_permute(topk_idx, rows, num_experts, po, workspace, reinterpret_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_expert_ffn(const void* h, const uint8_t* expert_blob, int32_t k, const moe_config* cfg,
@@ -355,16 +410,15 @@ moe_status moe_expert_ffn(const void* h, const uint8_t* expert_blob, int32_t k, 
   if (!workspace || workspace_bytes < l.total) return MOE_ERR_WORKSPACE;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   void* ws = workspace;
-  int32_t* counts = at<int32_t>(ws, l.counts);
-  int32_t* offsets = at<int32_t>(ws, l.offsets);
   int32_t* perm = at<int32_t>(ws, l.perm);
-  MOE_TRY(dev(launch_permute(routing->topk_idx, c.num_tokens * k, c.num_experts, counts, offsets, perm,
-                             at<int32_t>(ws, l.active), at<int32_t>(ws, l.nact), at<void>(ws, l.permws), st)));
-  ExpertArgs ea = expert_args(c, k, h, expert_blob, ws, l, counts, offsets, perm, y);
-  MOE_TRY(dev(launch_expert_gateup(ea, st)));
-  MOE_TRY(dev(launch_expert_down(ea, st)));
-  if (a_out)
-    MOE_TRY(dev(launch_unpermute_rows(ea.a, perm, c.num_tokens * k, c.d_ffn, static_cast<uint16_t*>(a_out), st)));
+  PermOut po{at<int32_t>(ws, l.counts), at<int32_t>(ws, l.offsets), perm, at<int4>(ws, l.tiles),
+             at<int32_t>(ws, l.nact), max_tiles(c.num_tokens * k, c.num_experts)};
+  MOE_TRY(dev(launch_permute(routing->topk_idx, c.num_tokens * k, c.num_experts, po, at<void>(ws, l.permws), st)));
+  MOE_TRY(dev(launch_quantize_rows(static_cast<const uint16_t*>(h), c.num_tokens, c.d_latent, hq_rows(ws, l), st)));
+  MxArgs mx = mx_args(c, k, expert_blob, ws, l, perm, y);
+  mx.a_bf16 = static_cast<uint16_t*>(a_out);
+  MOE_TRY(dev(launch_gateup_mx(mx, st)));
+  MOE_TRY(dev(launch_down_mx(mx, st)));
   return MOE_OK;
 }
 

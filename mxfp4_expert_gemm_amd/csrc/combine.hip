@@ -1,5 +1,6 @@
 // Weighted combine of the k expert outputs of each token in the latent space:
-// z[t][l] = bf16(sum_j w[t][j] * y[t*k + j][l]), fp32 accumulation in slot order
+// z[t][l] = bf16(sum_j w[t][j] * y[t*k + j][l]), accumulated in fp64 in slot order
+// (the fp32 products are exact in fp64), rounded once
 // (kimi-k3-mlx digest: router weights are probabilities over the kept experts;
 // Stable LatentMoE combines before the single up-projection).
 #include "common.h"
@@ -13,18 +14,18 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
   const int64_t t = blockIdx.y;
   const int l = 4 * (blockIdx.x * blockDim.x + threadIdx.x);
   if (t >= T || l >= L) return;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  double ax = 0.0, ay = 0.0, az = 0.0, aw = 0.0;
   for (int j = 0; j < k; ++j) {
-    const float wj = w[t * k + j];
+    const double wj = (double)w[t * k + j];
     const float4 v = *reinterpret_cast<const float4*>(y + (t * k + j) * L + l);
-    acc.x = fmaf(wj, v.x, acc.x);
-    acc.y = fmaf(wj, v.y, acc.y);
-    acc.z = fmaf(wj, v.z, acc.z);
-    acc.w = fmaf(wj, v.w, acc.w);
+    ax += wj * (double)v.x;
+    ay += wj * (double)v.y;
+    az += wj * (double)v.z;
+    aw += wj * (double)v.w;
   }
   uint2 o;
-  o.x = (uint32_t)f32_to_bf16(acc.x) | ((uint32_t)f32_to_bf16(acc.y) << 16);
-  o.y = (uint32_t)f32_to_bf16(acc.z) | ((uint32_t)f32_to_bf16(acc.w) << 16);
+  o.x = (uint32_t)f64_to_bf16(ax) | ((uint32_t)f64_to_bf16(ay) << 16);
+  o.y = (uint32_t)f64_to_bf16(az) | ((uint32_t)f64_to_bf16(aw) << 16);
   *reinterpret_cast<uint2*>(z + t * L + l) = o;
 }
 

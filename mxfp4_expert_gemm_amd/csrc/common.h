@@ -26,6 +26,23 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// fp64 -> bf16 bits, round to nearest even in one step (no detour through fp32):
+// the value is rounded to the 8-significant-bit grid of its binade (spacing 2^-133 in
+// the subnormal range), overflow gives inf.
+__device__ __forceinline__ uint16_t f64_to_bf16(double v) {
+  const uint64_t u = __double_as_longlong(v);
+  const uint32_t ex = (uint32_t)(u >> 52) & 0x7FFu;
+  const uint16_t sign = (uint16_t)((u >> 48) & 0x8000u);
+  if (ex == 0x7FFu) return (u & 0xFFFFFFFFFFFFFull) ? (uint16_t)0x7FC0 : (uint16_t)(sign | 0x7F80);
+  if (ex == 0u) return sign;  // below 2^-1022: rounds to zero in bf16
+  int q = (int)ex - 1023 - 7;
+  if (q < -133) q = -133;
+  const double step = __longlong_as_double((long long)(q + 1023) << 52);
+  const double r = rint(v / step) * step;  // both operations exact; rint ties to even
+  if (fabs(r) >= 0x1p128) return (uint16_t)(sign | 0x7F80);
+  return (uint16_t)(__float_as_uint((float)r) >> 16);  // r has at most 8 significant bits
+}
+
 __device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2_t, v); }
 
 // acc + a.lo*b.lo + a.hi*b.hi
@@ -54,6 +71,114 @@ __device__ __forceinline__ uint4 load_nt16(const void* p) {
 }
 
 // ---------------------------------------------------------- wave reductions
+//
+// DPP reductions (GFX9 data-parallel primitives, no LDS round trip): two quad
+// permutes and two row rotations give every lane its 16-lane row total, two row
+// broadcasts fold rows 0..3 into lane 63, which readlane hands to the whole wave.
+// The association order is fixed, so results are deterministic.
+
+constexpr int DPP_QUAD_1032 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int DPP_QUAD_2301 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int DPP_ROW_ROR4 = 0x124;
+constexpr int DPP_ROW_ROR8 = 0x128;
+constexpr int DPP_ROW_BCAST15 = 0x142;
+constexpr int DPP_ROW_BCAST31 = 0x143;
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_f32(float v, float old) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), CTRL, ROW_MASK, 0xF, false));
+}
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ double dpp_f64(double v, double old) {
+  int2 a = __builtin_bit_cast(int2, v), o = __builtin_bit_cast(int2, old);
+  int2 r;
+  r.x = __builtin_amdgcn_update_dpp(o.x, a.x, CTRL, ROW_MASK, 0xF, false);
+  r.y = __builtin_amdgcn_update_dpp(o.y, a.y, CTRL, ROW_MASK, 0xF, false);
+  return __builtin_bit_cast(double, r);
+}
+
+__device__ __forceinline__ float readlane63(float v) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+__device__ __forceinline__ double readlane63(double v) {
+  int2 a = __builtin_bit_cast(int2, v);
+  a.x = __builtin_amdgcn_readlane(a.x, 63);
+  a.y = __builtin_amdgcn_readlane(a.y, 63);
+  return __builtin_bit_cast(double, a);
+}
+
+// sum over the 64 lanes, returned to every lane
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += dpp_f32<DPP_QUAD_1032>(v, 0.f);
+  v += dpp_f32<DPP_QUAD_2301>(v, 0.f);
+  v += dpp_f32<DPP_ROW_ROR4>(v, 0.f);
+  v += dpp_f32<DPP_ROW_ROR8>(v, 0.f);
+  v += dpp_f32<DPP_ROW_BCAST15, 0xA>(v, 0.f);
+  v += dpp_f32<DPP_ROW_BCAST31, 0xC>(v, 0.f);
+  return readlane63(v);
+}
+
+__device__ __forceinline__ double wave_sum_dpp(double v) {
+  v += dpp_f64<DPP_QUAD_1032>(v, 0.0);
+  v += dpp_f64<DPP_QUAD_2301>(v, 0.0);
+  v += dpp_f64<DPP_ROW_ROR4>(v, 0.0);
+  v += dpp_f64<DPP_ROW_ROR8>(v, 0.0);
+  v += dpp_f64<DPP_ROW_BCAST15, 0xA>(v, 0.0);
+  v += dpp_f64<DPP_ROW_BCAST31, 0xC>(v, 0.0);
+  return readlane63(v);
+}
+
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  const float lo = -__builtin_inff();
+  v = fmaxf(v, dpp_f32<DPP_QUAD_1032>(v, lo));
+  v = fmaxf(v, dpp_f32<DPP_QUAD_2301>(v, lo));
+  v = fmaxf(v, dpp_f32<DPP_ROW_ROR4>(v, lo));
+  v = fmaxf(v, dpp_f32<DPP_ROW_ROR8>(v, lo));
+  v = fmaxf(v, dpp_f32<DPP_ROW_BCAST15, 0xA>(v, lo));
+  v = fmaxf(v, dpp_f32<DPP_ROW_BCAST31, 0xC>(v, lo));
+  return readlane63(v);
+}
+
+__device__ __forceinline__ float wave_min_dpp(float v) {
+  const float hi = __builtin_inff();
+  v = fminf(v, dpp_f32<DPP_QUAD_1032>(v, hi));
+  v = fminf(v, dpp_f32<DPP_QUAD_2301>(v, hi));
+  v = fminf(v, dpp_f32<DPP_ROW_ROR4>(v, hi));
+  v = fminf(v, dpp_f32<DPP_ROW_ROR8>(v, hi));
+  v = fminf(v, dpp_f32<DPP_ROW_BCAST15, 0xA>(v, hi));
+  v = fminf(v, dpp_f32<DPP_ROW_BCAST31, 0xC>(v, hi));
+  return readlane63(v);
+}
+
+// inclusive prefix sum over the 64 lanes: Hillis-Steele row shifts inside each row of
+// 16, then the two row broadcasts carry the row totals forward
+constexpr int DPP_ROW_SHR1 = 0x111;
+constexpr int DPP_ROW_SHR2 = 0x112;
+constexpr int DPP_ROW_SHR4 = 0x114;
+constexpr int DPP_ROW_SHR8 = 0x118;
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int dpp_i32(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, false);  // 0 where there is no source
+}
+__device__ __forceinline__ int wave_incl_scan_dpp(int v) {
+  v += dpp_i32<DPP_ROW_SHR1>(v);
+  v += dpp_i32<DPP_ROW_SHR2>(v);
+  v += dpp_i32<DPP_ROW_SHR4>(v);
+  v += dpp_i32<DPP_ROW_SHR8>(v);
+  v += dpp_i32<DPP_ROW_BCAST15, 0xA>(v);
+  v += dpp_i32<DPP_ROW_BCAST31, 0xC>(v);
+  return v;
+}
+// exclusive prefix sum; total receives the wave's sum
+__device__ __forceinline__ int wave_excl_scan(int v, int& total) {
+  const int inc = wave_incl_scan_dpp(v);
+  total = __builtin_amdgcn_readlane(inc, 63);
+  return inc - v;
+}
+
+// shuffle-based reductions (any lane count pattern); kept for the exact-recompute path
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -77,5 +202,145 @@ __device__ __forceinline__ int lane_id() { return threadIdx.x & (WAVE - 1); }
 
 __host__ __device__ constexpr inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 __host__ __device__ constexpr inline size_t align_up(size_t a, size_t b) { return (a + b - 1) / b * b; }
+
+// ------------------------------------------------ two-term e4m3 activations
+//
+// The scaled MFMA (v_mfma_scale_f32_16x16x128_f8f6f4) multiplies MXFP4 weights by
+// 8-bit activations with one e8m0 scale per 32 values.  A bf16 value has 8
+// significant bits and e4m3 has 4, so each 32-block of bf16 activations x is split
+// into hi = e4m3(x / S_hi) and lo = e4m3((x - hi S_hi) / S_lo) with S_hi = 2^(E-7),
+// E the exponent of the block maximum, and S_lo chosen the same way from the
+// residuals.  The residual of an element within 2^13 of the block maximum has at
+// most 4 significant bits, so hi S_hi + lo S_lo reproduces it exactly; smaller
+// elements keep an absolute error below 2^-20 of the block maximum.  Two MFMAs (hi
+// and lo) then give the product of the bf16 activations with the MXFP4 weights,
+// accumulated in fp32.
+
+// round |v| < 448 to e4m3 (OCP E4M3: bias 7, 3 mantissa bits, subnormals of 2^-9),
+// nearest-even; returns the code and the rounded value
+__device__ __forceinline__ uint32_t e4m3_rne(float v, float& rounded) {
+  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  const float a = fabsf(v);
+  if (a < 0x1p-6f) {
+    const float q = rintf(a * 512.f);  // exact scaling; 0..8, 8 is the smallest normal
+    rounded = __uint_as_float(__float_as_uint(q * 0x1p-9f) | (sign << 24));
+    return sign | (uint32_t)q;
+  }
+  uint32_t u = __float_as_uint(a);
+  u += 0x7FFFFu + ((u >> 20) & 1u);  // nearest-even on the 3 kept mantissa bits
+  u &= 0xFFF00000u;
+  rounded = __uint_as_float(u | (sign << 24));
+  return sign | ((((u >> 23) - 127u + 7u) & 15u) << 3) | ((u >> 20) & 7u);
+}
+
+// power-of-two exponent of |a| > 0 (subnormals included)
+__device__ __forceinline__ int exponent_of(float a) {
+  const uint32_t u = __float_as_uint(a) & 0x7FFFFFFFu;
+  if (u >= 0x00800000u) return (int)(u >> 23) - 127;
+  return -118 - (int)__clz(u);  // subnormal: value = u * 2^-149
+}
+
+__device__ __forceinline__ float pow2f(int e) {  // 2^e for -149 <= e <= 127
+  if (e >= -126) return __uint_as_float((uint32_t)(e + 127) << 23);
+  return __uint_as_float(1u << (e + 149));
+}
+
+// e8m0 byte for a block whose largest magnitude is amax: 2^(E-7), clamped to the
+// e8m0 range; returns the byte and the scale's reciprocal as fp32
+__device__ __forceinline__ uint32_t block_scale(float amax, float& inv) {
+  if (!(amax > 0.f)) {
+    inv = 1.f;
+    return 127u;
+  }
+  int se = exponent_of(amax) - 7;
+  if (se < -127) se = -127;
+  if (se > 127) se = 127;
+  inv = pow2f(-se);
+  return (uint32_t)(se + 127);
+}
+
+// The split of one 32-value block held by the 4 lanes of a quad (8 consecutive values
+// each; quad = lanes 4j..4j+3): the block maxima are combined with two quad permutes.
+// Returns this lane's 8 hi and 8 lo codes (value i in byte i % 4 of dword i / 4) and
+// the block's two scale bytes.
+__device__ __forceinline__ float quad_max(float v) {
+  v = fmaxf(v, dpp_f32<DPP_QUAD_1032>(v, 0.f));
+  return fmaxf(v, dpp_f32<DPP_QUAD_2301>(v, 0.f));
+}
+__device__ __forceinline__ void quantize_quad8(const float (&v)[8], uint32_t (&hi)[2], uint32_t (&lo)[2], uint32_t& shi,
+                                               uint32_t& slo) {
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  amax = quad_max(amax);
+  float inv;
+  shi = block_scale(amax, inv);
+  const float s_hi = 1.f / inv;
+  float r[8];
+  float rmax = 0.f;
+  hi[0] = hi[1] = 0u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float q;
+    hi[i / 4] |= e4m3_rne(v[i] * inv, q) << (8 * (i % 4));
+    r[i] = v[i] - q * s_hi;
+    rmax = fmaxf(rmax, fabsf(r[i]));
+  }
+  rmax = quad_max(rmax);
+  slo = block_scale(rmax, inv);
+  lo[0] = lo[1] = 0u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float q;
+    lo[i / 4] |= e4m3_rne(r[i] * inv, q) << (8 * (i % 4));
+  }
+}
+
+// Quantised activation rows: codes [rows][K] (hi and lo) and e8m0 scales [rows][K/32].
+struct QRows {
+  uint8_t* hi;
+  uint8_t* lo;
+  uint8_t* shi;
+  uint8_t* slo;
+};
+
+// Quantise n bf16 values (n a multiple of 32) in groups of 8, one group per lane:
+// groups j0, j0 + jstride, ... (j0 and jstride chosen so that the four groups of a scale
+// block sit in one quad of lanes).  All loads of a lane are issued before any group is
+// converted.
+__device__ __forceinline__ void quantize_quads(const uint16_t* __restrict__ src, QRows q, int64_t n, int64_t j0,
+                                               int64_t jstride) {
+  constexpr int U = 2;
+  const int64_t ng = n / 8;
+  for (int64_t base = j0; base < ng; base += U * jstride) {
+    uint4 raw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t j = base + u * jstride;
+      raw[u] = j < ng ? *reinterpret_cast<const uint4*>(src + 8 * j) : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t j = base + u * jstride;
+      if (j < ng) {
+        const uint32_t w[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+        float v[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v[2 * i] = bf16lo(w[i]);
+          v[2 * i + 1] = bf16hi(w[i]);
+        }
+        uint32_t hi[2], lo[2], shi, slo;
+        quantize_quad8(v, hi, lo, shi, slo);
+        *reinterpret_cast<uint2*>(q.hi + 8 * j) = make_uint2(hi[0], hi[1]);
+        *reinterpret_cast<uint2*>(q.lo + 8 * j) = make_uint2(lo[0], lo[1]);
+        if ((j & 3) == 0) {
+          q.shi[j >> 2] = (uint8_t)shi;
+          q.slo[j >> 2] = (uint8_t)slo;
+        }
+      }
+    }
+  }
+}
 
 }  // namespace moe

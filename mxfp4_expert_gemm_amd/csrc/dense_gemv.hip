@@ -4,7 +4,9 @@
 // architecture table: the router scores 896 experts from the 7168-wide token;
 // Stable LatentMoE projects 7168 -> 3584 and back with bf16 matrices).
 //
-// Memory-bound: every weight byte is read once per token group.  One wave owns one
+// Memory-bound: every weight byte is read once per token group, so sums are kept in
+// fp64 (fp32 partials of 8 exact products folded into fp64) at no cost in time; the
+// bf16 outputs are then the correctly rounded sums but for fp64-level ties.  One wave owns one
 // row; lane l reads 16 bytes (8 bf16) at column 8*(64c + l) for chunk c, so each
 // load instruction covers 1 KiB of the row contiguously and the token values the
 // lane needs stay in registers for the whole row.  Products of bf16 pairs are exact
@@ -35,16 +37,24 @@ __global__ void __launch_bounds__(256) dense_gemv_kernel(DenseParams p) {
   const int lane = lane_id();
   const int wave = threadIdx.x / WAVE;
   int64_t row = (int64_t)blockIdx.x * 4 + wave;
-  int si = 0;
-  if (row >= p.seg[0].rows) {
+  // the segment is chosen with scalar selects so every field stays in kernel-argument
+  // registers (an indexed p.seg[si] would be read from memory after the loads)
+  const bool second = row >= p.seg[0].rows;
+  if (second) {
     row -= p.seg[0].rows;
-    si = 1;
-    if (si >= p.nseg || row >= p.seg[1].rows) return;
+    if (p.nseg < 2 || row >= p.seg[1].rows) return;
   }
-  const DenseSeg& s = p.seg[si];
+  const DenseSeg s = second ? p.seg[1] : p.seg[0];
   const int32_t K = p.K;
   const int64_t t0 = (int64_t)blockIdx.y * G;
 
+  uint4 wr[NCH];
+  const uint16_t* wrow = s.W + row * K;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    int col = 8 * (64 * c + lane);
+    wr[c] = col < K ? load_nt16(wrow + col) : make_uint4(0, 0, 0, 0);
+  }
   uint4 xr[G][NCH];
 #pragma unroll
   for (int g = 0; g < G; ++g)
@@ -57,33 +67,26 @@ __global__ void __launch_bounds__(256) dense_gemv_kernel(DenseParams p) {
         xr[g][c] = make_uint4(0, 0, 0, 0);
     }
 
-  uint4 wr[NCH];
-  const uint16_t* wrow = s.W + row * K;
-#pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    int col = 8 * (64 * c + lane);
-    wr[c] = col < K ? load_nt16(wrow + col)
-                    : make_uint4(0, 0, 0, 0);
-  }
-
   if (!s.router) {
-    float acc[G];
+    // latent projections: fp32 chunk partials folded into fp64, rounded once to bf16
+    double acc[G];
 #pragma unroll
-    for (int g = 0; g < G; ++g) acc[g] = 0.f;
+    for (int g = 0; g < G; ++g) acc[g] = 0.0;
 #pragma unroll
     for (int c = 0; c < NCH; ++c)
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        acc[g] = dot2(xr[g][c].x, wr[c].x, acc[g]);
-        acc[g] = dot2(xr[g][c].y, wr[c].y, acc[g]);
-        acc[g] = dot2(xr[g][c].z, wr[c].z, acc[g]);
-        acc[g] = dot2(xr[g][c].w, wr[c].w, acc[g]);
+        float pc = dot2(xr[g][c].x, wr[c].x, 0.f);
+        pc = dot2(xr[g][c].y, wr[c].y, pc);
+        pc = dot2(xr[g][c].z, wr[c].z, pc);
+        pc = dot2(xr[g][c].w, wr[c].w, pc);
+        acc[g] += (double)pc;
       }
     uint16_t* out = reinterpret_cast<uint16_t*>(s.out);
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      float v = wave_sum(acc[g]);
-      if (lane == 0 && t0 + g < p.T) out[(t0 + g) * s.rows + row] = f32_to_bf16(v);
+      const double v = wave_sum_dpp(acc[g]);
+      if (lane == 0 && t0 + g < p.T) out[(t0 + g) * s.rows + row] = f64_to_bf16(v);
     }
     return;
   }
@@ -111,10 +114,10 @@ __global__ void __launch_bounds__(256) dense_gemv_kernel(DenseParams p) {
   float* out = reinterpret_cast<float*>(s.out);
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    double v = wave_sum(acc[g]);
+    double v = wave_sum_dpp(acc[g]);
     if (lane == 0 && t0 + g < p.T) out[(t0 + g) * s.rows + row] = (float)v;
   }
-  wn = wave_sum(wn);
+  wn = wave_sum_dpp(wn);
   if (lane == 0 && blockIdx.y == 0) s.wnorm2[row] = wn;
   if (row == 0) {  // one wave per token group writes the token norms
 #pragma unroll
@@ -127,7 +130,7 @@ __global__ void __launch_bounds__(256) dense_gemv_kernel(DenseParams p) {
         xn = dot2(xr[g][c].z, xr[g][c].z, xn);
         xn = dot2(xr[g][c].w, xr[g][c].w, xn);
       }
-      xn = wave_sum(xn);
+      xn = wave_sum_dpp(xn);
       if (lane == 0 && t0 + g < p.T) s.xnorm2[t0 + g] = xn;
     }
   }

@@ -1,0 +1,602 @@
+// Routed experts on the CDNA4 block-scaled matrix cores.
+//
+// Expert e is a GLU FFN in the latent space (kimi-k3-mlx digest, architecture table
+// and the LatentMoE and SiTU-GLU bullets; kimi-k3-in-c post, MXFP4 section: three
+// 3584 x 3072 matrices of 4-bit codes with one 8-bit exponent per 32 weights):
+//   g = W_g h, u = W_u h (fp32), a = bf16(silu(g) * u) in fp32, y = W_dn a (fp32).
+//
+// Every product runs on v_mfma_scale_f32_16x16x128_f8f6f4 with the weights in their
+// checkpoint encoding as the FP4 operand: in that instruction a lane holds 32
+// consecutive K values (16 bytes) of one of 16 columns and supplies the e8m0 scale of
+// exactly those 32 values, which is one code block and one scale byte of a weight row.
+// So no instruction is spent expanding weights.  The activations are the FP8 operand,
+// split exactly into two e4m3 terms (hi, lo) with their own e8m0 scales (see
+// quantize_quad8), so two MFMAs per K step give the bf16 x MXFP4 product.
+//
+// Two weight layouts feed the same arithmetic (the MFMA operands are identical, so the
+// results are bit-identical):
+//  * RecordW streams the checkpoint record as it is: a lane loads its row's 16-byte
+//    block, so one wave load touches 16 rows x 64 bytes.  Scale bytes are fetched 16 K
+//    steps at a time (one 16-byte load per lane, SBlock) and handed to the lane that
+//    needs them with a cross-lane permute.
+//  * PackedW streams the layout written by moe_pack_experts, where the 1024 bytes one
+//    K step of 16 rows needs are contiguous in lane order and the scales of 4 steps
+//    are one dword per lane (the matrix core's scale byte select picks the step), so
+//    every wave load is a contiguous 1 KB or 256 B run.
+//
+// Accuracy: one such instruction sums its 128 scaled products with an error of about
+// 2^-22 of their absolute sum (measured), which is the level of an fp32 dot product;
+// the fp32 accumulator chains the K steps.
+//
+// A 16x16 MFMA tile covers 16 weight rows x 16 tokens of one expert.  Decode has one
+// or two tokens per expert, so most of the tile is idle arithmetic, which costs
+// nothing here: the kernels stream weights at HBM speed while the matrix cores stay
+// mostly idle.  Weight loads run a fixed number of steps ahead of their MFMAs; the
+// activations come from LDS, staged after the first weight loads are issued, because
+// vmcnt retires loads in order and a late global load would drain the weight ring.
+//
+// Operand layout of v_mfma_scale_f32_16x16x128_f8f6f4 (measured on gfx950): lane l
+// works on row/column l%16 and K block g = l/16; an FP4 operand holds K = 32g..32g+31
+// (low nibble first), an FP8 operand holds K = 16g..16g+15 in its first four
+// registers and 64+16g..64+16g+15 in the last four; lane (r + 16 b) supplies the
+// scale of row/column r, K block b for both operands, the byte of its scale register
+// chosen by the instruction's scale select; the result register j of lane l is
+// D[4(l/16)+j][l%16].
+#include <type_traits>
+#include <utility>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <int OPSEL_B>
+__device__ __forceinline__ f32x4 mx_mfma(const i32x8& a, const i32x8& b, f32x4 c, uint32_t sa, uint32_t sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0 /*A: fp8 e4m3*/, 4 /*B: fp4 e2m1*/, 0,
+                                                          (int)sa, OPSEL_B, (int)sb);
+}
+
+// calls f(std::integral_constant<int, J>) for J = 0..15
+template <class Fn, int... J>
+__device__ __forceinline__ void unroll16_impl(Fn&& f, std::integer_sequence<int, J...>) {
+  (f(std::integral_constant<int, J>{}), ...);
+}
+template <class Fn>
+__device__ __forceinline__ void unroll16(Fn&& f) {
+  unroll16_impl(f, std::make_integer_sequence<int, 16>{});
+}
+
+__device__ __forceinline__ i32x8 as_b(const uint4& q) {
+  i32x8 b;
+  b[0] = (int)q.x; b[1] = (int)q.y; b[2] = (int)q.z; b[3] = (int)q.w;
+  b[4] = 0; b[5] = 0; b[6] = 0; b[7] = 0;
+  return b;
+}
+
+// --------------------------------------------------------------- weight streams
+
+// Scale bytes of one 16-step block of K for the lane (see the two streams).
+struct SBlock {
+  uint32_t d[4];
+};
+
+enum { MAT_GATE = 0, MAT_UP = 1, MAT_DOWN = 2 };
+
+// Checkpoint record: per expert gate [F][L], up [F][L], down [L][F], each its codes
+// row-major then its e8m0 scales row-major.
+struct RecordW {
+  const uint8_t* c;  // codes of the lane's row + 16 g
+  const uint8_t* s;  // scales of the lane's row
+  int nsb, n, g;     // scale bytes per row; lane row and K block
+
+  // matrix `mat` of expert e, rows 16 grp .. 16 grp + 15
+  __device__ static RecordW make(const uint8_t* blob, int e, int L, int F, int mat, int grp, int lane) {
+    const int64_t mbytes = (int64_t)F * L / 2 + (int64_t)F * L / 32;
+    const int K = mat == MAT_DOWN ? F : L;
+    const uint8_t* m = blob + (int64_t)e * 3 * mbytes + mat * mbytes;
+    const int64_t row = 16 * grp + (lane & 15);
+    RecordW w;
+    w.n = lane & 15;
+    w.g = lane >> 4;
+    w.nsb = K / 32;
+    w.c = m + row * (K / 2) + 16 * w.g;
+    w.s = m + (int64_t)(mat == MAT_DOWN ? L : F) * (K / 2) + row * (K / 32);
+    return w;
+  }
+  __device__ __forceinline__ uint4 load(int ks) const { return load_nt16(c + 64 * ks); }
+  // lane (n, g) takes bytes 64 blk + 16 g .. +15 of row n: dword i holds the four block
+  // scales of step 16 blk + 4 g + i
+  __device__ __forceinline__ void sblock(SBlock& b, int blk) const {
+    const int off = 64 * blk + 16 * g;
+    if ((nsb & 15) == 0) {  // rows of whole 16-byte groups: one aligned load
+      uint4 v = make_uint4(0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu);
+      if (off < nsb) v = *reinterpret_cast<const uint4*>(s + off);
+      b.d[0] = v.x; b.d[1] = v.y; b.d[2] = v.z; b.d[3] = v.w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        b.d[i] = off + 4 * i < nsb ? *reinterpret_cast<const uint32_t*>(s + off + 4 * i) : 0x7F7F7F7Fu;
+    }
+  }
+  // scale of step 16 blk + J, from the lane of the same row that holds it
+  template <int J>
+  __device__ __forceinline__ uint32_t scale(const SBlock& b) const {
+    return (uint32_t)__shfl((int)b.d[J & 3], n + 16 * (J >> 2)) >> (8 * g);
+  }
+  static constexpr int opsel(int) { return 0; }
+};
+
+// Packed layout (moe_pack_experts): a matrix of R rows and K columns is R/16 row groups
+// of packed_group_bytes(K): K/128 code tiles of 1024 bytes (tile s, bytes 16 l .. +15:
+// row l%16 of the group, K values 128 s + 32 (l/16) .. +31), then ceil(K/512) scale
+// tiles of 256 bytes (tile c, byte 4 l + j: the scale of those 32 values at step
+// s = 4c + j; 127 past the last step).
+struct PackedW {
+  const uint8_t* c;  // code tile 0 + 16 lane
+  const uint8_t* s;  // scale tile 0 + 4 lane
+  int nsc;           // scale tiles
+
+  __device__ static PackedW make(const uint8_t* blob, int e, int L, int F, int mat, int grp, int lane) {
+    const int K = mat == MAT_DOWN ? F : L;
+    const int64_t gu = (int64_t)(F / 16) * packed_group_bytes(L);
+    const uint8_t* m =
+        blob + (int64_t)e * packed_expert_bytes(L, F) + (mat == MAT_GATE ? 0 : mat == MAT_UP ? gu : 2 * gu);
+    const uint8_t* grp0 = m + (int64_t)grp * packed_group_bytes(K);
+    PackedW w;
+    w.c = grp0 + 16 * lane;
+    w.s = grp0 + (int64_t)(K / 128) * 1024 + 4 * lane;
+    w.nsc = (K / 128 + 3) / 4;
+    return w;
+  }
+  __device__ __forceinline__ uint4 load(int ks) const { return load_nt16(c + 1024 * ks); }
+  __device__ __forceinline__ void sblock(SBlock& b, int blk) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      b.d[i] = 4 * blk + i < nsc ? *reinterpret_cast<const uint32_t*>(s + 256 * (4 * blk + i)) : 0x7F7F7F7Fu;
+  }
+  template <int J>
+  __device__ __forceinline__ uint32_t scale(const SBlock& b) const {
+    return b.d[J >> 2];
+  }
+  static constexpr int opsel(int j) { return j & 3; }
+};
+
+// ------------------------------------------------------------ staged activations
+
+// Activations of up to MX_TOK rows staged in LDS: codes [MX_TOK][K] hi, then lo, then
+// the e8m0 bytes [MX_TOK][K/32] hi, then lo.
+constexpr int MX_TOK = 4;
+constexpr size_t MX_LDS_MAX = 60 * 1024;  // dynamic LDS the gate/up and down kernels may take
+__host__ __device__ constexpr size_t mx_lds_bytes(int K) { return (size_t)MX_TOK * (2 * K + 2 * (K / 32)); }
+
+struct ALds {
+  uint8_t* hi;
+  uint8_t* lo;
+  uint8_t* shi;
+  uint8_t* slo;
+};
+__device__ __forceinline__ ALds alds(uint8_t* smem, int K, int rows) {
+  return {smem, smem + rows * K, smem + 2 * rows * K, smem + 2 * rows * K + rows * (K / 32)};
+}
+
+// Copy rows src_rows[0..ntok) of q into LDS rows 0..ntok-1 of d; every thread of the
+// block takes part.  The caller syncs.
+__device__ __forceinline__ void stage_rows(const ALds& d, const QRows& q, const int64_t* src_rows, int ntok,
+                                           int K) {
+  const int per = K / 16;  // 16-byte chunks per row and term
+  for (int c = threadIdx.x; c < 2 * ntok * per; c += blockDim.x) {
+    const int term = c / (ntok * per), rem = c - term * ntok * per;
+    const int i = rem / per, off = 16 * (rem - i * per);
+    const uint8_t* src = (term ? q.lo : q.hi) + src_rows[i] * K + off;
+    uint8_t* dst = (term ? d.lo : d.hi) + i * K + off;
+    *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+  }
+  const int nsb = K / 32;
+  for (int c = threadIdx.x; c < 2 * ntok * nsb; c += blockDim.x) {
+    const int term = c / (ntok * nsb), rem = c - term * ntok * nsb;
+    const int i = rem / nsb, b = rem - i * nsb;
+    (term ? d.slo : d.shi)[i * nsb + b] = (term ? q.slo : q.shi)[src_rows[i] * nsb + b];
+  }
+}
+
+// activation operand of one K step for tile row m (zero unless m < ntok)
+struct AStep {
+  i32x8 hi, lo;
+  uint32_t shi, slo;
+};
+__device__ __forceinline__ void read_a(AStep& a, const ALds& d, int m, int ntok, int K, int ks, int g) {
+  if (m < ntok) {
+    const uint8_t* h = d.hi + m * K + 128 * ks + 16 * g;
+    const uint8_t* l = d.lo + m * K + 128 * ks + 16 * g;
+    const uint4 h0 = *reinterpret_cast<const uint4*>(h), h1 = *reinterpret_cast<const uint4*>(h + 64);
+    const uint4 l0 = *reinterpret_cast<const uint4*>(l), l1 = *reinterpret_cast<const uint4*>(l + 64);
+    a.hi[0] = (int)h0.x; a.hi[1] = (int)h0.y; a.hi[2] = (int)h0.z; a.hi[3] = (int)h0.w;
+    a.hi[4] = (int)h1.x; a.hi[5] = (int)h1.y; a.hi[6] = (int)h1.z; a.hi[7] = (int)h1.w;
+    a.lo[0] = (int)l0.x; a.lo[1] = (int)l0.y; a.lo[2] = (int)l0.z; a.lo[3] = (int)l0.w;
+    a.lo[4] = (int)l1.x; a.lo[5] = (int)l1.y; a.lo[6] = (int)l1.z; a.lo[7] = (int)l1.w;
+    a.shi = d.shi[m * (K / 32) + 4 * ks + g];
+    a.slo = d.slo[m * (K / 32) + 4 * ks + g];
+  } else {
+    for (int i = 0; i < 8; ++i) a.hi[i] = a.lo[i] = 0;
+    a.shi = a.slo = 127u;
+  }
+}
+
+// a = bf16(silu(g) u) for the fp32 values g and u; the activation and the product are
+// evaluated in fp64 (the GLU is specified in fp32 or better), g e^g / (1 + e^g) for
+// g < 0 so a large |g| cannot overflow
+__device__ __forceinline__ uint16_t glu_bf16(float g, float u) {
+  const double gd = (double)g;
+  double s;
+  if (gd >= 0.0) {
+    s = gd / (1.0 + exp(-gd));
+  } else {
+    const double e = exp(gd);
+    s = gd * e / (1.0 + e);
+  }
+  return f64_to_bf16(s * (double)u);
+}
+
+// One weight row group (16 rows) times the staged activation rows: acc += A W^T over
+// all K steps with the weights PF steps in flight (ring[q][d] holds steps d < PF on
+// entry).  The NMAT weight streams share the activations (gate and up: 2).
+template <class W, int NMAT, int PF>
+__device__ __forceinline__ void stream_group(const W (&w)[NMAT], uint4 (&ring)[NMAT][PF], const ALds& ad, int m,
+                                             int ntok, int K, int g, f32x4 (&acc)[NMAT]) {
+  const int nks = K / 128, nc = (nks + 15) / 16;
+  SBlock sb[NMAT], sbn[NMAT];
+#pragma unroll
+  for (int q = 0; q < NMAT; ++q) w[q].sblock(sb[q], 0);
+  for (int c = 0; c < nc; ++c) {
+    if (c + 1 < nc) {
+#pragma unroll
+      for (int q = 0; q < NMAT; ++q) w[q].sblock(sbn[q], c + 1);
+    }
+    unroll16([&](auto jc) {
+      constexpr int J = decltype(jc)::value;
+      const int ks = 16 * c + J;
+      if (ks < nks) {
+        uint4 cw[NMAT];
+#pragma unroll
+        for (int q = 0; q < NMAT; ++q) {
+          cw[q] = ring[q][J % PF];
+          if (ks + PF < nks) ring[q][J % PF] = w[q].load(ks + PF);
+        }
+        AStep a;
+        read_a(a, ad, m, ntok, K, ks, g);
+#pragma unroll
+        for (int q = 0; q < NMAT; ++q) {
+          const uint32_t sw = w[q].template scale<J>(sb[q]);
+          const i32x8 b = as_b(cw[q]);
+          acc[q] = mx_mfma<W::opsel(J)>(a.hi, b, acc[q], a.shi, sw);
+          acc[q] = mx_mfma<W::opsel(J)>(a.lo, b, acc[q], a.slo, sw);
+        }
+      }
+    });
+    if (c + 1 < nc) {
+#pragma unroll
+      for (int q = 0; q < NMAT; ++q) sb[q] = sbn[q];
+    }
+  }
+}
+
+constexpr int MX_ROWS = 64;  // weight rows per block (4 waves x 16)
+constexpr int MX_PF = 4;     // K steps of weights in flight per wave (gate/up: per matrix)
+static_assert(8 * MX_TOK <= 256 && MX_ROWS == 64, "gate/up requantisation: a quad per token and scale block");
+static_assert(16 % MX_PF == 0, "ring slots must repeat every 16 steps");
+
+// ---------------------------------------------------------------- gate / up
+
+// Block: one active expert x 64 rows of gate and up.  Writes a = bf16(silu(g) u) of
+// its rows for every token of the expert, re-quantised to two e4m3 terms for the
+// down projection (64 rows = two complete scale blocks per token).  Tokens go in
+// passes of MX_TOK with their latent rows staged in LDS.
+template <class W>
+__global__ void __launch_bounds__(256, 3) gateup_mx_kernel(MxArgs p) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  __shared__ float atile[MX_TOK][MX_ROWS + 1];
+  __shared__ int64_t srows[MX_TOK];
+  __shared__ int sslot[MX_TOK];
+  const int nrt = p.F / MX_ROWS;
+  const int slot = blockIdx.x / nrt;
+  const int4 tile = p.tiles[slot];
+  const int e = tile.x, r0 = tile.y, ne = tile.z;
+  if (e < 0) return;
+  const int rt = blockIdx.x - slot * nrt;
+  const int lane = lane_id(), wave = threadIdx.x / WAVE;
+  const int n = lane & 15, g = lane >> 4;
+  const int L = p.L, F = p.F, nks = L / 128;
+  const int f = rt * MX_ROWS + 16 * wave + n;  // weight row of this lane
+  const W w[2] = {W::make(p.blob, e, L, F, MAT_GATE, rt * 4 + wave, lane),
+                  W::make(p.blob, e, L, F, MAT_UP, rt * 4 + wave, lane)};
+  const ALds ad = alds(smem, L, MX_TOK);
+
+  for (int p0 = 0; p0 < ne; p0 += MX_TOK) {
+    const int ntok = ne - p0 < MX_TOK ? ne - p0 : MX_TOK;
+    if (threadIdx.x < MX_TOK) {
+      const int sl = threadIdx.x >= ntok ? -1 : ne == 1 ? tile.w : p.perm[r0 + p0 + threadIdx.x];
+      sslot[threadIdx.x] = sl;
+      srows[threadIdx.x] = sl >= 0 ? sl / p.k : 0;
+    }
+    __syncthreads();
+    // weights first: the wait for the staged rows then also covers the first steps
+    uint4 ring[2][MX_PF];
+#pragma unroll
+    for (int d = 0; d < MX_PF; ++d)
+      if (d < nks) {
+        ring[0][d] = w[0].load(d);
+        ring[1][d] = w[1].load(d);
+      }
+    stage_rows(ad, p.hq, srows, ntok, L);
+    __syncthreads();
+    f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    stream_group<W, 2, MX_PF>(w, ring, ad, n, ntok, L, g, acc);
+    // lane holds g, u of tile rows 4g+j for weight row f; rows < ntok are tokens
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int mm = 4 * g + j;
+      if (mm < ntok) {
+        const uint16_t ab = glu_bf16(acc[0][j], acc[1][j]);
+        atile[mm][16 * wave + n] = bf16f(ab);
+        if (p.a_bf16) p.a_bf16[(int64_t)sslot[mm] * F + f] = ab;
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x < 8 * MX_TOK) {
+      // a quad of lanes per (token, scale block), 8 GLU outputs per lane
+      const int mm = threadIdx.x >> 3, blk = (threadIdx.x >> 2) & 1, sub = threadIdx.x & 3;
+      if (mm < ntok) {
+        const int srow = sslot[mm];
+        float v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = atile[mm][32 * blk + 8 * sub + i];
+        uint32_t hi[2], lo[2], shi, slo;
+        quantize_quad8(v, hi, lo, shi, slo);
+        const int64_t off = (int64_t)srow * F + rt * MX_ROWS + 32 * blk + 8 * sub;
+        *reinterpret_cast<uint2*>(p.aq.hi + off) = make_uint2(hi[0], hi[1]);
+        *reinterpret_cast<uint2*>(p.aq.lo + off) = make_uint2(lo[0], lo[1]);
+        if (sub == 0) {
+          const int64_t soff = (int64_t)srow * (F / 32) + (rt * MX_ROWS) / 32 + blk;
+          p.aq.shi[soff] = (uint8_t)shi;
+          p.aq.slo[soff] = (uint8_t)slo;
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// -------------------------------------------------------------------- down
+
+// Block: one active expert x 64 rows of down; y[slot][l] for every token of the expert.
+template <class W>
+__global__ void __launch_bounds__(256) down_mx_kernel(MxArgs p) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  __shared__ int64_t srows[MX_TOK];
+  const int nrt = p.L / MX_ROWS;
+  const int slot = blockIdx.x / nrt;
+  const int4 tile = p.tiles[slot];
+  const int e = tile.x, r0 = tile.y, ne = tile.z;
+  if (e < 0) return;
+  const int rt = blockIdx.x - slot * nrt;
+  const int lane = lane_id(), wave = threadIdx.x / WAVE;
+  const int n = lane & 15, g = lane >> 4;
+  const int L = p.L, F = p.F, nks = F / 128;
+  const int l = rt * MX_ROWS + 16 * wave + n;
+  const W w[1] = {W::make(p.blob, e, L, F, MAT_DOWN, rt * 4 + wave, lane)};
+  const ALds ad = alds(smem, F, MX_TOK);
+
+  for (int p0 = 0; p0 < ne; p0 += MX_TOK) {
+    const int ntok = ne - p0 < MX_TOK ? ne - p0 : MX_TOK;
+    if (threadIdx.x < MX_TOK)
+      srows[threadIdx.x] = threadIdx.x >= ntok ? 0 : ne == 1 ? tile.w : p.perm[r0 + p0 + threadIdx.x];
+    __syncthreads();
+    uint4 ring[1][MX_PF];
+#pragma unroll
+    for (int d = 0; d < MX_PF; ++d)
+      if (d < nks) ring[0][d] = w[0].load(d);
+    stage_rows(ad, p.aq, srows, ntok, F);
+    __syncthreads();
+    f32x4 acc[1] = {{0.f, 0.f, 0.f, 0.f}};
+    stream_group<W, 1, MX_PF>(w, ring, ad, n, ntok, F, g, acc);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int mm = 4 * g + j;
+      if (mm < ntok) p.y[srows[mm] * L + l] = acc[0][j];
+    }
+    __syncthreads();
+  }
+}
+
+// Small batches (T*k <= 64): the down projection of every routed row and the weighted
+// combine in one kernel.  Block b owns latent rows 16b..16b+15 for all T*k rows t*k+j.
+// The rows are staged in LDS, up to DCM_WAVES at a time, one wave per row; y stays in
+// LDS and the block sums it per token in slot order in fp64,
+// z[t][l] = bf16(sum_j w[t][j] y[t*k+j][l]), exactly as the combine kernel.  With the
+// activations in LDS the registers go to a deep weight ring: 16 waves of DCM_PF steps
+// of 1 KB keep enough bytes in flight on every CU.  Only tile row 0 carries the routed
+// row; the result's row 0 is used.
+constexpr int DCM_SLOTS = 64;
+constexpr int DCM_WAVES = 16;
+constexpr int DCM_PF = 8;
+constexpr size_t DCM_LDS_MAX = 150 * 1024;
+static_assert(16 % DCM_PF == 0, "ring slots must repeat every 16 steps");
+// LDS of one staged row (hi and lo codes, hi and lo scales), padded to 16 bytes
+__host__ __device__ constexpr size_t dcm_row_bytes(int F) { return ((size_t)2 * F + F / 16 + 15) & ~(size_t)15; }
+__host__ __device__ constexpr int dcm_rows_per_pass(int F) {
+  return (int)(DCM_LDS_MAX / dcm_row_bytes(F)) < DCM_WAVES ? (int)(DCM_LDS_MAX / dcm_row_bytes(F)) : DCM_WAVES;
+}
+
+template <class W>
+__global__ void __launch_bounds__(DCM_WAVES * WAVE) down_combine_mx_kernel(MxArgs p, const int32_t* __restrict__ idx,
+                                                                         const float* __restrict__ w,
+                                                                         uint16_t* __restrict__ z) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  __shared__ float ys[DCM_SLOTS][16];
+  const int lane = lane_id(), wave = threadIdx.x / WAVE;
+  const int n = lane & 15, g = lane >> 4;
+  const int L = p.L, F = p.F, k = p.k, nks = F / 128;
+  const int nslot = (int)p.T * k;
+  const int S = dcm_rows_per_pass(F);
+  const size_t rb = dcm_row_bytes(F);
+  for (int s0 = 0; s0 < nslot; s0 += S) {
+    const int ns = nslot - s0 < S ? nslot - s0 : S;
+    const int s = s0 + wave;
+    const bool mine = wave < ns;
+    W wr[1];
+    uint4 ring[1][DCM_PF];
+    if (mine) {
+      wr[0] = W::make(p.blob, idx[s], L, F, MAT_DOWN, blockIdx.x, lane);
+#pragma unroll
+      for (int d = 0; d < DCM_PF; ++d)
+        if (d < nks) ring[0][d] = wr[0].load(d);
+    }
+    __syncthreads();  // the previous pass is done with the LDS rows
+    // row i of the pass at smem + i * rb: hi codes, lo codes, hi scales, lo scales
+    for (int c = threadIdx.x; c < ns * (F / 8); c += blockDim.x) {
+      const int i = c / (F / 8), q = c - i * (F / 8);
+      const int term = q / (F / 16), off = 16 * (q - term * (F / 16));
+      *reinterpret_cast<uint4*>(smem + i * rb + term * F + off) =
+          *reinterpret_cast<const uint4*>((term ? p.aq.lo : p.aq.hi) + (int64_t)(s0 + i) * F + off);
+    }
+    for (int c = threadIdx.x; c < ns * (F / 16); c += blockDim.x) {
+      const int i = c / (F / 16), q = c - i * (F / 16);
+      const int term = q / (F / 32), b = q - term * (F / 32);
+      smem[i * rb + 2 * F + term * (F / 32) + b] = (term ? p.aq.slo : p.aq.shi)[(int64_t)(s0 + i) * (F / 32) + b];
+    }
+    __syncthreads();
+    if (mine) {
+      uint8_t* row = smem + wave * rb;
+      const ALds ad{row, row + F, row + 2 * F, row + 2 * F + F / 32};
+      f32x4 acc[1] = {{0.f, 0.f, 0.f, 0.f}};
+      stream_group<W, 1, DCM_PF>(wr, ring, ad, n, 1, F, g, acc);
+      if (g == 0) ys[s][n] = acc[0][0];  // D[0][n]
+    }
+  }
+  __syncthreads();
+  for (int q = threadIdx.x; q < (int)p.T * 16; q += blockDim.x) {
+    const int t = q >> 4, nn = q & 15;
+    double acc = 0.0;
+    for (int j = 0; j < k; ++j) acc += (double)w[t * k + j] * (double)ys[t * k + j][nn];
+    z[(int64_t)t * L + blockIdx.x * 16 + nn] = f64_to_bf16(acc);
+  }
+}
+
+// ------------------------------------------------------------------ packing
+
+// One thread per 16-byte code unit or per scale dword of the packed layout.
+__global__ void __launch_bounds__(256) pack_experts_kernel(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
+                                                           int E, int L, int F) {
+  const int64_t mrec = (int64_t)F * L / 2 + (int64_t)F * L / 32;
+  const int64_t prec = packed_expert_bytes(L, F);
+  const int64_t gu = (int64_t)(F / 16) * packed_group_bytes(L);
+  // units per matrix: R/16 groups x (code tiles + scale tiles) x 64 lanes
+  auto units = [](int K, int R) -> int64_t { return (int64_t)(R / 16) * ((K / 128) + (K / 128 + 3) / 4) * 64; };
+  const int64_t u_gate = units(L, F), u_exp = 2 * u_gate + units(F, L);
+  const int64_t total = (int64_t)E * u_exp;
+  for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < total; u += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t e = u / u_exp;
+    int64_t r = u - e * u_exp;
+    const int mat = r < u_gate ? MAT_GATE : r < 2 * u_gate ? MAT_UP : MAT_DOWN;
+    r -= mat * u_gate;
+    const int K = mat == MAT_DOWN ? F : L, R = mat == MAT_DOWN ? L : F;
+    const int nks = K / 128, nsc = (nks + 3) / 4;
+    const int64_t per_grp = (int64_t)(nks + nsc) * 64;
+    const int grp = (int)(r / per_grp);
+    const int within = (int)(r - grp * per_grp);
+    const int tile = within / 64, lane = within % 64;
+    const int row = 16 * grp + (lane & 15), kb = lane >> 4;
+    const uint8_t* m = src + e * 3 * mrec + mat * mrec;
+    uint8_t* pg = dst + e * prec + (mat == MAT_GATE ? 0 : mat == MAT_UP ? gu : 2 * gu) +
+                  (int64_t)grp * packed_group_bytes(K);
+    if (tile < nks) {
+      *reinterpret_cast<uint4*>(pg + 1024 * tile + 16 * lane) =
+          *reinterpret_cast<const uint4*>(m + (int64_t)row * (K / 2) + 64 * tile + 16 * kb);
+    } else {
+      const int c = tile - nks;
+      const uint8_t* srow = m + (int64_t)R * (K / 2) + (int64_t)row * (K / 32);
+      uint32_t v = 0;
+      for (int j = 0; j < 4; ++j) {
+        const int s = 4 * c + j;
+        v |= (s < nks ? (uint32_t)srow[4 * s + kb] : 127u) << (8 * j);
+      }
+      *reinterpret_cast<uint32_t*>(pg + (int64_t)nks * 1024 + 256 * c + 4 * lane) = v;
+    }
+  }
+}
+
+hipError_t launch_pack_experts(const uint8_t* src, uint8_t* dst, int E, int L, int F, hipStream_t st) {
+  if (E == 0) return hipSuccess;
+  if (L % 128 || F % 128) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(pack_experts_kernel, dim3(8192), dim3(256), 0, st, src, dst, E, L, F);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ launchers
+
+hipError_t launch_gateup_mx(const MxArgs& p, hipStream_t st) {
+  if (p.T == 0 || p.max_active == 0) return hipSuccess;
+  if (p.F % MX_ROWS || p.L % 128) return hipErrorInvalidValue;
+  if (mx_lds_bytes(p.L) > MX_LDS_MAX) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(p.max_active * (p.F / MX_ROWS)));
+  if (p.packed)
+    hipLaunchKernelGGL(gateup_mx_kernel<PackedW>, grid, dim3(256), mx_lds_bytes(p.L), st, p);
+  else
+    hipLaunchKernelGGL(gateup_mx_kernel<RecordW>, grid, dim3(256), mx_lds_bytes(p.L), st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_down_mx(const MxArgs& p, hipStream_t st) {
+  if (p.T == 0 || p.max_active == 0) return hipSuccess;
+  if (p.L % MX_ROWS || p.F % 128) return hipErrorInvalidValue;
+  if (mx_lds_bytes(p.F) > MX_LDS_MAX) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(p.max_active * (p.L / MX_ROWS)));
+  if (p.packed)
+    hipLaunchKernelGGL(down_mx_kernel<PackedW>, grid, dim3(256), mx_lds_bytes(p.F), st, p);
+  else
+    hipLaunchKernelGGL(down_mx_kernel<RecordW>, grid, dim3(256), mx_lds_bytes(p.F), st, p);
+  return hipGetLastError();
+}
+
+bool down_combine_fits(int64_t T, int32_t k) { return T * k <= DCM_SLOTS; }
+
+hipError_t launch_down_combine_mx(const MxArgs& p, const int32_t* idx, const float* w, uint16_t* z,
+                                  hipStream_t st) {
+  if (p.T == 0) return hipSuccess;
+  if (!down_combine_fits(p.T, p.k) || p.L % 16 || p.F % 128 || dcm_rows_per_pass(p.F) < 1)
+    return hipErrorInvalidValue;
+  const int S = dcm_rows_per_pass(p.F);
+  const int nslot = (int)(p.T * p.k);
+  const size_t lds = (size_t)(nslot < S ? nslot : S) * dcm_row_bytes(p.F);
+  const dim3 grid((unsigned)(p.L / 16)), block(DCM_WAVES * WAVE);
+  const void* fn = p.packed ? reinterpret_cast<const void*>(&down_combine_mx_kernel<PackedW>)
+                            : reinterpret_cast<const void*>(&down_combine_mx_kernel<RecordW>);
+  const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)DCM_LDS_MAX);
+  if (e != hipSuccess) return e;
+  if (p.packed)
+    hipLaunchKernelGGL(down_combine_mx_kernel<PackedW>, grid, block, lds, st, p, idx, w, z);
+  else
+    hipLaunchKernelGGL(down_combine_mx_kernel<RecordW>, grid, block, lds, st, p, idx, w, z);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------- activation quantisation
+
+__global__ void __launch_bounds__(256) quantize_rows_kernel(const uint16_t* __restrict__ src, int64_t rows, int K,
+                                                            QRows q) {
+  quantize_quads(src, q, rows * K, (int64_t)blockIdx.x * blockDim.x + threadIdx.x, (int64_t)gridDim.x * blockDim.x);
+}
+
+hipError_t launch_quantize_rows(const uint16_t* src, int64_t rows, int K, const QRows& q, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  if (K % 32) return hipErrorInvalidValue;
+  int64_t blocks = ceil_div(rows * (K / 8), 256);
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(quantize_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, st, src, rows, K, q);
+  return hipGetLastError();
+}
+
+}  // namespace moe

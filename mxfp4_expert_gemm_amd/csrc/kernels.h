@@ -44,34 +44,68 @@ struct RouteArgs {
   float* w;                  // [T][k]
   float* logits_out;         // nullable [T][E] biased logits
   int32_t* stats;            // [4] counters: tokens needing recompute, logits recomputed, Kulisch uses
+  const uint16_t* h;         // nullable [T][L] latent rows to quantise for the experts
+  int32_t L;
+  QRows hq;
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t st);
+
+// Grouping of routed rows by expert.  tiles[0, n_active) = {expert, offset, count, first
+// row} of the active experts, ascending; tiles[n_active, max_tiles) = {-1, 0, 0, -1}.
+struct PermOut {
+  int32_t* counts;    // [E]
+  int32_t* offsets;   // [E+1]
+  int32_t* perm;      // [T*k]
+  int4* tiles;        // [max_tiles]
+  int32_t* n_active;  // [1]
+  int32_t max_tiles;  // min(E, T*k)
+};
+// routing, quantisation of h and the grouping in one block, for T <= ROUTE_FUSED_TOKENS
+constexpr int ROUTE_FUSED_TOKENS = 8;
+hipError_t launch_route_permute_small(const RouteArgs& a, const PermOut& p, hipStream_t st);
+// grouping of the rows of routed tokens (distinct valid experts per token),
+// T <= 64 and T*k <= ROUTE_SMALL_ROWS
+constexpr int ROUTE_SMALL_ROWS = 1024;
+constexpr int ROUTE_PLACE_TOKENS = 64;
+hipError_t launch_place_rows(const int32_t* idx, int64_t T, int32_t k, int32_t E, const PermOut& p,
+                             hipStream_t st);
 
 // ---- permute.hip
 constexpr int PERM_CHUNK = 2048;
 size_t permute_ws_bytes(int64_t rows, int32_t E);
-hipError_t launch_permute(const int32_t* idx, int64_t rows, int32_t E, int32_t* counts, int32_t* offsets,
-                          int32_t* perm, int32_t* active, int32_t* n_active, void* ws, hipStream_t st);
+hipError_t launch_permute(const int32_t* idx, int64_t rows, int32_t E, const PermOut& out, void* ws,
+                          hipStream_t st);
 
-// ---- expert_gemv.hip
-struct ExpertArgs {
-  const uint16_t* h;         // [T][L] bf16
+// ---- expert_mfma.hip
+// Packed expert layout (moe_pack_experts): bytes of one 16-row group of a matrix with K
+// columns, and of one expert.
+__host__ __device__ constexpr int64_t packed_group_bytes(int K) {
+  return (int64_t)(K / 128) * 1024 + (int64_t)((K / 128 + 3) / 4) * 256;
+}
+__host__ __device__ constexpr int64_t packed_expert_bytes(int L, int F) {
+  return 2 * (int64_t)(F / 16) * packed_group_bytes(L) + (int64_t)(L / 16) * packed_group_bytes(F);
+}
+hipError_t launch_pack_experts(const uint8_t* src, uint8_t* dst, int E, int L, int F, hipStream_t st);
+
+struct MxArgs {
   const uint8_t* blob;
+  int32_t packed;            // 1: blob in the packed layout, 0: checkpoint records
   int32_t L, F, k;
   int64_t T;
-  const int32_t* counts;     // [E]
-  const int32_t* offsets;    // [E+1]
-  const int32_t* perm;       // [T*k]
-  const int32_t* active;     // [E] active experts, ascending
-  const int32_t* n_active;   // [1]
+  const int4* tiles;         // [max_active] {expert, offset in perm, rows, first row}; expert -1: none
   int32_t max_active;        // grid bound: min(E, T*k)
-  uint16_t* a;               // [T*k][F] bf16, permuted row order
-  float* y;                  // [T*k][L] fp32, slot order (row t*k+j)
+  const int32_t* perm;       // [T*k] slots t*k+j grouped by expert
+  QRows hq;                  // [T][L] latent rows h, two-term e4m3
+  QRows aq;                  // [T*k][F] GLU outputs by slot, two-term e4m3
+  uint16_t* a_bf16;          // nullable [T*k][F] GLU outputs by slot, bf16
+  float* y;                  // [T*k][L] down outputs by slot
 };
-hipError_t launch_expert_gateup(const ExpertArgs& a, hipStream_t st);
-hipError_t launch_expert_down(const ExpertArgs& a, hipStream_t st);
-hipError_t launch_unpermute_rows(const uint16_t* a_perm, const int32_t* perm, int64_t rows, int32_t F,
-                                 uint16_t* a_slot, hipStream_t st);
+hipError_t launch_gateup_mx(const MxArgs& p, hipStream_t st);
+hipError_t launch_down_mx(const MxArgs& p, hipStream_t st);
+bool down_combine_fits(int64_t T, int32_t k);
+hipError_t launch_down_combine_mx(const MxArgs& p, const int32_t* idx, const float* w, uint16_t* z,
+                                  hipStream_t st);
+hipError_t launch_quantize_rows(const uint16_t* src, int64_t rows, int K, const QRows& q, hipStream_t st);
 
 // ---- combine.hip
 hipError_t launch_combine(const float* y, const float* w, int64_t T, int32_t k, int32_t L, uint16_t* z,

@@ -15,9 +15,12 @@ namespace moe {
 constexpr int PERM_THREADS = 1024;
 constexpr uint32_t PAD_KEY = 0xFFFFFFFFu;
 
+// workspace: chunk counts [nchunks][E], then the tile slot of each expert [E]
+static size_t cc_bytes(int64_t rows, int32_t E) {
+  return align_up((size_t)ceil_div(rows, PERM_CHUNK) * (size_t)E * sizeof(int32_t), 256);
+}
 size_t permute_ws_bytes(int64_t rows, int32_t E) {
-  int64_t nchunks = ceil_div(rows, PERM_CHUNK);
-  return align_up((size_t)nchunks * (size_t)E * sizeof(int32_t), 256);
+  return cc_bytes(rows, E) + align_up((size_t)E * sizeof(int32_t), 256);
 }
 
 // exclusive scan of n ints in LDS, in place; returns the total.  All threads call it.
@@ -70,8 +73,9 @@ __global__ void __launch_bounds__(PERM_THREADS) perm_count_kernel(const int32_t*
 __global__ void __launch_bounds__(PERM_THREADS) perm_scan_kernel(int32_t* __restrict__ cc, int nchunks,
                                                                  int32_t E, int32_t* __restrict__ counts,
                                                                  int32_t* __restrict__ offsets,
-                                                                 int32_t* __restrict__ active,
-                                                                 int32_t* __restrict__ n_active) {
+                                                                 int4* __restrict__ tiles,
+                                                                 int32_t* __restrict__ n_active, int max_tiles,
+                                                                 int32_t* __restrict__ slot_of) {
   extern __shared__ int sh[];
   int* tot = sh;               // E
   int* act = sh + E;           // E
@@ -92,9 +96,11 @@ __global__ void __launch_bounds__(PERM_THREADS) perm_scan_kernel(int32_t* __rest
   int nact = block_exclusive_scan(act, E, partial);
   for (int e = threadIdx.x; e < E; e += PERM_THREADS) {
     offsets[e] = tot[e];
-    if (counts[e] > 0) active[act[e]] = e;
+    if (counts[e] > 0) tiles[act[e]] = make_int4(e, tot[e], counts[e], -1);  // first row: scatter
+    slot_of[e] = act[e];
     for (int c = 0; c < nchunks; ++c) cc[(int64_t)c * E + e] += tot[e];
   }
+  for (int sl = nact + threadIdx.x; sl < max_tiles; sl += PERM_THREADS) tiles[sl] = make_int4(-1, 0, 0, -1);
   if (threadIdx.x == 0) {
     offsets[E] = total;
     *n_active = nact;
@@ -122,7 +128,10 @@ __device__ void bitonic_sort_keys(uint32_t* keys) {
 __global__ void __launch_bounds__(PERM_THREADS) perm_scatter_kernel(const int32_t* __restrict__ idx,
                                                                     int64_t rows, int32_t E,
                                                                     const int32_t* __restrict__ cbase,
-                                                                    int32_t* __restrict__ perm) {
+                                                                    const int32_t* __restrict__ offsets,
+                                                                    const int32_t* __restrict__ slot_of,
+                                                                    int32_t* __restrict__ perm,
+                                                                    int4* __restrict__ tiles) {
   extern __shared__ int sh[];
   uint32_t* keys = reinterpret_cast<uint32_t*>(sh);  // PERM_CHUNK
   int* sstart = sh + PERM_CHUNK;                     // E
@@ -146,7 +155,9 @@ __global__ void __launch_bounds__(PERM_THREADS) perm_scatter_kernel(const int32_
     uint32_t key = keys[p];
     if (key != PAD_KEY) {
       uint32_t e = key >> 11, i = key & (PERM_CHUNK - 1);
-      perm[cbase[(int64_t)blockIdx.x * E + e] + (p - sstart[e])] = (int32_t)(base + i);
+      const int pos = cbase[(int64_t)blockIdx.x * E + e] + (p - sstart[e]);
+      perm[pos] = (int32_t)(base + i);
+      if (pos == offsets[e]) tiles[slot_of[e]].w = (int32_t)(base + i);
     }
   }
 }
@@ -157,14 +168,16 @@ __global__ void __launch_bounds__(PERM_THREADS) perm_small_kernel(const int32_t*
                                                                   int32_t* __restrict__ counts,
                                                                   int32_t* __restrict__ offsets,
                                                                   int32_t* __restrict__ perm,
-                                                                  int32_t* __restrict__ active,
-                                                                  int32_t* __restrict__ n_active) {
+                                                                  int4* __restrict__ tiles,
+                                                                  int32_t* __restrict__ n_active,
+                                                                  int max_tiles) {
   extern __shared__ int sh[];
   uint32_t* keys = reinterpret_cast<uint32_t*>(sh);  // PERM_CHUNK
   int* hist = sh + PERM_CHUNK;                       // E
   int* act = hist + E;                               // E
   int* sstart = act + E;                             // E
-  int* partial = sstart + E;                         // PERM_THREADS
+  int* cnt = sstart + E;                             // E
+  int* partial = cnt + E;                            // PERM_THREADS
   for (int e = threadIdx.x; e < E; e += PERM_THREADS) hist[e] = 0;
   __syncthreads();
   for (int i = threadIdx.x; i < PERM_CHUNK; i += PERM_THREADS) {
@@ -176,15 +189,14 @@ __global__ void __launch_bounds__(PERM_THREADS) perm_small_kernel(const int32_t*
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += PERM_THREADS) {
     counts[e] = hist[e];
+    cnt[e] = hist[e];
     act[e] = hist[e] > 0;
   }
   __syncthreads();
   int total = block_exclusive_scan(hist, E, partial);
   int nact = block_exclusive_scan(act, E, partial);
-  for (int e = threadIdx.x; e < E; e += PERM_THREADS) {
-    offsets[e] = hist[e];
-    if (counts[e] > 0) active[act[e]] = e;
-  }
+  for (int e = threadIdx.x; e < E; e += PERM_THREADS) offsets[e] = hist[e];
+  for (int sl = nact + threadIdx.x; sl < max_tiles; sl += PERM_THREADS) tiles[sl] = make_int4(-1, 0, 0, -1);
   if (threadIdx.x == 0) {
     offsets[E] = total;
     *n_active = nact;
@@ -203,30 +215,33 @@ __global__ void __launch_bounds__(PERM_THREADS) perm_small_kernel(const int32_t*
     if (key != PAD_KEY) {
       uint32_t e = key >> 11, i = key & (PERM_CHUNK - 1);
       perm[hist[e] + (p - sstart[e])] = (int32_t)i;
+      if (p == sstart[e]) tiles[act[e]] = make_int4((int)e, hist[e], cnt[e], (int32_t)i);
     }
   }
 }
 
-hipError_t launch_permute(const int32_t* idx, int64_t rows, int32_t E, int32_t* counts, int32_t* offsets,
-                          int32_t* perm, int32_t* active, int32_t* n_active, void* ws, hipStream_t st) {
+hipError_t launch_permute(const int32_t* idx, int64_t rows, int32_t E, const PermOut& o, void* ws,
+                          hipStream_t st) {
   if (rows <= PERM_CHUNK) {
-    size_t lds = (PERM_CHUNK + 3 * (size_t)E + PERM_THREADS) * sizeof(int);
-    hipLaunchKernelGGL(perm_small_kernel, dim3(1), dim3(PERM_THREADS), lds, st, idx, rows, E, counts, offsets,
-                       perm, active, n_active);
+    size_t lds = (PERM_CHUNK + 4 * (size_t)E + PERM_THREADS) * sizeof(int);
+    hipLaunchKernelGGL(perm_small_kernel, dim3(1), dim3(PERM_THREADS), lds, st, idx, rows, E, o.counts, o.offsets,
+                       o.perm, o.tiles, o.n_active, o.max_tiles);
     return hipGetLastError();
   }
   int nchunks = (int)ceil_div(rows, PERM_CHUNK);
   int32_t* cc = reinterpret_cast<int32_t*>(ws);
+  int32_t* slot_of = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + cc_bytes(rows, E));
   hipLaunchKernelGGL(perm_count_kernel, dim3(nchunks), dim3(PERM_THREADS), (size_t)E * sizeof(int), st, idx,
                      rows, E, cc);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(PERM_THREADS), (2 * (size_t)E + PERM_THREADS) * sizeof(int),
-                     st, cc, nchunks, E, counts, offsets, active, n_active);
+                     st, cc, nchunks, E, o.counts, o.offsets, o.tiles, o.n_active, o.max_tiles, slot_of);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(perm_scatter_kernel, dim3(nchunks), dim3(PERM_THREADS),
-                     (PERM_CHUNK + (size_t)E) * sizeof(int), st, idx, rows, E, cc, perm);
+                     (PERM_CHUNK + (size_t)E) * sizeof(int), st, idx, rows, E, cc, o.offsets, slot_of, o.perm,
+                     o.tiles);
   return hipGetLastError();
 }
 

@@ -186,123 +186,198 @@ __device__ float exact_dot_wave(const uint16_t* __restrict__ x, const uint16_t* 
   return __shfl(r, 0);
 }
 
-// ---- the routing kernel
+// ---- selection by keys
 
-__global__ void __launch_bounds__(256) route_kernel(RouteArgs a) {
-  __shared__ WaveScratch scratch[4];
+// neighbouring floats (finite inputs; the infinities stay put)
+__device__ __forceinline__ float next_down(float f) {
+  if (f != f || f == -__builtin_inff()) return f;
+  if (f == 0.f) return -__uint_as_float(1u);
+  uint32_t u = __float_as_uint(f);
+  return __uint_as_float(f > 0.f ? u - 1u : u + 1u);
+}
+__device__ __forceinline__ float next_up(float f) { return -next_down(-f); }
+
+// order-preserving 32-bit key of a float: larger value -> larger key; -0 == +0;
+// NaN maps to 1, below every number (every number's key is >= 0x007FFFFF); 0 is
+// reserved for "not a candidate".
+__device__ __forceinline__ uint32_t order_key(float v) {
+  if (v != v) return 1u;
+  uint32_t u = __float_as_uint(v == 0.f ? 0.f : v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Marks in `sel` the kk largest keys of the wave (ties to the lower expert index,
+// e = 64 i + lane).  Keys of 0 are never taken when at least kk keys are nonzero.
+// Radix select on the key bits with ballot counts: no cross-lane data movement.
+__device__ __forceinline__ uint32_t select_top(const uint32_t (&key)[ROUTE_MAXI], int kk) {
+  uint32_t tau = 0;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t cand = tau | (1u << b);
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < ROUTE_MAXI; ++i) cnt += __popcll(__ballot(key[i] >= cand));
+    if (cnt >= kk) tau = cand;
+  }
+  uint32_t sel = 0;
+  int need = kk;
+#pragma unroll
+  for (int i = 0; i < ROUTE_MAXI; ++i) {
+    const bool gt = key[i] > tau;
+    need -= __popcll(__ballot(gt));
+    if (gt) sel |= 1u << i;
+  }
   const int lane = lane_id();
-  const int wave = threadIdx.x / WAVE;
-  const int64_t t = (int64_t)blockIdx.x * 4 + wave;
-  if (t >= a.T) return;
-  const int E = a.E, k = a.k;
-  const int NI = (E + WAVE - 1) / WAVE;
-  const bool topk_mode = a.exact_logits != nullptr;
-  WaveScratch* ws = &scratch[wave];
+#pragma unroll
+  for (int i = 0; i < ROUTE_MAXI; ++i) {
+    unsigned long long m = __ballot(key[i] == tau && tau != 0u);
+    unsigned long long take = 0;
+    while (need > 0 && m) {
+      unsigned long long low = m & (0ull - m);
+      take |= low;
+      m ^= low;
+      --need;
+    }
+    if ((take >> lane) & 1ull) sel |= 1u << i;
+  }
+  return sel;
+}
 
-  double cen[ROUTE_MAXI], rad[ROUTE_MAXI];
-  float val[ROUTE_MAXI];  // the logit used for weights and export
-  double xn = topk_mode ? 0.0 : sqrt((double)a.xnorm2[t]);
+// ---- routing of one token by one wave
+
+
+// Per-wave LDS of the routing: Kulisch digits, the candidate list of the fast path and
+// the selected (expert, logit) pairs in output order.
+constexpr int ROUTE_CAND = WAVE;
+struct RouteLds {
+  WaveScratch ks;
+  uint32_t ckey[ROUTE_CAND];
+  int cidx[ROUTE_CAND];
+  float cval[ROUTE_CAND], crad[ROUTE_CAND];
+  int oidx[WAVE];
+  float oval[WAVE];
+};
+
+// Writes idx/w of token t from the k selected (expert, logit) pairs in L->oidx/oval,
+// ascending expert order.  Renormalised weights: softmax over the k logits (max and a
+// fixed DPP tree, the same in every path).  Otherwise: over all E logits, whose
+// max and sum over experts the caller passes in.
+__device__ __forceinline__ void emit_topk(const RouteArgs& a, int64_t t, const RouteLds* L, float mx_all,
+                                          float den_all) {
+  const int lane = lane_id(), k = a.k;
+  const bool mine = lane < k;
+  const float v = mine ? L->oval[lane] : -__builtin_inff();
+  float mx = mx_all, den = den_all;
+  float ex;
+  if (a.renormalize) {
+    mx = wave_max_dpp(v);
+    ex = mine ? expf(v - mx) : 0.f;
+    den = wave_sum_dpp(ex);
+  } else {
+    ex = expf(v - mx);
+  }
+  if (mine) {
+    a.idx[t * k + lane] = L->oidx[lane];
+    a.w[t * k + lane] = ex / den;
+  }
+}
+
+// max and sum of exp(v - max) over all experts of the lane arrays (softmax over E)
+__device__ __forceinline__ void softmax_all(const float (&val)[ROUTE_MAXI], int E, float& mx, float& den) {
+  const int lane = lane_id();
+  mx = -__builtin_inff();
+#pragma unroll
+  for (int i = 0; i < ROUTE_MAXI; ++i)
+    if (i * WAVE + lane < E) mx = fmaxf(mx, val[i]);
+  mx = wave_max_dpp(mx);
+  den = 0.f;
+#pragma unroll
+  for (int i = 0; i < ROUTE_MAXI; ++i)
+    if (i * WAVE + lane < E) den += expf(val[i] - mx);
+  den = wave_sum_dpp(den);
+}
+
+// General path: selection over every expert by radix select on the keys, certification,
+// exact recompute of the ambiguous logits.  Kept out of line: it runs only when the
+// fast path below cannot decide (many ties, an uncertain boundary, MOE_ROUTE_EXACT_ALL).
+__device__ __noinline__ void route_token_general(const RouteArgs& a, int64_t t, RouteLds* L) {
+  const int lane = lane_id();
+  const int E = a.E, k = a.k;
+  const bool topk_mode = a.exact_logits != nullptr;
+  float val[ROUTE_MAXI];      // logit used for weights and export (exact where recomputed)
+  float lo[ROUTE_MAXI], hi[ROUTE_MAXI];
+  uint32_t key[ROUTE_MAXI];
+  const double xn = topk_mode ? 0.0 : sqrt((double)a.xnorm2[t]);
   const double abs_pad = (double)a.d * 0x1p-125;
 #pragma unroll
   for (int i = 0; i < ROUTE_MAXI; ++i) {
-    int e = i * WAVE + lane;
-    cen[i] = -__builtin_inf();
-    rad[i] = 0.0;
+    const int e = i * WAVE + lane;
     val[i] = -__builtin_inff();
-    if (i < NI && e < E) {
+    lo[i] = -__builtin_inff();
+    hi[i] = -__builtin_inff();
+    key[i] = 0u;
+    if (e < E) {
       if (topk_mode) {
-        float v = a.exact_logits[t * E + e];
-        val[i] = v;
-        cen[i] = (double)v;  // NaN handled by ranks_before
+        val[i] = a.exact_logits[t * E + e];
+        key[i] = order_key(val[i]);
       } else {
-        float lf = a.logits_fast[t * E + e];
-        float b = a.bias ? a.bias[t * a.bias_stride + e] : 0.f;
+        const float lf = a.logits_fast[t * E + e];
+        const float b = a.bias ? a.bias[t * a.bias_stride + e] : 0.f;
         val[i] = lf + b;  // the fast biased logit, one fp32 rounding
-        double beta = a.gamma * xn * sqrt((double)a.wnorm2[e]) * (1.0 + 0x1p-20) + abs_pad;
-        double r = beta + 0x1p-21 * ((double)fabsf(lf) + (double)fabsf(b));
+        const double r = a.gamma * xn * sqrt((double)a.wnorm2[e]) * (1.0 + 0x1p-20) + abs_pad +
+                         0x1p-21 * ((double)fabsf(lf) + (double)fabsf(b));
+        const double c = (double)lf + (double)b;
         if (__builtin_isfinite(lf) && __builtin_isfinite(b) && __builtin_isfinite(r)) {
-          cen[i] = (double)lf + (double)b;
-          rad[i] = r;
-        } else {
-          cen[i] = -__builtin_inf();
-          rad[i] = __builtin_inf();
+          // outward-rounded fp32 ends of the interval holding the exact biased logit
+          float l32 = (float)(c - r), h32 = (float)(c + r);
+          if ((double)l32 > c - r) l32 = next_down(l32);
+          if ((double)h32 < c + r) h32 = next_up(h32);
+          lo[i] = l32;
+          hi[i] = h32;
+          key[i] = order_key((float)c);
+        } else {  // unknown: must be recomputed if it can matter
+          lo[i] = -__builtin_inff();
+          hi[i] = __builtin_inff();
+          key[i] = order_key(-__builtin_inff());
         }
       }
     }
   }
 
-  uint32_t sel = 0;
-  if (topk_mode) {
-    for (int j = 0; j < k; ++j) {
-      double bv = __builtin_nan("");
-      int bi = 0x7FFFFFFF;
-#pragma unroll
-      for (int i = 0; i < ROUTE_MAXI; ++i) {
-        int e = i * WAVE + lane;
-        if (i < NI && e < E && !(sel >> i & 1u) && ranks_before(cen[i], e, bv, bi)) {
-          bv = cen[i];
-          bi = e;
-        }
-      }
-      wave_best(bv, bi);
-      if (bi < E && (bi & (WAVE - 1)) == lane) sel |= 1u << (bi / WAVE);
-    }
-  } else {
-    // tentative top-k by centre
-    for (int j = 0; j < k; ++j) {
-      double bv = __builtin_nan("");
-      int bi = 0x7FFFFFFF;
-#pragma unroll
-      for (int i = 0; i < ROUTE_MAXI; ++i) {
-        int e = i * WAVE + lane;
-        if (i < NI && e < E && !(sel >> i & 1u) && ranks_before(cen[i], e, bv, bi)) {
-          bv = cen[i];
-          bi = e;
-        }
-      }
-      wave_best(bv, bi);
-      if (bi < E && (bi & (WAVE - 1)) == lane) sel |= 1u << (bi / WAVE);
-    }
-    double Mloc = __builtin_inf(), mloc = -__builtin_inf();
+  uint32_t sel = select_top(key, k);
+  if (!topk_mode) {
+    float mloc = -__builtin_inff(), Mloc = __builtin_inff();
 #pragma unroll
     for (int i = 0; i < ROUTE_MAXI; ++i) {
-      int e = i * WAVE + lane;
-      if (i < NI && e < E) {
-        double lo = rad[i] == __builtin_inf() ? -__builtin_inf() : cen[i] - rad[i];
-        double hi = rad[i] == __builtin_inf() ? __builtin_inf() : cen[i] + rad[i];
-        if (sel >> i & 1u) Mloc = fmin(Mloc, lo);
-        else mloc = fmax(mloc, hi);
+      const int e = i * WAVE + lane;
+      if (e < E) {
+        if ((sel >> i) & 1u) Mloc = fminf(Mloc, lo[i]);
+        else mloc = fmaxf(mloc, hi[i]);
       }
     }
-    const double M = wave_min_d(Mloc), m = wave_max_d(mloc);
+    const float M = wave_min_dpp(Mloc), m = wave_max_dpp(mloc);
     const bool all = (a.flags & MOE_ROUTE_EXACT_ALL) != 0;
     if (all || (k < E && !(M > m))) {
-      // certainly-in experts keep their place; the ambiguous ones are recomputed
       uint32_t amb = 0, cin = 0;
 #pragma unroll
       for (int i = 0; i < ROUTE_MAXI; ++i) {
-        int e = i * WAVE + lane;
-        if (i < NI && e < E) {
-          double lo = rad[i] == __builtin_inf() ? -__builtin_inf() : cen[i] - rad[i];
-          double hi = rad[i] == __builtin_inf() ? __builtin_inf() : cen[i] + rad[i];
+        const int e = i * WAVE + lane;
+        if (e < E) {
           if (all) amb |= 1u << i;
-          else if ((sel >> i & 1u) && lo > m) cin |= 1u << i;
-          else if (lo <= m && hi >= M) amb |= 1u << i;
+          else if (((sel >> i) & 1u) && lo[i] > m) cin |= 1u << i;
+          else if (lo[i] <= m && hi[i] >= M) amb |= 1u << i;
         }
       }
-      int n_in = 0;
-#pragma unroll
-      for (int i = 0; i < ROUTE_MAXI; ++i) n_in += __popcll(__ballot((cin >> i) & 1u));
-      int n_amb = 0;
+      int n_in = 0, n_amb = 0;
 #pragma unroll
       for (int i = 0; i < ROUTE_MAXI; ++i) {
+        n_in += __popcll(__ballot((cin >> i) & 1u));
         unsigned long long bal = __ballot((amb >> i) & 1u);
         n_amb += __popcll(bal);
         while (bal) {
-          int l = __ffsll((long long)bal) - 1;
+          const int l = __ffsll((long long)bal) - 1;
           bal &= bal - 1;
-          int e = i * WAVE + l;
-          float v = exact_dot_wave(a.x + t * a.d, a.router_w + (int64_t)e * a.d, a.d, ws, a.stats);
+          const int e = i * WAVE + l;
+          float v = exact_dot_wave(a.x + t * a.d, a.router_w + (int64_t)e * a.d, a.d, &L->ks, a.stats);
           if (a.bias) v = v + a.bias[t * a.bias_stride + e];
           if (lane == l) val[i] = v;
         }
@@ -311,63 +386,301 @@ __global__ void __launch_bounds__(256) route_kernel(RouteArgs a) {
         atomicAdd(&a.stats[0], 1);
         atomicAdd(&a.stats[1], n_amb);
       }
-      // final set: certainly-in plus the best (k - n_in) of the ambiguous by exact value
-      sel = cin;
-      for (int j = n_in; j < k; ++j) {
-        double bv = __builtin_nan("");
-        int bi = 0x7FFFFFFF;
+      uint32_t ekey[ROUTE_MAXI];
 #pragma unroll
-        for (int i = 0; i < ROUTE_MAXI; ++i) {
-          int e = i * WAVE + lane;
-          if ((amb >> i & 1u) && !(sel >> i & 1u) && ranks_before((double)val[i], e, bv, bi)) {
-            bv = (double)val[i];
-            bi = e;
-          }
-        }
-        wave_best(bv, bi);
-        if (bi < E && (bi & (WAVE - 1)) == lane) sel |= 1u << (bi / WAVE);
-      }
+      for (int i = 0; i < ROUTE_MAXI; ++i) ekey[i] = ((amb >> i) & 1u) ? order_key(val[i]) : 0u;
+      sel = cin | select_top(ekey, k - n_in);
     }
   }
 
-  // weights over the selected logits (or all when not renormalising)
-  float mx = -__builtin_inff();
-#pragma unroll
-  for (int i = 0; i < ROUTE_MAXI; ++i) {
-    int e = i * WAVE + lane;
-    bool use = a.renormalize ? (sel >> i & 1u) : (i < NI && e < E);
-    if (use) mx = fmaxf(mx, val[i]);
-  }
-  mx = wave_max(mx);
-  float den = 0.f;
-#pragma unroll
-  for (int i = 0; i < ROUTE_MAXI; ++i) {
-    int e = i * WAVE + lane;
-    bool use = a.renormalize ? (sel >> i & 1u) : (i < NI && e < E);
-    if (use) den += expf(val[i] - mx);
-  }
-  den = wave_sum(den);
-
-  // ascending ids, then weights; export logits
+  // selected pairs in ascending expert order, then the weights
   int base = 0;
 #pragma unroll
   for (int i = 0; i < ROUTE_MAXI; ++i) {
-    unsigned long long bal = __ballot((sel >> i) & 1u);
+    const unsigned long long bal = __ballot((sel >> i) & 1u);
     if ((sel >> i) & 1u) {
-      int pos = base + __popcll(bal & ((1ull << lane) - 1ull));
-      a.idx[t * k + pos] = i * WAVE + lane;
-      a.w[t * k + pos] = expf(val[i] - mx) / den;
+      const int pos = base + __popcll(bal & ((1ull << lane) - 1ull));
+      L->oidx[pos] = i * WAVE + lane;
+      L->oval[pos] = val[i];
     }
     base += __popcll(bal);
-    int e = i * WAVE + lane;
-    if (a.logits_out && i < NI && e < E) a.logits_out[t * E + e] = val[i];
+    const int e = i * WAVE + lane;
+    if (a.logits_out && e < E) a.logits_out[t * E + e] = val[i];
   }
+  float mx_all = 0.f, den_all = 1.f;
+  if (!a.renormalize) softmax_all(val, E, mx_all, den_all);
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  emit_topk(a, t, L, mx_all, den_all);
+}
+
+// k-th largest of one key per lane (radix select with ballots), k <= WAVE
+__device__ __forceinline__ uint32_t kth_of_lanes(uint32_t v, int k) {
+  uint32_t tau = 0;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t cand = tau | (1u << b);
+    if (__popcll(__ballot(v >= cand)) >= k) tau = cand;
+  }
+  return tau;
+}
+
+// Routing of token t (fills idx/w, ascending ids, and optionally logits_out).
+//
+// Fast path.  The keys of the fast biased logits c_e are cut at tau, the k-th largest
+// of the 64 per-lane maxima: at least k keys reach tau, so the k best are among the
+// candidates (key >= tau), usually a few dozen.  The candidates are ranked against
+// each other, one per lane, and the selection is certified as in the general path
+// with fp32 interval ends: radius R_e = gamma' |x||w_e| + pad' + 2^-20 (|lf| + |b|),
+// with gamma' = gamma (1 + 2^-18) and pad' = d 2^-124, covers the radius of the
+// general path plus the roundings of c_e = lf + b and of R_e itself (a few ulp of
+// 2^-24 each, the square roots within one ulp), and the ends c - R and c + R are
+// pushed one ulp outwards.  More than 64
+// candidates or an uncertified boundary go to the general path, which starts over.
+__device__ void route_token(const RouteArgs& a, int64_t t, RouteLds* L) {
+  const int lane = lane_id();
+  const int E = a.E, k = a.k;
+  const bool topk_mode = a.exact_logits != nullptr;
+  if (a.flags & MOE_ROUTE_EXACT_ALL) {
+    route_token_general(a, t, L);
+    return;
+  }
+  float c[ROUTE_MAXI], R[ROUTE_MAXI];
+  uint32_t key[ROUTE_MAXI];
+  const float xn = topk_mode ? 0.f : __builtin_amdgcn_sqrtf(a.xnorm2[t]);  // within 1 ulp
+  const float gam = (float)a.gamma * (1.f + 0x1p-18f) * xn;
+  const float pad = (float)a.d * 0x1p-124f;
+  uint32_t kmax = 0;
+#pragma unroll
+  for (int i = 0; i < ROUTE_MAXI; ++i) {
+    const int e = i * WAVE + lane;
+    c[i] = -__builtin_inff();
+    R[i] = 0.f;
+    key[i] = 0u;
+    if (e < E) {
+      if (topk_mode) {
+        c[i] = a.exact_logits[t * E + e];
+      } else {
+        const float lf = a.logits_fast[t * E + e];
+        const float b = a.bias ? a.bias[t * a.bias_stride + e] : 0.f;
+        c[i] = lf + b;
+        R[i] = gam * __builtin_amdgcn_sqrtf(a.wnorm2[e]) + pad + 0x1p-20f * (fabsf(lf) + fabsf(b));
+        if (!(__builtin_isfinite(c[i]) && __builtin_isfinite(R[i]))) {
+          c[i] = -__builtin_inff();  // unknown: the general path recomputes it if it can matter
+          R[i] = __builtin_inff();
+        }
+      }
+      key[i] = order_key(c[i]);
+      kmax = key[i] > kmax ? key[i] : kmax;
+    }
+  }
+  const uint32_t tau = kth_of_lanes(kmax, k);
+  // candidates: keys >= tau, compacted in (lane, i) order
+  int mine = 0;
+#pragma unroll
+  for (int i = 0; i < ROUTE_MAXI; ++i) mine += (key[i] != 0u && key[i] >= tau);
+  int n_c = 0;
+  int pos = wave_excl_scan(mine, n_c);
+  if (n_c > ROUTE_CAND) {
+    route_token_general(a, t, L);
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < ROUTE_MAXI; ++i)
+    if (key[i] != 0u && key[i] >= tau) {
+      L->ckey[pos] = key[i];
+      L->cidx[pos] = i * WAVE + lane;
+      L->cval[pos] = c[i];
+      L->crad[pos] = R[i];
+      ++pos;
+    }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  // rank of this lane's candidate: (key descending, expert ascending)
+  const bool live = lane < n_c;
+  const uint32_t mk = live ? L->ckey[lane] : 0u;
+  const int me = live ? L->cidx[lane] : 0x7FFFFFFF;
+  int rank = 0;
+  for (int j = 0; j < n_c; ++j) {  // register broadcasts: no memory round trip per step
+    const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)mk, j);
+    const int ej = __builtin_amdgcn_readlane(me, j);
+    rank += (kj > mk) || (kj == mk && ej < me);
+  }
+  const bool sel = live && rank < k;
+  const float mc = live ? L->cval[lane] : 0.f, mr = live ? L->crad[lane] : 0.f;
+  if (!topk_mode && k < E) {
+    // certification: min lower end over the selected, max upper end over the rest
+    float Mloc = __builtin_inff(), mloc = -__builtin_inff();
+    if (sel) Mloc = mr == __builtin_inff() ? -__builtin_inff() : next_down(mc - mr);
+    if (live && !sel) mloc = mr == __builtin_inff() ? __builtin_inff() : next_up(mc + mr);
+#pragma unroll
+    for (int i = 0; i < ROUTE_MAXI; ++i)
+      if (key[i] != 0u && key[i] < tau) mloc = fmaxf(mloc, R[i] == __builtin_inff() ? __builtin_inff() : next_up(c[i] + R[i]));
+    const float M = wave_min_dpp(Mloc), m = wave_max_dpp(mloc);
+    if (!(M > m)) {
+      route_token_general(a, t, L);
+      return;
+    }
+  }
+  // output order: ascending expert id among the selected
+  int op = 0;
+  for (unsigned long long sm = __ballot(sel); sm; sm &= sm - 1)
+    op += __builtin_amdgcn_readlane(me, __ffsll((long long)sm) - 1) < me;
+  if (sel) {
+    L->oidx[op] = me;
+    L->oval[op] = mc;
+  }
+  if (a.logits_out) {
+#pragma unroll
+    for (int i = 0; i < ROUTE_MAXI; ++i) {
+      const int e = i * WAVE + lane;
+      if (e < E) a.logits_out[t * E + e] = c[i];
+    }
+  }
+  float mx_all = 0.f, den_all = 1.f;
+  if (!a.renormalize) softmax_all(c, E, mx_all, den_all);
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  emit_topk(a, t, L, mx_all, den_all);
+}
+
+// the token's latent row h as two e4m3 terms for the expert kernels (eight values per lane)
+__device__ __forceinline__ void quantize_token_h(const RouteArgs& a, int64_t t) {
+  if (!a.h) return;
+  const QRows q{a.hq.hi + t * a.L, a.hq.lo + t * a.L, a.hq.shi + t * (a.L / 32), a.hq.slo + t * (a.L / 32)};
+  quantize_quads(a.h + t * a.L, q, a.L, lane_id(), WAVE);
+}
+
+__global__ void __launch_bounds__(256) route_kernel(RouteArgs a) {
+  __shared__ RouteLds scratch[4];
+  const int wave = threadIdx.x / WAVE;
+  const int64_t t = (int64_t)blockIdx.x * 4 + wave;
+  if (t >= a.T) return;
+  route_token(a, t, &scratch[wave]);
+  quantize_token_h(a, t);
 }
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
   if (a.T == 0) return hipSuccess;
   if (a.E > ROUTE_MAXI * WAVE) return hipErrorInvalidValue;
   hipLaunchKernelGGL(route_kernel, dim3((unsigned)ceil_div(a.T, 4)), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+// ---- small batches: the grouping of routed rows by expert
+
+// Block-wide grouping of the T*k routed rows r = t*k + j (expert sidx[r]; the k experts
+// of a token are distinct and valid; T <= 64) by expert: counts, offsets, perm with
+// tokens ascending inside each group, and the tile list.  Per expert, LDS holds the row
+// count, the 64-bit mask of its tokens and its first row, all built with integer
+// atomics (order-free); a row's place inside its group is the number of lower tokens in
+// the mask.  One packed prefix sum over the experts gives offsets (low 16 bits) and tile
+// slots (high 16 bits) together.
+constexpr int PLACE_MAX_TOKENS = ROUTE_PLACE_TOKENS;
+struct PlaceLds {
+  int cnt[ROUTE_MAXI * WAVE];
+  unsigned long long tmask[ROUTE_MAXI * WAVE];
+  int first[ROUTE_MAXI * WAVE];
+  int wsum[16];
+};
+
+__device__ void place_rows_block(const int* sidx, int T, int k, int E, PlaceLds* S, const PermOut& p) {
+  const int tid = threadIdx.x, nt = blockDim.x, nw = nt / WAVE, wave = tid / WAVE, lane = lane_id();
+  for (int e = tid; e < E; e += nt) {
+    S->cnt[e] = 0;
+    S->tmask[e] = 0ull;
+    S->first[e] = 0x7FFFFFFF;
+  }
+  __syncthreads();
+  const int rows = T * k;
+  for (int r = tid; r < rows; r += nt) {
+    const int e = sidx[r];
+    atomicAdd(&S->cnt[e], 1);
+    atomicOr(&S->tmask[e], 1ull << (r / k));
+    atomicMin(&S->first[e], r);
+  }
+  __syncthreads();
+  const int per = (E + nt - 1) / nt;  // consecutive experts per thread
+  int loc = 0;
+  for (int q = 0; q < per; ++q) {
+    const int e = tid * per + q;
+    if (e < E) loc += S->cnt[e] | ((S->cnt[e] > 0) << 16);
+  }
+  int wtot = 0;
+  const int wex = wave_excl_scan(loc, wtot);
+  if (lane == 0) S->wsum[wave] = wtot;
+  __syncthreads();
+  int run = wex, totals = 0;
+  for (int w = 0; w < nw; ++w) {
+    run += w < wave ? S->wsum[w] : 0;
+    totals += S->wsum[w];
+  }
+  for (int q = 0; q < per; ++q) {
+    const int e = tid * per + q;
+    if (e < E) {
+      const int c = S->cnt[e], off = run & 0xFFFF;
+      p.counts[e] = c;
+      p.offsets[e] = off;
+      if (c > 0) p.tiles[run >> 16] = make_int4(e, off, c, S->first[e]);
+      run += c | ((c > 0) << 16);
+      S->cnt[e] = off;  // from here on: the group's first position
+    }
+  }
+  const int nact = totals >> 16;
+  if (tid == 0) {
+    p.offsets[E] = totals & 0xFFFF;
+    *p.n_active = nact;
+  }
+  for (int sl = nact + tid; sl < p.max_tiles; sl += nt) p.tiles[sl] = make_int4(-1, 0, 0, -1);
+  __syncthreads();
+  for (int r = tid; r < rows; r += nt) {
+    const int e = sidx[r], t = r / k;
+    p.perm[S->cnt[e] + __popcll(S->tmask[e] & ((1ull << t) - 1ull))] = r;
+  }
+}
+
+// Routing of T <= ROUTE_FUSED_TOKENS tokens, the quantisation of their latent rows and
+// the grouping by expert in one block.
+__global__ void __launch_bounds__(512) route_permute_small_kernel(RouteArgs a, PermOut p) {
+  __shared__ RouteLds scratch[8];
+  __shared__ int sidx[ROUTE_FUSED_TOKENS * WAVE];
+  __shared__ PlaceLds pl;
+  const int wave = threadIdx.x / WAVE, nw = blockDim.x / WAVE;
+  const int k = a.k, T = (int)a.T;
+  for (int t = wave; t < T; t += nw) route_token(a, t, &scratch[wave]);
+  // eight latent values per thread, counted from the last thread down so that the
+  // waves with fewer tokens to route take the first ones
+  if (a.h) quantize_quads(a.h, a.hq, (int64_t)T * a.L, blockDim.x - 1 - threadIdx.x, blockDim.x);
+  __syncthreads();  // idx of every token is in global memory (same block: visible after the barrier)
+  for (int r = threadIdx.x; r < T * k; r += blockDim.x) sidx[r] = a.idx[r];
+  __syncthreads();
+  place_rows_block(sidx, T, k, a.E, &pl, p);
+}
+
+// Grouping of the rows of routed tokens (distinct, valid experts per token) for
+// T <= PLACE_MAX_TOKENS and T*k <= ROUTE_SMALL_ROWS, after route_kernel.
+__global__ void __launch_bounds__(1024) place_rows_kernel(const int32_t* __restrict__ idx, int T, int k, int E,
+                                                          PermOut p) {
+  __shared__ int sidx[ROUTE_SMALL_ROWS];
+  __shared__ PlaceLds pl;
+  for (int r = threadIdx.x; r < T * k; r += blockDim.x) sidx[r] = idx[r];
+  __syncthreads();
+  place_rows_block(sidx, T, k, E, &pl, p);
+}
+
+hipError_t launch_place_rows(const int32_t* idx, int64_t T, int32_t k, int32_t E, const PermOut& p,
+                             hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  if (E > ROUTE_MAXI * WAVE || T > PLACE_MAX_TOKENS || T * k > ROUTE_SMALL_ROWS || k > WAVE)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(place_rows_kernel, dim3(1), dim3(1024), 0, st, idx, (int)T, k, E, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_permute_small(const RouteArgs& a, const PermOut& p, hipStream_t st) {
+  if (a.T == 0) return hipSuccess;
+  if (a.E > ROUTE_MAXI * WAVE || a.T > ROUTE_FUSED_TOKENS || a.k > WAVE) return hipErrorInvalidValue;
+  const int nw = a.T <= 4 ? 4 : 8;
+  hipLaunchKernelGGL(route_permute_small_kernel, dim3(1), dim3(nw * WAVE), 0, st, a, p);
   return hipGetLastError();
 }
 

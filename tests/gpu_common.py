@@ -65,3 +65,15 @@ def k3_dev_weights():
     log("uploading the K3 layer to the GPU ...")
     return dict(router_w=to_dev(d["router_w"]), latent_down=to_dev(d["latent_down"]),
                 latent_up=to_dev(d["latent_up"]), blob=to_dev(k3_blob()))
+
+
+@functools.lru_cache(maxsize=None)
+def dev_packed(name: str):
+    """The device blob of a workload in the packed expert layout."""
+    import mxfp4_expert_gemm_amd as moe
+    c = synth.CONFIGS[name]
+    if c.d == 7168:
+        name = "decode1"  # the K3 workloads share one blob
+    t = moe.pack_experts(dev_weights(name)["blob"], c.E, c.L, c.F)
+    torch.cuda.synchronize()
+    return t

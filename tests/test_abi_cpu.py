@@ -44,7 +44,8 @@ def k3(T=1, **kw):
     c = dict(num_tokens=T, d_model=7168, d_latent=3584, d_ffn=3072, num_experts=896)
     c.update(kw)
     return moe.MoEConfig(c["num_tokens"], c["d_model"], c["d_latent"], c["d_ffn"], c["num_experts"],
-                         kw.get("act", 0), kw.get("renormalize", 1), kw.get("bias_row_stride", 0))
+                         kw.get("act", 0), kw.get("renormalize", 1), kw.get("bias_row_stride", 0),
+                         kw.get("expert_layout", 0))
 
 
 def ws_status(cfg, k):
@@ -66,6 +67,8 @@ def test_workspace_size_valid_and_invalid():
     assert ws_status(k3(bias_row_stride=5), 16)[0] == -1
     assert ws_status(k3(num_experts=2048), 16)[0] == -2
     assert ws_status(k3(T=-1), 16)[0] == -1
+    assert ws_status(k3(expert_layout=1), 16)[0] == 0
+    assert ws_status(k3(expert_layout=2), 16)[0] == -1
     assert moe.lib().moe_workspace_size(None, 16, ctypes.byref(ctypes.c_size_t())) == -1
 
 
@@ -110,3 +113,20 @@ def test_stage_argument_errors():
     r = moe.RoutingOut(FAKE, FAKE, FAKE, None, None, None)
     assert L.moe_route(FAKE, FAKE, None, ctypes.byref(k3()), 16, 8, ctypes.byref(r), FAKE, 1 << 40, None) == -1
     assert L.moe_expert_ffn(FAKE, FAKE, 16, ctypes.byref(k3()), None, FAKE, None, FAKE, 1 << 40, None) == -1
+
+
+def test_packed_layout_sizes_and_pack_errors():
+    # same bytes as the record when L and F are multiples of 512; one padded scale tile
+    # per 16-row group of a matrix whose K/128 is not a multiple of 4
+    assert moe.packed_expert_bytes(3584, 3072) == moe.expert_bytes(3584, 3072)
+    # L = 384: gate/up groups hold 12 scale bytes per row (3 steps) in a 16-byte slot;
+    # F = 256: down groups 8 in 16
+    assert moe.packed_expert_bytes(384, 256) == moe.expert_bytes(384, 256) + 2 * (256 // 16) * 64 + (384 // 16) * 128
+    assert moe.packed_expert_bytes(100, 128) == 0 and moe.packed_expert_bytes(160, 128) == 0
+    pack = moe.lib().moe_pack_experts
+    assert pack(FAKE, 0, 3584, 3072, FAKE + (1 << 40), None) == 0        # nothing to do
+    assert pack(FAKE, 4, 3584, 3000, FAKE + (1 << 40), None) == -1       # F not a multiple of 128
+    assert pack(FAKE, -1, 3584, 3072, FAKE + (1 << 40), None) == -1
+    assert pack(None, 4, 3584, 3072, FAKE + (1 << 40), None) == -1
+    assert pack(FAKE + 8, 4, 3584, 3072, FAKE + (1 << 40), None) == -1   # misaligned
+    assert pack(FAKE, 4, 3584, 3072, FAKE + 4096, None) == -1            # overlapping buffers

@@ -169,13 +169,24 @@ def test_expert_ffn(name, T):
                           want_a=True)
     y, a = from_dev(y), from_dev(a)
     rec = c.record_bytes
+    ulps, yerr = [], []
     for t in range(Tn):
         for j in range(c.k):
             e = int(idx[t, j])
             wa, wy = oracle.expert(hl[t], h["blob"][e * rec:(e + 1) * rec], c.L, c.F)
             r = t * c.k + j
-            assert rel_l2(y[r], wy) < 1e-4, (t, j, rel_l2(y[r], wy))
-            assert np.mean(a[r] == wa) > 0.98
+            # same-sign bf16 patterns are ordered like the values they encode
+            ulps.append(np.abs(a[r].astype(np.int64) - wa.astype(np.int64)))
+            yerr.append(rel_l2(y[r], wy))
+    ulps = np.concatenate(ulps)
+    log(f"  a: exact {np.mean(ulps == 0):.4f}, within 1 ulp {np.mean(ulps <= 1):.5f}; "
+        f"y rel-L2 max {max(yerr):.3g} mean {np.mean(yerr):.3g}")
+    # a is bf16 of silu(g) u with g, u summed on the matrix cores (about 2^-22 of the sum of
+    # |products| per 128-product instruction) and exactly by the oracle: where the two
+    # straddle a rounding boundary a moves by an ulp (a few ulps where g or u cancel to a
+    # tiny value), which moves y by about 2^-8 sqrt(flip fraction) relative
+    assert np.mean(ulps == 0) > 0.95 and np.mean(ulps <= 1) > 0.99
+    assert max(yerr) < 1e-3
 
 
 def test_combine():
@@ -241,6 +252,22 @@ def test_layer_decode1():
 
 def test_layer_decode64_sampled():
     _layer_case("decode64", sample=[0, 17, 33, 63])
+
+
+@pytest.mark.parametrize("T", [40, 600, 1100])
+def test_layer_tiny_weights_every_dispatch_path(T):
+    """T*k of 80, 1200 and 2200 rows: the unfused down + combine kernels, the routing kernel
+    without the fused permutation, and the chunked permutation."""
+    c = synth.CONFIGS["tiny"]
+    h = host_layer("tiny")
+    dw = dev_weights("tiny")
+    x = synth.make_tokens(c, T=T)
+    idx = torch.empty((T, c.k), dtype=torch.int32, device="cuda")
+    out = moe.layer_forward(to_dev(x), dw["router_w"], dw["latent_down"], dw["latent_up"], dw["blob"], c.k,
+                            d_ffn=c.F, routing={"topk_idx": idx})
+    ref = oracle.layer_forward(x, h["router_w"], h["latent_down"], h["latent_up"], h["blob"], c.k, c.L, c.F)
+    assert np.array_equal(from_dev(idx), ref["idx"])
+    assert rel_l2(bf16_bits_to_f64(from_dev(out)), bf16_bits_to_f64(ref["out"])) <= TOL_OUT
 
 
 def test_layer_deterministic():
