@@ -64,6 +64,21 @@ class HipEvents:
             self.rt.hipEventDestroy(e)
 
 
+def recorded_traffic(config: str, packed: bool):
+    """HBM bytes per gate/up launch from the counter summary in profiles/, if it was taken
+    on this workload from the current sources of the expert kernels (else None)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{config}_hbm_counters.md")
+    if not packed or not os.path.exists(path):
+        return None
+    csrc = os.path.join(ROOT, "mxfp4_expert_gemm_amd", "csrc")
+    src = b"".join(open(os.path.join(csrc, f), "rb").read() for f in ("expert_mfma.hip", "common.h", "kernels.h"))
+    fields = dict(line.split(": ", 1) for line in open(path).read().splitlines() if ": " in line)
+    if fields.get("source_sha256 (expert_mfma.hip + common.h + kernels.h)") != hashlib.sha256(src).hexdigest():
+        return None
+    return int(fields["gate_up_traffic_bytes"])
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -73,6 +88,8 @@ def main():
     ap.add_argument("--dense-copies", type=int, default=3)
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0, help="0 skips the oracle baseline")
     ap.add_argument("--breakdown", action="store_true", help="also time every stage (extra untimed pass)")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run a plain device copy of this many bytes 5 times (calibrates HBM byte counters)")
     ap.add_argument("--layout", default="packed", choices=["packed", "record"],
                     help="expert weights as packed once by moe_pack_experts (default) or as checkpoint records")
     args = ap.parse_args()
@@ -83,6 +100,15 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_bytes > 0:
+        src = torch.ones(args.copy_bytes // 4, dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": src.numel() * 4, "launches": 5}), flush=True)
+        return
 
     import mxfp4_expert_gemm_amd as moe
     import synth
@@ -227,7 +253,7 @@ def main():
                    "expert_layout": "packed by moe_pack_experts at load" if packed else "checkpoint records"},
         "roofline": {"bound": "hbm", "kernel": "gate_up (MXFP4 gate/up GEMV + fp32 GLU)",
                      "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(c.name, packed),
                      "kernel_us": round(1e3 * float(np.mean(dom_ms)), 2),
                      "bytes_per_launch": int(np.mean(dom_bytes))},
         "layer_hbm": {"achieved_GBs": round(layer_gbs, 1), "frac": round(layer_gbs / HBM_PEAK_GBS, 4),
