@@ -254,6 +254,19 @@ def test_layer_decode64_sampled():
     _layer_case("decode64", sample=[0, 17, 33, 63])
 
 
+def test_layer_prefill4k_full_size_sampled():
+    """All 4096 tokens through the layer; routing, grouping and outputs checked on a seeded
+    sample of tokens (first, last, and spread), the grouping of every token against the
+    oracle's grouping of the GPU's routing."""
+    rng = np.random.default_rng(0x4096)
+    _layer_case("prefill4k", sample=[0, 4095] + rng.choice(4096, 10, replace=False).tolist())
+
+
+def test_layer_prefill32k_full_size_sampled():
+    rng = np.random.default_rng(0x32768)
+    _layer_case("prefill32k", sample=[0, 32767] + rng.choice(32768, 6, replace=False).tolist())
+
+
 @pytest.mark.parametrize("T", [40, 600, 1100])
 def test_layer_tiny_weights_every_dispatch_path(T):
     """T*k of 80, 1200 and 2200 rows: the unfused down + combine kernels, the routing kernel
