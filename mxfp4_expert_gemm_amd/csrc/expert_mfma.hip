@@ -68,6 +68,11 @@ template <class Fn>
 __device__ __forceinline__ void unroll16(Fn&& f) {
   unroll16_impl(f, std::make_integer_sequence<int, 16>{});
 }
+// calls f(std::integral_constant<int, U>) for U = 0..N-1
+template <int N, class Fn>
+__device__ __forceinline__ void unroll_n(Fn&& f) {
+  unroll16_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 __device__ __forceinline__ i32x8 as_b(const uint4& q) {
   i32x8 b;
@@ -182,12 +187,12 @@ __device__ __forceinline__ ALds alds(uint8_t* smem, int K, int rows) {
   return {smem, smem + rows * K, smem + 2 * rows * K, smem + 2 * rows * K + rows * (K / 32)};
 }
 
-// Copy rows src_rows[0..ntok) of q into LDS rows 0..ntok-1 of d; every thread of the
-// block takes part.  The caller syncs.
-__device__ __forceinline__ void stage_rows(const ALds& d, const QRows& q, const int64_t* src_rows, int ntok,
-                                           int K) {
+// Copy rows src_rows[0..ntok) of q into LDS rows 0..ntok-1 of d; threads tid of
+// nthreads (default: the whole block) take part.  The caller syncs.
+__device__ __forceinline__ void stage_rows(const ALds& d, const QRows& q, const int64_t* src_rows, int ntok, int K,
+                                           int tid = threadIdx.x, int nthreads = blockDim.x) {
   const int per = K / 16;  // 16-byte chunks per row and term
-  for (int c = threadIdx.x; c < 2 * ntok * per; c += blockDim.x) {
+  for (int c = tid; c < 2 * ntok * per; c += nthreads) {
     const int term = c / (ntok * per), rem = c - term * ntok * per;
     const int i = rem / per, off = 16 * (rem - i * per);
     const uint8_t* src = (term ? q.lo : q.hi) + src_rows[i] * K + off;
@@ -195,12 +200,119 @@ __device__ __forceinline__ void stage_rows(const ALds& d, const QRows& q, const 
     *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
   }
   const int nsb = K / 32;
-  for (int c = threadIdx.x; c < 2 * ntok * nsb; c += blockDim.x) {
+  for (int c = tid; c < 2 * ntok * nsb; c += nthreads) {
     const int term = c / (ntok * nsb), rem = c - term * ntok * nsb;
     const int i = rem / nsb, b = rem - i * nsb;
     (term ? d.slo : d.shi)[i * nsb + b] = (term ? q.slo : q.shi)[src_rows[i] * nsb + b];
   }
 }
+
+// Staging in two phases, so that weight loads can be issued between them: the loads of
+// this thread's chunks into registers, later their stores to LDS.  Fits when the rows
+// take at most NREG 16-byte chunks and 2 scale dwords per thread.
+template <int NREG>
+struct StageRegs {
+  u32x4_t v[NREG];  // native vectors: HIP's uint4 wrapper can keep the array in memory
+  uint32_t s[2];
+};
+template <int NREG>
+__device__ __forceinline__ bool stage_fits(int ntok, int K, int nthreads) {
+  return 2 * ntok * (K / 16) <= NREG * nthreads && 2 * ntok * (K / 128) <= 2 * nthreads;
+}
+// thread `tid` of `nthreads`; chunks c = tid + u nthreads (u a compile-time index, so
+// the registers never go to memory)
+template <int NREG>
+__device__ __forceinline__ void stage_load(StageRegs<NREG>& r, const QRows& q, const int64_t* src_rows, int ntok,
+                                           int K, int tid, int nthreads) {
+  const int per = K / 16, nsd = K / 128;
+  unroll_n<NREG>([&](auto uc) {
+    constexpr int u = decltype(uc)::value;
+    const int c = tid + u * nthreads;
+    if (c < 2 * ntok * per) {
+      const int term = c / (ntok * per), rem = c - term * ntok * per;
+      const int i = rem / per, off = 16 * (rem - i * per);
+      r.v[u] = *reinterpret_cast<const u32x4_t*>((term ? q.lo : q.hi) + src_rows[i] * K + off);
+    }
+  });
+  unroll_n<2>([&](auto uc) {
+    constexpr int u = decltype(uc)::value;
+    const int c = tid + u * nthreads;
+    if (c < 2 * ntok * nsd) {
+      const int term = c / (ntok * nsd), rem = c - term * ntok * nsd;
+      const int i = rem / nsd, b = rem - i * nsd;
+      r.s[u] = *reinterpret_cast<const uint32_t*>((term ? q.slo : q.shi) + src_rows[i] * (K / 32) + 4 * b);
+    }
+  });
+}
+template <int NREG>
+__device__ __forceinline__ void stage_store(const StageRegs<NREG>& r, const ALds& d, int ntok, int K, int tid,
+                                            int nthreads) {
+  const int per = K / 16, nsd = K / 128;
+  unroll_n<NREG>([&](auto uc) {
+    constexpr int u = decltype(uc)::value;
+    const int c = tid + u * nthreads;
+    if (c < 2 * ntok * per) {
+      const int term = c / (ntok * per), rem = c - term * ntok * per;
+      const int i = rem / per, off = 16 * (rem - i * per);
+      *reinterpret_cast<u32x4_t*>((term ? d.lo : d.hi) + i * K + off) = r.v[u];
+    }
+  });
+  unroll_n<2>([&](auto uc) {
+    constexpr int u = decltype(uc)::value;
+    const int c = tid + u * nthreads;
+    if (c < 2 * ntok * nsd) {
+      const int term = c / (ntok * nsd), rem = c - term * ntok * nsd;
+      const int i = rem / nsd, b = rem - i * nsd;
+      *reinterpret_cast<uint32_t*>((term ? d.slo : d.shi) + i * (K / 32) + 4 * b) = r.s[u];
+    }
+  });
+}
+// One row (a wave's own) in the same two phases: lane l takes 16-byte chunks
+// l + 64u of the hi and of the lo codes and scale dword l.  Fits when K <= 1024 NH.
+template <int NH>
+struct RowRegs {
+  u32x4_t h[NH], l[NH];
+  uint32_t s;
+};
+template <int NH>
+__device__ __forceinline__ bool row_fits(int K) {
+  return K / 16 <= WAVE * NH && K / 64 <= WAVE;
+}
+template <int NH>
+__device__ __forceinline__ void row_load(RowRegs<NH>& r, const QRows& q, int K, int lane) {
+  unroll_n<NH>([&](auto uc) {
+    constexpr int u = decltype(uc)::value;
+    const int c = lane + WAVE * u;
+    if (c < K / 16) {
+      r.h[u] = *reinterpret_cast<const u32x4_t*>(q.hi + 16 * c);
+      r.l[u] = *reinterpret_cast<const u32x4_t*>(q.lo + 16 * c);
+    }
+  });
+  if (lane < K / 64)
+    r.s = lane < K / 128 ? *reinterpret_cast<const uint32_t*>(q.shi + 4 * lane)
+                         : *reinterpret_cast<const uint32_t*>(q.slo + 4 * (lane - K / 128));
+}
+template <int NH>
+__device__ __forceinline__ void row_store(const RowRegs<NH>& r, const ALds& d, int K, int lane) {
+  unroll_n<NH>([&](auto uc) {
+    constexpr int u = decltype(uc)::value;
+    const int c = lane + WAVE * u;
+    if (c < K / 16) {
+      *reinterpret_cast<u32x4_t*>(d.hi + 16 * c) = r.h[u];
+      *reinterpret_cast<u32x4_t*>(d.lo + 16 * c) = r.l[u];
+    }
+  });
+  if (lane < K / 64) {
+    if (lane < K / 128) *reinterpret_cast<uint32_t*>(d.shi + 4 * lane) = r.s;
+    else *reinterpret_cast<uint32_t*>(d.slo + 4 * (lane - K / 128)) = r.s;
+  }
+}
+
+// the rows of a QRows view that starts at row r
+__device__ __forceinline__ QRows qrows_from(const QRows& q, int64_t r, int K) {
+  return QRows{q.hi + r * K, q.lo + r * K, q.shi + r * (K / 32), q.slo + r * (K / 32)};
+}
+__constant__ int64_t kRow0[1] = {0};
 
 // activation operand of one K step for tile row m (zero unless m < ntok)
 struct AStep {
@@ -240,16 +352,28 @@ __device__ __forceinline__ uint16_t glu_bf16(float g, float u) {
   return f64_to_bf16(s * (double)u);
 }
 
-// One weight row group (16 rows) times the staged activation rows: acc += A W^T over
-// all K steps with the weights PF steps in flight (ring[q][d] holds steps d < PF on
-// entry).  The NMAT weight streams share the activations (gate and up: 2).
+// The first loads of a weight stream, in the order the first step needs them: the
+// scales of steps 0..15, then PF steps of codes (an index past the last step reloads
+// the last one, so the loads are unconditional and vmcnt can be counted statically).
 template <class W, int NMAT, int PF>
-__device__ __forceinline__ void stream_group(const W (&w)[NMAT], uint4 (&ring)[NMAT][PF], const ALds& ad, int m,
-                                             int ntok, int K, int g, f32x4 (&acc)[NMAT]) {
-  const int nks = K / 128, nc = (nks + 15) / 16;
-  SBlock sb[NMAT], sbn[NMAT];
+__device__ __forceinline__ void prime_stream(const W (&w)[NMAT], SBlock (&sb)[NMAT], uint4 (&ring)[NMAT][PF],
+                                             int nks) {
 #pragma unroll
   for (int q = 0; q < NMAT; ++q) w[q].sblock(sb[q], 0);
+#pragma unroll
+  for (int d = 0; d < PF; ++d)
+#pragma unroll
+    for (int q = 0; q < NMAT; ++q) ring[q][d] = w[q].load(d < nks ? d : nks - 1);
+}
+
+// One weight row group (16 rows) times the staged activation rows: acc += A W^T over
+// all K steps with the weights PF steps in flight (prime_stream filled sb and ring).
+// The NMAT weight streams share the activations (gate and up: 2).
+template <class W, int NMAT, int PF>
+__device__ __forceinline__ void stream_group(const W (&w)[NMAT], SBlock (&sb)[NMAT], uint4 (&ring)[NMAT][PF],
+                                             const ALds& ad, int m, int ntok, int K, int g, f32x4 (&acc)[NMAT]) {
+  const int nks = K / 128, nc = (nks + 15) / 16;
+  SBlock sbn[NMAT];
   for (int c = 0; c < nc; ++c) {
     if (c + 1 < nc) {
 #pragma unroll
@@ -284,7 +408,7 @@ __device__ __forceinline__ void stream_group(const W (&w)[NMAT], uint4 (&ring)[N
 }
 
 constexpr int MX_ROWS = 64;  // weight rows per block (4 waves x 16)
-constexpr int MX_PF = 4;     // K steps of weights in flight per wave (gate/up: per matrix)
+constexpr int MX_PF = 2;     // K steps of weights in flight per wave (gate/up: per matrix)
 static_assert(8 * MX_TOK <= 256 && MX_ROWS == 64, "gate/up requantisation: a quad per token and scale block");
 static_assert(16 % MX_PF == 0, "ring slots must repeat every 16 steps");
 
@@ -322,18 +446,21 @@ __global__ void __launch_bounds__(256, 3) gateup_mx_kernel(MxArgs p) {
       srows[threadIdx.x] = sl >= 0 ? sl / p.k : 0;
     }
     __syncthreads();
-    // weights first: the wait for the staged rows then also covers the first steps
+    // loads in the order they are needed: the token rows, the first scales, the ring
+    SBlock sb[2];
     uint4 ring[2][MX_PF];
-#pragma unroll
-    for (int d = 0; d < MX_PF; ++d)
-      if (d < nks) {
-        ring[0][d] = w[0].load(d);
-        ring[1][d] = w[1].load(d);
-      }
-    stage_rows(ad, p.hq, srows, ntok, L);
+    if (stage_fits<4>(ntok, L, blockDim.x)) {
+      StageRegs<4> sr;
+      stage_load(sr, p.hq, srows, ntok, L, threadIdx.x, blockDim.x);
+      prime_stream<W, 2, MX_PF>(w, sb, ring, nks);
+      stage_store(sr, ad, ntok, L, threadIdx.x, blockDim.x);
+    } else {
+      stage_rows(ad, p.hq, srows, ntok, L);
+      prime_stream<W, 2, MX_PF>(w, sb, ring, nks);
+    }
     __syncthreads();
     f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    stream_group<W, 2, MX_PF>(w, ring, ad, n, ntok, L, g, acc);
+    stream_group<W, 2, MX_PF>(w, sb, ring, ad, n, ntok, L, g, acc);
     // lane holds g, u of tile rows 4g+j for weight row f; rows < ntok are tokens
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -394,14 +521,20 @@ __global__ void __launch_bounds__(256) down_mx_kernel(MxArgs p) {
     if (threadIdx.x < MX_TOK)
       srows[threadIdx.x] = threadIdx.x >= ntok ? 0 : ne == 1 ? tile.w : p.perm[r0 + p0 + threadIdx.x];
     __syncthreads();
+    SBlock sb[1];
     uint4 ring[1][MX_PF];
-#pragma unroll
-    for (int d = 0; d < MX_PF; ++d)
-      if (d < nks) ring[0][d] = w[0].load(d);
-    stage_rows(ad, p.aq, srows, ntok, F);
+    if (stage_fits<4>(ntok, F, blockDim.x)) {
+      StageRegs<4> sr;
+      stage_load(sr, p.aq, srows, ntok, F, threadIdx.x, blockDim.x);
+      prime_stream<W, 1, MX_PF>(w, sb, ring, nks);
+      stage_store(sr, ad, ntok, F, threadIdx.x, blockDim.x);
+    } else {
+      stage_rows(ad, p.aq, srows, ntok, F);
+      prime_stream<W, 1, MX_PF>(w, sb, ring, nks);
+    }
     __syncthreads();
     f32x4 acc[1] = {{0.f, 0.f, 0.f, 0.f}};
-    stream_group<W, 1, MX_PF>(w, ring, ad, n, ntok, F, g, acc);
+    stream_group<W, 1, MX_PF>(w, sb, ring, ad, n, ntok, F, g, acc);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int mm = 4 * g + j;
@@ -412,23 +545,19 @@ __global__ void __launch_bounds__(256) down_mx_kernel(MxArgs p) {
 }
 
 // Small batches (T*k <= 64): the down projection of every routed row and the weighted
-// combine in one kernel.  Block b owns latent rows 16b..16b+15 for all T*k rows t*k+j.
-// The rows are staged in LDS, up to DCM_WAVES at a time, one wave per row; y stays in
-// LDS and the block sums it per token in slot order in fp64,
-// z[t][l] = bf16(sum_j w[t][j] y[t*k+j][l]), exactly as the combine kernel.  With the
-// activations in LDS the registers go to a deep weight ring: 16 waves of DCM_PF steps
-// of 1 KB keep enough bytes in flight on every CU.  Only tile row 0 carries the routed
-// row; the result's row 0 is used.
+// combine in one kernel.  Block b owns latent rows 16b..16b+15 for all T*k rows t*k+j,
+// one wave per routed row (DCM_WAVES waves); y stays in LDS and the block sums it per
+// token in slot order in fp64, z[t][l] = bf16(sum_j w[t][j] y[t*k+j][l]), exactly as the
+// combine kernel.  Each wave stages its routed row in its own LDS region, so no block
+// barrier sits between a wave's first loads and its first step, and the registers hold
+// a deep weight ring.  Only tile row 0 carries the routed row; the result's row 0 is used.
 constexpr int DCM_SLOTS = 64;
 constexpr int DCM_WAVES = 16;
-constexpr int DCM_PF = 8;
-constexpr size_t DCM_LDS_MAX = 150 * 1024;
+constexpr int DCM_PF = 4;
 static_assert(16 % DCM_PF == 0, "ring slots must repeat every 16 steps");
 // LDS of one staged row (hi and lo codes, hi and lo scales), padded to 16 bytes
 __host__ __device__ constexpr size_t dcm_row_bytes(int F) { return ((size_t)2 * F + F / 16 + 15) & ~(size_t)15; }
-__host__ __device__ constexpr int dcm_rows_per_pass(int F) {
-  return (int)(DCM_LDS_MAX / dcm_row_bytes(F)) < DCM_WAVES ? (int)(DCM_LDS_MAX / dcm_row_bytes(F)) : DCM_WAVES;
-}
+constexpr size_t DCM_LDS_MAX = 160 * 1024 - DCM_SLOTS * 16 * sizeof(float);
 
 template <class W>
 __global__ void __launch_bounds__(DCM_WAVES * WAVE) down_combine_mx_kernel(MxArgs p, const int32_t* __restrict__ idx,
@@ -440,41 +569,31 @@ __global__ void __launch_bounds__(DCM_WAVES * WAVE) down_combine_mx_kernel(MxArg
   const int n = lane & 15, g = lane >> 4;
   const int L = p.L, F = p.F, k = p.k, nks = F / 128;
   const int nslot = (int)p.T * k;
-  const int S = dcm_rows_per_pass(F);
-  const size_t rb = dcm_row_bytes(F);
-  for (int s0 = 0; s0 < nslot; s0 += S) {
-    const int ns = nslot - s0 < S ? nslot - s0 : S;
-    const int s = s0 + wave;
-    const bool mine = wave < ns;
-    W wr[1];
+  uint8_t* row = smem + wave * dcm_row_bytes(F);
+  const ALds ad{row, row + F, row + 2 * F, row + 2 * F + F / 32};
+  for (int s = wave; s < nslot; s += DCM_WAVES) {
+    const QRows arow = qrows_from(p.aq, s, F);
+    W wr[1] = {W::make(p.blob, idx[s], L, F, MAT_DOWN, blockIdx.x, lane)};
+    SBlock sb[1];
     uint4 ring[1][DCM_PF];
-    if (mine) {
-      wr[0] = W::make(p.blob, idx[s], L, F, MAT_DOWN, blockIdx.x, lane);
-#pragma unroll
-      for (int d = 0; d < DCM_PF; ++d)
-        if (d < nks) ring[0][d] = wr[0].load(d);
+    if (row_fits<3>(F)) {
+      RowRegs<3> rr;
+      row_load(rr, arow, F, lane);
+      prime_stream<W, 1, DCM_PF>(wr, sb, ring, nks);
+      row_store(rr, ad, F, lane);
+    } else {
+      stage_rows(ad, arow, kRow0, 1, F, lane, WAVE);
+      prime_stream<W, 1, DCM_PF>(wr, sb, ring, nks);
     }
-    __syncthreads();  // the previous pass is done with the LDS rows
-    // row i of the pass at smem + i * rb: hi codes, lo codes, hi scales, lo scales
-    for (int c = threadIdx.x; c < ns * (F / 8); c += blockDim.x) {
-      const int i = c / (F / 8), q = c - i * (F / 8);
-      const int term = q / (F / 16), off = 16 * (q - term * (F / 16));
-      *reinterpret_cast<uint4*>(smem + i * rb + term * F + off) =
-          *reinterpret_cast<const uint4*>((term ? p.aq.lo : p.aq.hi) + (int64_t)(s0 + i) * F + off);
-    }
-    for (int c = threadIdx.x; c < ns * (F / 16); c += blockDim.x) {
-      const int i = c / (F / 16), q = c - i * (F / 16);
-      const int term = q / (F / 32), b = q - term * (F / 32);
-      smem[i * rb + 2 * F + term * (F / 32) + b] = (term ? p.aq.slo : p.aq.shi)[(int64_t)(s0 + i) * (F / 32) + b];
-    }
-    __syncthreads();
-    if (mine) {
-      uint8_t* row = smem + wave * rb;
-      const ALds ad{row, row + F, row + 2 * F, row + 2 * F + F / 32};
-      f32x4 acc[1] = {{0.f, 0.f, 0.f, 0.f}};
-      stream_group<W, 1, DCM_PF>(wr, ring, ad, n, 1, F, g, acc);
-      if (g == 0) ys[s][n] = acc[0][0];  // D[0][n]
-    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    f32x4 acc[1] = {{0.f, 0.f, 0.f, 0.f}};
+    stream_group<W, 1, DCM_PF>(wr, sb, ring, ad, n, 1, F, g, acc);
+    if (g == 0) ys[s][n] = acc[0][0];  // D[0][n]
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");  // the next row may overwrite this one
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
   __syncthreads();
   for (int q = threadIdx.x; q < (int)p.T * 16; q += blockDim.x) {
@@ -563,23 +682,31 @@ hipError_t launch_down_mx(const MxArgs& p, hipStream_t st) {
 
 bool down_combine_fits(int64_t T, int32_t k) { return T * k <= DCM_SLOTS; }
 
+template <class W>
+static hipError_t down_combine_lds_limit() {
+  // the per-wave rows exceed the 64 KB default: raise this kernel's limit once
+  static const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&down_combine_mx_kernel<W>),
+                                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)DCM_LDS_MAX);
+  return e;
+}
+
 hipError_t launch_down_combine_mx(const MxArgs& p, const int32_t* idx, const float* w, uint16_t* z,
                                   hipStream_t st) {
   if (p.T == 0) return hipSuccess;
-  if (!down_combine_fits(p.T, p.k) || p.L % 16 || p.F % 128 || dcm_rows_per_pass(p.F) < 1)
-    return hipErrorInvalidValue;
-  const int S = dcm_rows_per_pass(p.F);
   const int nslot = (int)(p.T * p.k);
-  const size_t lds = (size_t)(nslot < S ? nslot : S) * dcm_row_bytes(p.F);
+  const int waves = nslot < DCM_WAVES ? nslot : DCM_WAVES;
+  const size_t lds = (size_t)waves * dcm_row_bytes(p.F);
+  if (!down_combine_fits(p.T, p.k) || p.L % 16 || p.F % 128 || lds > DCM_LDS_MAX) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(p.L / 16)), block(DCM_WAVES * WAVE);
-  const void* fn = p.packed ? reinterpret_cast<const void*>(&down_combine_mx_kernel<PackedW>)
-                            : reinterpret_cast<const void*>(&down_combine_mx_kernel<RecordW>);
-  const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)DCM_LDS_MAX);
-  if (e != hipSuccess) return e;
-  if (p.packed)
+  if (p.packed) {
+    const hipError_t e = down_combine_lds_limit<PackedW>();
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(down_combine_mx_kernel<PackedW>, grid, block, lds, st, p, idx, w, z);
-  else
+  } else {
+    const hipError_t e = down_combine_lds_limit<RecordW>();
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(down_combine_mx_kernel<RecordW>, grid, block, lds, st, p, idx, w, z);
+  }
   return hipGetLastError();
 }
 
