@@ -16,7 +16,7 @@ constexpr int MAX_DIM = 8192;  // columns a GEMV wave holds in registers
 constexpr int MAX_EXPERT_DIM = 7168;  // latent / FFN width whose staged activation rows fit LDS
 
 struct Layout {
-  size_t logits_fast, xnorm2, wnorm2, idx, w, counts, offsets, perm, tiles, nact, permws, h, y, z;
+  size_t logits_fast, xnorm, wnorm, idx, w, counts, offsets, perm, tiles, nact, permws, h, y, z;
   size_t hq_hi, hq_lo, hq_shi, hq_slo, aq_hi, aq_lo, aq_shi, aq_slo;
   size_t total;
 };
@@ -32,8 +32,8 @@ Layout layout(const moe_config& c, int k) {
   const size_t T = (size_t)c.num_tokens, E = (size_t)c.num_experts, L = (size_t)c.d_latent,
                F = (size_t)c.d_ffn, K = (size_t)k;
   l.logits_fast = take(T * E * 4);
-  l.xnorm2 = take(T * 4);
-  l.wnorm2 = take(E * 4);
+  l.xnorm = take(T * 4);
+  l.wnorm = take(E * 4);
   l.idx = take(T * K * 4);
   l.w = take(T * K * 4);
   l.counts = take(E * 4);
@@ -116,16 +116,16 @@ moe_status run_router_and_down(const moe_config& c, const void* x, const void* r
   segs[0].rows = c.num_experts;
   segs[0].router = 1;
   segs[0].out = at<float>(ws, l.logits_fast);
-  segs[0].wnorm2 = at<float>(ws, l.wnorm2);
-  segs[0].xnorm2 = at<float>(ws, l.xnorm2);
+  segs[0].wnorm = at<float>(ws, l.wnorm);
+  segs[0].xnorm = at<float>(ws, l.xnorm);
   int nseg = 1;
   if (latent_down) {
     segs[1].W = static_cast<const uint16_t*>(latent_down);
     segs[1].rows = c.d_latent;
     segs[1].router = 0;
     segs[1].out = at<uint16_t>(ws, l.h);
-    segs[1].wnorm2 = nullptr;
-    segs[1].xnorm2 = nullptr;
+    segs[1].wnorm = nullptr;
+    segs[1].xnorm = nullptr;
     nseg = 2;
   }
   return dev(launch_dense_gemv(static_cast<const uint16_t*>(x), c.num_tokens, c.d_model, segs, nseg, st));
@@ -135,8 +135,8 @@ RouteArgs route_args(const moe_config& c, int k, int flags, const void* x, const
                      int32_t* idx, float* w, float* logits_out, void* ws, const Layout& l) {
   RouteArgs a;
   a.logits_fast = at<float>(ws, l.logits_fast);
-  a.xnorm2 = at<float>(ws, l.xnorm2);
-  a.wnorm2 = at<float>(ws, l.wnorm2);
+  a.xnorm = at<float>(ws, l.xnorm);
+  a.wnorm = at<float>(ws, l.wnorm);
   a.gamma = GEMV_ROUTER_GAMMA;
   a.exact_logits = nullptr;
   a.bias = bias;
@@ -311,8 +311,8 @@ static moe_status forward_impl(const void* x, const void* router_w, const void* 
   up.rows = c.d_model;
   up.router = 0;
   up.out = out;
-  up.wnorm2 = nullptr;
-  up.xnorm2 = nullptr;
+  up.wnorm = nullptr;
+  up.xnorm = nullptr;
   MOE_TRY(mark(MOE_STAGE_UP, true));
   MOE_TRY(dev(launch_dense_gemv(at<uint16_t>(ws, l.z), c.num_tokens, c.d_latent, &up, 1, st)));
   return mark(MOE_STAGE_UP, false);
@@ -441,8 +441,8 @@ moe_status moe_linear_bf16(const void* in, const void* W, int64_t num_tokens, in
   s.rows = n_out;
   s.router = 0;
   s.out = out;
-  s.wnorm2 = nullptr;
-  s.xnorm2 = nullptr;
+  s.wnorm = nullptr;
+  s.xnorm = nullptr;
   return dev(launch_dense_gemv(static_cast<const uint16_t*>(in), num_tokens, n_in, &s, 1,
                                reinterpret_cast<hipStream_t>(stream)));
 }

@@ -118,7 +118,7 @@ __global__ void __launch_bounds__(256) dense_gemv_kernel(DenseParams p) {
     if (lane == 0 && t0 + g < p.T) out[(t0 + g) * s.rows + row] = (float)v;
   }
   wn = wave_sum_dpp(wn);
-  if (lane == 0 && blockIdx.y == 0) s.wnorm2[row] = wn;
+  if (lane == 0 && blockIdx.y == 0) s.wnorm[row] = sqrtf(wn);
   if (row == 0) {  // one wave per token group writes the token norms
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -131,7 +131,7 @@ __global__ void __launch_bounds__(256) dense_gemv_kernel(DenseParams p) {
         xn = dot2(xr[g][c].w, xr[g][c].w, xn);
       }
       xn = wave_sum_dpp(xn);
-      if (lane == 0 && t0 + g < p.T) s.xnorm2[t0 + g] = xn;
+      if (lane == 0 && t0 + g < p.T) s.xnorm[t0 + g] = sqrtf(xn);
     }
   }
 }

@@ -15,10 +15,10 @@ hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, int64_t r
 struct DenseSeg {
   const uint16_t* W;
   int32_t rows;
-  int32_t router;    // 0: out = bf16 [T][rows]; 1: out = fp32 [T][rows] (fp64-folded), wnorm2, xnorm2
+  int32_t router;    // 0: out = bf16 [T][rows]; 1: out = fp32 [T][rows] (fp64-folded), wnorm, xnorm
   void* out;
-  float* wnorm2;     // router only: [rows] squared row norms of W
-  float* xnorm2;     // router only: [T] squared norms of the tokens
+  float* wnorm;      // router only: [rows] Euclidean row norms of W (fp32 sum of squares, rounded sqrt)
+  float* xnorm;      // router only: [T] Euclidean norms of the tokens
 };
 // Relative accumulation error bound of router logits from launch_dense_gemv, per
 // unit of |x_t| |w_e| (see the kernel for its derivation).
@@ -29,8 +29,8 @@ hipError_t launch_dense_gemv(const uint16_t* x, int64_t T, int32_t K, const Dens
 // ---- route.hip
 struct RouteArgs {
   const float* logits_fast;  // [T][E] unbiased fast logits (nullptr in topk mode)
-  const float* xnorm2;       // [T]
-  const float* wnorm2;       // [E]
+  const float* xnorm;       // [T]
+  const float* wnorm;       // [E]
   double gamma;              // relative error bound of logits_fast per |x||w|
   const float* exact_logits; // topk mode: [T][E] caller logits taken as exact (already biased)
   const float* bias;         // nullable

@@ -66,7 +66,7 @@ __device__ __forceinline__ double wave_max_d(double v) {
 
 // ---- exact dot product of two bf16 rows, correctly rounded to fp32
 
-__device__ void kulisch_add(WaveScratch* ws, uint32_t a, uint32_t b) {
+__device__ __forceinline__ void kulisch_add(WaveScratch* ws, uint32_t a, uint32_t b) {
   uint32_t sa = a >> 15, sb = b >> 15;
   uint32_t ea = (a >> 7) & 0xFFu, eb = (b >> 7) & 0xFFu;
   uint32_t fa = a & 0x7Fu, fb = b & 0x7Fu;
@@ -96,7 +96,7 @@ __device__ void kulisch_add(WaveScratch* ws, uint32_t a, uint32_t b) {
 }
 
 // digits (signed, lazy carries) -> correctly rounded fp32; run by one lane
-__device__ float kulisch_round(const WaveScratch* ws) {
+__device__ __forceinline__ float kulisch_round(const WaveScratch* ws) {
   if ((ws->special & 1) || (ws->special & 6) == 6) return __uint_as_float(0x7FC00000u);
   if (ws->special & 2) return __uint_as_float(0x7F800000u);
   if (ws->special & 4) return __uint_as_float(0xFF800000u);
@@ -133,7 +133,7 @@ __device__ float kulisch_round(const WaveScratch* ws) {
   return neg ? -r : r;
 }
 
-__device__ float exact_dot_wave(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int d,
+__device__ __forceinline__ float exact_dot_wave(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int d,
                                 WaveScratch* ws, int32_t* stats) {
   const int lane = lane_id();
   double s = 0.0, sa = 0.0;
@@ -299,14 +299,14 @@ __device__ __forceinline__ void softmax_all(const float (&val)[ROUTE_MAXI], int 
 // General path: selection over every expert by radix select on the keys, certification,
 // exact recompute of the ambiguous logits.  Kept out of line: it runs only when the
 // fast path below cannot decide (many ties, an uncertain boundary, MOE_ROUTE_EXACT_ALL).
-__device__ __noinline__ void route_token_general(const RouteArgs& a, int64_t t, RouteLds* L) {
+__device__ __forceinline__ void route_token_general(const RouteArgs& a, int64_t t, RouteLds* L) {
   const int lane = lane_id();
   const int E = a.E, k = a.k;
   const bool topk_mode = a.exact_logits != nullptr;
   float val[ROUTE_MAXI];      // logit used for weights and export (exact where recomputed)
   float lo[ROUTE_MAXI], hi[ROUTE_MAXI];
   uint32_t key[ROUTE_MAXI];
-  const double xn = topk_mode ? 0.0 : sqrt((double)a.xnorm2[t]);
+  const double xn = topk_mode ? 0.0 : (double)a.xnorm[t];
   const double abs_pad = (double)a.d * 0x1p-125;
 #pragma unroll
   for (int i = 0; i < ROUTE_MAXI; ++i) {
@@ -323,7 +323,7 @@ __device__ __noinline__ void route_token_general(const RouteArgs& a, int64_t t, 
         const float lf = a.logits_fast[t * E + e];
         const float b = a.bias ? a.bias[t * a.bias_stride + e] : 0.f;
         val[i] = lf + b;  // the fast biased logit, one fp32 rounding
-        const double r = a.gamma * xn * sqrt((double)a.wnorm2[e]) * (1.0 + 0x1p-20) + abs_pad +
+        const double r = a.gamma * xn * (double)a.wnorm[e] * (1.0 + 0x1p-20) + abs_pad +
                          0x1p-21 * ((double)fabsf(lf) + (double)fabsf(b));
         const double c = (double)lf + (double)b;
         if (__builtin_isfinite(lf) && __builtin_isfinite(b) && __builtin_isfinite(r)) {
@@ -433,10 +433,9 @@ __device__ __forceinline__ uint32_t kth_of_lanes(uint32_t v, int k) {
 // with fp32 interval ends: radius R_e = gamma' |x||w_e| + pad' + 2^-20 (|lf| + |b|),
 // with gamma' = gamma (1 + 2^-18) and pad' = d 2^-124, covers the radius of the
 // general path plus the roundings of c_e = lf + b and of R_e itself (a few ulp of
-// 2^-24 each, the square roots within one ulp), and the ends c - R and c + R are
-// pushed one ulp outwards.  More than 64
+// 2^-24 each), and the ends c - R and c + R are pushed one ulp outwards.  More than 64
 // candidates or an uncertified boundary go to the general path, which starts over.
-__device__ void route_token(const RouteArgs& a, int64_t t, RouteLds* L) {
+__device__ __forceinline__ void route_token(const RouteArgs& a, int64_t t, RouteLds* L) {
   const int lane = lane_id();
   const int E = a.E, k = a.k;
   const bool topk_mode = a.exact_logits != nullptr;
@@ -446,9 +445,23 @@ __device__ void route_token(const RouteArgs& a, int64_t t, RouteLds* L) {
   }
   float c[ROUTE_MAXI], R[ROUTE_MAXI];
   uint32_t key[ROUTE_MAXI];
-  const float xn = topk_mode ? 0.f : __builtin_amdgcn_sqrtf(a.xnorm2[t]);  // within 1 ulp
+  const float xn = topk_mode ? 0.f : a.xnorm[t];
   const float gam = (float)a.gamma * (1.f + 0x1p-18f) * xn;
   const float pad = (float)a.d * 0x1p-124f;
+  // every load unconditional (lanes past E read the last expert and are masked after),
+  // so all of them are in flight together
+  float lf[ROUTE_MAXI], bv[ROUTE_MAXI], wn[ROUTE_MAXI];
+#pragma unroll
+  for (int i = 0; i < ROUTE_MAXI; ++i) {
+    const int e = i * WAVE + lane < E ? i * WAVE + lane : E - 1;
+    if (topk_mode) {
+      lf[i] = a.exact_logits[t * E + e];
+    } else {
+      lf[i] = a.logits_fast[t * E + e];
+      bv[i] = a.bias ? a.bias[t * a.bias_stride + e] : 0.f;
+      wn[i] = a.wnorm[e];
+    }
+  }
   uint32_t kmax = 0;
 #pragma unroll
   for (int i = 0; i < ROUTE_MAXI; ++i) {
@@ -458,12 +471,10 @@ __device__ void route_token(const RouteArgs& a, int64_t t, RouteLds* L) {
     key[i] = 0u;
     if (e < E) {
       if (topk_mode) {
-        c[i] = a.exact_logits[t * E + e];
+        c[i] = lf[i];
       } else {
-        const float lf = a.logits_fast[t * E + e];
-        const float b = a.bias ? a.bias[t * a.bias_stride + e] : 0.f;
-        c[i] = lf + b;
-        R[i] = gam * __builtin_amdgcn_sqrtf(a.wnorm2[e]) + pad + 0x1p-20f * (fabsf(lf) + fabsf(b));
+        c[i] = lf[i] + bv[i];
+        R[i] = gam * wn[i] + pad + 0x1p-20f * (fabsf(lf[i]) + fabsf(bv[i]));
         if (!(__builtin_isfinite(c[i]) && __builtin_isfinite(R[i]))) {
           c[i] = -__builtin_inff();  // unknown: the general path recomputes it if it can matter
           R[i] = __builtin_inff();
