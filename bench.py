@@ -5,6 +5,10 @@ One step = one pass of the whole layer (router, latent down projection, top-k,
 permutation, MXFP4 gate/up with the fp32 GLU, MXFP4 down, combine, latent up)
 over one batch of synthetic tokens, through the C ABI (moe_layer_forward).
 
+The timed region replays one HIP graph per token batch, captured from the same C-ABI
+call (--no-graph times the eager calls instead; both are reported): decode steps are
+short enough that host launch overhead would otherwise show.
+
 Inputs are resident in HBM before the timed region.  So that a step does not find
 the previous step's weights in the 256 MB Infinity Cache, step i takes token
 batch i (distinct tokens route to distinct experts) and dense-weight copy
@@ -88,6 +92,9 @@ def main():
     ap.add_argument("--dense-copies", type=int, default=3)
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0, help="0 skips the oracle baseline")
     ap.add_argument("--breakdown", action="store_true", help="also time every stage (extra untimed pass)")
+    ap.add_argument("--graph", action=argparse.BooleanOptionalAction, default=True,
+                    help="time replays of HIP graphs captured from the layer call, one per token batch "
+                         "(default); --no-graph times the eager calls")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device copy of this many bytes 5 times (calibrates HBM byte counters)")
     ap.add_argument("--layout", default="packed", choices=["packed", "record"],
@@ -166,21 +173,44 @@ def main():
         ev.end[dom] = kev[2 * i + 1]
         return ev
 
-    for i in range(W):
-        step(i, dom_events(i))
-    torch.cuda.synchronize()
-
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     hip.rt.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+
+    # eager pass: warm-up, then K timed calls with events around the dominant kernel
+    for i in range(W):
+        step(i, dom_events(i))
     torch.cuda.synchronize()
     hip.rt.hipEventRecord(ev_start, stream)
     for i in range(W, W + K):
         step(i, dom_events(i))
     hip.rt.hipEventRecord(ev_stop, stream)
     torch.cuda.synchronize()
-    total_ms = hip.elapsed_ms(ev_start, ev_stop)
-    ms_per_step = total_ms / K
+    eager_ms = hip.elapsed_ms(ev_start, ev_stop)
     dom_ms = [hip.elapsed_ms(kev[2 * i], kev[2 * i + 1]) for i in range(W, W + K)]
+
+    total_ms = eager_ms
+    if args.graph:
+        # one graph per token batch, captured from the same call (the library launches on
+        # the capturing stream and neither allocates nor synchronises)
+        graphs = []
+        for i in range(W + K):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(i)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        for i in range(W):
+            graphs[i].replay()
+        torch.cuda.synchronize()
+        stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        hip.rt.hipEventRecord(ev_start, stream)
+        for i in range(W, W + K):
+            graphs[i].replay()
+        hip.rt.hipEventRecord(ev_stop, stream)
+        torch.cuda.synchronize()
+        total_ms = hip.elapsed_ms(ev_start, ev_stop)
+        del graphs
+    ms_per_step = total_ms / K
 
     # algorithmic bytes of the dominant kernel per launch: gate and up codes+scales of every
     # active expert, the latent rows it reads and the GLU rows it writes
@@ -241,6 +271,8 @@ def main():
         "steps": K,
         "warmup": W,
         "ms_per_step": round(ms_per_step, 5),
+        "timing": ("replays of one captured HIP graph per token batch" if args.graph else "eager calls"),
+        "eager_ms_per_step": round(eager_ms / K, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

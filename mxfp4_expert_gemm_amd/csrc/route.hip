@@ -661,8 +661,25 @@ __global__ void __launch_bounds__(512) route_permute_small_kernel(RouteArgs a, P
   // eight latent values per thread, counted from the last thread down so that the
   // waves with fewer tokens to route take the first ones
   if (a.h) quantize_quads(a.h, a.hq, (int64_t)T * a.L, blockDim.x - 1 - threadIdx.x, blockDim.x);
-  __syncthreads();  // idx of every token is in global memory (same block: visible after the barrier)
-  for (int r = threadIdx.x; r < T * k; r += blockDim.x) sidx[r] = a.idx[r];
+  __syncthreads();  // token t's selection, ascending, is in scratch[t].oidx (one wave per token)
+  if (T == 1) {
+    // one token: its k distinct experts in ascending order are the k groups, one row each
+    const int* sel = scratch[0].oidx;
+    for (int e = threadIdx.x; e <= a.E; e += blockDim.x) {
+      int below = 0;
+      for (int j = 0; j < k; ++j) below += sel[j] < e;
+      p.offsets[e] = below;
+      if (e < a.E) p.counts[e] = below < k && sel[below] == e;
+    }
+    for (int j = threadIdx.x; j < k; j += blockDim.x) {
+      p.perm[j] = j;
+      p.tiles[j] = make_int4(sel[j], j, 1, j);
+    }
+    for (int sl = k + threadIdx.x; sl < p.max_tiles; sl += blockDim.x) p.tiles[sl] = make_int4(-1, 0, 0, -1);
+    if (threadIdx.x == 0) *p.n_active = k;
+    return;
+  }
+  for (int r = threadIdx.x; r < T * k; r += blockDim.x) sidx[r] = scratch[r / k].oidx[r % k];
   __syncthreads();
   place_rows_block(sidx, T, k, a.E, &pl, p);
 }
