@@ -10,8 +10,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe_layer.so")
-SOURCES = ["dequant.hip", "dense_gemv.hip", "route.hip", "permute.hip", "expert_mfma.hip", "combine.hip",
-           "capi.hip"]
+SOURCES = ["dequant.hip", "dense_gemv.hip", "route.hip", "permute.hip", "expert_mfma.hip", "expert_gemm.hip",
+           "combine.hip", "capi.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

@@ -16,7 +16,7 @@ constexpr int MAX_DIM = 8192;  // columns a GEMV wave holds in registers
 constexpr int MAX_EXPERT_DIM = 7168;  // latent / FFN width whose staged activation rows fit LDS
 
 struct Layout {
-  size_t logits_fast, xnorm, wnorm, idx, w, counts, offsets, perm, tiles, nact, permws, h, y, z;
+  size_t logits_fast, xnorm, wnorm, idx, w, counts, offsets, perm, tiles, nact, permws, h, y, z, gtiles;
   size_t hq_hi, hq_lo, hq_shi, hq_slo, aq_hi, aq_lo, aq_shi, aq_slo;
   size_t total;
 };
@@ -53,6 +53,7 @@ Layout layout(const moe_config& c, int k) {
   l.aq_slo = take(T * K * F / 32);
   l.y = take(T * K * L * 4);
   l.z = take(T * L * 2);
+  l.gtiles = take((size_t)gemm_max_tiles((int64_t)(T * K), (int32_t)E) * 16);
   l.total = off;
   return l;
 }
@@ -90,6 +91,10 @@ moe_status check_config(const moe_config* c, int32_t k) {
 
 int32_t max_tiles(int64_t rows, int32_t E) { return (int32_t)(rows < E ? rows : E); }
 
+// Experts run as grouped GEMMs over 64-row tiles once they hold 8 routed rows on
+// average; below that, the streaming kernels that read each expert once per 4 rows.
+bool use_gemm(int64_t rows, int32_t E) { return rows >= 8 * (int64_t)E; }
+
 moe_status dev(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_DEVICE; }
 
 #define MOE_TRY(expr)                 \
@@ -97,6 +102,21 @@ moe_status dev(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_DEVICE;
     moe_status _s = (expr);           \
     if (_s != MOE_OK) return _s;      \
   } while (0)
+
+// gate/up then down (y fp32 by routed row) with the kernel family the batch calls for
+moe_status run_experts(const MxArgs& mx, const moe_config& c, int k, const int32_t* counts, const int32_t* offsets,
+                       void* ws, const Layout& l, hipStream_t st) {
+  const int64_t rows = c.num_tokens * k;
+  if (use_gemm(rows, c.num_experts)) {
+    const int64_t mt = gemm_max_tiles(rows, c.num_experts);
+    int4* gt = at<int4>(ws, l.gtiles);
+    MOE_TRY(dev(launch_gemm_tiles(counts, offsets, c.num_experts, gt, mt, st)));
+    MOE_TRY(dev(launch_gateup_gemm(mx, gt, mt, st)));
+    return dev(launch_down_gemm(mx, gt, mt, st));
+  }
+  MOE_TRY(dev(launch_gateup_mx(mx, st)));
+  return dev(launch_down_mx(mx, st));
+}
 
 __global__ void fill_i32_kernel(int32_t* p, int n, int32_t v) {
   int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -289,18 +309,30 @@ static moe_status forward_impl(const void* x, const void* router_w, const void* 
   }
   MOE_TRY(mark(MOE_STAGE_PERMUTE, false));
   const MxArgs mx = mx_args(c, k, expert_blob, ws, l, perm, at<float>(ws, l.y));
-  MOE_TRY(mark(MOE_STAGE_GATE_UP, true));
-  MOE_TRY(dev(launch_gateup_mx(mx, st)));
-  MOE_TRY(mark(MOE_STAGE_GATE_UP, false));
   if (down_combine_fits(c.num_tokens, k)) {
+    MOE_TRY(mark(MOE_STAGE_GATE_UP, true));
+    MOE_TRY(dev(launch_gateup_mx(mx, st)));
+    MOE_TRY(mark(MOE_STAGE_GATE_UP, false));
     MOE_TRY(mark(MOE_STAGE_DOWN, true));
     MOE_TRY(dev(launch_down_combine_mx(mx, idx, w, at<uint16_t>(ws, l.z), st)));
     MOE_TRY(mark(MOE_STAGE_DOWN, false));
     MOE_TRY(mark(MOE_STAGE_COMBINE, true));
     MOE_TRY(mark(MOE_STAGE_COMBINE, false));
   } else {
+    const int64_t rows = c.num_tokens * k;
+    const int64_t mt = gemm_max_tiles(rows, c.num_experts);
+    int4* gt = at<int4>(ws, l.gtiles);
+    const bool gemm = use_gemm(rows, c.num_experts);
+    MOE_TRY(mark(MOE_STAGE_GATE_UP, true));
+    if (gemm) {
+      MOE_TRY(dev(launch_gemm_tiles(counts, offsets, c.num_experts, gt, mt, st)));
+      MOE_TRY(dev(launch_gateup_gemm(mx, gt, mt, st)));
+    } else {
+      MOE_TRY(dev(launch_gateup_mx(mx, st)));
+    }
+    MOE_TRY(mark(MOE_STAGE_GATE_UP, false));
     MOE_TRY(mark(MOE_STAGE_DOWN, true));
-    MOE_TRY(dev(launch_down_mx(mx, st)));
+    MOE_TRY(dev(gemm ? launch_down_gemm(mx, gt, mt, st) : launch_down_mx(mx, st)));
     MOE_TRY(mark(MOE_STAGE_DOWN, false));
     MOE_TRY(mark(MOE_STAGE_COMBINE, true));
     MOE_TRY(dev(launch_combine(at<float>(ws, l.y), w, c.num_tokens, k, c.d_latent, at<uint16_t>(ws, l.z), st)));
@@ -417,9 +449,7 @@ moe_status moe_expert_ffn(const void* h, const uint8_t* expert_blob, int32_t k, 
   MOE_TRY(dev(launch_quantize_rows(static_cast<const uint16_t*>(h), c.num_tokens, c.d_latent, hq_rows(ws, l), st)));
   MxArgs mx = mx_args(c, k, expert_blob, ws, l, perm, y);
   mx.a_bf16 = static_cast<uint16_t*>(a_out);
-  MOE_TRY(dev(launch_gateup_mx(mx, st)));
-  MOE_TRY(dev(launch_down_mx(mx, st)));
-  return MOE_OK;
+  return run_experts(mx, c, k, at<int32_t>(ws, l.counts), at<int32_t>(ws, l.offsets), ws, l, st);
 }
 
 moe_status moe_combine(const float* y, const float* topk_w, int64_t num_tokens, int32_t k, int32_t d_latent,

@@ -35,139 +35,11 @@
 // activations come from LDS, staged after the first weight loads are issued, because
 // vmcnt retires loads in order and a late global load would drain the weight ring.
 //
-// Operand layout of v_mfma_scale_f32_16x16x128_f8f6f4 (measured on gfx950): lane l
-// works on row/column l%16 and K block g = l/16; an FP4 operand holds K = 32g..32g+31
-// (low nibble first), an FP8 operand holds K = 16g..16g+15 in its first four
-// registers and 64+16g..64+16g+15 in the last four; lane (r + 16 b) supplies the
-// scale of row/column r, K block b for both operands, the byte of its scale register
-// chosen by the instruction's scale select; the result register j of lane l is
-// D[4(l/16)+j][l%16].
-#include <type_traits>
-#include <utility>
-
-#include "common.h"
-#include "kernels.h"
+// The matrix-core wrapper, the weight streams and the staged activation operand are in
+// mfma_stream.h.
+#include "mfma_stream.h"
 
 namespace moe {
-
-typedef int i32x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-template <int OPSEL_B>
-__device__ __forceinline__ f32x4 mx_mfma(const i32x8& a, const i32x8& b, f32x4 c, uint32_t sa, uint32_t sb) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0 /*A: fp8 e4m3*/, 4 /*B: fp4 e2m1*/, 0,
-                                                          (int)sa, OPSEL_B, (int)sb);
-}
-
-// calls f(std::integral_constant<int, J>) for J = 0..15
-template <class Fn, int... J>
-__device__ __forceinline__ void unroll16_impl(Fn&& f, std::integer_sequence<int, J...>) {
-  (f(std::integral_constant<int, J>{}), ...);
-}
-template <class Fn>
-__device__ __forceinline__ void unroll16(Fn&& f) {
-  unroll16_impl(f, std::make_integer_sequence<int, 16>{});
-}
-// calls f(std::integral_constant<int, U>) for U = 0..N-1
-template <int N, class Fn>
-__device__ __forceinline__ void unroll_n(Fn&& f) {
-  unroll16_impl(f, std::make_integer_sequence<int, N>{});
-}
-
-__device__ __forceinline__ i32x8 as_b(const uint4& q) {
-  i32x8 b;
-  b[0] = (int)q.x; b[1] = (int)q.y; b[2] = (int)q.z; b[3] = (int)q.w;
-  b[4] = 0; b[5] = 0; b[6] = 0; b[7] = 0;
-  return b;
-}
-
-// --------------------------------------------------------------- weight streams
-
-// Scale bytes of one 16-step block of K for the lane (see the two streams).
-struct SBlock {
-  uint32_t d[4];
-};
-
-enum { MAT_GATE = 0, MAT_UP = 1, MAT_DOWN = 2 };
-
-// Checkpoint record: per expert gate [F][L], up [F][L], down [L][F], each its codes
-// row-major then its e8m0 scales row-major.
-struct RecordW {
-  const uint8_t* c;  // codes of the lane's row + 16 g
-  const uint8_t* s;  // scales of the lane's row
-  int nsb, n, g;     // scale bytes per row; lane row and K block
-
-  // matrix `mat` of expert e, rows 16 grp .. 16 grp + 15
-  __device__ static RecordW make(const uint8_t* blob, int e, int L, int F, int mat, int grp, int lane) {
-    const int64_t mbytes = (int64_t)F * L / 2 + (int64_t)F * L / 32;
-    const int K = mat == MAT_DOWN ? F : L;
-    const uint8_t* m = blob + (int64_t)e * 3 * mbytes + mat * mbytes;
-    const int64_t row = 16 * grp + (lane & 15);
-    RecordW w;
-    w.n = lane & 15;
-    w.g = lane >> 4;
-    w.nsb = K / 32;
-    w.c = m + row * (K / 2) + 16 * w.g;
-    w.s = m + (int64_t)(mat == MAT_DOWN ? L : F) * (K / 2) + row * (K / 32);
-    return w;
-  }
-  __device__ __forceinline__ uint4 load(int ks) const { return load_nt16(c + 64 * ks); }
-  // lane (n, g) takes bytes 64 blk + 16 g .. +15 of row n: dword i holds the four block
-  // scales of step 16 blk + 4 g + i
-  __device__ __forceinline__ void sblock(SBlock& b, int blk) const {
-    const int off = 64 * blk + 16 * g;
-    if ((nsb & 15) == 0) {  // rows of whole 16-byte groups: one aligned load
-      uint4 v = make_uint4(0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu);
-      if (off < nsb) v = *reinterpret_cast<const uint4*>(s + off);
-      b.d[0] = v.x; b.d[1] = v.y; b.d[2] = v.z; b.d[3] = v.w;
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        b.d[i] = off + 4 * i < nsb ? *reinterpret_cast<const uint32_t*>(s + off + 4 * i) : 0x7F7F7F7Fu;
-    }
-  }
-  // scale of step 16 blk + J, from the lane of the same row that holds it
-  template <int J>
-  __device__ __forceinline__ uint32_t scale(const SBlock& b) const {
-    return (uint32_t)__shfl((int)b.d[J & 3], n + 16 * (J >> 2)) >> (8 * g);
-  }
-  static constexpr int opsel(int) { return 0; }
-};
-
-// Packed layout (moe_pack_experts): a matrix of R rows and K columns is R/16 row groups
-// of packed_group_bytes(K): K/128 code tiles of 1024 bytes (tile s, bytes 16 l .. +15:
-// row l%16 of the group, K values 128 s + 32 (l/16) .. +31), then ceil(K/512) scale
-// tiles of 256 bytes (tile c, byte 4 l + j: the scale of those 32 values at step
-// s = 4c + j; 127 past the last step).
-struct PackedW {
-  const uint8_t* c;  // code tile 0 + 16 lane
-  const uint8_t* s;  // scale tile 0 + 4 lane
-  int nsc;           // scale tiles
-
-  __device__ static PackedW make(const uint8_t* blob, int e, int L, int F, int mat, int grp, int lane) {
-    const int K = mat == MAT_DOWN ? F : L;
-    const int64_t gu = (int64_t)(F / 16) * packed_group_bytes(L);
-    const uint8_t* m =
-        blob + (int64_t)e * packed_expert_bytes(L, F) + (mat == MAT_GATE ? 0 : mat == MAT_UP ? gu : 2 * gu);
-    const uint8_t* grp0 = m + (int64_t)grp * packed_group_bytes(K);
-    PackedW w;
-    w.c = grp0 + 16 * lane;
-    w.s = grp0 + (int64_t)(K / 128) * 1024 + 4 * lane;
-    w.nsc = (K / 128 + 3) / 4;
-    return w;
-  }
-  __device__ __forceinline__ uint4 load(int ks) const { return load_nt16(c + 1024 * ks); }
-  __device__ __forceinline__ void sblock(SBlock& b, int blk) const {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      b.d[i] = 4 * blk + i < nsc ? *reinterpret_cast<const uint32_t*>(s + 256 * (4 * blk + i)) : 0x7F7F7F7Fu;
-  }
-  template <int J>
-  __device__ __forceinline__ uint32_t scale(const SBlock& b) const {
-    return b.d[J >> 2];
-  }
-  static constexpr int opsel(int j) { return j & 3; }
-};
 
 // ------------------------------------------------------------ staged activations
 
@@ -176,16 +48,6 @@ struct PackedW {
 constexpr int MX_TOK = 4;
 constexpr size_t MX_LDS_MAX = 60 * 1024;  // dynamic LDS the gate/up and down kernels may take
 __host__ __device__ constexpr size_t mx_lds_bytes(int K) { return (size_t)MX_TOK * (2 * K + 2 * (K / 32)); }
-
-struct ALds {
-  uint8_t* hi;
-  uint8_t* lo;
-  uint8_t* shi;
-  uint8_t* slo;
-};
-__device__ __forceinline__ ALds alds(uint8_t* smem, int K, int rows) {
-  return {smem, smem + rows * K, smem + 2 * rows * K, smem + 2 * rows * K + rows * (K / 32)};
-}
 
 // Copy rows src_rows[0..ntok) of q into LDS rows 0..ntok-1 of d; threads tid of
 // nthreads (default: the whole block) take part.  The caller syncs.
@@ -313,58 +175,6 @@ __device__ __forceinline__ QRows qrows_from(const QRows& q, int64_t r, int K) {
   return QRows{q.hi + r * K, q.lo + r * K, q.shi + r * (K / 32), q.slo + r * (K / 32)};
 }
 __constant__ int64_t kRow0[1] = {0};
-
-// activation operand of one K step for tile row m (zero unless m < ntok)
-struct AStep {
-  i32x8 hi, lo;
-  uint32_t shi, slo;
-};
-__device__ __forceinline__ void read_a(AStep& a, const ALds& d, int m, int ntok, int K, int ks, int g) {
-  if (m < ntok) {
-    const uint8_t* h = d.hi + m * K + 128 * ks + 16 * g;
-    const uint8_t* l = d.lo + m * K + 128 * ks + 16 * g;
-    const uint4 h0 = *reinterpret_cast<const uint4*>(h), h1 = *reinterpret_cast<const uint4*>(h + 64);
-    const uint4 l0 = *reinterpret_cast<const uint4*>(l), l1 = *reinterpret_cast<const uint4*>(l + 64);
-    a.hi[0] = (int)h0.x; a.hi[1] = (int)h0.y; a.hi[2] = (int)h0.z; a.hi[3] = (int)h0.w;
-    a.hi[4] = (int)h1.x; a.hi[5] = (int)h1.y; a.hi[6] = (int)h1.z; a.hi[7] = (int)h1.w;
-    a.lo[0] = (int)l0.x; a.lo[1] = (int)l0.y; a.lo[2] = (int)l0.z; a.lo[3] = (int)l0.w;
-    a.lo[4] = (int)l1.x; a.lo[5] = (int)l1.y; a.lo[6] = (int)l1.z; a.lo[7] = (int)l1.w;
-    a.shi = d.shi[m * (K / 32) + 4 * ks + g];
-    a.slo = d.slo[m * (K / 32) + 4 * ks + g];
-  } else {
-    for (int i = 0; i < 8; ++i) a.hi[i] = a.lo[i] = 0;
-    a.shi = a.slo = 127u;
-  }
-}
-
-// a = bf16(silu(g) u) for the fp32 values g and u; the activation and the product are
-// evaluated in fp64 (the GLU is specified in fp32 or better), g e^g / (1 + e^g) for
-// g < 0 so a large |g| cannot overflow
-__device__ __forceinline__ uint16_t glu_bf16(float g, float u) {
-  const double gd = (double)g;
-  double s;
-  if (gd >= 0.0) {
-    s = gd / (1.0 + exp(-gd));
-  } else {
-    const double e = exp(gd);
-    s = gd * e / (1.0 + e);
-  }
-  return f64_to_bf16(s * (double)u);
-}
-
-// The first loads of a weight stream, in the order the first step needs them: the
-// scales of steps 0..15, then PF steps of codes (an index past the last step reloads
-// the last one, so the loads are unconditional and vmcnt can be counted statically).
-template <class W, int NMAT, int PF>
-__device__ __forceinline__ void prime_stream(const W (&w)[NMAT], SBlock (&sb)[NMAT], uint4 (&ring)[NMAT][PF],
-                                             int nks) {
-#pragma unroll
-  for (int q = 0; q < NMAT; ++q) w[q].sblock(sb[q], 0);
-#pragma unroll
-  for (int d = 0; d < PF; ++d)
-#pragma unroll
-    for (int q = 0; q < NMAT; ++q) ring[q][d] = w[q].load(d < nks ? d : nks - 1);
-}
 
 // One weight row group (16 rows) times the staged activation rows: acc += A W^T over
 // all K steps with the weights PF steps in flight (prime_stream filled sb and ring).

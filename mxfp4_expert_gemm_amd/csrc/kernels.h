@@ -107,6 +107,14 @@ hipError_t launch_down_combine_mx(const MxArgs& p, const int32_t* idx, const flo
                                   hipStream_t st);
 hipError_t launch_quantize_rows(const uint16_t* src, int64_t rows, int K, const QRows& q, hipStream_t st);
 
+// ---- expert_gemm.hip: grouped GEMMs for experts with many routed rows
+// tiles of up to 64 routed rows per active expert, built from counts/offsets
+int64_t gemm_max_tiles(int64_t rows, int32_t E);
+hipError_t launch_gemm_tiles(const int32_t* counts, const int32_t* offsets, int32_t E, int4* gtiles,
+                             int64_t max_gtiles, hipStream_t st);
+hipError_t launch_gateup_gemm(const MxArgs& p, const int4* gtiles, int64_t max_gtiles, hipStream_t st);
+hipError_t launch_down_gemm(const MxArgs& p, const int4* gtiles, int64_t max_gtiles, hipStream_t st);
+
 // ---- combine.hip
 hipError_t launch_combine(const float* y, const float* w, int64_t T, int32_t k, int32_t L, uint16_t* z,
                           hipStream_t st);

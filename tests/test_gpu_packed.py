@@ -83,7 +83,7 @@ def test_layer_packed_bit_identical_tiny(T):
     assert np.array_equal(ia, ib) and np.array_equal(a, b)
 
 
-@pytest.mark.parametrize("name,T", [("decode1", None), ("decode64", None), ("prefill4k", 64)])
+@pytest.mark.parametrize("name,T", [("decode1", None), ("decode64", None), ("prefill4k", 64), ("prefill4k", None)])
 def test_layer_packed_k3(name, T):
     h = host_layer(name, T)
     c = h["cfg"]
