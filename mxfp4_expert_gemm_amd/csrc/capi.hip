@@ -148,7 +148,7 @@ moe_status run_router_and_down(const moe_config& c, const void* x, const void* r
     segs[1].xnorm = nullptr;
     nseg = 2;
   }
-  return dev(launch_dense_gemv(static_cast<const uint16_t*>(x), c.num_tokens, c.d_model, segs, nseg, st));
+  return dev(launch_dense(static_cast<const uint16_t*>(x), c.num_tokens, c.d_model, segs, nseg, st));
 }
 
 RouteArgs route_args(const moe_config& c, int k, int flags, const void* x, const void* router_w, const float* bias,
@@ -157,7 +157,7 @@ RouteArgs route_args(const moe_config& c, int k, int flags, const void* x, const
   a.logits_fast = at<float>(ws, l.logits_fast);
   a.xnorm = at<float>(ws, l.xnorm);
   a.wnorm = at<float>(ws, l.wnorm);
-  a.gamma = GEMV_ROUTER_GAMMA;
+  a.gamma = dense_router_gamma(c.num_tokens, c.d_model);
   a.exact_logits = nullptr;
   a.bias = bias;
   a.bias_stride = c.bias_row_stride;
@@ -346,7 +346,7 @@ static moe_status forward_impl(const void* x, const void* router_w, const void* 
   up.wnorm = nullptr;
   up.xnorm = nullptr;
   MOE_TRY(mark(MOE_STAGE_UP, true));
-  MOE_TRY(dev(launch_dense_gemv(at<uint16_t>(ws, l.z), c.num_tokens, c.d_latent, &up, 1, st)));
+  MOE_TRY(dev(launch_dense(at<uint16_t>(ws, l.z), c.num_tokens, c.d_latent, &up, 1, st)));
   return mark(MOE_STAGE_UP, false);
 }
 
@@ -473,7 +473,7 @@ moe_status moe_linear_bf16(const void* in, const void* W, int64_t num_tokens, in
   s.out = out;
   s.wnorm = nullptr;
   s.xnorm = nullptr;
-  return dev(launch_dense_gemv(static_cast<const uint16_t*>(in), num_tokens, n_in, &s, 1,
+  return dev(launch_dense(static_cast<const uint16_t*>(in), num_tokens, n_in, &s, 1,
                                reinterpret_cast<hipStream_t>(stream)));
 }
 

@@ -4,6 +4,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 #include "../../include/moe_layer.h"
 
 namespace moe {
@@ -50,6 +53,10 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a), as_bf16x2(b), acc, false);
 }
 
+// 1 if either bf16 half of d is subnormal (zero exponent field, nonzero fraction)
+__device__ __forceinline__ uint32_t bf16x2_subnormal(uint32_t d) {
+  return ((d & 0x7F80u) == 0u && (d & 0x7Fu) != 0u) | ((d & 0x7F800000u) == 0u && (d & 0x7F0000u) != 0u);
+}
 // e8m0 scale byte -> fp32 2^(s-127); s = 0 is the subnormal 2^-127, s = 255 NaN.
 __device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
   if (s == 0) return __uint_as_float(0x00400000u);
@@ -196,6 +203,20 @@ __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
   return v;
+}
+
+// compile-time unrolling: f(std::integral_constant<int, J>) for J = 0..15, or 0..N-1
+template <class Fn, int... J>
+__device__ __forceinline__ void unroll_impl(Fn&& f, std::integer_sequence<int, J...>) {
+  (f(std::integral_constant<int, J>{}), ...);
+}
+template <class Fn>
+__device__ __forceinline__ void unroll16(Fn&& f) {
+  unroll_impl(f, std::make_integer_sequence<int, 16>{});
+}
+template <int N, class Fn>
+__device__ __forceinline__ void unroll_n(Fn&& f) {
+  unroll_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (WAVE - 1); }

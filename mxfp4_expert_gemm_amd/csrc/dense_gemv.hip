@@ -19,6 +19,8 @@
 // (NCH + 6) * 2^-53 relative to the sum of |products|.  With S = sum |x_i w_i|
 // <= |x| |w|, the error of the fp64 logit is below 8.0001 * 2^-23 * |x||w|;
 // GEMV_ROUTER_GAMMA = 16 * 2^-23 leaves a factor of two for the fp32 norm sums.
+// A token or router row holding a subnormal bf16 value (which the dot instructions
+// might flush) gets the norm +inf: its logits are all recomputed exactly.
 #include "common.h"
 #include "kernels.h"
 
@@ -94,6 +96,7 @@ __global__ void __launch_bounds__(256) dense_gemv_kernel(DenseParams p) {
   // router row: fp32 chunk partials folded into fp64
   double acc[G];
   float wn = 0.f;
+  uint32_t wsub = 0;
 #pragma unroll
   for (int g = 0; g < G; ++g) acc[g] = 0.0;
 #pragma unroll
@@ -102,6 +105,8 @@ __global__ void __launch_bounds__(256) dense_gemv_kernel(DenseParams p) {
     wn = dot2(wr[c].y, wr[c].y, wn);
     wn = dot2(wr[c].z, wr[c].z, wn);
     wn = dot2(wr[c].w, wr[c].w, wn);
+    wsub |= bf16x2_subnormal(wr[c].x) | bf16x2_subnormal(wr[c].y) | bf16x2_subnormal(wr[c].z) |
+            bf16x2_subnormal(wr[c].w);
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       float pc = dot2(xr[g][c].x, wr[c].x, 0.f);
@@ -118,20 +123,25 @@ __global__ void __launch_bounds__(256) dense_gemv_kernel(DenseParams p) {
     if (lane == 0 && t0 + g < p.T) out[(t0 + g) * s.rows + row] = (float)v;
   }
   wn = wave_sum_dpp(wn);
-  if (lane == 0 && blockIdx.y == 0) s.wnorm[row] = sqrtf(wn);
+  const bool wany = __any(wsub != 0u);
+  if (lane == 0 && blockIdx.y == 0) s.wnorm[row] = wany ? __builtin_inff() : sqrtf(wn);
   if (row == 0) {  // one wave per token group writes the token norms
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       float xn = 0.f;
+      uint32_t xsub = 0;
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
         xn = dot2(xr[g][c].x, xr[g][c].x, xn);
         xn = dot2(xr[g][c].y, xr[g][c].y, xn);
         xn = dot2(xr[g][c].z, xr[g][c].z, xn);
         xn = dot2(xr[g][c].w, xr[g][c].w, xn);
+        xsub |= bf16x2_subnormal(xr[g][c].x) | bf16x2_subnormal(xr[g][c].y) | bf16x2_subnormal(xr[g][c].z) |
+                bf16x2_subnormal(xr[g][c].w);
       }
       xn = wave_sum_dpp(xn);
-      if (lane == 0 && t0 + g < p.T) s.xnorm[t0 + g] = sqrtf(xn);
+      const bool xany = __any(xsub != 0u);
+      if (lane == 0 && t0 + g < p.T) s.xnorm[t0 + g] = xany ? __builtin_inff() : sqrtf(xn);
     }
   }
 }

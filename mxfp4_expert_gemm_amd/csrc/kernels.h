@@ -26,6 +26,15 @@ constexpr double GEMV_ROUTER_GAMMA = 16.0 / 8388608.0;  // 16 * 2^-23
 hipError_t launch_dense_gemv(const uint16_t* x, int64_t T, int32_t K, const DenseSeg* segs, int nseg,
                              hipStream_t st);
 
+// ---- dense_mfma.hip: the same projections on the matrix cores for token batches
+constexpr double DENSE_MFMA_ROUTER_GAMMA = 66.0 / 8388608.0;  // 66 * 2^-23
+bool dense_uses_mfma(int64_t T, int32_t K);
+// relative error bound of the router logits of launch_dense for T tokens of width K
+double dense_router_gamma(int64_t T, int32_t K);
+hipError_t launch_dense_mfma(const uint16_t* x, int64_t T, int32_t K, const DenseSeg& s, hipStream_t st);
+// the GEMV for few tokens, the matrix-core GEMM otherwise
+hipError_t launch_dense(const uint16_t* x, int64_t T, int32_t K, const DenseSeg* segs, int nseg, hipStream_t st);
+
 // ---- route.hip
 struct RouteArgs {
   const float* logits_fast;  // [T][E] unbiased fast logits (nullptr in topk mode)

@@ -11,9 +11,6 @@
 // D[4(l/16)+j][l%16].
 #pragma once
 
-#include <type_traits>
-#include <utility>
-
 #include "common.h"
 #include "kernels.h"
 
@@ -26,21 +23,6 @@ template <int OPSEL_B>
 __device__ __forceinline__ f32x4 mx_mfma(const i32x8& a, const i32x8& b, f32x4 c, uint32_t sa, uint32_t sb) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0 /*A: fp8 e4m3*/, 4 /*B: fp4 e2m1*/, 0,
                                                           (int)sa, OPSEL_B, (int)sb);
-}
-
-// calls f(std::integral_constant<int, J>) for J = 0..15
-template <class Fn, int... J>
-__device__ __forceinline__ void unroll16_impl(Fn&& f, std::integer_sequence<int, J...>) {
-  (f(std::integral_constant<int, J>{}), ...);
-}
-template <class Fn>
-__device__ __forceinline__ void unroll16(Fn&& f) {
-  unroll16_impl(f, std::make_integer_sequence<int, 16>{});
-}
-// calls f(std::integral_constant<int, U>) for U = 0..N-1
-template <int N, class Fn>
-__device__ __forceinline__ void unroll_n(Fn&& f) {
-  unroll16_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 __device__ __forceinline__ i32x8 as_b(const uint4& q) {

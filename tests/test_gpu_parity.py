@@ -128,6 +128,24 @@ def test_route_indices_bit_exact(name, T):
     assert np.allclose(from_dev(w), want_w, rtol=1e-4, atol=1e-6)
 
 
+@pytest.mark.parametrize("T", [3, 40, 300])
+def test_route_subnormal_inputs_recomputed(T):
+    """Tokens and router rows holding subnormal bf16 values (which the matrix cores or
+    dot instructions may flush) are routed exactly: their norms are +inf, so every
+    logit that can matter is recomputed.  T = 3 takes the GEMV, 40 and 300 the GEMM."""
+    d, E, k = 256, 64, 6
+    x = synth.normal_bf16(77 + T, 1, 1.0, (T, d))
+    W = synth.normal_bf16(77 + T, 2, 0.05, (E, d))
+    x[0, 5] = 0x0001             # smallest positive subnormal
+    x[T - 1, d - 1] = 0x807F     # largest negative subnormal
+    W[9, 17] = 0x0040
+    logits, idx, w = moe.route(to_dev(x), to_dev(W), k)
+    want_l = oracle.router_logits(x, W)
+    want_idx, _ = oracle.select(want_l, k)
+    assert np.array_equal(from_dev(idx), want_idx)
+    assert np.max(np.abs(from_dev(logits).astype(np.float64) - want_l)) < 1e-3
+
+
 # ------------------------------------------------------------- permutation
 
 @pytest.mark.parametrize("T,k,E", [(1, 16, 896), (16, 2, 8), (64, 16, 896), (3, 5, 100), (4096, 16, 896),
@@ -146,7 +164,10 @@ def test_permute_bit_exact(T, k, E):
 
 # --------------------------------------------------------- dense + experts
 
-@pytest.mark.parametrize("T,n_in,n_out", [(1, 7168, 3584), (3, 3584, 7168), (16, 256, 128), (5, 128, 96)])
+@pytest.mark.parametrize("T,n_in,n_out", [(1, 7168, 3584), (3, 3584, 7168), (16, 256, 128), (5, 128, 96),
+                                          # matrix-core GEMM: ragged token and row tiles, fewer K tiles
+                                          # than are prefetched, both tile shapes
+                                          (33, 64, 16), (40, 256, 96), (257, 192, 200), (512, 7168, 3584)])
 def test_linear_bf16(T, n_in, n_out):
     a = synth.normal_bf16(5, 1, 1.0, (T, n_in))
     W = synth.normal_bf16(5, 2, 0.02, (n_out, n_in))
