@@ -219,6 +219,12 @@ __device__ __forceinline__ void unroll_n(Fn&& f) {
   unroll_impl(f, std::make_integer_sequence<int, N>{});
 }
 
+// Workgroup barrier that hands over LDS only: it waits for this wave's LDS operations
+// and not for its global loads in flight.  (__syncthreads also waits for every
+// outstanding global load, which empties a prefetch pipeline at each barrier.)  The
+// memory clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (WAVE - 1); }
 
 __host__ __device__ constexpr inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

@@ -15,8 +15,10 @@
 // tiles of 64: both operand tiles are loaded by the whole block into registers PF tiles
 // ahead (every address clamped into the matrix, so the loads are unconditional and
 // retire in issue order), written to one of two LDS buffers, and read back in MFMA
-// order; one barrier per K tile hands the buffers over.  LDS rows are 128 data bytes
-// padded to 144, so the 16-byte reads of 16 consecutive rows hit distinct banks.
+// order; one barrier per K tile hands the buffers over.  An LDS row holds the tile's 128
+// bytes with 16-byte chunk c stored at chunk c ^ (row & 7): the MFMA-order reads of 16
+// consecutive rows and the row-order writes are then free of bank conflicts on gfx950
+// (padding rows to 144 bytes is not: it costs 4 conflict cycles per 16-byte read).
 //
 // The grid is rasterised in groups of 8 token tiles (the blocks resident at one time
 // share a few operand panels) and remapped so that each XCD (blocks b with the same
@@ -42,7 +44,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int DM_BK = 64;     // K per tile
-constexpr int DM_RS = 144;    // LDS row stride in bytes
+constexpr int DM_RS = 128;    // LDS row stride in bytes (no padding: chunks are swizzled)
 constexpr int DM_GROUP = 8;   // token tiles per raster group
 
 struct DenseMfmaArgs {
@@ -95,7 +97,8 @@ __global__ void __launch_bounds__(256, 2) dense_mfma_kernel(DenseMfmaArgs p) {
   }
   auto dst_off = [&](int u) {
     const int j = tid + 256 * (u < AP ? u : u - AP);
-    return (u < AP ? 0 : A_BYTES) + (j >> 3) * DM_RS + 16 * (j & 7);
+    const int row = j >> 3;
+    return (u < AP ? 0 : A_BYTES) + row * DM_RS + 16 * ((j & 7) ^ (row & 7));
   };
   u32x4_t ring[PF][NP];
   auto gload = [&](u32x4_t (&r)[NP], int kt) {
@@ -123,14 +126,17 @@ __global__ void __launch_bounds__(256, 2) dense_mfma_kernel(DenseMfmaArgs p) {
         for (int r = 0; r < 4; ++r) accd[i][jn][r] = 0.0;
   }
 
-  // prologue: tiles 0 .. PF-1 in flight, tile 0 into buffer 0, tile PF into its slot
+  // prologue: tiles 0 .. PF-1 in flight, tile 0 into buffer 0, tile PF into its slot.
+  // Every load is issued with its tile clamped into the matrix (the loop runs over whole
+  // groups of PF tiles and skips only the math past the end), so the loads in flight are
+  // the same on every path and the compiler's waits for them are exact.
   unroll_n<PF>([&](auto uc) {
     constexpr int U = decltype(uc)::value;
     gload(ring[U], U < nkt ? U : nkt - 1);
   });
   lstore(ring[0], 0);
-  if (PF < nkt) gload(ring[0], PF);
-  __syncthreads();
+  gload(ring[0], PF < nkt ? PF : nkt - 1);
+  lds_barrier();
 
   const int arow = 16 * WM * wm + nl, brow = 16 * WN * wn + nl;
   for (int kt0 = 0; kt0 < nkt; kt0 += PF) {
@@ -143,34 +149,34 @@ __global__ void __launch_bounds__(256, 2) dense_mfma_kernel(DenseMfmaArgs p) {
         for (int ks = 0; ks < DM_BK / 32; ++ks) {
           bf16x8_t a[WM], b[WN];
 #pragma unroll
-          for (int i = 0; i < WM; ++i)
-            a[i] = *reinterpret_cast<const bf16x8_t*>(s + (arow + 16 * i) * DM_RS + 64 * ks + 16 * g);
+          for (int i = 0; i < WM; ++i)  // rows arow + 16 i share arow & 7 = nl & 7
+            a[i] = *reinterpret_cast<const bf16x8_t*>(s + (arow + 16 * i) * DM_RS + 16 * ((4 * ks + g) ^ (nl & 7)));
 #pragma unroll
           for (int jn = 0; jn < WN; ++jn)
-            b[jn] = *reinterpret_cast<const bf16x8_t*>(s + A_BYTES + (brow + 16 * jn) * DM_RS + 64 * ks + 16 * g);
+            b[jn] = *reinterpret_cast<const bf16x8_t*>(s + A_BYTES + (brow + 16 * jn) * DM_RS +
+                                                       16 * ((4 * ks + g) ^ (nl & 7)));
 #pragma unroll
           for (int i = 0; i < WM; ++i)
 #pragma unroll
             for (int jn = 0; jn < WN; ++jn)
               acc[i][jn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[jn], acc[i][jn], 0, 0, 0);
         }
-        if (kt + 1 < nkt) {
-          // buffer (kt+1)&1 was last read in tile kt-1, which every wave has finished
-          constexpr int S = (U + 1) % PF;
-          lstore(ring[S], (kt + 1) & 1);
-          if (kt + 1 + PF < nkt) gload(ring[S], kt + 1 + PF);
-        }
-        __syncthreads();
-        if constexpr (ROUTER) {
+      }
+      // tile kt+1 into buffer (kt+1)&1, last read in tile kt-1, which every wave has
+      // finished; its slot takes tile kt+1+PF
+      constexpr int S = (U + 1) % PF;
+      lstore(ring[S], (kt + 1) & 1);
+      gload(ring[S], kt + 1 + PF < nkt ? kt + 1 + PF : nkt - 1);
+      lds_barrier();
+      if constexpr (ROUTER) {
 #pragma unroll
-          for (int i = 0; i < WM; ++i)
+        for (int i = 0; i < WM; ++i)
 #pragma unroll
-            for (int jn = 0; jn < WN; ++jn) {
+          for (int jn = 0; jn < WN; ++jn) {
 #pragma unroll
-              for (int r = 0; r < 4; ++r) accd[i][jn][r] += (double)acc[i][jn][r];
-              acc[i][jn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            }
-        }
+            for (int r = 0; r < 4; ++r) accd[i][jn][r] += (double)acc[i][jn][r];
+            acc[i][jn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          }
       }
     });
   }

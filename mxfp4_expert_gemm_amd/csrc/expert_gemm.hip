@@ -25,14 +25,17 @@ namespace moe {
 
 constexpr int GT_TOK = 64;    // routed rows per tile
 constexpr int GT_ROWS = 64;   // weight rows per block (4 waves x 16)
-constexpr int GT_PF = 4;      // K steps of weights in flight per wave and matrix
+constexpr int GT_PF_GATEUP = 2;  // K steps of weights in flight per wave and matrix (gate/up: two matrices)
+constexpr int GT_PF_DOWN = 4;
 constexpr int GT_CHUNK = 2;   // K steps per LDS activation chunk
-constexpr int GT_RS = 144;    // LDS row stride of a step's 128 code bytes (9 x 16: conflict-free)
+constexpr int GT_RS = 128;    // LDS row of a step's 128 code bytes, 16-byte chunk c at c ^ (row & 7)
 // one K step of the tile in LDS: hi codes [64][GT_RS], lo codes [64][GT_RS], hi scales
-// [64][4], lo scales [64][4]
+// [64][4], lo scales [64][4].  The chunk swizzle keeps the MFMA-order reads of 16
+// consecutive rows and the row-order writes free of bank conflicts on gfx950.
 constexpr int GT_STEP_BYTES = 2 * GT_TOK * GT_RS + 2 * GT_TOK * 4;
 constexpr int GT_BUF_BYTES = GT_CHUNK * GT_STEP_BYTES;
-static_assert(16 % GT_PF == 0 && 16 % GT_CHUNK == 0, "ring and chunks repeat every 16 steps");
+static_assert(16 % GT_PF_GATEUP == 0 && 16 % GT_PF_DOWN == 0 && 16 % GT_CHUNK == 0,
+              "ring and chunks repeat every 16 steps");
 
 // This thread's share of one chunk: 8 16-byte code pieces and one scale dword.
 struct GtRegs {
@@ -41,49 +44,49 @@ struct GtRegs {
 };
 
 // Loads chunk c (steps GT_CHUNK c ..) of the tile's rows: item j = tid + 256 u is
-// (step, row, term, 16-byte piece); rows >= n and steps >= nks are skipped.
-__device__ __forceinline__ void gt_load(GtRegs& r, const QRows& q, const int64_t* srow, int n, int K, int nks,
-                                        int c) {
+// (step, term, row, 16-byte piece), so a wave moves 8 whole rows of one term.  Every
+// load is issued: rows past the tile read the row srow holds for them (a valid token)
+// and steps past the end re-read the last step, so the loads in flight are the same on
+// every path (see prime_stream); what they bring for such rows and steps is never used.
+__device__ __forceinline__ void gt_load(GtRegs& r, const QRows& q, const int64_t* srow, int K, int nks, int c) {
   const int tid = threadIdx.x;
   unroll_n<8>([&](auto uc) {
     constexpr int u = decltype(uc)::value;
-    const int j = tid + 256 * u;  // 2048 = GT_CHUNK x 64 rows x 2 terms x 8 pieces
-    const int s = j >> 10, m = (j >> 4) & 63, term = (j >> 3) & 1, part = j & 7;
-    const int ks = GT_CHUNK * c + s;
-    if (m < n && ks < nks)
-      r.v[u] = *reinterpret_cast<const u32x4_t*>((term ? q.lo : q.hi) + srow[m] * K + 128 * ks + 16 * part);
+    const int j = tid + 256 * u;  // 2048 = GT_CHUNK x 2 terms x 64 rows x 8 pieces
+    const int s = j >> 10, term = (j >> 9) & 1, m = (j >> 3) & 63, part = j & 7;
+    const int ks = GT_CHUNK * c + s < nks ? GT_CHUNK * c + s : nks - 1;
+    r.v[u] = *reinterpret_cast<const u32x4_t*>((term ? q.lo : q.hi) + srow[m] * K + 128 * ks + 16 * part);
   });
   {
     const int s = tid >> 7, m = (tid >> 1) & 63, term = tid & 1;  // 256 = GT_CHUNK x 64 rows x 2 terms
-    const int ks = GT_CHUNK * c + s;
-    if (m < n && ks < nks)
-      r.s = *reinterpret_cast<const uint32_t*>((term ? q.slo : q.shi) + srow[m] * (K / 32) + 4 * ks);
+    const int ks = GT_CHUNK * c + s < nks ? GT_CHUNK * c + s : nks - 1;
+    r.s = *reinterpret_cast<const uint32_t*>((term ? q.slo : q.shi) + srow[m] * (K / 32) + 4 * ks);
   }
 }
 
-__device__ __forceinline__ void gt_store(const GtRegs& r, uint8_t* buf, int n, int nks, int c) {
+__device__ __forceinline__ void gt_store(const GtRegs& r, uint8_t* buf) {
   const int tid = threadIdx.x;
   unroll_n<8>([&](auto uc) {
     constexpr int u = decltype(uc)::value;
     const int j = tid + 256 * u;
-    const int s = j >> 10, m = (j >> 4) & 63, term = (j >> 3) & 1, part = j & 7;
-    if (m < n && GT_CHUNK * c + s < nks)
-      *reinterpret_cast<u32x4_t*>(buf + s * GT_STEP_BYTES + term * GT_TOK * GT_RS + m * GT_RS + 16 * part) = r.v[u];
+    const int s = j >> 10, term = (j >> 9) & 1, m = (j >> 3) & 63, part = j & 7;
+    *reinterpret_cast<u32x4_t*>(buf + s * GT_STEP_BYTES + term * GT_TOK * GT_RS + m * GT_RS + 16 * (part ^ (m & 7))) =
+        r.v[u];
   });
   {
     const int s = tid >> 7, m = (tid >> 1) & 63, term = tid & 1;
-    if (m < n && GT_CHUNK * c + s < nks)
-      *reinterpret_cast<uint32_t*>(buf + s * GT_STEP_BYTES + 2 * GT_TOK * GT_RS + term * GT_TOK * 4 + m * 4) = r.s;
+    *reinterpret_cast<uint32_t*>(buf + s * GT_STEP_BYTES + 2 * GT_TOK * GT_RS + term * GT_TOK * 4 + m * 4) = r.s;
   }
 }
 
-// activation operand of step s of a chunk for tile row m
+// activation operand of step s of a chunk for tile row m (chunks g and 4 + g of the row)
 __device__ __forceinline__ void gt_read(AStep& a, const uint8_t* buf, int s, int m, int g) {
   const uint8_t* st = buf + s * GT_STEP_BYTES;
-  const uint4 h0 = *reinterpret_cast<const uint4*>(st + m * GT_RS + 16 * g);
-  const uint4 h1 = *reinterpret_cast<const uint4*>(st + m * GT_RS + 16 * g + 64);
-  const uint4 l0 = *reinterpret_cast<const uint4*>(st + GT_TOK * GT_RS + m * GT_RS + 16 * g);
-  const uint4 l1 = *reinterpret_cast<const uint4*>(st + GT_TOK * GT_RS + m * GT_RS + 16 * g + 64);
+  const int c0 = 16 * (g ^ (m & 7)), c1 = 16 * ((4 + g) ^ (m & 7));
+  const uint4 h0 = *reinterpret_cast<const uint4*>(st + m * GT_RS + c0);
+  const uint4 h1 = *reinterpret_cast<const uint4*>(st + m * GT_RS + c1);
+  const uint4 l0 = *reinterpret_cast<const uint4*>(st + GT_TOK * GT_RS + m * GT_RS + c0);
+  const uint4 l1 = *reinterpret_cast<const uint4*>(st + GT_TOK * GT_RS + m * GT_RS + c1);
   a.hi[0] = (int)h0.x; a.hi[1] = (int)h0.y; a.hi[2] = (int)h0.z; a.hi[3] = (int)h0.w;
   a.hi[4] = (int)h1.x; a.hi[5] = (int)h1.y; a.hi[6] = (int)h1.z; a.hi[7] = (int)h1.w;
   a.lo[0] = (int)l0.x; a.lo[1] = (int)l0.y; a.lo[2] = (int)l0.z; a.lo[3] = (int)l0.w;
@@ -97,40 +100,42 @@ __device__ __forceinline__ void gt_read(AStep& a, const uint8_t* buf, int s, int
 __device__ __forceinline__ int gt_logical_block(int b, int nb) { return (b & 7) * (nb >> 3) + (b >> 3); }
 
 // The K loop of one tile: acc[q][tt] += A(token sub-tile tt) x W_q^T over all K steps.
-template <class W, int NMAT>
+// The loop runs over whole 16-step blocks; steps past the end issue their (clamped)
+// loads, stores and barriers like the others and skip only the math, so every path
+// issues the same loads and the waits for them are exact.
+template <class W, int NMAT, int GT_PF>
 __device__ __forceinline__ void gt_mainloop(const W (&w)[NMAT], const QRows& q, const int64_t* srow, int n, int K,
                                             uint8_t* lds, f32x4 (&acc)[NMAT][4]) {
   const int lane = lane_id(), g = lane >> 4, nl = lane & 15;
   const int nks = K / 128, nc = (nks + 15) / 16;
-  const int nchunks = (nks + GT_CHUNK - 1) / GT_CHUNK;
+  const int ntt = (n + 15) / 16;  // token sub-tiles holding rows
   // chunk 0 into buffer 0, chunk 1 into registers, the first weight steps in flight
   GtRegs rg;
-  gt_load(rg, q, srow, n, K, nks, 0);
+  gt_load(rg, q, srow, K, nks, 0);
   SBlock sb[NMAT], sbn[NMAT];
   uint4 ring[NMAT][GT_PF];
   prime_stream<W, NMAT, GT_PF>(w, sb, ring, nks);
-  gt_store(rg, lds, n, nks, 0);
-  if (nchunks > 1) gt_load(rg, q, srow, n, K, nks, 1);
-  __syncthreads();
+  gt_store(rg, lds);
+  gt_load(rg, q, srow, K, nks, 1);
+  lds_barrier();
   for (int cb = 0; cb < nc; ++cb) {
-    if (cb + 1 < nc) {
 #pragma unroll
-      for (int mq = 0; mq < NMAT; ++mq) w[mq].sblock(sbn[mq], cb + 1);
-    }
+    for (int mq = 0; mq < NMAT; ++mq) w[mq].sblock(sbn[mq], cb + 1 < nc ? cb + 1 : cb);
     unroll16([&](auto jc) {
       constexpr int J = decltype(jc)::value;
       const int ks = 16 * cb + J;
-      if (ks < nks) {
-        const int ch = ks / GT_CHUNK;
-        const uint8_t* buf = lds + (ch & 1) * GT_BUF_BYTES;
-        uint4 cw[NMAT];
+      const int ch = ks / GT_CHUNK;
+      const uint8_t* buf = lds + (ch & 1) * GT_BUF_BYTES;
+      uint4 cw[NMAT];
 #pragma unroll
-        for (int mq = 0; mq < NMAT; ++mq) {
-          cw[mq] = ring[mq][J % GT_PF];
-          if (ks + GT_PF < nks) ring[mq][J % GT_PF] = w[mq].load(ks + GT_PF);
-        }
+      for (int mq = 0; mq < NMAT; ++mq) {
+        cw[mq] = ring[mq][J % GT_PF];
+        ring[mq][J % GT_PF] = w[mq].load(ks + GT_PF < nks ? ks + GT_PF : nks - 1);
+      }
+      if (ks < nks) {
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
+          if (tt >= ntt) continue;  // token sub-tile past the tile's rows
           AStep a;
           gt_read(a, buf, J % GT_CHUNK, 16 * tt + nl, g);
 #pragma unroll
@@ -141,21 +146,17 @@ __device__ __forceinline__ void gt_mainloop(const W (&w)[NMAT], const QRows& q, 
             acc[mq][tt] = mx_mfma<W::opsel(J)>(a.lo, b, acc[mq][tt], a.slo, sw);
           }
         }
-        if (J % GT_CHUNK == GT_CHUNK - 1 || ks + 1 == nks) {
-          // end of chunk ch: the registers hold chunk ch+1; every wave is past chunk ch-1,
-          // so its buffer is free
-          if (ch + 1 < nchunks) {
-            gt_store(rg, lds + ((ch + 1) & 1) * GT_BUF_BYTES, n, nks, ch + 1);
-            if (ch + 2 < nchunks) gt_load(rg, q, srow, n, K, nks, ch + 2);
-          }
-          __syncthreads();
-        }
+      }
+      if constexpr (J % GT_CHUNK == GT_CHUNK - 1) {
+        // end of chunk ch: the registers hold chunk ch+1; every wave is past chunk ch-1,
+        // so its buffer is free
+        gt_store(rg, lds + ((ch + 1) & 1) * GT_BUF_BYTES);
+        gt_load(rg, q, srow, K, nks, ch + 2);
+        lds_barrier();
       }
     });
-    if (cb + 1 < nc) {
 #pragma unroll
-      for (int mq = 0; mq < NMAT; ++mq) sb[mq] = sbn[mq];
-    }
+    for (int mq = 0; mq < NMAT; ++mq) sb[mq] = sbn[mq];
   }
 }
 
@@ -188,7 +189,7 @@ __global__ void __launch_bounds__(256, 2) gateup_gemm_kernel(MxArgs p, const int
   for (int mq = 0; mq < 2; ++mq)
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) acc[mq][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  gt_mainloop<W, 2>(w, p.hq, srow, n, L, lds, acc);
+  gt_mainloop<W, 2, GT_PF_GATEUP>(w, p.hq, srow, n, L, lds, acc);
   // GLU into an LDS tile (the activation buffers are free now), then the requantisation
   float* at = reinterpret_cast<float*>(lds);  // [64 tokens][65]
   const int f = rt * GT_ROWS + 16 * wave + nl;
@@ -245,7 +246,7 @@ __global__ void __launch_bounds__(256, 2) down_gemm_kernel(MxArgs p, const int4*
   f32x4 acc[1][4];
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt) acc[0][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  gt_mainloop<W, 1>(w, p.aq, srow, n, F, lds, acc);
+  gt_mainloop<W, 1, GT_PF_DOWN>(w, p.aq, srow, n, F, lds, acc);
   const int l = rt * GT_ROWS + 16 * wave + nl;
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt)

@@ -185,20 +185,20 @@ __device__ __forceinline__ void stream_group(const W (&w)[NMAT], SBlock (&sb)[NM
   const int nks = K / 128, nc = (nks + 15) / 16;
   SBlock sbn[NMAT];
   for (int c = 0; c < nc; ++c) {
-    if (c + 1 < nc) {
+    // the loads of every step are issued, clamped (see prime_stream); only the math of
+    // steps past the end is skipped
 #pragma unroll
-      for (int q = 0; q < NMAT; ++q) w[q].sblock(sbn[q], c + 1);
-    }
+    for (int q = 0; q < NMAT; ++q) w[q].sblock(sbn[q], c + 1 < nc ? c + 1 : c);
     unroll16([&](auto jc) {
       constexpr int J = decltype(jc)::value;
       const int ks = 16 * c + J;
-      if (ks < nks) {
-        uint4 cw[NMAT];
+      uint4 cw[NMAT];
 #pragma unroll
-        for (int q = 0; q < NMAT; ++q) {
-          cw[q] = ring[q][J % PF];
-          if (ks + PF < nks) ring[q][J % PF] = w[q].load(ks + PF);
-        }
+      for (int q = 0; q < NMAT; ++q) {
+        cw[q] = ring[q][J % PF];
+        ring[q][J % PF] = w[q].load(ks + PF < nks ? ks + PF : nks - 1);
+      }
+      if (ks < nks) {
         AStep a;
         read_a(a, ad, m, ntok, K, ks, g);
 #pragma unroll
@@ -210,10 +210,8 @@ __device__ __forceinline__ void stream_group(const W (&w)[NMAT], SBlock (&sb)[NM
         }
       }
     });
-    if (c + 1 < nc) {
 #pragma unroll
-      for (int q = 0; q < NMAT; ++q) sb[q] = sbn[q];
-    }
+    for (int q = 0; q < NMAT; ++q) sb[q] = sbn[q];
   }
 }
 
@@ -268,7 +266,7 @@ __global__ void __launch_bounds__(256, 3) gateup_mx_kernel(MxArgs p) {
       stage_rows(ad, p.hq, srows, ntok, L);
       prime_stream<W, 2, MX_PF>(w, sb, ring, nks);
     }
-    __syncthreads();
+    lds_barrier();  // the primed weight loads stay in flight
     f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
     stream_group<W, 2, MX_PF>(w, sb, ring, ad, n, ntok, L, g, acc);
     // lane holds g, u of tile rows 4g+j for weight row f; rows < ntok are tokens
@@ -342,7 +340,7 @@ __global__ void __launch_bounds__(256) down_mx_kernel(MxArgs p) {
       stage_rows(ad, p.aq, srows, ntok, F);
       prime_stream<W, 1, MX_PF>(w, sb, ring, nks);
     }
-    __syncthreads();
+    lds_barrier();  // the primed weight loads stay in flight
     f32x4 acc[1] = {{0.f, 0.f, 0.f, 0.f}};
     stream_group<W, 1, MX_PF>(w, sb, ring, ad, n, ntok, F, g, acc);
 #pragma unroll

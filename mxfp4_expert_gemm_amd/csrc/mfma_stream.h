@@ -64,17 +64,15 @@ struct RecordW {
   }
   __device__ __forceinline__ uint4 load(int ks) const { return load_nt16(c + 64 * ks); }
   // lane (n, g) takes bytes 64 blk + 16 g .. +15 of row n: dword i holds the four block
-  // scales of step 16 blk + 4 g + i
+  // scales of step 16 blk + 4 g + i.  All four loads are issued (a position past the row
+  // reloads its last dword and is replaced by 127s), so every path issues the same loads.
   __device__ __forceinline__ void sblock(SBlock& b, int blk) const {
     const int off = 64 * blk + 16 * g;
-    if ((nsb & 15) == 0) {  // rows of whole 16-byte groups: one aligned load
-      uint4 v = make_uint4(0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu);
-      if (off < nsb) v = *reinterpret_cast<const uint4*>(s + off);
-      b.d[0] = v.x; b.d[1] = v.y; b.d[2] = v.z; b.d[3] = v.w;
-    } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        b.d[i] = off + 4 * i < nsb ? *reinterpret_cast<const uint32_t*>(s + off + 4 * i) : 0x7F7F7F7Fu;
+    for (int i = 0; i < 4; ++i) {
+      const int o = off + 4 * i;
+      const uint32_t v = *reinterpret_cast<const uint32_t*>(s + (o < nsb ? o : nsb - 4));
+      b.d[i] = o < nsb ? v : 0x7F7F7F7Fu;
     }
   }
   // scale of step 16 blk + J, from the lane of the same row that holds it
@@ -108,10 +106,14 @@ struct PackedW {
     return w;
   }
   __device__ __forceinline__ uint4 load(int ks) const { return load_nt16(c + 1024 * ks); }
+  // all four loads issued (a tile past the last reloads the last one), see RecordW
   __device__ __forceinline__ void sblock(SBlock& b, int blk) const {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      b.d[i] = 4 * blk + i < nsc ? *reinterpret_cast<const uint32_t*>(s + 256 * (4 * blk + i)) : 0x7F7F7F7Fu;
+    for (int i = 0; i < 4; ++i) {
+      const int t = 4 * blk + i;
+      const uint32_t v = *reinterpret_cast<const uint32_t*>(s + 256 * (t < nsc ? t : nsc - 1));
+      b.d[i] = t < nsc ? v : 0x7F7F7F7Fu;
+    }
   }
   template <int J>
   __device__ __forceinline__ uint32_t scale(const SBlock& b) const {
@@ -122,7 +124,12 @@ struct PackedW {
 
 // The first loads of a weight stream, in the order the first step needs them: the
 // scales of steps 0..15, then PF steps of codes (an index past the last step reloads
-// the last one, so the loads are unconditional and vmcnt can be counted statically).
+// the last one).
+//
+// Every load of a stream is unconditional, with indices clamped into the matrix: the
+// compiler counts loads in flight per path, and a load skipped on some path makes it
+// wait for all of them (vmcnt(0)) where one step's data would do, which empties the
+// prefetch ring at every step.
 template <class W, int NMAT, int PF>
 __device__ __forceinline__ void prime_stream(const W (&w)[NMAT], SBlock (&sb)[NMAT], uint4 (&ring)[NMAT][PF],
                                              int nks) {
