@@ -216,7 +216,7 @@ __device__ __forceinline__ void stream_group(const W (&w)[NMAT], SBlock (&sb)[NM
 }
 
 constexpr int MX_ROWS = 64;  // weight rows per block (4 waves x 16)
-constexpr int MX_PF = 2;     // K steps of weights in flight per wave (gate/up: per matrix)
+constexpr int MX_PF = 4;     // K steps of weights in flight per wave (gate/up: per matrix)
 static_assert(8 * MX_TOK <= 256 && MX_ROWS == 64, "gate/up requantisation: a quad per token and scale block");
 static_assert(16 % MX_PF == 0, "ring slots must repeat every 16 steps");
 
@@ -227,7 +227,7 @@ static_assert(16 % MX_PF == 0, "ring slots must repeat every 16 steps");
 // down projection (64 rows = two complete scale blocks per token).  Tokens go in
 // passes of MX_TOK with their latent rows staged in LDS.
 template <class W>
-__global__ void __launch_bounds__(256, 3) gateup_mx_kernel(MxArgs p) {
+__global__ void __launch_bounds__(256, 2) gateup_mx_kernel(MxArgs p) {
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ float atile[MX_TOK][MX_ROWS + 1];
   __shared__ int64_t srows[MX_TOK];

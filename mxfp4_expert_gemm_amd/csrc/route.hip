@@ -658,18 +658,42 @@ __global__ void __launch_bounds__(512) route_permute_small_kernel(RouteArgs a, P
   const int wave = threadIdx.x / WAVE, nw = blockDim.x / WAVE;
   const int k = a.k, T = (int)a.T;
   for (int t = wave; t < T; t += nw) route_token(a, t, &scratch[wave]);
-  // eight latent values per thread, counted from the last thread down so that the
-  // waves with fewer tokens to route take the first ones
-  if (a.h) quantize_quads(a.h, a.hq, (int64_t)T * a.L, blockDim.x - 1 - threadIdx.x, blockDim.x);
+  // eight latent values per thread: by the waves that route no token when there are
+  // some (they start at once), else by every thread, counted from the last one down so
+  // that the waves with fewer tokens to route take the first ones
+  if (a.h) {
+    if (T < nw) {
+      if (wave >= T)
+        quantize_quads(a.h, a.hq, (int64_t)T * a.L, threadIdx.x - T * WAVE, blockDim.x - T * WAVE);
+    } else {
+      quantize_quads(a.h, a.hq, (int64_t)T * a.L, blockDim.x - 1 - threadIdx.x, blockDim.x);
+    }
+  }
   __syncthreads();  // token t's selection, ascending, is in scratch[t].oidx (one wave per token)
   if (T == 1) {
-    // one token: its k distinct experts in ascending order are the k groups, one row each
+    // one token: its k distinct experts in ascending order are the k groups, one row
+    // each.  Thread experts e = tid + i nt (i < NE, NE nt > E): offsets[e] = selections
+    // below e, counts[e] = 1 if e is selected; each selection is read once.
+    constexpr int NE = (ROUTE_MAXI * WAVE + 1 + 4 * WAVE - 1) / (4 * WAVE);
     const int* sel = scratch[0].oidx;
-    for (int e = threadIdx.x; e <= a.E; e += blockDim.x) {
-      int below = 0;
-      for (int j = 0; j < k; ++j) below += sel[j] < e;
-      p.offsets[e] = below;
-      if (e < a.E) p.counts[e] = below < k && sel[below] == e;
+    const int nt = blockDim.x;
+    int below[NE], upto[NE];
+#pragma unroll
+    for (int i = 0; i < NE; ++i) below[i] = upto[i] = 0;
+    for (int j = 0; j < k; ++j) {
+      const int sj = sel[j];
+#pragma unroll
+      for (int i = 0; i < NE; ++i) {
+        const int e = threadIdx.x + i * nt;
+        below[i] += sj < e;
+        upto[i] += sj <= e;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NE; ++i) {
+      const int e = threadIdx.x + i * nt;
+      if (e <= a.E) p.offsets[e] = below[i];
+      if (e < a.E) p.counts[e] = upto[i] - below[i];
     }
     for (int j = threadIdx.x; j < k; j += blockDim.x) {
       p.perm[j] = j;
@@ -707,7 +731,9 @@ hipError_t launch_place_rows(const int32_t* idx, int64_t T, int32_t k, int32_t E
 hipError_t launch_route_permute_small(const RouteArgs& a, const PermOut& p, hipStream_t st) {
   if (a.T == 0) return hipSuccess;
   if (a.E > ROUTE_MAXI * WAVE || a.T > ROUTE_FUSED_TOKENS || a.k > WAVE) return hipErrorInvalidValue;
-  const int nw = a.T <= 4 ? 4 : 8;
+  // a wave per token, and at least one wave more that quantises the latent rows meanwhile
+  // for T < 8
+  const int nw = a.T < 4 ? 4 : 8;
   hipLaunchKernelGGL(route_permute_small_kernel, dim3(1), dim3(nw * WAVE), 0, st, a, p);
   return hipGetLastError();
 }
