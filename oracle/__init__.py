@@ -21,6 +21,7 @@ _LIB = os.path.join(_HERE, "libmoe_ref.so")
 
 OK, ERR_ARG, ERR_UNSUPPORTED = 0, -1, -2
 ACT_SILU, ACT_SITU = 0, 1
+ACT_BF16, ACT_MXFP8 = 0, 1  # activation format at the expert GEMM inputs
 
 
 def build() -> str:
@@ -60,12 +61,19 @@ def lib():
         L.moe_ref_silu.argtypes = [ctypes.c_double]
         L.moe_ref_silu.restype = ctypes.c_double
         L.moe_ref_expert.argtypes = [vp, vp, i32, i32, i32, vp, vp]
+        L.moe_ref_expert_fmt.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp]
+        L.moe_ref_e4m3_value.argtypes = [i32]
+        L.moe_ref_e4m3_value.restype = ctypes.c_double
+        L.moe_ref_mxfp8_block.argtypes = [vp, vp, vp]
+        L.moe_ref_layer_forward_fmt.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, i64, vp,
+                                                vp, vp, vp, i64, vp, vp, vp, vp, vp, vp]
         L.moe_ref_combine.argtypes = [vp, vp, i64, i32, i32, vp]
         L.moe_ref_layer_forward.argtypes = [i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, i64, vp,
                                             vp, vp, vp, i64, vp, vp, vp, vp, vp, vp]
         for name in ("moe_ref_dequant_matrix", "moe_ref_router_logits", "moe_ref_select",
                      "moe_ref_permute", "moe_ref_linear_bf16", "moe_ref_expert", "moe_ref_combine",
-                     "moe_ref_layer_forward"):
+                     "moe_ref_layer_forward", "moe_ref_expert_fmt", "moe_ref_mxfp8_block",
+                     "moe_ref_layer_forward_fmt"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -166,12 +174,27 @@ def silu(g: float) -> float:
     return float(lib().moe_ref_silu(float(g)))
 
 
-def expert(h: np.ndarray, record: np.ndarray, d_latent: int, d_ffn: int, act: int = ACT_SILU):
+def e4m3_value(code: int) -> float:
+    return float(lib().moe_ref_e4m3_value(code))
+
+
+def mxfp8_block(v) -> tuple:
+    """MXFP8 of 32 values (OCP MX convention): (codes uint8 [32], e8m0 scale byte)."""
+    v = np.ascontiguousarray(np.asarray(v, dtype=np.float64))
+    assert v.shape == (32,)
+    codes = np.empty(32, dtype=np.uint8)
+    sc = np.empty(1, dtype=np.uint8)
+    _check(lib().moe_ref_mxfp8_block(_p(v), _p(codes), _p(sc)), "mxfp8_block")
+    return codes, int(sc[0])
+
+
+def expert(h: np.ndarray, record: np.ndarray, d_latent: int, d_ffn: int, act: int = ACT_SILU,
+           act_format: int = ACT_BF16):
     """One expert on one latent row: returns (a bf16 bits [F], y fp32 [L])."""
     a = np.empty(d_ffn, dtype=np.uint16)
     y = np.empty(d_latent, dtype=np.float32)
-    _check(lib().moe_ref_expert(_p(np.ascontiguousarray(h)), _p(np.ascontiguousarray(record)), d_latent,
-                                d_ffn, act, _p(a), _p(y)), "expert")
+    _check(lib().moe_ref_expert_fmt(_p(np.ascontiguousarray(h)), _p(np.ascontiguousarray(record)), d_latent,
+                                    d_ffn, act, act_format, _p(a), _p(y)), "expert")
     return a, y
 
 
@@ -187,7 +210,7 @@ def combine(y: np.ndarray, w: np.ndarray) -> np.ndarray:
 
 def layer_forward(x, router_w, latent_down, latent_up, blob, k: int, d_latent: int, d_ffn: int,
                   bias: Optional[np.ndarray] = None, tokens: Optional[Sequence[int]] = None,
-                  act: int = ACT_SILU, renormalize: bool = True) -> dict:
+                  act: int = ACT_SILU, renormalize: bool = True, act_format: int = ACT_BF16) -> dict:
     """Whole layer for `tokens` (default: all).  Returns dict of out, idx, w, logits, h, z."""
     T, d = x.shape
     E = router_w.shape[0]
@@ -200,7 +223,8 @@ def layer_forward(x, router_w, latent_down, latent_up, blob, k: int, d_latent: i
     logits = np.empty((n, E), dtype=np.float32)
     h = np.empty((n, d_latent), dtype=np.uint16)
     z = np.empty((n, d_latent), dtype=np.uint16)
-    rc = lib().moe_ref_layer_forward(d, d_latent, d_ffn, E, k, act, int(renormalize), _p(x), _p(router_w),
+    rc = lib().moe_ref_layer_forward_fmt(d, d_latent, d_ffn, E, k, act, act_format, int(renormalize), _p(x),
+                                         _p(router_w),
                                      _p(bias), bias_stride, _p(latent_down), _p(latent_up), _p(blob),
                                      _p(tok), n, _p(out), _p(idx), _p(w), _p(logits), _p(h), _p(z))
     _check(rc, "layer_forward")

@@ -316,9 +316,78 @@ double moe_ref_silu(double g) { return g / (1.0 + exp(-g)); }
  * (kimi-k3-in-c post, MXFP4 section: 33,030,144 = 3 * 3584 * 3072), with the
  * activation in fp32 or better (kimi-k3-mlx digest, SiTU-GLU bullet):
  *   g = RN32(W_g h), u = RN32(W_u h), a = bf16(act(g) * u), y = RN32(W_dn a). */
-int moe_ref_expert(const uint16_t* h, const uint8_t* record, int32_t L, int32_t F, int32_t act,
-                   uint16_t* a_out, float* y) {
+/* ------------------------------------------------- MXFP8 activations (OCP MX) */
+
+/* E4M3 (OCP FP8, bias 7, no infinities): sign bit 7, exponent bits 6..3, mantissa
+ * bits 2..0; exponent field 0 holds the subnormals m * 2^-9; S.1111.111 is NaN, so
+ * the largest finite magnitude is 1.75 * 2^8 = 448. */
+double moe_ref_e4m3_value(int32_t code) {
+  const int sign = (code >> 7) & 1, ef = (code >> 3) & 15, m = code & 7;
+  double v;
+  if (ef == 15 && m == 7) return NAN;
+  if (ef == 0)
+    v = ldexp((double)m, -9);
+  else
+    v = ldexp(1.0 + m / 8.0, ef - 7);
+  return sign ? -v : v;
+}
+
+/* the e4m3 code of |q| rounded to nearest, ties to the even mantissa, saturated to 448 */
+static int32_t e4m3_code_of(double q) {
+  const int sign = signbit(q) ? 0x80 : 0;
+  double a = fabs(q);
+  if (a >= 448.0) return sign | 0x7E;
+  if (a == 0.0) return sign;
+  int e;
+  frexp(a, &e);                 /* a = f 2^e, f in [0.5, 1): the binade is 2^(e-1) */
+  int b = e - 1;
+  if (b < -6) b = -6;           /* the subnormal range shares the spacing of 2^-6 */
+  const double step = ldexp(1.0, b - 3);
+  const double r = nearbyint(a / step) * step;  /* default rounding: ties to even */
+  if (r == 0.0) return sign;
+  if (r < ldexp(1.0, -6)) return sign | (int32_t)(r / ldexp(1.0, -9));  /* subnormal */
+  frexp(r, &e);
+  const int rb = e - 1;         /* r may have moved up to the next binade */
+  const int m = (int)((r / ldexp(1.0, rb) - 1.0) * 8.0);
+  return sign | ((rb + 7) << 3) | m;
+}
+
+/* One block of 32 values as MXFP8 (OCP Microscaling v1.0 convention, E4M3 elements):
+ * shared exponent X = floor(log2(max |v|)) - 8 (8 = E4M3's largest normal exponent),
+ * limited to the e8m0 range [-127, 127]; element codes = v / 2^X rounded to nearest
+ * even E4M3, saturated to +-448; scale byte X + 127.  A block of zeros gets scale byte
+ * 0 and zero codes (signs kept). */
+int moe_ref_mxfp8_block(const double* v, uint8_t* codes, uint8_t* scale) {
+  if (!v || !codes || !scale) return MOE_REF_ERR_ARG;
+  double amax = 0.0;
+  for (int i = 0; i < 32; ++i)
+    if (fabs(v[i]) > amax) amax = fabs(v[i]);
+  int X = -127;
+  if (amax > 0.0) {
+    int e;
+    frexp(amax, &e);
+    X = (e - 1) - 8;
+    if (X < -127) X = -127;
+    if (X > 127) X = 127;
+  }
+  for (int i = 0; i < 32; ++i) codes[i] = (uint8_t)e4m3_code_of(ldexp(v[i], -X));
+  *scale = (uint8_t)(X + 127);
+  return MOE_REF_OK;
+}
+
+/* the values a row of n (multiple of 32) takes after MXFP8 quantisation */
+static void mxfp8_row(const double* v, int64_t n, double* out) {
+  uint8_t codes[32], sc;
+  for (int64_t b = 0; b < n; b += 32) {
+    moe_ref_mxfp8_block(v + b, codes, &sc);
+    for (int i = 0; i < 32; ++i) out[b + i] = ldexp(moe_ref_e4m3_value(codes[i]), (int)sc - 127);
+  }
+}
+
+int moe_ref_expert_fmt(const uint16_t* h, const uint8_t* record, int32_t L, int32_t F, int32_t act,
+                       int32_t act_format, uint16_t* a_out, float* y) {
   if (!h || !record || !y || L <= 0 || F <= 0 || L % 32 || F % 32) return MOE_REF_ERR_ARG;
+  if (act_format != MOE_REF_ACT_BF16 && act_format != MOE_REF_ACT_MXFP8) return MOE_REF_ERR_ARG;
   if (act != MOE_REF_ACT_SILU) return MOE_REF_ERR_UNSUPPORTED;
   const int64_t ncode = (int64_t)F * L / 2, mat = ncode + (int64_t)F * L / 32;
   const uint8_t* gate = record;
@@ -328,28 +397,46 @@ int moe_ref_expert(const uint16_t* h, const uint8_t* record, int32_t L, int32_t 
   uint16_t* a = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)F);
   float* wg = (float*)malloc(sizeof(float) * (size_t)wmax);
   float* wu = (float*)malloc(sizeof(float) * (size_t)wmax);
-  if (!a || !wg || !wu) { free(a); free(wg); free(wu); return MOE_REF_ERR_ARG; }
+  double* hv = (double*)malloc(sizeof(double) * (size_t)wmax);  /* the GEMM inputs as used */
+  double* tmp = (double*)malloc(sizeof(double) * (size_t)wmax);
+  if (!a || !wg || !wu || !hv || !tmp) { free(a); free(wg); free(wu); free(hv); free(tmp); return MOE_REF_ERR_ARG; }
+  /* h as the gate/up input: the bf16 values, or their MXFP8 quantisation */
+  for (int32_t l = 0; l < L; ++l) tmp[l] = bf16_to_f64(h[l]);
+  if (act_format == MOE_REF_ACT_MXFP8)
+    mxfp8_row(tmp, L, hv);
+  else
+    memcpy(hv, tmp, sizeof(double) * (size_t)L);
   for (int32_t f = 0; f < F; ++f) {
     mx_row(gate, gate + ncode, L, f, wg);
     mx_row(up, up + ncode, L, f, wu);
     double sg = 0.0, su = 0.0;
     for (int32_t l = 0; l < L; ++l) {
-      double hl = bf16_to_f64(h[l]);
-      sg += hl * (double)wg[l];
-      su += hl * (double)wu[l];
+      sg += hv[l] * (double)wg[l];
+      su += hv[l] * (double)wu[l];
     }
     float g = (float)sg, u = (float)su;
     a[f] = moe_ref_bf16_from_f64(moe_ref_silu((double)g) * (double)u);
   }
+  /* a as the down input, likewise */
+  for (int32_t f = 0; f < F; ++f) tmp[f] = bf16_to_f64(a[f]);
+  if (act_format == MOE_REF_ACT_MXFP8)
+    mxfp8_row(tmp, F, hv);
+  else
+    memcpy(hv, tmp, sizeof(double) * (size_t)F);
   for (int32_t l = 0; l < L; ++l) {
     mx_row(down, down + ncode, F, l, wg);
     double s = 0.0;
-    for (int32_t f = 0; f < F; ++f) s += bf16_to_f64(a[f]) * (double)wg[f];
+    for (int32_t f = 0; f < F; ++f) s += hv[f] * (double)wg[f];
     y[l] = (float)s;
   }
   if (a_out) memcpy(a_out, a, sizeof(uint16_t) * (size_t)F);
-  free(a); free(wg); free(wu);
+  free(a); free(wg); free(wu); free(hv); free(tmp);
   return MOE_REF_OK;
+}
+
+int moe_ref_expert(const uint16_t* h, const uint8_t* record, int32_t L, int32_t F, int32_t act,
+                   uint16_t* a_out, float* y) {
+  return moe_ref_expert_fmt(h, record, L, F, act, MOE_REF_ACT_BF16, a_out, y);
 }
 
 /* weighted combine of the k expert outputs of each token, in latent space */
@@ -366,8 +453,8 @@ int moe_ref_combine(const float* y, const float* w, int64_t T, int32_t k, int32_
 
 /* ------------------------------------------------------------ whole layer */
 
-int moe_ref_layer_forward(int32_t d, int32_t L, int32_t F, int32_t E, int32_t k, int32_t act,
-                          int32_t renormalize, const uint16_t* x, const uint16_t* router_w,
+int moe_ref_layer_forward_fmt(int32_t d, int32_t L, int32_t F, int32_t E, int32_t k, int32_t act,
+                              int32_t act_format, int32_t renormalize, const uint16_t* x, const uint16_t* router_w,
                           const float* bias, int64_t bias_stride, const uint16_t* latent_down,
                           const uint16_t* latent_up, const uint8_t* blob, const int32_t* tokens,
                           int64_t n_tokens, uint16_t* out, int32_t* idx, float* w, float* logits,
@@ -393,7 +480,7 @@ int moe_ref_layer_forward(int32_t d, int32_t L, int32_t F, int32_t E, int32_t k,
     moe_ref_select(lg, 1, E, k, renormalize, id, wt);
     moe_ref_linear_bf16(xt, latent_down, 1, d, L, h);
     for (int32_t j = 0; j < k && rc == MOE_REF_OK; ++j)
-      rc = moe_ref_expert(h, blob + (size_t)id[j] * rec, L, F, act, NULL, y + (size_t)j * L);
+      rc = moe_ref_expert_fmt(h, blob + (size_t)id[j] * rec, L, F, act, act_format, NULL, y + (size_t)j * L);
     moe_ref_combine(y, wt, 1, k, L, z);
     moe_ref_linear_bf16(z, latent_up, 1, L, d, out + i * d);
     if (idx) memcpy(idx + i * k, id, sizeof(int32_t) * (size_t)k);
@@ -404,4 +491,15 @@ int moe_ref_layer_forward(int32_t d, int32_t L, int32_t F, int32_t E, int32_t k,
   }
   free(lg); free(id); free(wt); free(h); free(y); free(z);
   return rc;
+}
+
+int moe_ref_layer_forward(int32_t d, int32_t L, int32_t F, int32_t E, int32_t k, int32_t act,
+                          int32_t renormalize, const uint16_t* x, const uint16_t* router_w,
+                          const float* bias, int64_t bias_stride, const uint16_t* latent_down,
+                          const uint16_t* latent_up, const uint8_t* blob, const int32_t* tokens,
+                          int64_t n_tokens, uint16_t* out, int32_t* idx, float* w, float* logits,
+                          uint16_t* h_out, uint16_t* z_out) {
+  return moe_ref_layer_forward_fmt(d, L, F, E, k, act, MOE_REF_ACT_BF16, renormalize, x, router_w, bias,
+                                   bias_stride, latent_down, latent_up, blob, tokens, n_tokens, out, idx, w,
+                                   logits, h_out, z_out);
 }

@@ -57,6 +57,14 @@ extern "C" {
 
 enum { MOE_REF_OK = 0, MOE_REF_ERR_ARG = -1, MOE_REF_ERR_UNSUPPORTED = -2 };
 enum { MOE_REF_ACT_SILU = 0, MOE_REF_ACT_SITU = 1 };
+/* activation format at the expert GEMM inputs: the bf16 values themselves, or their
+ * MXFP8 (E4M3 + e8m0 per 32) quantisation (OCP Microscaling v1.0 convention) */
+enum { MOE_REF_ACT_BF16 = 0, MOE_REF_ACT_MXFP8 = 1 };
+
+/* value of an E4M3 code (NaN for S.1111.111) */
+double moe_ref_e4m3_value(int32_t code);
+/* MXFP8 of one block of 32 values: codes[32] and the e8m0 scale byte */
+int moe_ref_mxfp8_block(const double* v, uint8_t* codes, uint8_t* scale);
 
 /* bytes of one expert record: 3 * d_latent * d_ffn weights at 0.53125 B */
 size_t moe_ref_expert_bytes(int32_t d_latent, int32_t d_ffn);
@@ -99,6 +107,9 @@ double moe_ref_silu(double g);
 /* one routed expert on one latent row: a (bf16 [F], nullable) and y (fp32 [L]) */
 int moe_ref_expert(const uint16_t* h, const uint8_t* record, int32_t d_latent, int32_t d_ffn,
                    int32_t act, uint16_t* a_out, float* y);
+/* the same with the activation format of h and a at the GEMM inputs */
+int moe_ref_expert_fmt(const uint16_t* h, const uint8_t* record, int32_t d_latent, int32_t d_ffn,
+                       int32_t act, int32_t act_format, uint16_t* a_out, float* y);
 
 /* z[t][l] = bf16(sum_j w[t][j] * y[t*k+j][l]) */
 int moe_ref_combine(const float* y, const float* w, int64_t T, int32_t k, int32_t d_latent,
@@ -117,6 +128,14 @@ int moe_ref_layer_forward(int32_t d_model, int32_t d_latent, int32_t d_ffn, int3
                           const uint8_t* expert_blob, const int32_t* tokens, int64_t n_tokens,
                           uint16_t* out, int32_t* idx, float* w, float* logits, uint16_t* h,
                           uint16_t* z);
+/* the same with the activation format of the expert GEMM inputs */
+int moe_ref_layer_forward_fmt(int32_t d_model, int32_t d_latent, int32_t d_ffn, int32_t num_experts,
+                              int32_t k, int32_t act, int32_t act_format, int32_t renormalize,
+                              const uint16_t* x, const uint16_t* router_w, const float* bias,
+                              int64_t bias_stride, const uint16_t* latent_down, const uint16_t* latent_up,
+                              const uint8_t* expert_blob, const int32_t* tokens, int64_t n_tokens,
+                              uint16_t* out, int32_t* idx, float* w, float* logits, uint16_t* h,
+                              uint16_t* z);
 
 #ifdef __cplusplus
 }
