@@ -73,6 +73,19 @@ typedef enum {
 
 typedef enum { MOE_ACT_SILU = 0, MOE_ACT_SITU = 1 } moe_act;
 
+/* Activation format at the expert GEMM inputs (moe_config.act_format).
+ *  MOE_ACT_FMT_BF16: the bf16 latent rows h and GLU rows a as they are (the products
+ *    are those of the bf16 values; the kernels split each value exactly into two e4m3
+ *    terms).  The default.
+ *  MOE_ACT_FMT_MXFP8: h and a quantised to MXFP8 first, the format the hardware
+ *    deep-dive blog's QAT section names for the activations: per 32 consecutive
+ *    values an e8m0 scale 2^X, X = floor(log2 max|v|) - 8 (clamped to the e8m0 range;
+ *    byte 0 for a block of zeros), and E4M3 elements v / 2^X rounded to nearest even and
+ *    saturated to +-448 (the OCP Microscaling v1.0 convention; the pages give no
+ *    rounding or saturation rule).  One matrix-core product per K step instead of two;
+ *    the output moves by the E4M3 rounding (about 4% relative at the K3 shapes). */
+typedef enum { MOE_ACT_FMT_BF16 = 0, MOE_ACT_FMT_MXFP8 = 1 } moe_act_format;
+
 /* Expert weight layouts (moe_config.expert_layout).
  *  MOE_LAYOUT_RECORD: E records of moe_expert_bytes(L, F) in the checkpoint order of
  *    the kimi-k3-in-c post, MXFP4 section: gate [F][L], up [F][L], down [L][F], each
@@ -105,6 +118,7 @@ typedef struct {
   int32_t renormalize;  /* 1: softmax over the k selected logits; 0: over all E */
   int64_t bias_row_stride; /* router bias: 0 -> one fp32 [E] row for all tokens; E -> fp32 [T][E] */
   int32_t expert_layout;   /* moe_expert_layout of expert_blob */
+  int32_t act_format;      /* moe_act_format of the expert GEMM inputs */
 } moe_config;
 
 /* Optional routing outputs of moe_layer_forward / inputs+outputs of the stage

@@ -22,6 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe_layer.so")
 ACT_SILU, ACT_SITU = 0, 1
 ROUTE_EXACT_ALL = 1
 LAYOUT_RECORD, LAYOUT_PACKED = 0, 1
+ACT_FMT_BF16, ACT_FMT_MXFP8 = 0, 1  # activation format at the expert GEMM inputs
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED", -3: "MOE_ERR_WORKSPACE",
           -4: "MOE_ERR_DEVICE"}
 EXPORTS = ["moe_expert_bytes", "moe_packed_expert_bytes", "moe_pack_experts", "moe_status_string",
@@ -41,7 +42,7 @@ class MoEConfig(ctypes.Structure):
     _fields_ = [("num_tokens", ctypes.c_int64), ("d_model", ctypes.c_int32), ("d_latent", ctypes.c_int32),
                 ("d_ffn", ctypes.c_int32), ("num_experts", ctypes.c_int32), ("act", ctypes.c_int32),
                 ("renormalize", ctypes.c_int32), ("bias_row_stride", ctypes.c_int64),
-                ("expert_layout", ctypes.c_int32)]
+                ("expert_layout", ctypes.c_int32), ("act_format", ctypes.c_int32)]
 
 
 NUM_STAGES = 7
@@ -116,10 +117,10 @@ def _stream(stream=None):
 
 def make_config(num_tokens: int, d_model: int, d_latent: int, d_ffn: int, num_experts: int, *,
                 act: int = ACT_SILU, renormalize: bool = True, bias: Optional[torch.Tensor] = None,
-                packed: bool = False) -> MoEConfig:
+                packed: bool = False, act_format: int = ACT_FMT_BF16) -> MoEConfig:
     stride = 0 if bias is None or bias.dim() == 1 else num_experts
     return MoEConfig(num_tokens, d_model, d_latent, d_ffn, num_experts, act, int(renormalize), stride,
-                     LAYOUT_PACKED if packed else LAYOUT_RECORD)
+                     LAYOUT_PACKED if packed else LAYOUT_RECORD, act_format)
 
 
 def expert_bytes(d_latent: int, d_ffn: int) -> int:
@@ -159,12 +160,14 @@ def _routing(r: Optional[dict]) -> Optional[RoutingOut]:
 def layer_forward(x, router_w, latent_down, latent_up, expert_blob, k: int, *, d_ffn: int,
                   bias: Optional[torch.Tensor] = None, renormalize: bool = True, act: int = ACT_SILU,
                   out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                  routing: Optional[dict] = None, stream=None, packed: bool = False) -> torch.Tensor:
+                  routing: Optional[dict] = None, stream=None, packed: bool = False,
+                  act_format: int = ACT_FMT_BF16) -> torch.Tensor:
     """out = layer(x); routing (dict of preallocated tensors) receives the routing if given."""
     T, d = x.shape
     E = router_w.shape[0]
     L = latent_down.shape[0]
-    cfg = make_config(T, d, L, d_ffn, E, act=act, renormalize=renormalize, bias=bias, packed=packed)
+    cfg = make_config(T, d, L, d_ffn, E, act=act, renormalize=renormalize, bias=bias, packed=packed,
+                      act_format=act_format)
     if out is None:
         out = torch.empty((T, d), dtype=x.dtype, device=x.device)
     if workspace is None:
@@ -179,11 +182,12 @@ def layer_forward(x, router_w, latent_down, latent_up, expert_blob, k: int, *, d
 def layer_forward_profiled(x, router_w, latent_down, latent_up, expert_blob, k: int, events: "StageEvents", *,
                            d_ffn: int, bias: Optional[torch.Tensor] = None, renormalize: bool = True,
                            out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                           routing: Optional[dict] = None, stream=None, packed: bool = False) -> torch.Tensor:
+                           routing: Optional[dict] = None, stream=None, packed: bool = False,
+                           act_format: int = ACT_FMT_BF16) -> torch.Tensor:
     """layer_forward that records the caller's HIP events around each stage (see StageEvents)."""
     T, d = x.shape
     cfg = make_config(T, d, latent_down.shape[0], d_ffn, router_w.shape[0], renormalize=renormalize, bias=bias,
-                      packed=packed)
+                      packed=packed, act_format=act_format)
     if out is None:
         out = torch.empty((T, d), dtype=x.dtype, device=x.device)
     if workspace is None:
@@ -244,11 +248,12 @@ def permute(idx: torch.Tensor, num_experts: int):
 
 
 def expert_ffn(h: torch.Tensor, expert_blob: torch.Tensor, idx: torch.Tensor, *, d_model: int, d_ffn: int,
-               num_experts: int, want_a: bool = False, workspace=None, packed: bool = False):
+               num_experts: int, want_a: bool = False, workspace=None, packed: bool = False,
+               act_format: int = ACT_FMT_BF16):
     """Routed experts on latent rows h [T, L]: returns y fp32 [T*k, L] (and a bf16 [T*k, F])."""
     T, L = h.shape
     k = idx.shape[1]
-    cfg = make_config(T, d_model, L, d_ffn, num_experts, packed=packed)
+    cfg = make_config(T, d_model, L, d_ffn, num_experts, packed=packed, act_format=act_format)
     y = torch.empty((T * k, L), dtype=torch.float32, device=h.device)
     a = torch.empty((T * k, d_ffn), dtype=h.dtype, device=h.device) if want_a else None
     if workspace is None:
@@ -276,6 +281,6 @@ def linear_bf16(inp: torch.Tensor, W: torch.Tensor) -> torch.Tensor:
 
 
 __all__ = ["lib", "MoEConfig", "RoutingOut", "MoEError", "make_config", "expert_bytes", "packed_expert_bytes",
-           "pack_experts", "LAYOUT_RECORD", "LAYOUT_PACKED", "workspace_size",
+           "pack_experts", "LAYOUT_RECORD", "LAYOUT_PACKED", "ACT_FMT_BF16", "ACT_FMT_MXFP8", "workspace_size",
            "alloc_workspace", "layer_forward", "layer_forward_profiled", "StageEvents", "STAGES", "dequant_mxfp4", "route", "topk", "permute", "expert_ffn", "combine",
            "linear_bf16", "ACT_SILU", "ACT_SITU", "ROUTE_EXACT_ALL", "EXPORTS", "LIB_PATH"]

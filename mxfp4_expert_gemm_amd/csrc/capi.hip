@@ -80,6 +80,7 @@ moe_status check_config(const moe_config* c, int32_t k) {
   if (c->renormalize != 0 && c->renormalize != 1) return MOE_ERR_INVALID_ARG;
   if (c->bias_row_stride != 0 && c->bias_row_stride != c->num_experts) return MOE_ERR_INVALID_ARG;
   if (c->expert_layout != MOE_LAYOUT_RECORD && c->expert_layout != MOE_LAYOUT_PACKED) return MOE_ERR_INVALID_ARG;
+  if (c->act_format != MOE_ACT_FMT_BF16 && c->act_format != MOE_ACT_FMT_MXFP8) return MOE_ERR_INVALID_ARG;
   if (c->act == MOE_ACT_SITU) return MOE_ERR_UNSUPPORTED;  // formula not defined on the pages
   // sizes this build's kernels hold in registers; the expert GEMV also needs 128-column multiples
   if (c->num_experts > MAX_E || c->d_model > MAX_DIM || c->d_latent > MAX_EXPERT_DIM || c->d_ffn > MAX_EXPERT_DIM ||
@@ -175,6 +176,7 @@ RouteArgs route_args(const moe_config& c, int k, int flags, const void* x, const
   a.stats = nullptr;
   a.h = nullptr;
   a.L = c.d_latent;
+  a.mxfp8 = c.act_format == MOE_ACT_FMT_MXFP8;
   a.hq = QRows{nullptr, nullptr, nullptr, nullptr};
   return a;
 }
@@ -200,6 +202,7 @@ MxArgs mx_args(const moe_config& c, int k, const uint8_t* blob, void* ws, const 
   m.perm = perm;
   m.hq = hq_rows(ws, l);
   m.aq = aq_rows(ws, l);
+  m.mxfp8 = c.act_format == MOE_ACT_FMT_MXFP8;
   m.a_bf16 = nullptr;
   m.y = y;
   return m;
@@ -446,7 +449,8 @@ moe_status moe_expert_ffn(const void* h, const uint8_t* expert_blob, int32_t k, 
   PermOut po{at<int32_t>(ws, l.counts), at<int32_t>(ws, l.offsets), perm, at<int4>(ws, l.tiles),
              at<int32_t>(ws, l.nact), max_tiles(c.num_tokens * k, c.num_experts)};
   MOE_TRY(dev(launch_permute(routing->topk_idx, c.num_tokens * k, c.num_experts, po, at<void>(ws, l.permws), st)));
-  MOE_TRY(dev(launch_quantize_rows(static_cast<const uint16_t*>(h), c.num_tokens, c.d_latent, hq_rows(ws, l), st)));
+  MOE_TRY(dev(launch_quantize_rows(static_cast<const uint16_t*>(h), c.num_tokens, c.d_latent, hq_rows(ws, l),
+                                   c.act_format == MOE_ACT_FMT_MXFP8, st)));
   MxArgs mx = mx_args(c, k, expert_blob, ws, l, perm, y);
   mx.a_bf16 = static_cast<uint16_t*>(a_out);
   return run_experts(mx, c, k, at<int32_t>(ws, l.counts), at<int32_t>(ws, l.offsets), ws, l, st);

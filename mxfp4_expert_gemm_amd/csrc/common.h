@@ -323,6 +323,45 @@ __device__ __forceinline__ void quantize_quad8(const float (&v)[8], uint32_t (&h
   }
 }
 
+// MXFP8 of one 32-value block held by a quad (the activation format of the MXFP8 mode,
+// OCP Microscaling v1.0 convention): shared exponent X = floor(log2 max|v|) - 8, e8m0
+// byte X + 127 (clamped to the e8m0 range; 0 for a block of zeros), codes = v / 2^X
+// rounded to nearest-even E4M3 and saturated to +-448.  Written into the hi term; the lo
+// term is zero (codes 0, scale byte 127), so the two-term kernels compute the same
+// product and the grouped GEMMs skip it.
+__device__ __forceinline__ void quantize_quad8_mx(const float (&v)[8], uint32_t (&hi)[2], uint32_t (&lo)[2],
+                                                  uint32_t& shi, uint32_t& slo) {
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  amax = quad_max(amax);
+  int X = -127;
+  if (amax > 0.f) {
+    X = exponent_of(amax) - 8;
+    X = X < -127 ? -127 : X > 127 ? 127 : X;
+  }
+  shi = (uint32_t)(X + 127);
+  const float inv = pow2f(-X);
+  hi[0] = hi[1] = 0u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float q;
+    const float t = fminf(fmaxf(v[i] * inv, -448.f), 448.f);  // exact scaling, then saturation
+    hi[i / 4] |= e4m3_rne(t, q) << (8 * (i % 4));
+  }
+  lo[0] = lo[1] = 0u;
+  slo = 127u;
+}
+
+// the activation split of the layer's format: two exact e4m3 terms, or MXFP8
+__device__ __forceinline__ void quantize_quad8_fmt(const float (&v)[8], uint32_t (&hi)[2], uint32_t (&lo)[2],
+                                                   uint32_t& shi, uint32_t& slo, bool mxfp8) {
+  if (mxfp8)
+    quantize_quad8_mx(v, hi, lo, shi, slo);
+  else
+    quantize_quad8(v, hi, lo, shi, slo);
+}
+
 // Quantised activation rows: codes [rows][K] (hi and lo) and e8m0 scales [rows][K/32].
 struct QRows {
   uint8_t* hi;
@@ -336,7 +375,7 @@ struct QRows {
 // block sit in one quad of lanes).  All loads of a lane are issued before any group is
 // converted.
 __device__ __forceinline__ void quantize_quads(const uint16_t* __restrict__ src, QRows q, int64_t n, int64_t j0,
-                                               int64_t jstride) {
+                                               int64_t jstride, bool mxfp8 = false) {
   constexpr int U = 2;
   const int64_t ng = n / 8;
   for (int64_t base = j0; base < ng; base += U * jstride) {
@@ -358,7 +397,7 @@ __device__ __forceinline__ void quantize_quads(const uint16_t* __restrict__ src,
           v[2 * i + 1] = bf16hi(w[i]);
         }
         uint32_t hi[2], lo[2], shi, slo;
-        quantize_quad8(v, hi, lo, shi, slo);
+        quantize_quad8_fmt(v, hi, lo, shi, slo, mxfp8);
         *reinterpret_cast<uint2*>(q.hi + 8 * j) = make_uint2(hi[0], hi[1]);
         *reinterpret_cast<uint2*>(q.lo + 8 * j) = make_uint2(lo[0], lo[1]);
         if ((j & 3) == 0) {

@@ -213,7 +213,7 @@ __global__ void __launch_bounds__(256, 2) gateup_gemm_kernel(MxArgs p, const int
 #pragma unroll
       for (int i = 0; i < 8; ++i) v[i] = at[m * 65 + 32 * blk + 8 * sub + i];
       uint32_t hi[2], lo[2], shi, slo;
-      quantize_quad8(v, hi, lo, shi, slo);
+      quantize_quad8_fmt(v, hi, lo, shi, slo, p.mxfp8 != 0);
       const int64_t off = (int64_t)sslot[m] * F + rt * GT_ROWS + 32 * blk + 8 * sub;
       *reinterpret_cast<uint2*>(p.aq.hi + off) = make_uint2(hi[0], hi[1]);
       *reinterpret_cast<uint2*>(p.aq.lo + off) = make_uint2(lo[0], lo[1]);

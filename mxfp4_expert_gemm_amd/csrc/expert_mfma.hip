@@ -289,7 +289,7 @@ __global__ void __launch_bounds__(256, 2) gateup_mx_kernel(MxArgs p) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] = atile[mm][32 * blk + 8 * sub + i];
         uint32_t hi[2], lo[2], shi, slo;
-        quantize_quad8(v, hi, lo, shi, slo);
+        quantize_quad8_fmt(v, hi, lo, shi, slo, p.mxfp8 != 0);
         const int64_t off = (int64_t)srow * F + rt * MX_ROWS + 32 * blk + 8 * sub;
         *reinterpret_cast<uint2*>(p.aq.hi + off) = make_uint2(hi[0], hi[1]);
         *reinterpret_cast<uint2*>(p.aq.lo + off) = make_uint2(lo[0], lo[1]);
@@ -521,16 +521,17 @@ hipError_t launch_down_combine_mx(const MxArgs& p, const int32_t* idx, const flo
 // ------------------------------------------------- activation quantisation
 
 __global__ void __launch_bounds__(256) quantize_rows_kernel(const uint16_t* __restrict__ src, int64_t rows, int K,
-                                                            QRows q) {
-  quantize_quads(src, q, rows * K, (int64_t)blockIdx.x * blockDim.x + threadIdx.x, (int64_t)gridDim.x * blockDim.x);
+                                                            QRows q, int mxfp8) {
+  quantize_quads(src, q, rows * K, (int64_t)blockIdx.x * blockDim.x + threadIdx.x, (int64_t)gridDim.x * blockDim.x,
+                 mxfp8 != 0);
 }
 
-hipError_t launch_quantize_rows(const uint16_t* src, int64_t rows, int K, const QRows& q, hipStream_t st) {
+hipError_t launch_quantize_rows(const uint16_t* src, int64_t rows, int K, const QRows& q, bool mxfp8, hipStream_t st) {
   if (rows == 0) return hipSuccess;
   if (K % 32) return hipErrorInvalidValue;
   int64_t blocks = ceil_div(rows * (K / 8), 256);
   if (blocks > 8192) blocks = 8192;
-  hipLaunchKernelGGL(quantize_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, st, src, rows, K, q);
+  hipLaunchKernelGGL(quantize_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, st, src, rows, K, q, (int)mxfp8);
   return hipGetLastError();
 }
 

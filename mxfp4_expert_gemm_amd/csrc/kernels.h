@@ -55,6 +55,7 @@ struct RouteArgs {
   int32_t* stats;            // [4] counters: tokens needing recompute, logits recomputed, Kulisch uses
   const uint16_t* h;         // nullable [T][L] latent rows to quantise for the experts
   int32_t L;
+  int32_t mxfp8;             // 1: quantise h as MXFP8 (one term), 0: two exact e4m3 terms
   QRows hq;
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t st);
@@ -105,7 +106,8 @@ struct MxArgs {
   int32_t max_active;        // grid bound: min(E, T*k)
   const int32_t* perm;       // [T*k] slots t*k+j grouped by expert
   QRows hq;                  // [T][L] latent rows h, two-term e4m3
-  QRows aq;                  // [T*k][F] GLU outputs by slot, two-term e4m3
+  QRows aq;                  // [T*k][F] GLU outputs by slot, two-term e4m3 (MXFP8 mode: lo term zero)
+  int32_t mxfp8;             // activation format of aq (and of hq): MXFP8, else two exact e4m3 terms
   uint16_t* a_bf16;          // nullable [T*k][F] GLU outputs by slot, bf16
   float* y;                  // [T*k][L] down outputs by slot
 };
@@ -114,7 +116,7 @@ hipError_t launch_down_mx(const MxArgs& p, hipStream_t st);
 bool down_combine_fits(int64_t T, int32_t k);
 hipError_t launch_down_combine_mx(const MxArgs& p, const int32_t* idx, const float* w, uint16_t* z,
                                   hipStream_t st);
-hipError_t launch_quantize_rows(const uint16_t* src, int64_t rows, int K, const QRows& q, hipStream_t st);
+hipError_t launch_quantize_rows(const uint16_t* src, int64_t rows, int K, const QRows& q, bool mxfp8, hipStream_t st);
 
 // ---- expert_gemm.hip: grouped GEMMs for experts with many routed rows
 // tiles of up to 64 routed rows per active expert, built from counts/offsets

@@ -558,7 +558,7 @@ __device__ __forceinline__ void route_token(const RouteArgs& a, int64_t t, Route
 __device__ __forceinline__ void quantize_token_h(const RouteArgs& a, int64_t t) {
   if (!a.h) return;
   const QRows q{a.hq.hi + t * a.L, a.hq.lo + t * a.L, a.hq.shi + t * (a.L / 32), a.hq.slo + t * (a.L / 32)};
-  quantize_quads(a.h + t * a.L, q, a.L, lane_id(), WAVE);
+  quantize_quads(a.h + t * a.L, q, a.L, lane_id(), WAVE, a.mxfp8 != 0);
 }
 
 __global__ void __launch_bounds__(256) route_kernel(RouteArgs a) {
@@ -664,9 +664,9 @@ __global__ void __launch_bounds__(512) route_permute_small_kernel(RouteArgs a, P
   if (a.h) {
     if (T < nw) {
       if (wave >= T)
-        quantize_quads(a.h, a.hq, (int64_t)T * a.L, threadIdx.x - T * WAVE, blockDim.x - T * WAVE);
+        quantize_quads(a.h, a.hq, (int64_t)T * a.L, threadIdx.x - T * WAVE, blockDim.x - T * WAVE, a.mxfp8 != 0);
     } else {
-      quantize_quads(a.h, a.hq, (int64_t)T * a.L, blockDim.x - 1 - threadIdx.x, blockDim.x);
+      quantize_quads(a.h, a.hq, (int64_t)T * a.L, blockDim.x - 1 - threadIdx.x, blockDim.x, a.mxfp8 != 0);
     }
   }
   __syncthreads();  // token t's selection, ascending, is in scratch[t].oidx (one wave per token)

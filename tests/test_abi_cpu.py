@@ -45,7 +45,7 @@ def k3(T=1, **kw):
     c.update(kw)
     return moe.MoEConfig(c["num_tokens"], c["d_model"], c["d_latent"], c["d_ffn"], c["num_experts"],
                          kw.get("act", 0), kw.get("renormalize", 1), kw.get("bias_row_stride", 0),
-                         kw.get("expert_layout", 0))
+                         kw.get("expert_layout", 0), kw.get("act_format", 0))
 
 
 def ws_status(cfg, k):
@@ -69,6 +69,8 @@ def test_workspace_size_valid_and_invalid():
     assert ws_status(k3(T=-1), 16)[0] == -1
     assert ws_status(k3(expert_layout=1), 16)[0] == 0
     assert ws_status(k3(expert_layout=2), 16)[0] == -1
+    assert ws_status(k3(act_format=1), 16)[0] == 0   # MXFP8 activations
+    assert ws_status(k3(act_format=2), 16)[0] == -1
     assert moe.lib().moe_workspace_size(None, 16, ctypes.byref(ctypes.c_size_t())) == -1
 
 
@@ -130,3 +132,19 @@ def test_packed_layout_sizes_and_pack_errors():
     assert pack(None, 4, 3584, 3072, FAKE + (1 << 40), None) == -1
     assert pack(FAKE + 8, 4, 3584, 3072, FAKE + (1 << 40), None) == -1   # misaligned
     assert pack(FAKE, 4, 3584, 3072, FAKE + 4096, None) == -1            # overlapping buffers
+
+
+def test_config_struct_layout_matches_header(tmp_path):
+    """The ctypes mirror of moe_config has the header's size and field offsets."""
+    import subprocess
+    fields = [f[0] for f in moe.MoEConfig._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "moe_layer.h"\nint main(void) {\n'
+                   '  printf("%zu\\n", sizeof(moe_config));\n' +
+                   "".join(f'  printf("%zu\\n", offsetof(moe_config, {f}));\n' for f in fields) + "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    subprocess.run(["gcc", "-std=c99", "-I", inc, str(src), "-o", str(exe)], check=True)
+    got = [int(v) for v in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()]
+    assert got[0] == ctypes.sizeof(moe.MoEConfig)
+    assert got[1:] == [getattr(moe.MoEConfig, f).offset for f in fields]
