@@ -25,8 +25,12 @@ namespace moe {
 
 constexpr int GT_TOK = 64;    // routed rows per tile
 constexpr int GT_ROWS = 64;   // weight rows per block (4 waves x 16)
-constexpr int GT_PF_GATEUP = 2;  // K steps of weights in flight per wave and matrix (gate/up: two matrices)
-constexpr int GT_PF_DOWN = 4;
+// K steps of weights in flight per wave and matrix: as deep as the registers allow (the
+// one-term kernels hold half the activation operands)
+template <int TERMS>
+constexpr int gt_pf_gateup() { return TERMS == 2 ? 2 : 4; }
+template <int TERMS>
+constexpr int gt_pf_down() { return TERMS == 2 ? 4 : 8; }
 constexpr int GT_CHUNK = 2;   // K steps per LDS activation chunk
 constexpr int GT_RS = 128;    // LDS row of a step's 128 code bytes, 16-byte chunk c at c ^ (row & 7)
 // one K step of the tile in LDS: hi codes [64][GT_RS], lo codes [64][GT_RS], hi scales
@@ -34,12 +38,16 @@ constexpr int GT_RS = 128;    // LDS row of a step's 128 code bytes, 16-byte chu
 // consecutive rows and the row-order writes free of bank conflicts on gfx950.
 constexpr int GT_STEP_BYTES = 2 * GT_TOK * GT_RS + 2 * GT_TOK * 4;
 constexpr int GT_BUF_BYTES = GT_CHUNK * GT_STEP_BYTES;
-static_assert(16 % GT_PF_GATEUP == 0 && 16 % GT_PF_DOWN == 0 && 16 % GT_CHUNK == 0,
+static_assert(16 % gt_pf_gateup<1>() == 0 && 16 % gt_pf_gateup<2>() == 0 && 16 % gt_pf_down<1>() == 0 &&
+                  16 % gt_pf_down<2>() == 0 && 16 % GT_CHUNK == 0,
               "ring and chunks repeat every 16 steps");
 
-// This thread's share of one chunk: 8 16-byte code pieces and one scale dword.
+// This thread's share of one chunk: 4 TERMS 16-byte code pieces and one scale dword.
+// TERMS = 2: the two exact e4m3 terms of bf16 activations; TERMS = 1: the MXFP8 mode,
+// whose second term is zero and is neither moved nor multiplied.
+template <int TERMS>
 struct GtRegs {
-  u32x4_t v[8];
+  u32x4_t v[4 * TERMS];
   uint32_t s;
 };
 
@@ -48,51 +56,61 @@ struct GtRegs {
 // load is issued: rows past the tile read the row srow holds for them (a valid token)
 // and steps past the end re-read the last step, so the loads in flight are the same on
 // every path (see prime_stream); what they bring for such rows and steps is never used.
-__device__ __forceinline__ void gt_load(GtRegs& r, const QRows& q, const int64_t* srow, int K, int nks, int c) {
+// With one term, threads 128.. repeat the scale loads of threads 0..127 (and do not
+// store them), for the same reason.
+template <int TERMS>
+__device__ __forceinline__ void gt_load(GtRegs<TERMS>& r, const QRows& q, const int64_t* srow, int K, int nks,
+                                        int c) {
   const int tid = threadIdx.x;
-  unroll_n<8>([&](auto uc) {
+  unroll_n<4 * TERMS>([&](auto uc) {
     constexpr int u = decltype(uc)::value;
-    const int j = tid + 256 * u;  // 2048 = GT_CHUNK x 2 terms x 64 rows x 8 pieces
-    const int s = j >> 10, term = (j >> 9) & 1, m = (j >> 3) & 63, part = j & 7;
+    const int j = tid + 256 * u;  // GT_CHUNK x TERMS x 64 rows x 8 pieces
+    const int s = j >> (8 + TERMS), term = TERMS == 2 ? (j >> 9) & 1 : 0, m = (j >> 3) & 63, part = j & 7;
     const int ks = GT_CHUNK * c + s < nks ? GT_CHUNK * c + s : nks - 1;
     r.v[u] = *reinterpret_cast<const u32x4_t*>((term ? q.lo : q.hi) + srow[m] * K + 128 * ks + 16 * part);
   });
   {
-    const int s = tid >> 7, m = (tid >> 1) & 63, term = tid & 1;  // 256 = GT_CHUNK x 64 rows x 2 terms
+    const int it = TERMS == 2 ? tid : tid & 127;  // GT_CHUNK x 64 rows x TERMS
+    const int s = it >> (6 + TERMS - 1), m = (it >> (TERMS - 1)) & 63, term = TERMS == 2 ? it & 1 : 0;
     const int ks = GT_CHUNK * c + s < nks ? GT_CHUNK * c + s : nks - 1;
     r.s = *reinterpret_cast<const uint32_t*>((term ? q.slo : q.shi) + srow[m] * (K / 32) + 4 * ks);
   }
 }
 
-__device__ __forceinline__ void gt_store(const GtRegs& r, uint8_t* buf) {
+template <int TERMS>
+__device__ __forceinline__ void gt_store(const GtRegs<TERMS>& r, uint8_t* buf) {
   const int tid = threadIdx.x;
-  unroll_n<8>([&](auto uc) {
+  unroll_n<4 * TERMS>([&](auto uc) {
     constexpr int u = decltype(uc)::value;
     const int j = tid + 256 * u;
-    const int s = j >> 10, term = (j >> 9) & 1, m = (j >> 3) & 63, part = j & 7;
+    const int s = j >> (8 + TERMS), term = TERMS == 2 ? (j >> 9) & 1 : 0, m = (j >> 3) & 63, part = j & 7;
     *reinterpret_cast<u32x4_t*>(buf + s * GT_STEP_BYTES + term * GT_TOK * GT_RS + m * GT_RS + 16 * (part ^ (m & 7))) =
         r.v[u];
   });
-  {
-    const int s = tid >> 7, m = (tid >> 1) & 63, term = tid & 1;
+  if (TERMS == 2 || tid < 128) {
+    const int it = tid;
+    const int s = it >> (6 + TERMS - 1), m = (it >> (TERMS - 1)) & 63, term = TERMS == 2 ? it & 1 : 0;
     *reinterpret_cast<uint32_t*>(buf + s * GT_STEP_BYTES + 2 * GT_TOK * GT_RS + term * GT_TOK * 4 + m * 4) = r.s;
   }
 }
 
 // activation operand of step s of a chunk for tile row m (chunks g and 4 + g of the row)
+template <int TERMS>
 __device__ __forceinline__ void gt_read(AStep& a, const uint8_t* buf, int s, int m, int g) {
   const uint8_t* st = buf + s * GT_STEP_BYTES;
   const int c0 = 16 * (g ^ (m & 7)), c1 = 16 * ((4 + g) ^ (m & 7));
   const uint4 h0 = *reinterpret_cast<const uint4*>(st + m * GT_RS + c0);
   const uint4 h1 = *reinterpret_cast<const uint4*>(st + m * GT_RS + c1);
-  const uint4 l0 = *reinterpret_cast<const uint4*>(st + GT_TOK * GT_RS + m * GT_RS + c0);
-  const uint4 l1 = *reinterpret_cast<const uint4*>(st + GT_TOK * GT_RS + m * GT_RS + c1);
   a.hi[0] = (int)h0.x; a.hi[1] = (int)h0.y; a.hi[2] = (int)h0.z; a.hi[3] = (int)h0.w;
   a.hi[4] = (int)h1.x; a.hi[5] = (int)h1.y; a.hi[6] = (int)h1.z; a.hi[7] = (int)h1.w;
-  a.lo[0] = (int)l0.x; a.lo[1] = (int)l0.y; a.lo[2] = (int)l0.z; a.lo[3] = (int)l0.w;
-  a.lo[4] = (int)l1.x; a.lo[5] = (int)l1.y; a.lo[6] = (int)l1.z; a.lo[7] = (int)l1.w;
   a.shi = st[2 * GT_TOK * GT_RS + m * 4 + g];
-  a.slo = st[2 * GT_TOK * GT_RS + GT_TOK * 4 + m * 4 + g];
+  if constexpr (TERMS == 2) {
+    const uint4 l0 = *reinterpret_cast<const uint4*>(st + GT_TOK * GT_RS + m * GT_RS + c0);
+    const uint4 l1 = *reinterpret_cast<const uint4*>(st + GT_TOK * GT_RS + m * GT_RS + c1);
+    a.lo[0] = (int)l0.x; a.lo[1] = (int)l0.y; a.lo[2] = (int)l0.z; a.lo[3] = (int)l0.w;
+    a.lo[4] = (int)l1.x; a.lo[5] = (int)l1.y; a.lo[6] = (int)l1.z; a.lo[7] = (int)l1.w;
+    a.slo = st[2 * GT_TOK * GT_RS + GT_TOK * 4 + m * 4 + g];
+  }
 }
 
 // logical block of physical block b: XCD x = b mod 8 runs logical blocks
@@ -103,20 +121,20 @@ __device__ __forceinline__ int gt_logical_block(int b, int nb) { return (b & 7) 
 // The loop runs over whole 16-step blocks; steps past the end issue their (clamped)
 // loads, stores and barriers like the others and skip only the math, so every path
 // issues the same loads and the waits for them are exact.
-template <class W, int NMAT, int GT_PF>
+template <class W, int NMAT, int GT_PF, int TERMS>
 __device__ __forceinline__ void gt_mainloop(const W (&w)[NMAT], const QRows& q, const int64_t* srow, int n, int K,
                                             uint8_t* lds, f32x4 (&acc)[NMAT][4]) {
   const int lane = lane_id(), g = lane >> 4, nl = lane & 15;
   const int nks = K / 128, nc = (nks + 15) / 16;
   const int ntt = (n + 15) / 16;  // token sub-tiles holding rows
   // chunk 0 into buffer 0, chunk 1 into registers, the first weight steps in flight
-  GtRegs rg;
-  gt_load(rg, q, srow, K, nks, 0);
+  GtRegs<TERMS> rg;
+  gt_load<TERMS>(rg, q, srow, K, nks, 0);
   SBlock sb[NMAT], sbn[NMAT];
   uint4 ring[NMAT][GT_PF];
   prime_stream<W, NMAT, GT_PF>(w, sb, ring, nks);
-  gt_store(rg, lds);
-  gt_load(rg, q, srow, K, nks, 1);
+  gt_store<TERMS>(rg, lds);
+  gt_load<TERMS>(rg, q, srow, K, nks, 1);
   lds_barrier();
   for (int cb = 0; cb < nc; ++cb) {
 #pragma unroll
@@ -137,21 +155,21 @@ __device__ __forceinline__ void gt_mainloop(const W (&w)[NMAT], const QRows& q, 
         for (int tt = 0; tt < 4; ++tt) {
           if (tt >= ntt) continue;  // token sub-tile past the tile's rows
           AStep a;
-          gt_read(a, buf, J % GT_CHUNK, 16 * tt + nl, g);
+          gt_read<TERMS>(a, buf, J % GT_CHUNK, 16 * tt + nl, g);
 #pragma unroll
           for (int mq = 0; mq < NMAT; ++mq) {
             const uint32_t sw = w[mq].template scale<J>(sb[mq]);
             const i32x8 b = as_b(cw[mq]);
             acc[mq][tt] = mx_mfma<W::opsel(J)>(a.hi, b, acc[mq][tt], a.shi, sw);
-            acc[mq][tt] = mx_mfma<W::opsel(J)>(a.lo, b, acc[mq][tt], a.slo, sw);
+            if constexpr (TERMS == 2) acc[mq][tt] = mx_mfma<W::opsel(J)>(a.lo, b, acc[mq][tt], a.slo, sw);
           }
         }
       }
       if constexpr (J % GT_CHUNK == GT_CHUNK - 1) {
         // end of chunk ch: the registers hold chunk ch+1; every wave is past chunk ch-1,
         // so its buffer is free
-        gt_store(rg, lds + ((ch + 1) & 1) * GT_BUF_BYTES);
-        gt_load(rg, q, srow, K, nks, ch + 2);
+        gt_store<TERMS>(rg, lds + ((ch + 1) & 1) * GT_BUF_BYTES);
+        gt_load<TERMS>(rg, q, srow, K, nks, ch + 2);
         lds_barrier();
       }
     });
@@ -162,7 +180,7 @@ __device__ __forceinline__ void gt_mainloop(const W (&w)[NMAT], const QRows& q, 
 
 // Gate/up with the GLU: a = bf16(silu(g) u) for the tile, re-quantised to two e4m3 terms
 // into aq (routed-row order), optionally also as bf16.
-template <class W>
+template <class W, int TERMS>
 __global__ void __launch_bounds__(256, 2) gateup_gemm_kernel(MxArgs p, const int4* __restrict__ gtiles, int ntiles,
                                                               int nb) {
   extern __shared__ __align__(16) uint8_t lds[];
@@ -189,7 +207,7 @@ __global__ void __launch_bounds__(256, 2) gateup_gemm_kernel(MxArgs p, const int
   for (int mq = 0; mq < 2; ++mq)
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) acc[mq][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  gt_mainloop<W, 2, GT_PF_GATEUP>(w, p.hq, srow, n, L, lds, acc);
+  gt_mainloop<W, 2, gt_pf_gateup<TERMS>(), TERMS>(w, p.hq, srow, n, L, lds, acc);
   // GLU into an LDS tile (the activation buffers are free now), then the requantisation
   float* at = reinterpret_cast<float*>(lds);  // [64 tokens][65]
   const int f = rt * GT_ROWS + 16 * wave + nl;
@@ -227,7 +245,7 @@ __global__ void __launch_bounds__(256, 2) gateup_gemm_kernel(MxArgs p, const int
 }
 
 // Down: y[slot][l] fp32 for the tile's routed rows.
-template <class W>
+template <class W, int TERMS>
 __global__ void __launch_bounds__(256, 2) down_gemm_kernel(MxArgs p, const int4* __restrict__ gtiles, int ntiles,
                                                             int nb) {
   extern __shared__ __align__(16) uint8_t lds[];
@@ -246,7 +264,7 @@ __global__ void __launch_bounds__(256, 2) down_gemm_kernel(MxArgs p, const int4*
   f32x4 acc[1][4];
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt) acc[0][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  gt_mainloop<W, 1, GT_PF_DOWN>(w, p.aq, srow, n, F, lds, acc);
+  gt_mainloop<W, 1, gt_pf_down<TERMS>(), TERMS>(w, p.aq, srow, n, F, lds, acc);
   const int l = rt * GT_ROWS + 16 * wave + nl;
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt)
@@ -298,10 +316,24 @@ hipError_t launch_gemm_tiles(const int32_t* counts, const int32_t* offsets, int3
   return hipGetLastError();
 }
 
-template <class W>
-static hipError_t gemm_lds_limit(const void* fn) {
-  (void)sizeof(W);
-  return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 2 * GT_BUF_BYTES);
+template <class W, int TERMS>
+static hipError_t gateup_gemm_go(const MxArgs& p, const int4* gtiles, int64_t max_gtiles, int64_t nb, hipStream_t st) {
+  static const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gateup_gemm_kernel<W, TERMS>),
+                                                  hipFuncAttributeMaxDynamicSharedMemorySize, 2 * GT_BUF_BYTES);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((gateup_gemm_kernel<W, TERMS>), dim3((unsigned)nb), dim3(256), 2 * GT_BUF_BYTES, st, p, gtiles,
+                     (int)max_gtiles, (int)nb);
+  return hipGetLastError();
+}
+
+template <class W, int TERMS>
+static hipError_t down_gemm_go(const MxArgs& p, const int4* gtiles, int64_t max_gtiles, int64_t nb, hipStream_t st) {
+  static const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&down_gemm_kernel<W, TERMS>),
+                                                  hipFuncAttributeMaxDynamicSharedMemorySize, 2 * GT_BUF_BYTES);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((down_gemm_kernel<W, TERMS>), dim3((unsigned)nb), dim3(256), 2 * GT_BUF_BYTES, st, p, gtiles,
+                     (int)max_gtiles, (int)nb);
+  return hipGetLastError();
 }
 
 hipError_t launch_gateup_gemm(const MxArgs& p, const int4* gtiles, int64_t max_gtiles, hipStream_t st) {
@@ -309,17 +341,11 @@ hipError_t launch_gateup_gemm(const MxArgs& p, const int4* gtiles, int64_t max_g
   if (p.F % GT_ROWS || p.L % 128) return hipErrorInvalidValue;
   const int64_t nb = (max_gtiles * (p.F / GT_ROWS) + 7) / 8 * 8;
   if (nb > 0x7FFFFFFF) return hipErrorInvalidValue;
-  const size_t lds = 2 * GT_BUF_BYTES;
-  if (p.packed) {
-    static const hipError_t e = gemm_lds_limit<PackedW>(reinterpret_cast<const void*>(&gateup_gemm_kernel<PackedW>));
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(gateup_gemm_kernel<PackedW>, dim3((unsigned)nb), dim3(256), lds, st, p, gtiles, (int)max_gtiles, (int)nb);
-  } else {
-    static const hipError_t e = gemm_lds_limit<RecordW>(reinterpret_cast<const void*>(&gateup_gemm_kernel<RecordW>));
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(gateup_gemm_kernel<RecordW>, dim3((unsigned)nb), dim3(256), lds, st, p, gtiles, (int)max_gtiles, (int)nb);
-  }
-  return hipGetLastError();
+  if (p.packed)
+    return p.mxfp8 ? gateup_gemm_go<PackedW, 1>(p, gtiles, max_gtiles, nb, st)
+                   : gateup_gemm_go<PackedW, 2>(p, gtiles, max_gtiles, nb, st);
+  return p.mxfp8 ? gateup_gemm_go<RecordW, 1>(p, gtiles, max_gtiles, nb, st)
+                 : gateup_gemm_go<RecordW, 2>(p, gtiles, max_gtiles, nb, st);
 }
 
 hipError_t launch_down_gemm(const MxArgs& p, const int4* gtiles, int64_t max_gtiles, hipStream_t st) {
@@ -327,17 +353,11 @@ hipError_t launch_down_gemm(const MxArgs& p, const int4* gtiles, int64_t max_gti
   if (p.L % GT_ROWS || p.F % 128) return hipErrorInvalidValue;
   const int64_t nb = (max_gtiles * (p.L / GT_ROWS) + 7) / 8 * 8;
   if (nb > 0x7FFFFFFF) return hipErrorInvalidValue;
-  const size_t lds = 2 * GT_BUF_BYTES;
-  if (p.packed) {
-    static const hipError_t e = gemm_lds_limit<PackedW>(reinterpret_cast<const void*>(&down_gemm_kernel<PackedW>));
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(down_gemm_kernel<PackedW>, dim3((unsigned)nb), dim3(256), lds, st, p, gtiles, (int)max_gtiles, (int)nb);
-  } else {
-    static const hipError_t e = gemm_lds_limit<RecordW>(reinterpret_cast<const void*>(&down_gemm_kernel<RecordW>));
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(down_gemm_kernel<RecordW>, dim3((unsigned)nb), dim3(256), lds, st, p, gtiles, (int)max_gtiles, (int)nb);
-  }
-  return hipGetLastError();
+  if (p.packed)
+    return p.mxfp8 ? down_gemm_go<PackedW, 1>(p, gtiles, max_gtiles, nb, st)
+                   : down_gemm_go<PackedW, 2>(p, gtiles, max_gtiles, nb, st);
+  return p.mxfp8 ? down_gemm_go<RecordW, 1>(p, gtiles, max_gtiles, nb, st)
+                 : down_gemm_go<RecordW, 2>(p, gtiles, max_gtiles, nb, st);
 }
 
 }  // namespace moe
