@@ -242,6 +242,23 @@ moe_status moe_expert_ffn(const void* h, const uint8_t* expert_blob, int32_t k, 
 moe_status moe_combine(const float* y, const float* topk_w, int64_t num_tokens, int32_t k,
                        int32_t d_latent, void* z, moe_stream_t stream);
 
+/* REAP saliency (kimi-k3-mlx digest, REAP section: the score of expert j is the mean
+ * over calibration tokens of the router weight g_j times the 2-norm of the expert's
+ * output).  For every routed row r (slot t*k + j) of expert e:
+ *   saliency[e] += topk_w[r] * ||y[r]||_2,
+ * the rows of an expert taken in the order of perm (tokens ascending), norms and sums
+ * in fp64.  y: fp32 [T*k][d_latent], the expert outputs by slot (moe_expert_ffn);
+ * topk_w: fp32 [T*k] (moe_route); perm, expert_offsets: [T*k], [E+1] (moe_permute);
+ * saliency: fp64 [num_experts] on the device, accumulated across calls (the caller
+ * zeroes it, and divides by the number of calibration tokens at the end).  All device
+ * pointers.  An expert pruned after scoring is a router bias of -inf on it in
+ * moe_layer_forward / moe_route: it is never selected and the weights are renormalised
+ * over the experts left (at least k must remain). */
+moe_status moe_reap_saliency(const float* y, const float* topk_w, const int32_t* perm,
+                             const int32_t* expert_offsets, int64_t num_tokens, int32_t k,
+                             int32_t d_latent, int32_t num_experts, double* saliency,
+                             moe_stream_t stream);
+
 /* Dense bf16 projection: out[t][o] = bf16(sum_i in[t][i] W[o][i]), fp32
  * accumulation (the latent down/up projections).  n_in multiple of 32. */
 moe_status moe_linear_bf16(const void* in, const void* W, int64_t num_tokens, int32_t n_in,

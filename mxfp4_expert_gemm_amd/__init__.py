@@ -29,7 +29,7 @@ EXPORTS = ["moe_expert_bytes", "moe_packed_expert_bytes", "moe_pack_experts", "m
            "moe_workspace_size", "moe_layer_forward",
            "moe_layer_forward_profiled",
            "moe_dequant_mxfp4", "moe_route", "moe_topk", "moe_permute", "moe_expert_ffn", "moe_combine",
-           "moe_linear_bf16"]
+           "moe_linear_bf16", "moe_reap_saliency"]
 
 
 class MoEError(RuntimeError):
@@ -86,6 +86,7 @@ def lib():
             "moe_expert_ffn": (ctypes.c_int, [vp, vp, i32, cfgp, rp, vp, vp, vp, sz, vp]),
             "moe_combine": (ctypes.c_int, [vp, vp, i64, i32, i32, vp, vp]),
             "moe_linear_bf16": (ctypes.c_int, [vp, vp, i64, i32, i32, vp, vp]),
+            "moe_reap_saliency": (ctypes.c_int, [vp, vp, vp, vp, i64, i32, i32, i32, vp, vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -280,7 +281,29 @@ def linear_bf16(inp: torch.Tensor, W: torch.Tensor) -> torch.Tensor:
     return out
 
 
+def reap_saliency(y: torch.Tensor, topk_w: torch.Tensor, perm: torch.Tensor, expert_offsets: torch.Tensor,
+                  num_experts: int, saliency: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Adds the REAP score sums of these routed rows to saliency (fp64 [E], zeros if None)."""
+    T, k = topk_w.shape
+    if saliency is None:
+        saliency = torch.zeros(num_experts, dtype=torch.float64, device=y.device)
+    _check(lib().moe_reap_saliency(_p(y), _p(topk_w), _p(perm), _p(expert_offsets), T, k, y.shape[1], num_experts,
+                                   _p(saliency), _stream()), "moe_reap_saliency")
+    return saliency
+
+
+def reap_prune_bias(saliency: torch.Tensor, n_keep: int) -> torch.Tensor:
+    """Router bias of a REAP-pruned layer: 0 on the n_keep experts of highest saliency
+    (ties to the lower index), -inf on the others (host logic: a top-n and a fill)."""
+    E = saliency.numel()
+    order = sorted(range(E), key=lambda e: (-float(saliency[e]), e))
+    bias = torch.full((E,), float("-inf"), dtype=torch.float32, device=saliency.device)
+    bias[torch.tensor(order[:n_keep], device=saliency.device)] = 0.0
+    return bias
+
+
 __all__ = ["lib", "MoEConfig", "RoutingOut", "MoEError", "make_config", "expert_bytes", "packed_expert_bytes",
            "pack_experts", "LAYOUT_RECORD", "LAYOUT_PACKED", "ACT_FMT_BF16", "ACT_FMT_MXFP8", "workspace_size",
            "alloc_workspace", "layer_forward", "layer_forward_profiled", "StageEvents", "STAGES", "dequant_mxfp4", "route", "topk", "permute", "expert_ffn", "combine",
-           "linear_bf16", "ACT_SILU", "ACT_SITU", "ROUTE_EXACT_ALL", "EXPORTS", "LIB_PATH"]
+           "linear_bf16", "reap_saliency", "reap_prune_bias", "ACT_SILU", "ACT_SITU", "ROUTE_EXACT_ALL", "EXPORTS",
+           "LIB_PATH"]

@@ -11,7 +11,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe_layer.so")
 SOURCES = ["dequant.hip", "dense_gemv.hip", "route.hip", "permute.hip", "expert_mfma.hip", "expert_gemm.hip", "dense_mfma.hip",
-           "combine.hip", "capi.hip"]
+           "combine.hip", "reap.hip", "capi.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

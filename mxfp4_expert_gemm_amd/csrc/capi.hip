@@ -464,6 +464,18 @@ moe_status moe_combine(const float* y, const float* topk_w, int64_t num_tokens, 
                             reinterpret_cast<hipStream_t>(stream)));
 }
 
+moe_status moe_reap_saliency(const float* y, const float* topk_w, const int32_t* perm, const int32_t* expert_offsets,
+                             int64_t num_tokens, int32_t k, int32_t d_latent, int32_t num_experts, double* saliency,
+                             moe_stream_t stream) {
+  if (!y || !topk_w || !perm || !expert_offsets || !saliency || num_tokens < 0 || k < 1 || k > MAX_K ||
+      d_latent <= 0 || num_experts < 1 || k > num_experts)
+    return MOE_ERR_INVALID_ARG;
+  if (num_tokens * k > (int64_t)INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return MOE_OK;
+  return dev(launch_reap_saliency(y, topk_w, perm, expert_offsets, num_experts, d_latent, saliency,
+                                  reinterpret_cast<hipStream_t>(stream)));
+}
+
 moe_status moe_linear_bf16(const void* in, const void* W, int64_t num_tokens, int32_t n_in, int32_t n_out, void* out,
                            moe_stream_t stream) {
   if (!in || !W || !out || num_tokens < 0 || n_in <= 0 || n_out <= 0 || n_in % 32) return MOE_ERR_INVALID_ARG;

@@ -126,6 +126,10 @@ hipError_t launch_gemm_tiles(const int32_t* counts, const int32_t* offsets, int3
 hipError_t launch_gateup_gemm(const MxArgs& p, const int4* gtiles, int64_t max_gtiles, hipStream_t st);
 hipError_t launch_down_gemm(const MxArgs& p, const int4* gtiles, int64_t max_gtiles, hipStream_t st);
 
+// ---- reap.hip: saliency[e] += sum over e's rows (perm order) of w[slot] ||y[slot]||_2
+hipError_t launch_reap_saliency(const float* y, const float* w, const int32_t* perm, const int32_t* offsets,
+                                int32_t E, int32_t L, double* saliency, hipStream_t st);
+
 // ---- combine.hip
 hipError_t launch_combine(const float* y, const float* w, int64_t T, int32_t k, int32_t L, uint16_t* z,
                           hipStream_t st);

@@ -326,7 +326,13 @@ __device__ __forceinline__ void route_token_general(const RouteArgs& a, int64_t 
         const double r = a.gamma * xn * (double)a.wnorm[e] * (1.0 + 0x1p-20) + abs_pad +
                          0x1p-21 * ((double)fabsf(lf) + (double)fabsf(b));
         const double c = (double)lf + (double)b;
-        if (__builtin_isfinite(lf) && __builtin_isfinite(b) && __builtin_isfinite(r)) {
+        if (b == -__builtin_inff() && __builtin_isfinite(lf) && __builtin_isfinite(r) &&
+            fabs((double)lf) + r < 0x1.fffffep127) {
+          // a bias of -inf (an expert pruned away): the exact logit is finite, so the
+          // biased logit is exactly -inf and never needs recomputing
+          val[i] = lo[i] = hi[i] = -__builtin_inff();
+          key[i] = order_key(-__builtin_inff());
+        } else if (__builtin_isfinite(lf) && __builtin_isfinite(b) && __builtin_isfinite(r)) {
           // outward-rounded fp32 ends of the interval holding the exact biased logit
           float l32 = (float)(c - r), h32 = (float)(c + r);
           if ((double)l32 > c - r) l32 = next_down(l32);
@@ -475,7 +481,14 @@ __device__ __forceinline__ void route_token(const RouteArgs& a, int64_t t, Route
       } else {
         c[i] = lf[i] + bv[i];
         R[i] = gam * wn[i] + pad + 0x1p-20f * (fabsf(lf[i]) + fabsf(bv[i]));
-        if (!(__builtin_isfinite(c[i]) && __builtin_isfinite(R[i]))) {
+        if (bv[i] == -__builtin_inff()) {
+          // pruned expert (bias -inf): exactly -inf when the exact logit is finite, which
+          // the radius shows; else unknown
+          const float rr = gam * wn[i] + pad + 0x1p-20f * fabsf(lf[i]);
+          const bool known = __builtin_isfinite(lf[i]) && __builtin_isfinite(rr) && fabsf(lf[i]) + rr < 0x1p127f;
+          c[i] = -__builtin_inff();
+          R[i] = known ? 0.f : __builtin_inff();
+        } else if (!(__builtin_isfinite(c[i]) && __builtin_isfinite(R[i]))) {
           c[i] = -__builtin_inff();  // unknown: the general path recomputes it if it can matter
           R[i] = __builtin_inff();
         }

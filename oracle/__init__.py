@@ -68,12 +68,13 @@ def lib():
         L.moe_ref_layer_forward_fmt.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, i64, vp,
                                                 vp, vp, vp, i64, vp, vp, vp, vp, vp, vp]
         L.moe_ref_combine.argtypes = [vp, vp, i64, i32, i32, vp]
+        L.moe_ref_reap_saliency.argtypes = [vp, vp, vp, i64, i32, i32, i32, vp]
         L.moe_ref_layer_forward.argtypes = [i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, i64, vp,
                                             vp, vp, vp, i64, vp, vp, vp, vp, vp, vp]
         for name in ("moe_ref_dequant_matrix", "moe_ref_router_logits", "moe_ref_select",
                      "moe_ref_permute", "moe_ref_linear_bf16", "moe_ref_expert", "moe_ref_combine",
                      "moe_ref_layer_forward", "moe_ref_expert_fmt", "moe_ref_mxfp8_block",
-                     "moe_ref_layer_forward_fmt"):
+                     "moe_ref_layer_forward_fmt", "moe_ref_reap_saliency"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -196,6 +197,17 @@ def expert(h: np.ndarray, record: np.ndarray, d_latent: int, d_ffn: int, act: in
     _check(lib().moe_ref_expert_fmt(_p(np.ascontiguousarray(h)), _p(np.ascontiguousarray(record)), d_latent,
                                     d_ffn, act, act_format, _p(a), _p(y)), "expert")
     return a, y
+
+
+def reap_saliency(y: np.ndarray, w: np.ndarray, idx: np.ndarray, num_experts: int) -> np.ndarray:
+    """Sum over routed rows of w * ||y||_2 per expert (fp64 [E]); y [T*k, L] by slot."""
+    T, k = idx.shape
+    s = np.zeros(num_experts, dtype=np.float64)
+    _check(lib().moe_ref_reap_saliency(_p(np.ascontiguousarray(y, dtype=np.float32)),
+                                       _p(np.ascontiguousarray(w, dtype=np.float32)),
+                                       _p(np.ascontiguousarray(idx, dtype=np.int32)), T, k, y.shape[1],
+                                       num_experts, _p(s)), "reap_saliency")
+    return s
 
 
 def combine(y: np.ndarray, w: np.ndarray) -> np.ndarray:

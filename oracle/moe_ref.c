@@ -451,6 +451,26 @@ int moe_ref_combine(const float* y, const float* w, int64_t T, int32_t k, int32_
   return MOE_REF_OK;
 }
 
+/* ------------------------------------------------------------- REAP saliency */
+
+/* The REAP score's sum (kimi-k3-mlx digest, REAP section): for each token t and slot j,
+ * the router weight w[t][j] times the 2-norm of that expert's output y[t*k+j] is added
+ * to s[idx[t][j]], in token order; squares and sums in fp64. */
+int moe_ref_reap_saliency(const float* y, const float* w, const int32_t* idx, int64_t T, int32_t k, int32_t L,
+                          int32_t E, double* s) {
+  if (!y || !w || !idx || !s || T < 0 || k < 1 || L <= 0 || E < 1) return MOE_REF_ERR_ARG;
+  for (int64_t t = 0; t < T; ++t)
+    for (int32_t j = 0; j < k; ++j) {
+      const int32_t e = idx[t * k + j];
+      if (e < 0 || e >= E) return MOE_REF_ERR_ARG;
+      const float* row = y + (t * k + j) * (int64_t)L;
+      double sq = 0.0;
+      for (int32_t l = 0; l < L; ++l) sq += (double)row[l] * (double)row[l];
+      s[e] += (double)w[t * k + j] * sqrt(sq);
+    }
+  return MOE_REF_OK;
+}
+
 /* ------------------------------------------------------------ whole layer */
 
 int moe_ref_layer_forward_fmt(int32_t d, int32_t L, int32_t F, int32_t E, int32_t k, int32_t act,

@@ -101,6 +101,10 @@ int moe_ref_permute(const int32_t* idx, int64_t T, int32_t k, int32_t E, int32_t
 int moe_ref_linear_bf16(const uint16_t* in, const uint16_t* W, int64_t T, int32_t n_in, int32_t n_out,
                         uint16_t* out);
 
+/* REAP saliency sum: s[idx[t][j]] += w[t][j] * ||y[t*k+j]||_2 (fp64), accumulated */
+int moe_ref_reap_saliency(const float* y, const float* w, const int32_t* idx, int64_t T, int32_t k,
+                          int32_t L, int32_t E, double* s);
+
 /* SiLU in double, the oracle's GLU activation */
 double moe_ref_silu(double g);
 
