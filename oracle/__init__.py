@@ -67,6 +67,8 @@ def lib():
         L.moe_ref_mxfp8_block.argtypes = [vp, vp, vp]
         L.moe_ref_layer_forward_fmt.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, i64, vp,
                                                 vp, vp, vp, i64, vp, vp, vp, vp, vp, vp]
+        L.moe_ref_layer_forward_shared.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, i64, vp,
+                                                   vp, vp, vp, i64, vp, vp, vp, vp, vp, vp, vp, i32, i32]
         L.moe_ref_combine.argtypes = [vp, vp, i64, i32, i32, vp]
         L.moe_ref_reap_saliency.argtypes = [vp, vp, vp, i64, i32, i32, i32, vp]
         L.moe_ref_layer_forward.argtypes = [i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, i64, vp,
@@ -74,7 +76,7 @@ def lib():
         for name in ("moe_ref_dequant_matrix", "moe_ref_router_logits", "moe_ref_select",
                      "moe_ref_permute", "moe_ref_linear_bf16", "moe_ref_expert", "moe_ref_combine",
                      "moe_ref_layer_forward", "moe_ref_expert_fmt", "moe_ref_mxfp8_block",
-                     "moe_ref_layer_forward_fmt", "moe_ref_reap_saliency"):
+                     "moe_ref_layer_forward_fmt", "moe_ref_reap_saliency", "moe_ref_layer_forward_shared"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -222,7 +224,8 @@ def combine(y: np.ndarray, w: np.ndarray) -> np.ndarray:
 
 def layer_forward(x, router_w, latent_down, latent_up, blob, k: int, d_latent: int, d_ffn: int,
                   bias: Optional[np.ndarray] = None, tokens: Optional[Sequence[int]] = None,
-                  act: int = ACT_SILU, renormalize: bool = True, act_format: int = ACT_BF16) -> dict:
+                  act: int = ACT_SILU, renormalize: bool = True, act_format: int = ACT_BF16,
+                  shared_blob: Optional[np.ndarray] = None, num_shared: int = 0, d_ffn_shared: int = 0) -> dict:
     """Whole layer for `tokens` (default: all).  Returns dict of out, idx, w, logits, h, z."""
     T, d = x.shape
     E = router_w.shape[0]
@@ -235,9 +238,10 @@ def layer_forward(x, router_w, latent_down, latent_up, blob, k: int, d_latent: i
     logits = np.empty((n, E), dtype=np.float32)
     h = np.empty((n, d_latent), dtype=np.uint16)
     z = np.empty((n, d_latent), dtype=np.uint16)
-    rc = lib().moe_ref_layer_forward_fmt(d, d_latent, d_ffn, E, k, act, act_format, int(renormalize), _p(x),
-                                         _p(router_w),
-                                     _p(bias), bias_stride, _p(latent_down), _p(latent_up), _p(blob),
-                                     _p(tok), n, _p(out), _p(idx), _p(w), _p(logits), _p(h), _p(z))
+    sb = None if shared_blob is None else np.ascontiguousarray(shared_blob)
+    rc = lib().moe_ref_layer_forward_shared(d, d_latent, d_ffn, E, k, act, act_format, int(renormalize), _p(x),
+                                            _p(router_w), _p(bias), bias_stride, _p(latent_down), _p(latent_up),
+                                            _p(blob), _p(tok), n, _p(out), _p(idx), _p(w), _p(logits), _p(h), _p(z),
+                                            _p(sb), num_shared, d_ffn_shared)
     _check(rc, "layer_forward")
     return dict(out=out, idx=idx, w=w, logits=logits, h=h, z=z)

@@ -473,12 +473,18 @@ int moe_ref_reap_saliency(const float* y, const float* w, const int32_t* idx, in
 
 /* ------------------------------------------------------------ whole layer */
 
-int moe_ref_layer_forward_fmt(int32_t d, int32_t L, int32_t F, int32_t E, int32_t k, int32_t act,
-                              int32_t act_format, int32_t renormalize, const uint16_t* x, const uint16_t* router_w,
+/* The layer with num_shared always-on shared experts (kimi-k3-mlx digest, architecture
+ * table and LatentMoE bullet: two per token, and they work at the full width, not in
+ * the latent).  Reading: each is a SiLU-GLU expert on the token x itself, an MXFP4 record
+ * of the routed format with (L, F) = (d, F_s), weight 1; its fp32 output joins the
+ * latent-up product before the one bf16 rounding of out. */
+int moe_ref_layer_forward_shared(int32_t d, int32_t L, int32_t F, int32_t E, int32_t k, int32_t act,
+                                 int32_t act_format, int32_t renormalize, const uint16_t* x, const uint16_t* router_w,
                           const float* bias, int64_t bias_stride, const uint16_t* latent_down,
                           const uint16_t* latent_up, const uint8_t* blob, const int32_t* tokens,
                           int64_t n_tokens, uint16_t* out, int32_t* idx, float* w, float* logits,
-                          uint16_t* h_out, uint16_t* z_out) {
+                          uint16_t* h_out, uint16_t* z_out, const uint8_t* shared_blob, int32_t num_shared,
+                          int32_t F_s) {
   if (!x || !router_w || !latent_down || !latent_up || !blob || !out || d <= 0 || L <= 0 ||
       F <= 0 || E <= 0 || k < 1 || k > E || n_tokens < 0 || L % 32 || F % 32)
     return MOE_REF_ERR_ARG;
@@ -490,8 +496,10 @@ int moe_ref_layer_forward_fmt(int32_t d, int32_t L, int32_t F, int32_t E, int32_
   uint16_t* h = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)L);
   float* y = (float*)malloc(sizeof(float) * (size_t)k * (size_t)L);
   uint16_t* z = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)L);
+  float* ys = num_shared > 0 ? (float*)malloc(sizeof(float) * (size_t)num_shared * (size_t)d) : NULL;
   int rc = MOE_REF_OK;
-  if (!lg || !id || !wt || !h || !y || !z) rc = MOE_REF_ERR_ARG;
+  if (!lg || !id || !wt || !h || !y || !z || (num_shared > 0 && (!ys || !shared_blob || F_s <= 0 || F_s % 32)))
+    rc = MOE_REF_ERR_ARG;
   for (int64_t i = 0; i < n_tokens && rc == MOE_REF_OK; ++i) {
     int64_t t = tokens ? tokens[i] : i;
     const uint16_t* xt = x + t * d;
@@ -502,15 +510,39 @@ int moe_ref_layer_forward_fmt(int32_t d, int32_t L, int32_t F, int32_t E, int32_
     for (int32_t j = 0; j < k && rc == MOE_REF_OK; ++j)
       rc = moe_ref_expert_fmt(h, blob + (size_t)id[j] * rec, L, F, act, act_format, NULL, y + (size_t)j * L);
     moe_ref_combine(y, wt, 1, k, L, z);
-    moe_ref_linear_bf16(z, latent_up, 1, L, d, out + i * d);
+    if (num_shared == 0) {
+      moe_ref_linear_bf16(z, latent_up, 1, L, d, out + i * d);
+    } else {
+      const size_t srec = moe_ref_expert_bytes(d, F_s);
+      for (int32_t sx = 0; sx < num_shared && rc == MOE_REF_OK; ++sx)
+        rc = moe_ref_expert_fmt(xt, shared_blob + (size_t)sx * srec, d, F_s, act, act_format, NULL,
+                                ys + (size_t)sx * d);
+      for (int32_t m = 0; m < d; ++m) {
+        double acc = 0.0;
+        for (int32_t l = 0; l < L; ++l) acc += bf16_to_f64(z[l]) * bf16_to_f64(latent_up[(int64_t)m * L + l]);
+        for (int32_t sx = 0; sx < num_shared; ++sx) acc += (double)ys[(size_t)sx * d + m];
+        out[i * d + m] = moe_ref_bf16_from_f64(acc);
+      }
+    }
     if (idx) memcpy(idx + i * k, id, sizeof(int32_t) * (size_t)k);
     if (w) memcpy(w + i * k, wt, sizeof(float) * (size_t)k);
     if (logits) memcpy(logits + i * E, lg, sizeof(float) * (size_t)E);
     if (h_out) memcpy(h_out + i * L, h, sizeof(uint16_t) * (size_t)L);
     if (z_out) memcpy(z_out + i * L, z, sizeof(uint16_t) * (size_t)L);
   }
-  free(lg); free(id); free(wt); free(h); free(y); free(z);
+  free(lg); free(id); free(wt); free(h); free(y); free(z); free(ys);
   return rc;
+}
+
+int moe_ref_layer_forward_fmt(int32_t d, int32_t L, int32_t F, int32_t E, int32_t k, int32_t act,
+                              int32_t act_format, int32_t renormalize, const uint16_t* x, const uint16_t* router_w,
+                              const float* bias, int64_t bias_stride, const uint16_t* latent_down,
+                              const uint16_t* latent_up, const uint8_t* blob, const int32_t* tokens,
+                              int64_t n_tokens, uint16_t* out, int32_t* idx, float* w, float* logits,
+                              uint16_t* h_out, uint16_t* z_out) {
+  return moe_ref_layer_forward_shared(d, L, F, E, k, act, act_format, renormalize, x, router_w, bias, bias_stride,
+                                      latent_down, latent_up, blob, tokens, n_tokens, out, idx, w, logits, h_out,
+                                      z_out, NULL, 0, 0);
 }
 
 int moe_ref_layer_forward(int32_t d, int32_t L, int32_t F, int32_t E, int32_t k, int32_t act,

@@ -132,6 +132,16 @@ int moe_ref_layer_forward(int32_t d_model, int32_t d_latent, int32_t d_ffn, int3
                           const uint8_t* expert_blob, const int32_t* tokens, int64_t n_tokens,
                           uint16_t* out, int32_t* idx, float* w, float* logits, uint16_t* h,
                           uint16_t* z);
+/* the same with num_shared shared experts (records of moe_ref_expert_bytes(d_model, F_s)
+ * in shared_blob, SiLU-GLU on x, weight 1, added to the latent-up product before the
+ * bf16 rounding of out) */
+int moe_ref_layer_forward_shared(int32_t d_model, int32_t d_latent, int32_t d_ffn, int32_t num_experts,
+                                 int32_t k, int32_t act, int32_t act_format, int32_t renormalize,
+                                 const uint16_t* x, const uint16_t* router_w, const float* bias,
+                                 int64_t bias_stride, const uint16_t* latent_down, const uint16_t* latent_up,
+                                 const uint8_t* expert_blob, const int32_t* tokens, int64_t n_tokens,
+                                 uint16_t* out, int32_t* idx, float* w, float* logits, uint16_t* h,
+                                 uint16_t* z, const uint8_t* shared_blob, int32_t num_shared, int32_t F_s);
 /* the same with the activation format of the expert GEMM inputs */
 int moe_ref_layer_forward_fmt(int32_t d_model, int32_t d_latent, int32_t d_ffn, int32_t num_experts,
                               int32_t k, int32_t act, int32_t act_format, int32_t renormalize,

@@ -439,3 +439,48 @@ def test_situ_activation_rejected():
     with pytest.raises(RuntimeError):
         oracle.layer_forward(Ly["x"], Ly["router_w"], Ly["latent_down"], Ly["latent_up"], Ly["blob"], c.k, c.L, c.F,
                              act=oracle.ACT_SITU)
+
+
+# ------------------------------------------------------------ shared experts
+
+def _zero_down(blob, L, F, E):
+    """The records with their down matrices' codes set to zero (+0), scales kept."""
+    out = blob.copy()
+    rec = synth.expert_record_bytes(L, F)
+    mat = F * L // 2 + F * L // 32
+    for e in range(E):
+        out[e * rec + 2 * mat:e * rec + 2 * mat + F * L // 2] = 0
+    return out
+
+
+def test_shared_experts_none_is_the_routed_layer():
+    x, Wr, Wd, Wu, blob, d, L, F, T = _tiny_layer(E=6, seed=61)
+    a = oracle.layer_forward(x, Wr, Wd, Wu, blob, 2, L, F)
+    b = oracle.layer_forward(x, Wr, Wd, Wu, blob, 2, L, F, shared_blob=synth.expert_blob(62, d, 64, 2), num_shared=0,
+                             d_ffn_shared=64)
+    for key in a:
+        assert np.array_equal(a[key], b[key]), key
+
+
+def test_shared_experts_alone_are_dense_glu_mlps_on_x():
+    """Routed experts whose down matrices are zero give z = 0, so out is the bf16 of the
+    sum of the shared experts' outputs, each a dense GLU MLP on the full-width x."""
+    E, k, F_s, S = 6, 2, 64, 2
+    x, Wr, Wd, Wu, blob, d, L, F, T = _tiny_layer(E=E, seed=63)
+    shared = synth.expert_blob(64, d, F_s, S)
+    r = oracle.layer_forward(x, Wr, Wd, Wu, _zero_down(blob, L, F, E), k, L, F, shared_blob=shared, num_shared=S,
+                             d_ffn_shared=F_s)
+    assert (r["z"] == 0).all()
+    srec = synth.expert_record_bytes(d, F_s)
+    for t in range(T):
+        ys = [_np_glu_expert(x[t], shared[s * srec:(s + 1) * srec], d, F_s)[1].astype(np.float64) for s in range(S)]
+        assert np.array_equal(r["out"][t], f64_to_bf16_bits(ys[0] + ys[1]))
+
+
+def test_shared_experts_with_zero_output_leave_the_layer():
+    E, k, F_s = 6, 2, 64
+    x, Wr, Wd, Wu, blob, d, L, F, T = _tiny_layer(E=E, seed=65)
+    shared = _zero_down(synth.expert_blob(66, d, F_s, 2), d, F_s, 2)
+    a = oracle.layer_forward(x, Wr, Wd, Wu, blob, k, L, F)
+    b = oracle.layer_forward(x, Wr, Wd, Wu, blob, k, L, F, shared_blob=shared, num_shared=2, d_ffn_shared=F_s)
+    assert np.array_equal(a["out"], b["out"])
