@@ -119,6 +119,8 @@ typedef struct {
   int64_t bias_row_stride; /* router bias: 0 -> one fp32 [E] row for all tokens; E -> fp32 [T][E] */
   int32_t expert_layout;   /* moe_expert_layout of expert_blob */
   int32_t act_format;      /* moe_act_format of the expert GEMM inputs */
+  int32_t num_shared;      /* always-on shared experts (0..8; needs moe_layer_forward_shared) */
+  int32_t d_ffn_shared;    /* their FFN width F_s (multiple of 128, at most 7168; 0 if none) */
 } moe_config;
 
 /* Optional routing outputs of moe_layer_forward / inputs+outputs of the stage
@@ -203,6 +205,25 @@ moe_status moe_layer_forward_profiled(const void* x, const void* router_w, const
                                       const moe_config* cfg, const float* router_bias, void* out,
                                       moe_routing_out* routing, void* workspace, size_t workspace_bytes,
                                       const moe_stage_events* events, moe_stream_t stream);
+
+/* The layer with cfg->num_shared always-on shared experts (kimi-k3-mlx digest,
+ * architecture table: two per token; LatentMoE bullet: they work at the full width,
+ * not in the latent).  The pages give neither their width nor their format; this
+ * build's reading: each is a SiLU-GLU expert on the token x, stored like a routed
+ * expert (the same record layout, cfg->expert_layout) with (L, F) = (d_model,
+ * d_ffn_shared), so shared_blob holds num_shared records of
+ * moe_expert_bytes(d_model, d_ffn_shared) (or the packed size); each has weight 1, and
+ * its fp32 output is added to the latent-up product before the one bf16 rounding:
+ *   out[t] = bf16(z[t] . W_u^T + sum_s y_s(x[t])).
+ * x is split for the matrix cores in cfg->act_format like h.  The workspace grows by
+ * the shared rows (moe_workspace_size accounts for them).  moe_layer_forward is this
+ * call with num_shared = 0; with num_shared > 0 it returns MOE_ERR_INVALID_ARG.
+ * shared_blob: device, 16-byte aligned. */
+moe_status moe_layer_forward_shared(const void* x, const void* router_w, const void* latent_down,
+                                    const void* latent_up, const uint8_t* expert_blob, int32_t k,
+                                    const moe_config* cfg, const float* router_bias, const uint8_t* shared_blob,
+                                    void* out, moe_routing_out* routing, void* workspace, size_t workspace_bytes,
+                                    moe_stream_t stream);
 
 /* ---- stage entry points (the same kernels moe_layer_forward runs) ---- */
 

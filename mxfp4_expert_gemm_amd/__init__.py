@@ -29,7 +29,7 @@ EXPORTS = ["moe_expert_bytes", "moe_packed_expert_bytes", "moe_pack_experts", "m
            "moe_workspace_size", "moe_layer_forward",
            "moe_layer_forward_profiled",
            "moe_dequant_mxfp4", "moe_route", "moe_topk", "moe_permute", "moe_expert_ffn", "moe_combine",
-           "moe_linear_bf16", "moe_reap_saliency"]
+           "moe_linear_bf16", "moe_reap_saliency", "moe_layer_forward_shared"]
 
 
 class MoEError(RuntimeError):
@@ -42,7 +42,8 @@ class MoEConfig(ctypes.Structure):
     _fields_ = [("num_tokens", ctypes.c_int64), ("d_model", ctypes.c_int32), ("d_latent", ctypes.c_int32),
                 ("d_ffn", ctypes.c_int32), ("num_experts", ctypes.c_int32), ("act", ctypes.c_int32),
                 ("renormalize", ctypes.c_int32), ("bias_row_stride", ctypes.c_int64),
-                ("expert_layout", ctypes.c_int32), ("act_format", ctypes.c_int32)]
+                ("expert_layout", ctypes.c_int32), ("act_format", ctypes.c_int32), ("num_shared", ctypes.c_int32),
+                ("d_ffn_shared", ctypes.c_int32)]
 
 
 NUM_STAGES = 7
@@ -87,6 +88,7 @@ def lib():
             "moe_combine": (ctypes.c_int, [vp, vp, i64, i32, i32, vp, vp]),
             "moe_linear_bf16": (ctypes.c_int, [vp, vp, i64, i32, i32, vp, vp]),
             "moe_reap_saliency": (ctypes.c_int, [vp, vp, vp, vp, i64, i32, i32, i32, vp, vp]),
+            "moe_layer_forward_shared": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, cfgp, vp, vp, vp, rp, vp, sz, vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -118,10 +120,11 @@ def _stream(stream=None):
 
 def make_config(num_tokens: int, d_model: int, d_latent: int, d_ffn: int, num_experts: int, *,
                 act: int = ACT_SILU, renormalize: bool = True, bias: Optional[torch.Tensor] = None,
-                packed: bool = False, act_format: int = ACT_FMT_BF16) -> MoEConfig:
+                packed: bool = False, act_format: int = ACT_FMT_BF16, num_shared: int = 0,
+                d_ffn_shared: int = 0) -> MoEConfig:
     stride = 0 if bias is None or bias.dim() == 1 else num_experts
     return MoEConfig(num_tokens, d_model, d_latent, d_ffn, num_experts, act, int(renormalize), stride,
-                     LAYOUT_PACKED if packed else LAYOUT_RECORD, act_format)
+                     LAYOUT_PACKED if packed else LAYOUT_RECORD, act_format, num_shared, d_ffn_shared)
 
 
 def expert_bytes(d_latent: int, d_ffn: int) -> int:
@@ -162,21 +165,29 @@ def layer_forward(x, router_w, latent_down, latent_up, expert_blob, k: int, *, d
                   bias: Optional[torch.Tensor] = None, renormalize: bool = True, act: int = ACT_SILU,
                   out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                   routing: Optional[dict] = None, stream=None, packed: bool = False,
-                  act_format: int = ACT_FMT_BF16) -> torch.Tensor:
-    """out = layer(x); routing (dict of preallocated tensors) receives the routing if given."""
+                  act_format: int = ACT_FMT_BF16, shared_blob: Optional[torch.Tensor] = None,
+                  num_shared: int = 0, d_ffn_shared: int = 0) -> torch.Tensor:
+    """out = layer(x); routing (dict of preallocated tensors) receives the routing if given;
+    shared_blob with num_shared records of width d_ffn_shared adds the shared experts."""
     T, d = x.shape
     E = router_w.shape[0]
     L = latent_down.shape[0]
     cfg = make_config(T, d, L, d_ffn, E, act=act, renormalize=renormalize, bias=bias, packed=packed,
-                      act_format=act_format)
+                      act_format=act_format, num_shared=num_shared, d_ffn_shared=d_ffn_shared)
     if out is None:
         out = torch.empty((T, d), dtype=x.dtype, device=x.device)
     if workspace is None:
         workspace = alloc_workspace(cfg, k, x.device)
     r = _routing(routing)
-    _check(lib().moe_layer_forward(_p(x), _p(router_w), _p(latent_down), _p(latent_up), _p(expert_blob), k,
-                                   ctypes.byref(cfg), _p(bias), _p(out), ctypes.byref(r) if r else None,
-                                   _p(workspace), workspace.numel(), _stream(stream)), "moe_layer_forward")
+    if num_shared > 0:
+        _check(lib().moe_layer_forward_shared(_p(x), _p(router_w), _p(latent_down), _p(latent_up), _p(expert_blob),
+                                              k, ctypes.byref(cfg), _p(bias), _p(shared_blob), _p(out),
+                                              ctypes.byref(r) if r else None, _p(workspace), workspace.numel(),
+                                              _stream(stream)), "moe_layer_forward_shared")
+    else:
+        _check(lib().moe_layer_forward(_p(x), _p(router_w), _p(latent_down), _p(latent_up), _p(expert_blob), k,
+                                       ctypes.byref(cfg), _p(bias), _p(out), ctypes.byref(r) if r else None,
+                                       _p(workspace), workspace.numel(), _stream(stream)), "moe_layer_forward")
     return out
 
 

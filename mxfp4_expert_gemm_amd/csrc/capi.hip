@@ -14,9 +14,13 @@ constexpr int MAX_K = 64;
 constexpr int MAX_E = 1024;    // experts held in registers by the routing wave
 constexpr int MAX_DIM = 8192;  // columns a GEMV wave holds in registers
 constexpr int MAX_EXPERT_DIM = 7168;  // latent / FFN width whose staged activation rows fit LDS
+constexpr int MAX_SHARED = 8;
 
 struct Layout {
   size_t logits_fast, xnorm, wnorm, idx, w, counts, offsets, perm, tiles, nact, permws, h, y, z, gtiles;
+  // shared experts: x split for the matrix cores, their grouping, GLU rows, outputs
+  size_t xq_hi, xq_lo, xq_shi, xq_slo, s_idx, s_counts, s_offsets, s_perm, s_tiles, s_nact, s_permws, sq_hi, sq_lo,
+      sq_shi, sq_slo, s_y, s_gtiles;
   size_t hq_hi, hq_lo, hq_shi, hq_slo, aq_hi, aq_lo, aq_shi, aq_slo;
   size_t total;
 };
@@ -54,6 +58,28 @@ Layout layout(const moe_config& c, int k) {
   l.y = take(T * K * L * 4);
   l.z = take(T * L * 2);
   l.gtiles = take((size_t)gemm_max_tiles((int64_t)(T * K), (int32_t)E) * 16);
+  const size_t S = (size_t)c.num_shared, D = (size_t)c.d_model, FS = (size_t)c.d_ffn_shared;
+  l.xq_hi = l.xq_lo = l.xq_shi = l.xq_slo = l.s_idx = l.s_counts = l.s_offsets = l.s_perm = l.s_tiles = l.s_nact =
+      l.s_permws = l.sq_hi = l.sq_lo = l.sq_shi = l.sq_slo = l.s_y = l.s_gtiles = 0;
+  if (S > 0) {
+    l.xq_hi = take(T * D);
+    l.xq_lo = take(T * D);
+    l.xq_shi = take(T * D / 32);
+    l.xq_slo = take(T * D / 32);
+    l.s_idx = take(T * S * 4);
+    l.s_counts = take(S * 4);
+    l.s_offsets = take((S + 1) * 4);
+    l.s_perm = take(T * S * 4);
+    l.s_tiles = take(S * 16);
+    l.s_nact = take(4);
+    l.s_permws = take(permute_ws_bytes((int64_t)(T * S), (int32_t)S));
+    l.sq_hi = take(T * S * FS);
+    l.sq_lo = take(T * S * FS);
+    l.sq_shi = take(T * S * FS / 32);
+    l.sq_slo = take(T * S * FS / 32);
+    l.s_y = take(T * S * D * 4);
+    l.s_gtiles = take((size_t)gemm_max_tiles((int64_t)(T * S), (int32_t)S) * 16);
+  }
   l.total = off;
   return l;
 }
@@ -81,6 +107,13 @@ moe_status check_config(const moe_config* c, int32_t k) {
   if (c->bias_row_stride != 0 && c->bias_row_stride != c->num_experts) return MOE_ERR_INVALID_ARG;
   if (c->expert_layout != MOE_LAYOUT_RECORD && c->expert_layout != MOE_LAYOUT_PACKED) return MOE_ERR_INVALID_ARG;
   if (c->act_format != MOE_ACT_FMT_BF16 && c->act_format != MOE_ACT_FMT_MXFP8) return MOE_ERR_INVALID_ARG;
+  if (c->num_shared < 0 || c->num_shared > MAX_SHARED || c->d_ffn_shared < 0 || c->d_ffn_shared % 32 ||
+      (c->num_shared > 0 && c->d_ffn_shared == 0))
+    return MOE_ERR_INVALID_ARG;
+  // shared experts run the expert kernels at the full width d
+  if (c->num_shared > 0 && (c->d_model > MAX_EXPERT_DIM || c->d_model % 128 || c->d_ffn_shared > MAX_EXPERT_DIM ||
+                            c->d_ffn_shared % 128))
+    return MOE_ERR_UNSUPPORTED;
   if (c->act == MOE_ACT_SITU) return MOE_ERR_UNSUPPORTED;  // formula not defined on the pages
   // sizes this build's kernels hold in registers; the expert GEMV also needs 128-column multiples
   if (c->num_experts > MAX_E || c->d_model > MAX_DIM || c->d_latent > MAX_EXPERT_DIM || c->d_ffn > MAX_EXPERT_DIM ||
@@ -105,18 +138,26 @@ moe_status dev(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_DEVICE;
   } while (0)
 
 // gate/up then down (y fp32 by routed row) with the kernel family the batch calls for
-moe_status run_experts(const MxArgs& mx, const moe_config& c, int k, const int32_t* counts, const int32_t* offsets,
-                       void* ws, const Layout& l, hipStream_t st) {
-  const int64_t rows = c.num_tokens * k;
-  if (use_gemm(rows, c.num_experts)) {
-    const int64_t mt = gemm_max_tiles(rows, c.num_experts);
-    int4* gt = at<int4>(ws, l.gtiles);
-    MOE_TRY(dev(launch_gemm_tiles(counts, offsets, c.num_experts, gt, mt, st)));
+moe_status run_experts_on(const MxArgs& mx, int64_t rows, int32_t E, const int32_t* counts, const int32_t* offsets,
+                          int4* gt, hipStream_t st) {
+  if (use_gemm(rows, E)) {
+    const int64_t mt = gemm_max_tiles(rows, E);
+    MOE_TRY(dev(launch_gemm_tiles(counts, offsets, E, gt, mt, st)));
     MOE_TRY(dev(launch_gateup_gemm(mx, gt, mt, st)));
     return dev(launch_down_gemm(mx, gt, mt, st));
   }
   MOE_TRY(dev(launch_gateup_mx(mx, st)));
   return dev(launch_down_mx(mx, st));
+}
+moe_status run_experts(const MxArgs& mx, const moe_config& c, int k, const int32_t* counts, const int32_t* offsets,
+                       void* ws, const Layout& l, hipStream_t st) {
+  return run_experts_on(mx, c.num_tokens * k, c.num_experts, counts, offsets, at<int4>(ws, l.gtiles), st);
+}
+
+// slot r of the shared experts' rows takes shared expert r % num_shared
+__global__ void shared_idx_kernel(int32_t* idx, int n, int ns) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) idx[i] = i % ns;
 }
 
 __global__ void fill_i32_kernel(int32_t* p, int n, int32_t v) {
@@ -255,10 +296,11 @@ moe_status moe_workspace_size(const moe_config* cfg, int32_t k, size_t* bytes) {
 
 static moe_status forward_impl(const void* x, const void* router_w, const void* latent_down, const void* latent_up,
                                const uint8_t* expert_blob, int32_t k, const moe_config* cfg, const float* router_bias,
-                               void* out, moe_routing_out* routing, void* workspace, size_t workspace_bytes,
-                               const moe_stage_events* ev, moe_stream_t stream) {
+                               const uint8_t* shared_blob, void* out, moe_routing_out* routing, void* workspace,
+                               size_t workspace_bytes, const moe_stage_events* ev, moe_stream_t stream) {
   MOE_TRY(check_config(cfg, k));
   const moe_config& c = *cfg;
+  if (c.num_shared > 0 && (!shared_blob || !aligned16(shared_blob))) return MOE_ERR_INVALID_ARG;
   if (c.num_tokens == 0) return MOE_OK;  // nothing to do; pointers may be NULL
   if (!x || !router_w || !latent_down || !latent_up || !expert_blob || !out) return MOE_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(router_w) || !aligned16(latent_down) || !aligned16(latent_up) ||
@@ -349,6 +391,42 @@ static moe_status forward_impl(const void* x, const void* router_w, const void* 
   up.wnorm = nullptr;
   up.xnorm = nullptr;
   MOE_TRY(mark(MOE_STAGE_UP, true));
+  if (c.num_shared > 0) {
+    // the shared experts on x at the full width: every token's rows t*S + s, grouped by
+    // shared expert, through the same expert kernels; their fp32 outputs join the
+    // latent-up product before its bf16 rounding
+    const int32_t S = c.num_shared;
+    const int64_t rows = c.num_tokens * S;
+    const QRows xq{at<uint8_t>(ws, l.xq_hi), at<uint8_t>(ws, l.xq_lo), at<uint8_t>(ws, l.xq_shi),
+                   at<uint8_t>(ws, l.xq_slo)};
+    MOE_TRY(dev(launch_quantize_rows(static_cast<const uint16_t*>(x), c.num_tokens, c.d_model, xq,
+                                     c.act_format == MOE_ACT_FMT_MXFP8, st)));
+    int32_t* sidx = at<int32_t>(ws, l.s_idx);
+    hipLaunchKernelGGL(shared_idx_kernel, dim3((unsigned)ceil_div(rows, 256)), dim3(256), 0, st, sidx, (int)rows, S);
+    MOE_TRY(dev(hipGetLastError()));
+    PermOut ps{at<int32_t>(ws, l.s_counts), at<int32_t>(ws, l.s_offsets), at<int32_t>(ws, l.s_perm),
+               at<int4>(ws, l.s_tiles), at<int32_t>(ws, l.s_nact), S};
+    MOE_TRY(dev(launch_permute(sidx, rows, S, ps, at<void>(ws, l.s_permws), st)));
+    MxArgs ms;
+    ms.blob = shared_blob;
+    ms.packed = c.expert_layout == MOE_LAYOUT_PACKED;
+    ms.L = c.d_model;
+    ms.F = c.d_ffn_shared;
+    ms.k = S;
+    ms.T = c.num_tokens;
+    ms.tiles = ps.tiles;
+    ms.max_active = S;
+    ms.perm = ps.perm;
+    ms.hq = xq;
+    ms.aq = QRows{at<uint8_t>(ws, l.sq_hi), at<uint8_t>(ws, l.sq_lo), at<uint8_t>(ws, l.sq_shi),
+                  at<uint8_t>(ws, l.sq_slo)};
+    ms.mxfp8 = c.act_format == MOE_ACT_FMT_MXFP8;
+    ms.a_bf16 = nullptr;
+    ms.y = at<float>(ws, l.s_y);
+    MOE_TRY(run_experts_on(ms, rows, S, ps.counts, ps.offsets, at<int4>(ws, l.s_gtiles), st));
+    up.add = ms.y;
+    up.add_rows = S;
+  }
   MOE_TRY(dev(launch_dense(at<uint16_t>(ws, l.z), c.num_tokens, c.d_latent, &up, 1, st)));
   return mark(MOE_STAGE_UP, false);
 }
@@ -357,8 +435,17 @@ moe_status moe_layer_forward(const void* x, const void* router_w, const void* la
                              const uint8_t* expert_blob, int32_t k, const moe_config* cfg,
                              const float* router_bias, void* out, moe_routing_out* routing, void* workspace,
                              size_t workspace_bytes, moe_stream_t stream) {
-  return forward_impl(x, router_w, latent_down, latent_up, expert_blob, k, cfg, router_bias, out, routing,
+  return forward_impl(x, router_w, latent_down, latent_up, expert_blob, k, cfg, router_bias, nullptr, out, routing,
                       workspace, workspace_bytes, nullptr, stream);
+}
+
+moe_status moe_layer_forward_shared(const void* x, const void* router_w, const void* latent_down,
+                                    const void* latent_up, const uint8_t* expert_blob, int32_t k,
+                                    const moe_config* cfg, const float* router_bias, const uint8_t* shared_blob,
+                                    void* out, moe_routing_out* routing, void* workspace, size_t workspace_bytes,
+                                    moe_stream_t stream) {
+  return forward_impl(x, router_w, latent_down, latent_up, expert_blob, k, cfg, router_bias, shared_blob, out,
+                      routing, workspace, workspace_bytes, nullptr, stream);
 }
 
 moe_status moe_layer_forward_profiled(const void* x, const void* router_w, const void* latent_down,
@@ -366,7 +453,7 @@ moe_status moe_layer_forward_profiled(const void* x, const void* router_w, const
                                       const moe_config* cfg, const float* router_bias, void* out,
                                       moe_routing_out* routing, void* workspace, size_t workspace_bytes,
                                       const moe_stage_events* events, moe_stream_t stream) {
-  return forward_impl(x, router_w, latent_down, latent_up, expert_blob, k, cfg, router_bias, out, routing,
+  return forward_impl(x, router_w, latent_down, latent_up, expert_blob, k, cfg, router_bias, nullptr, out, routing,
                       workspace, workspace_bytes, events, stream);
 }
 

@@ -87,8 +87,11 @@ __global__ void __launch_bounds__(256) dense_gemv_kernel(DenseParams p) {
     uint16_t* out = reinterpret_cast<uint16_t*>(s.out);
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const double v = wave_sum_dpp(acc[g]);
-      if (lane == 0 && t0 + g < p.T) out[(t0 + g) * s.rows + row] = f64_to_bf16(v);
+      double v = wave_sum_dpp(acc[g]);
+      if (lane == 0 && t0 + g < p.T) {
+        for (int a = 0; a < s.add_rows; ++a) v += (double)s.add[((t0 + g) * s.add_rows + a) * s.rows + row];
+        out[(t0 + g) * s.rows + row] = f64_to_bf16(v);
+      }
     }
     return;
   }

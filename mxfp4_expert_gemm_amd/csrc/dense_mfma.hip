@@ -55,6 +55,8 @@ struct DenseMfmaArgs {
   int32_t K, N;
   int32_t ntm, ntn;   // token tiles, row tiles
   int32_t nblocks;    // ntm * ntn (the grid is rounded up to a multiple of 8)
+  const float* add;   // nullable: fp32 [T][add_rows][N] added before the bf16 rounding
+  int32_t add_rows;
 };
 
 template <int WM, int WN, int PF, bool ROUTER>
@@ -192,8 +194,13 @@ __global__ void __launch_bounds__(256, 2) dense_mfma_kernel(DenseMfmaArgs p) {
         if (t < p.T && n < p.N) {
           if constexpr (ROUTER)
             static_cast<float*>(p.out)[t * p.N + n] = (float)accd[i][jn][r];
-          else
+          else if (p.add_rows == 0)
             static_cast<uint16_t*>(p.out)[t * p.N + n] = f32_to_bf16(acc[i][jn][r]);
+          else {
+            double v = (double)acc[i][jn][r];
+            for (int a = 0; a < p.add_rows; ++a) v += (double)p.add[(t * p.add_rows + a) * p.N + n];
+            static_cast<uint16_t*>(p.out)[t * p.N + n] = f64_to_bf16(v);
+          }
         }
       }
     }
@@ -266,6 +273,8 @@ hipError_t launch_dense_mfma(const uint16_t* x, int64_t T, int32_t K, const Dens
   a.T = T;
   a.K = K;
   a.N = s.rows;
+  a.add = s.add;
+  a.add_rows = s.add ? s.add_rows : 0;
   if (s.router) {
     hipLaunchKernelGGL(row_norms_kernel, dim3((unsigned)ceil_div(s.rows, 4)), dim3(256), 0, st, s.W,
                        (int64_t)s.rows, K, s.wnorm);

@@ -19,6 +19,8 @@ struct DenseSeg {
   void* out;
   float* wnorm;      // router only: [rows] Euclidean row norms of W (fp32 sum of squares, rounded sqrt)
   float* xnorm;      // router only: [T] Euclidean norms of the tokens
+  const float* add = nullptr;  // bf16 outputs only, nullable: fp32 [T][add_rows][rows] added before the rounding
+  int32_t add_rows = 0;
 };
 // Relative accumulation error bound of router logits from launch_dense_gemv, per
 // unit of |x_t| |w_e| (see the kernel for its derivation).

@@ -45,7 +45,8 @@ def k3(T=1, **kw):
     c.update(kw)
     return moe.MoEConfig(c["num_tokens"], c["d_model"], c["d_latent"], c["d_ffn"], c["num_experts"],
                          kw.get("act", 0), kw.get("renormalize", 1), kw.get("bias_row_stride", 0),
-                         kw.get("expert_layout", 0), kw.get("act_format", 0))
+                         kw.get("expert_layout", 0), kw.get("act_format", 0), kw.get("num_shared", 0),
+                         kw.get("d_ffn_shared", 0))
 
 
 def ws_status(cfg, k):
@@ -71,6 +72,11 @@ def test_workspace_size_valid_and_invalid():
     assert ws_status(k3(expert_layout=2), 16)[0] == -1
     assert ws_status(k3(act_format=1), 16)[0] == 0   # MXFP8 activations
     assert ws_status(k3(act_format=2), 16)[0] == -1
+    assert ws_status(k3(num_shared=2, d_ffn_shared=3072), 16)[0] == 0
+    assert ws_status(k3(num_shared=2, d_ffn_shared=3072), 16)[1] > ws_status(k3(), 16)[1]
+    assert ws_status(k3(num_shared=2, d_ffn_shared=0), 16)[0] == -1
+    assert ws_status(k3(num_shared=9, d_ffn_shared=3072), 16)[0] == -1
+    assert ws_status(k3(num_shared=1, d_ffn_shared=3104), 16)[0] == -2  # not a multiple of 128
     assert moe.lib().moe_workspace_size(None, 16, ctypes.byref(ctypes.c_size_t())) == -1
 
 
