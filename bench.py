@@ -102,6 +102,8 @@ def main():
                     help="only run a plain device copy of this many bytes 5 times (calibrates HBM byte counters)")
     ap.add_argument("--act-format", default="bf16", choices=["bf16", "mxfp8"],
                     help="expert GEMM inputs: the bf16 activations (default) or their MXFP8 quantisation")
+    ap.add_argument("--shared", type=int, default=0,
+                    help="always-on shared experts of FFN width d_ffn (the routed layer alone by default)")
     ap.add_argument("--layout", default="packed", choices=["packed", "record"],
                     help="expert weights as packed once by moe_pack_experts (default) or as checkpoint records")
     args = ap.parse_args()
@@ -153,7 +155,13 @@ def main():
     log(f"[bench] inputs resident in HBM ({time.time() - t0:.1f}s)")
 
     act_format = moe.ACT_FMT_MXFP8 if args.act_format == "mxfp8" else moe.ACT_FMT_BF16
-    cfg = moe.make_config(c.T, c.d, c.L, c.F, c.E, bias=bias, packed=packed, act_format=act_format)
+    shared = None
+    if args.shared > 0:
+        shared = up(synth.expert_blob(c.layer_seed + 77, c.d, c.F, args.shared))
+        if packed:
+            shared = moe.pack_experts(shared, args.shared, c.d, c.F)
+    cfg = moe.make_config(c.T, c.d, c.L, c.F, c.E, bias=bias, packed=packed, act_format=act_format,
+                          num_shared=args.shared, d_ffn_shared=c.F if args.shared else 0)
     ws = moe.alloc_workspace(cfg, c.k, dev)
     out = torch.empty((c.T, c.d), dtype=torch.int16, device=dev)
     counts = torch.zeros((nbatch, c.E), dtype=torch.int32, device=dev)
@@ -165,10 +173,11 @@ def main():
     def step(i, events=None):
         cp = copies[i % len(copies)]
         routing = {"expert_counts": counts[i]}
-        if events is None:
+        if events is None or args.shared:  # the stage events are not recorded with shared experts
             moe.layer_forward(xs[i], cp["router_w"], cp["latent_down"], cp["latent_up"], blob, c.k, d_ffn=c.F,
                               bias=bias, out=out, workspace=ws, routing=routing, packed=packed,
-                              act_format=act_format)
+                              act_format=act_format, shared_blob=shared, num_shared=args.shared,
+                              d_ffn_shared=c.F if args.shared else 0)
         else:
             moe.layer_forward_profiled(xs[i], cp["router_w"], cp["latent_down"], cp["latent_up"], blob, c.k,
                                        events, d_ffn=c.F, bias=bias, out=out, workspace=ws, routing=routing,
@@ -193,7 +202,8 @@ def main():
     hip.rt.hipEventRecord(ev_stop, stream)
     torch.cuda.synchronize()
     eager_ms = hip.elapsed_ms(ev_start, ev_stop)
-    dom_ms = [hip.elapsed_ms(kev[2 * i], kev[2 * i + 1]) for i in range(W, W + K)]
+    dom_ms = ([hip.elapsed_ms(kev[2 * i], kev[2 * i + 1]) for i in range(W, W + K)] if not args.shared
+              else [float("nan")] * K)
 
     total_ms = eager_ms
     if args.graph:
@@ -235,7 +245,7 @@ def main():
     layer_gbs = float(np.mean(layer_bytes) / (ms_per_step * 1e-3) / 1e9)
 
     stages = None
-    if args.breakdown:
+    if args.breakdown and not args.shared:
         evs = hip.create(2 * moe.NUM_STAGES)
         sums = np.zeros(moe.NUM_STAGES)
         n = min(K, 10)
@@ -308,6 +318,7 @@ def main():
                                    "MXFP8 (e4m3 + e8m0 per 32) at the expert GEMM inputs, fp32 accumulation, fp32 GLU"),
                    "parallelism": "single GPU",
                    "dense_weight_copies": len(copies), "mean_active_experts": float(np.mean(active)),
+                   "shared_experts": args.shared,
                    "expert_layout": "packed by moe_pack_experts at load" if packed else "checkpoint records"},
         "roofline": roofline,
         "layer_hbm": {"achieved_GBs": round(layer_gbs, 1), "frac": round(layer_gbs / HBM_PEAK_GBS, 4),

@@ -19,8 +19,8 @@ constexpr int MAX_SHARED = 8;
 struct Layout {
   size_t logits_fast, xnorm, wnorm, idx, w, counts, offsets, perm, tiles, nact, permws, h, y, z, gtiles;
   // shared experts: x split for the matrix cores, their grouping, GLU rows, outputs
-  size_t xq_hi, xq_lo, xq_shi, xq_slo, s_idx, s_counts, s_offsets, s_perm, s_tiles, s_nact, s_permws, sq_hi, sq_lo,
-      sq_shi, sq_slo, s_y, s_gtiles;
+  size_t xq_hi, xq_lo, xq_shi, xq_slo, s_counts, s_offsets, s_perm, s_tiles, s_nact, sq_hi, sq_lo, sq_shi, sq_slo, s_y,
+      s_gtiles;
   size_t hq_hi, hq_lo, hq_shi, hq_slo, aq_hi, aq_lo, aq_shi, aq_slo;
   size_t total;
 };
@@ -59,20 +59,18 @@ Layout layout(const moe_config& c, int k) {
   l.z = take(T * L * 2);
   l.gtiles = take((size_t)gemm_max_tiles((int64_t)(T * K), (int32_t)E) * 16);
   const size_t S = (size_t)c.num_shared, D = (size_t)c.d_model, FS = (size_t)c.d_ffn_shared;
-  l.xq_hi = l.xq_lo = l.xq_shi = l.xq_slo = l.s_idx = l.s_counts = l.s_offsets = l.s_perm = l.s_tiles = l.s_nact =
-      l.s_permws = l.sq_hi = l.sq_lo = l.sq_shi = l.sq_slo = l.s_y = l.s_gtiles = 0;
+  l.xq_hi = l.xq_lo = l.xq_shi = l.xq_slo = l.s_counts = l.s_offsets = l.s_perm = l.s_tiles = l.s_nact = l.sq_hi =
+      l.sq_lo = l.sq_shi = l.sq_slo = l.s_y = l.s_gtiles = 0;
   if (S > 0) {
     l.xq_hi = take(T * D);
     l.xq_lo = take(T * D);
     l.xq_shi = take(T * D / 32);
     l.xq_slo = take(T * D / 32);
-    l.s_idx = take(T * S * 4);
     l.s_counts = take(S * 4);
     l.s_offsets = take((S + 1) * 4);
     l.s_perm = take(T * S * 4);
     l.s_tiles = take(S * 16);
     l.s_nact = take(4);
-    l.s_permws = take(permute_ws_bytes((int64_t)(T * S), (int32_t)S));
     l.sq_hi = take(T * S * FS);
     l.sq_lo = take(T * S * FS);
     l.sq_shi = take(T * S * FS / 32);
@@ -154,10 +152,26 @@ moe_status run_experts(const MxArgs& mx, const moe_config& c, int k, const int32
   return run_experts_on(mx, c.num_tokens * k, c.num_experts, counts, offsets, at<int4>(ws, l.gtiles), st);
 }
 
-// slot r of the shared experts' rows takes shared expert r % num_shared
-__global__ void shared_idx_kernel(int32_t* idx, int n, int ns) {
-  int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) idx[i] = i % ns;
+// The grouping of the shared experts' rows, known in closed form: every token t has row
+// t*S + s for every shared expert s, so expert s owns rows s*T .. s*T + T-1 of perm
+// (tokens ascending), counts T and offset s*T; its tile is {s, s*T, T, s}.
+__global__ void shared_group_kernel(int32_t* counts, int32_t* offsets, int32_t* perm, int4* tiles, int32_t* nact,
+                                    int64_t T, int32_t S) {
+  const int64_t n = T * S;
+  for (int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; r < n; r += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t s = r / T, t = r - s * T;
+    perm[r] = (int32_t)(t * S + s);
+  }
+  if (blockIdx.x == 0) {
+    for (int s = threadIdx.x; s <= S; s += blockDim.x) {
+      offsets[s] = (int32_t)(s * T);
+      if (s < S) {
+        counts[s] = (int32_t)T;
+        tiles[s] = make_int4(s, (int)(s * T), (int)T, s);
+      }
+    }
+    if (threadIdx.x == 0) *nact = S;
+  }
 }
 
 __global__ void fill_i32_kernel(int32_t* p, int n, int32_t v) {
@@ -401,12 +415,12 @@ static moe_status forward_impl(const void* x, const void* router_w, const void* 
                    at<uint8_t>(ws, l.xq_slo)};
     MOE_TRY(dev(launch_quantize_rows(static_cast<const uint16_t*>(x), c.num_tokens, c.d_model, xq,
                                      c.act_format == MOE_ACT_FMT_MXFP8, st)));
-    int32_t* sidx = at<int32_t>(ws, l.s_idx);
-    hipLaunchKernelGGL(shared_idx_kernel, dim3((unsigned)ceil_div(rows, 256)), dim3(256), 0, st, sidx, (int)rows, S);
-    MOE_TRY(dev(hipGetLastError()));
     PermOut ps{at<int32_t>(ws, l.s_counts), at<int32_t>(ws, l.s_offsets), at<int32_t>(ws, l.s_perm),
                at<int4>(ws, l.s_tiles), at<int32_t>(ws, l.s_nact), S};
-    MOE_TRY(dev(launch_permute(sidx, rows, S, ps, at<void>(ws, l.s_permws), st)));
+    const int64_t gblocks = ceil_div(rows, 256) < 1024 ? ceil_div(rows, 256) : 1024;
+    hipLaunchKernelGGL(shared_group_kernel, dim3((unsigned)gblocks), dim3(256), 0, st, ps.counts, ps.offsets, ps.perm,
+                       ps.tiles, ps.n_active, c.num_tokens, S);
+    MOE_TRY(dev(hipGetLastError()));
     MxArgs ms;
     ms.blob = shared_blob;
     ms.packed = c.expert_layout == MOE_LAYOUT_PACKED;
