@@ -181,13 +181,8 @@ __device__ __forceinline__ void read_a(AStep& a, const ALds& d, int m, int ntok,
 // g < 0 so a large |g| cannot overflow
 __device__ __forceinline__ uint16_t glu_bf16(float g, float u) {
   const double gd = (double)g;
-  double s;
-  if (gd >= 0.0) {
-    s = gd / (1.0 + exp(-gd));
-  } else {
-    const double e = exp(gd);
-    s = gd * e / (1.0 + e);
-  }
+  const double e = exp(-fabs(gd));  // one exponential on either side
+  const double s = gd >= 0.0 ? gd / (1.0 + e) : gd * e / (1.0 + e);
   return f64_to_bf16(s * (double)u);
 }
 

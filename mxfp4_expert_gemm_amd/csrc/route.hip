@@ -253,7 +253,7 @@ struct RouteLds {
   uint32_t ckey[ROUTE_CAND];
   int cidx[ROUTE_CAND];
   float cval[ROUTE_CAND], crad[ROUTE_CAND];
-  int oidx[WAVE];
+  alignas(16) int oidx[WAVE];
   float oval[WAVE];
 };
 
@@ -721,6 +721,208 @@ __global__ void __launch_bounds__(512) route_permute_small_kernel(RouteArgs a, P
   place_rows_block(sidx, T, k, a.E, &pl, p);
 }
 
+// One token (decode) routed by a whole block, one expert per thread.  A single wave
+// holding 14 experts per lane spends most of its time in dependent instruction chains;
+// here the fast logits, radii and keys of route_token are computed once per thread
+// (the same fp32 values), the cut tau is the k-th largest of the maxima of 64 groups of
+// consecutive experts (at least k keys reach it, so the k best are candidates), and the
+// candidates are compacted in expert order and ranked by all waves (four each).  Wave 0
+// certifies the boundary against every other expert's upper end and writes the
+// selection, the same values route_token writes when its fast path decides; when this
+// one cannot decide (more than ROUTE_CAND candidates, an uncertain boundary, weights
+// over all experts) wave 0 runs route_token instead.  The other waves quantise the
+// latent row meanwhile (its loads are issued with the logits'); then every thread
+// writes the grouping entries of its expert.
+constexpr int RB_THREADS = 1024;
+constexpr int RB_WAVES = RB_THREADS / WAVE;
+constexpr int RB_GROUP = RB_THREADS / WAVE;  // experts per group: one group maximum per lane
+constexpr int RB_QT = RB_THREADS - WAVE;     // threads of the latent row's quantisation
+static_assert(ROUTE_CAND == WAVE && ROUTE_CAND <= 4 * RB_WAVES, "four candidates ranked per wave");
+
+struct RouteBlockLds {
+  RouteLds rl;  // wave 0's candidates, output pairs and fallback scratch
+  unsigned long long cpk[ROUTE_CAND];  // candidate (key, ~expert): larger ranks first
+  int crank[ROUTE_CAND];
+  int selpre[ROUTE_CAND + 1];  // selected candidates before candidate i
+  uint32_t gmax[WAVE];
+  int wcnt[RB_WAVES];
+  float wup[RB_WAVES];
+  uint32_t tau;
+  int decided;
+};
+
+// the 8 values of group j of a latent row, quantised (the quad of lanes holding the four
+// groups of a scale block is active together)
+__device__ __forceinline__ void quantize_group8(const uint4 raw, const QRows& q, int64_t j, bool mxfp8) {
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = bf16lo(w[i]);
+    v[2 * i + 1] = bf16hi(w[i]);
+  }
+  uint32_t hi[2], lo[2], shi, slo;
+  quantize_quad8_fmt(v, hi, lo, shi, slo, mxfp8);
+  *reinterpret_cast<uint2*>(q.hi + 8 * j) = make_uint2(hi[0], hi[1]);
+  *reinterpret_cast<uint2*>(q.lo + 8 * j) = make_uint2(lo[0], lo[1]);
+  if ((j & 3) == 0) {
+    q.shi[j >> 2] = (uint8_t)shi;
+    q.slo[j >> 2] = (uint8_t)slo;
+  }
+}
+
+// route_token as a call: its registers are not reserved in the block kernel, where it
+// runs only when the block's selection cannot decide
+__attribute__((noinline)) __device__ void route_token_call(RouteArgs a, RouteLds* L) { route_token(a, 0, L); }
+
+__global__ void __launch_bounds__(RB_THREADS) route_permute_one_kernel(RouteArgs a, PermOut p) {
+  __shared__ RouteBlockLds S;
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid / WAVE;
+  const int E = a.E, k = a.k;
+  const int e = tid;
+  const bool have = e < E;
+  const int ec = have ? e : E - 1;
+  const float lf = a.logits_fast[ec];
+  const float bv = a.bias ? a.bias[ec] : 0.f;
+  const float wn = a.wnorm[ec];
+  const float xn = a.xnorm[0];
+  // the first group of the latent row this thread quantises
+  const int64_t ng = a.h ? a.L / 8 : 0;
+  const int64_t jq = tid - WAVE;
+  const bool qg = wave > 0 && jq < ng;
+  const uint4 hraw = qg ? *reinterpret_cast<const uint4*>(a.h + 8 * jq) : make_uint4(0u, 0u, 0u, 0u);
+
+  const float gam = (float)a.gamma * (1.f + 0x1p-18f) * xn;
+  const float pad = (float)a.d * 0x1p-124f;
+  float c = -__builtin_inff(), R = 0.f;
+  uint32_t key = 0u;
+  if (have) {
+    c = lf + bv;
+    R = gam * wn + pad + 0x1p-20f * (fabsf(lf) + fabsf(bv));
+    if (bv == -__builtin_inff()) {
+      const float rr = gam * wn + pad + 0x1p-20f * fabsf(lf);
+      const bool known = __builtin_isfinite(lf) && __builtin_isfinite(rr) && fabsf(lf) + rr < 0x1p127f;
+      c = -__builtin_inff();
+      R = known ? 0.f : __builtin_inff();
+    } else if (!(__builtin_isfinite(c) && __builtin_isfinite(R))) {
+      c = -__builtin_inff();
+      R = __builtin_inff();
+    }
+    key = order_key(c);
+  }
+  uint32_t gm = key;
+#pragma unroll
+  for (int o = 1; o < RB_GROUP; o <<= 1) {
+    const uint32_t ov = (uint32_t)__shfl_xor((int)gm, o);
+    gm = ov > gm ? ov : gm;
+  }
+  if ((lane & (RB_GROUP - 1)) == 0) S.gmax[tid / RB_GROUP] = gm;
+  __syncthreads();
+  if (wave == 0) {
+    const uint32_t t0 = kth_of_lanes(S.gmax[lane], k);
+    if (lane == 0) S.tau = t0;
+  }
+  __syncthreads();
+  const uint32_t tau = S.tau;
+  const bool cand = key != 0u && key >= tau;
+  const unsigned long long cb = __ballot(cand);
+  float up = -__builtin_inff();
+  if (have && !cand) up = R == __builtin_inff() ? __builtin_inff() : next_up(c + R);
+  up = wave_max_dpp(up);
+  if (lane == 0) {
+    S.wcnt[wave] = __popcll(cb);
+    S.wup[wave] = up;
+  }
+  __syncthreads();
+  int base = 0, n_c = 0;
+#pragma unroll
+  for (int w = 0; w < RB_WAVES; ++w) {
+    const int cw = S.wcnt[w];
+    base += w < wave ? cw : 0;
+    n_c += cw;
+  }
+  // this expert's place in the candidate list (for a non-candidate: the candidates below it)
+  const int pos = base + __popcll(cb & ((1ull << lane) - 1ull));
+  const bool fits = n_c <= ROUTE_CAND;
+  if (fits && cand) {
+    S.cpk[pos] = ((unsigned long long)key << 32) | (uint32_t)~(uint32_t)e;
+    S.rl.cidx[pos] = e;
+    S.rl.cval[pos] = c;
+    S.rl.crad[pos] = R;
+  }
+  __syncthreads();
+  if (fits) {
+    // wave w ranks candidates 4w..4w+3 against all: rank = candidates ahead of it
+    const unsigned long long pj = lane < n_c ? S.cpk[lane] : 0ull;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = 4 * wave + u;
+      const unsigned long long pi = __shfl(pj, i);
+      const int r = __popcll(__ballot(lane < n_c && pj > pi));
+      if (lane == 0 && i < n_c) S.crank[i] = r;
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    bool fast = fits && a.renormalize && !(a.flags & MOE_ROUTE_EXACT_ALL);
+    if (fast) {
+      const bool live = lane < n_c;
+      const bool sel = live && S.crank[lane] < k;
+      const float mc = live ? S.rl.cval[lane] : 0.f, mr = live ? S.rl.crad[lane] : 0.f;
+      if (k < E) {
+        float Mloc = __builtin_inff(), mloc = -__builtin_inff();
+        if (sel) Mloc = mr == __builtin_inff() ? -__builtin_inff() : next_down(mc - mr);
+        if (live && !sel) mloc = mr == __builtin_inff() ? __builtin_inff() : next_up(mc + mr);
+        if (lane < RB_WAVES) mloc = fmaxf(mloc, S.wup[lane]);
+        fast = wave_min_dpp(Mloc) > wave_max_dpp(mloc);
+      }
+      if (fast) {
+        // candidates are in expert order, so the output place is the count of selected below
+        const unsigned long long sb = __ballot(sel);
+        const int op = __popcll(sb & ((1ull << lane) - 1ull));
+        S.selpre[lane] = op;
+        if (lane == 0) S.selpre[ROUTE_CAND] = __popcll(sb);
+        if (sel) {
+          S.rl.oidx[op] = S.rl.cidx[lane];
+          S.rl.oval[op] = mc;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        emit_topk(a, 0, &S.rl, 0.f, 1.f);
+      }
+    }
+    if (!fast) route_token_call(a, &S.rl);
+    if (lane == 0) S.decided = fast;
+  } else {
+    if (qg) quantize_group8(hraw, a.hq, jq, a.mxfp8 != 0);
+    if (ng > RB_QT) quantize_quads(a.h, a.hq, a.L, jq + RB_QT, RB_QT, a.mxfp8 != 0);
+  }
+  __syncthreads();  // the k selected experts, ascending, are in S.rl.oidx
+  const bool decided = S.decided;
+  if (decided && a.logits_out && have) a.logits_out[e] = c;
+  // one row per selected expert: offsets[e] = selected experts below e
+  int below = 0, upto = 0;
+  if (decided) {
+    below = S.selpre[pos < n_c ? pos : ROUTE_CAND];
+    upto = below + (cand && S.crank[pos] < k);
+  } else {
+    for (int j = 0; j < k; ++j) {
+      const int sj = S.rl.oidx[j];
+      below += sj < e;
+      upto += sj <= e;
+    }
+  }
+  if (e <= E) p.offsets[e] = below;
+  if (tid == 0 && E == RB_THREADS) p.offsets[E] = k;
+  if (have) p.counts[e] = upto - below;
+  if (tid < k) {
+    p.perm[tid] = tid;
+    p.tiles[tid] = make_int4(S.rl.oidx[tid], tid, 1, tid);
+  }
+  for (int sl = k + tid; sl < p.max_tiles; sl += RB_THREADS) p.tiles[sl] = make_int4(-1, 0, 0, -1);
+  if (tid == 0) *p.n_active = k;
+}
+
 // Grouping of the rows of routed tokens (distinct, valid experts per token) for
 // T <= PLACE_MAX_TOKENS and T*k <= ROUTE_SMALL_ROWS, after route_kernel.
 __global__ void __launch_bounds__(1024) place_rows_kernel(const int32_t* __restrict__ idx, int T, int k, int E,
@@ -744,6 +946,10 @@ hipError_t launch_place_rows(const int32_t* idx, int64_t T, int32_t k, int32_t E
 hipError_t launch_route_permute_small(const RouteArgs& a, const PermOut& p, hipStream_t st) {
   if (a.T == 0) return hipSuccess;
   if (a.E > ROUTE_MAXI * WAVE || a.T > ROUTE_FUSED_TOKENS || a.k > WAVE) return hipErrorInvalidValue;
+  if (a.T == 1 && a.E <= RB_THREADS && a.exact_logits == nullptr) {
+    hipLaunchKernelGGL(route_permute_one_kernel, dim3(1), dim3(RB_THREADS), 0, st, a, p);
+    return hipGetLastError();
+  }
   // a wave per token, and at least one wave more that quantises the latent rows meanwhile
   // for T < 8
   const int nw = a.T < 4 ? 4 : 8;

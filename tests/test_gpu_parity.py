@@ -348,6 +348,31 @@ def test_layer_ragged_shapes(T, d, L, F, E, k):
     assert rel_l2(bf16_bits_to_f64(from_dev(out)), bf16_bits_to_f64(ref["out"])) <= TOL_OUT
 
 
+@pytest.mark.parametrize("ndup", [12, 100])
+def test_layer_one_token_repeated_router_rows(ndup):
+    """One token (the block-wide routing kernel) whose ndup best router rows are copies of one
+    row: equal logits straddle the top-8 boundary, which no error radius can certify, and
+    with 100 copies there are more candidates than one wave ranks.  The selection is then
+    decided exactly: the copies with the lowest indices."""
+    T, d, L, F, E, k = 1, 256, 128, 128, 300, 8
+    s = 0xD0B + ndup
+    x = synth.normal_bf16(s, 1, 1.0, (T, d))
+    Wr = synth.normal_bf16(s, 2, 0.02, (E, d))
+    rows = synth.permutation(s, 3, E)[:ndup]
+    # a row aligned with the token, far above the random rows, repeated ndup times
+    Wr[rows] = np.where(bf16_bits_to_f64(x[0]) >= 0, 0x3CA4, 0xBCA4).astype(np.uint16)  # +-0.02
+    Wd = synth.normal_bf16(s, 4, 0.02, (L, d))
+    Wu = synth.normal_bf16(s, 5, 0.02, (d, L))
+    blob = synth.expert_blob(s, L, F, E)
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    out = moe.layer_forward(to_dev(x), to_dev(Wr), to_dev(Wd), to_dev(Wu), to_dev(blob), k, d_ffn=F,
+                            routing={"topk_idx": idx})
+    ref = oracle.layer_forward(x, Wr, Wd, Wu, blob, k, L, F)
+    assert np.array_equal(ref["idx"][0], np.sort(rows)[:k])
+    assert np.array_equal(from_dev(idx), ref["idx"])
+    assert rel_l2(bf16_bits_to_f64(from_dev(out)), bf16_bits_to_f64(ref["out"])) <= TOL_OUT
+
+
 def test_layer_zero_tokens_is_a_noop():
     dw = dev_weights("tiny")
     c = synth.CONFIGS["tiny"]
