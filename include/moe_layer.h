@@ -225,6 +225,31 @@ moe_status moe_layer_forward_shared(const void* x, const void* router_w, const v
                                     void* out, moe_routing_out* routing, void* workspace, size_t workspace_bytes,
                                     moe_stream_t stream);
 
+/* Bytes of the HBM slot buffer moe_layer_forward_streamed needs: one expert record
+ * (moe_expert_bytes, or moe_packed_expert_bytes for the packed layout) per expert a
+ * batch can activate, min(E, T*k) of them.  Host function. */
+moe_status moe_expert_slots_bytes(const moe_config* cfg, int32_t k, size_t* bytes);
+
+/* The layer with its expert records held in host memory (in-c post, sections on how the
+ * memory requirement shrinks and on streaming the trunk: only the experts a token routes
+ * to need to be near the compute; a Kimi K3 has 92 routed layers of 15.7 GB of experts,
+ * 1.45 TB, more than the 288 GB of HBM).  After the routing and the grouping, a kernel
+ * copies the record of every active expert (at most min(E, T*k)) from the host blob
+ * into expert_slots over the host link, and the expert kernels read the slots.  No host
+ * synchronisation: the active-expert list never leaves the device.  Same result as
+ * moe_layer_forward on the same records, bit for bit.
+ *  expert_blob_host: host memory allocated pinned (hipHostMalloc; torch pin_memory),
+ *    E records in cfg->expert_layout; the library maps it with hipHostGetDevicePointer
+ *    and returns MOE_ERR_INVALID_ARG for memory that is not pinned host memory.
+ *  expert_slots: device, 16-byte aligned, slots_bytes >= moe_expert_slots_bytes.
+ *  cfg->num_experts at most 1024; cfg->num_shared must be 0 (MOE_ERR_UNSUPPORTED).
+ *  Other arguments as moe_layer_forward; the routing outputs keep the global expert ids. */
+moe_status moe_layer_forward_streamed(const void* x, const void* router_w, const void* latent_down,
+                                      const void* latent_up, const uint8_t* expert_blob_host, int32_t k,
+                                      const moe_config* cfg, const float* router_bias, uint8_t* expert_slots,
+                                      size_t slots_bytes, void* out, moe_routing_out* routing, void* workspace,
+                                      size_t workspace_bytes, moe_stream_t stream);
+
 /* ---- stage entry points (the same kernels moe_layer_forward runs) ---- */
 
 /* Dequantise one [rows][cols] MXFP4 matrix (codes then scales as above) to

@@ -29,7 +29,8 @@ EXPORTS = ["moe_expert_bytes", "moe_packed_expert_bytes", "moe_pack_experts", "m
            "moe_workspace_size", "moe_layer_forward",
            "moe_layer_forward_profiled",
            "moe_dequant_mxfp4", "moe_route", "moe_topk", "moe_permute", "moe_expert_ffn", "moe_combine",
-           "moe_linear_bf16", "moe_reap_saliency", "moe_layer_forward_shared"]
+           "moe_linear_bf16", "moe_reap_saliency", "moe_layer_forward_shared", "moe_expert_slots_bytes",
+           "moe_layer_forward_streamed"]
 
 
 class MoEError(RuntimeError):
@@ -89,6 +90,9 @@ def lib():
             "moe_linear_bf16": (ctypes.c_int, [vp, vp, i64, i32, i32, vp, vp]),
             "moe_reap_saliency": (ctypes.c_int, [vp, vp, vp, vp, i64, i32, i32, i32, vp, vp]),
             "moe_layer_forward_shared": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, cfgp, vp, vp, vp, rp, vp, sz, vp]),
+            "moe_expert_slots_bytes": (ctypes.c_int, [cfgp, i32, ctypes.POINTER(sz)]),
+            "moe_layer_forward_streamed": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, cfgp, vp, vp, sz, vp, rp, vp, sz,
+                                                          vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -188,6 +192,48 @@ def layer_forward(x, router_w, latent_down, latent_up, expert_blob, k: int, *, d
         _check(lib().moe_layer_forward(_p(x), _p(router_w), _p(latent_down), _p(latent_up), _p(expert_blob), k,
                                        ctypes.byref(cfg), _p(bias), _p(out), ctypes.byref(r) if r else None,
                                        _p(workspace), workspace.numel(), _stream(stream)), "moe_layer_forward")
+    return out
+
+
+def expert_slots_bytes(cfg: MoEConfig, k: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().moe_expert_slots_bytes(ctypes.byref(cfg), k, ctypes.byref(n)), "moe_expert_slots_bytes")
+    return int(n.value)
+
+
+def alloc_expert_slots(cfg: MoEConfig, k: int, device="cuda") -> torch.Tensor:
+    """The HBM slot buffer of moe_layer_forward_streamed for this batch shape."""
+    return torch.empty(max(expert_slots_bytes(cfg, k), 256), dtype=torch.uint8, device=device)
+
+
+def layer_forward_streamed(x, router_w, latent_down, latent_up, expert_blob_host: torch.Tensor, k: int, *,
+                           d_ffn: int, expert_slots: Optional[torch.Tensor] = None,
+                           bias: Optional[torch.Tensor] = None, renormalize: bool = True, act: int = ACT_SILU,
+                           out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                           routing: Optional[dict] = None, stream=None, packed: bool = False,
+                           act_format: int = ACT_FMT_BF16) -> torch.Tensor:
+    """layer_forward with the expert records in pinned host memory (expert_blob_host, a CPU
+    tensor with pin_memory): the routed experts are fetched into expert_slots (HBM) on the
+    device before the expert kernels run."""
+    if expert_blob_host.is_cuda or not expert_blob_host.is_pinned():
+        raise ValueError("expert_blob_host must be a pinned host tensor")
+    T, d = x.shape
+    E = router_w.shape[0]
+    L = latent_down.shape[0]
+    cfg = make_config(T, d, L, d_ffn, E, act=act, renormalize=renormalize, bias=bias, packed=packed,
+                      act_format=act_format)
+    if out is None:
+        out = torch.empty((T, d), dtype=x.dtype, device=x.device)
+    if workspace is None:
+        workspace = alloc_workspace(cfg, k, x.device)
+    if expert_slots is None:
+        expert_slots = alloc_expert_slots(cfg, k, x.device)
+    r = _routing(routing)
+    _check(lib().moe_layer_forward_streamed(_p(x), _p(router_w), _p(latent_down), _p(latent_up),
+                                            expert_blob_host.data_ptr(), k, ctypes.byref(cfg), _p(bias),
+                                            _p(expert_slots), expert_slots.numel(), _p(out),
+                                            ctypes.byref(r) if r else None, _p(workspace), workspace.numel(),
+                                            _stream(stream)), "moe_layer_forward_streamed")
     return out
 
 
@@ -317,4 +363,4 @@ __all__ = ["lib", "MoEConfig", "RoutingOut", "MoEError", "make_config", "expert_
            "pack_experts", "LAYOUT_RECORD", "LAYOUT_PACKED", "ACT_FMT_BF16", "ACT_FMT_MXFP8", "workspace_size",
            "alloc_workspace", "layer_forward", "layer_forward_profiled", "StageEvents", "STAGES", "dequant_mxfp4", "route", "topk", "permute", "expert_ffn", "combine",
            "linear_bf16", "reap_saliency", "reap_prune_bias", "ACT_SILU", "ACT_SITU", "ROUTE_EXACT_ALL", "EXPORTS",
-           "LIB_PATH"]
+           "LIB_PATH", "expert_slots_bytes", "alloc_expert_slots", "layer_forward_streamed"]

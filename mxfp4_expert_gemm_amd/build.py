@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe_layer.so")
-SOURCES = ["dequant.hip", "dense_gemv.hip", "route.hip", "permute.hip", "expert_mfma.hip", "expert_gemm.hip", "dense_mfma.hip",
+SOURCES = ["dequant.hip", "dense_gemv.hip", "route.hip", "permute.hip", "expert_mfma.hip", "expert_gemm.hip", "dense_mfma.hip", "stream.hip",
            "combine.hip", "reap.hip", "capi.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")

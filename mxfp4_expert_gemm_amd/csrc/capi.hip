@@ -18,6 +18,8 @@ constexpr int MAX_SHARED = 8;
 
 struct Layout {
   size_t logits_fast, xnorm, wnorm, idx, w, counts, offsets, perm, tiles, nact, permws, h, y, z, gtiles;
+  // the grouping renumbered to HBM slots (experts fetched from host memory)
+  size_t tiles_s, counts_s, offsets_s, idx_s;
   // shared experts: x split for the matrix cores, their grouping, GLU rows, outputs
   size_t xq_hi, xq_lo, xq_shi, xq_slo, s_counts, s_offsets, s_perm, s_tiles, s_nact, sq_hi, sq_lo, sq_shi, sq_slo, s_y,
       s_gtiles;
@@ -58,6 +60,10 @@ Layout layout(const moe_config& c, int k) {
   l.y = take(T * K * L * 4);
   l.z = take(T * L * 2);
   l.gtiles = take((size_t)gemm_max_tiles((int64_t)(T * K), (int32_t)E) * 16);
+  l.tiles_s = take(E * 16);
+  l.counts_s = take(E * 4);
+  l.offsets_s = take((E + 1) * 4);
+  l.idx_s = take(T * K * 4);
   const size_t S = (size_t)c.num_shared, D = (size_t)c.d_model, FS = (size_t)c.d_ffn_shared;
   l.xq_hi = l.xq_lo = l.xq_shi = l.xq_slo = l.s_counts = l.s_offsets = l.s_perm = l.s_tiles = l.s_nact = l.sq_hi =
       l.sq_lo = l.sq_shi = l.sq_slo = l.s_y = l.s_gtiles = 0;
@@ -308,10 +314,13 @@ moe_status moe_workspace_size(const moe_config* cfg, int32_t k, size_t* bytes) {
   return MOE_OK;
 }
 
+// expert_slots non-null: expert_blob is device-readable host memory, and the experts
+// the batch routes to are copied into the slots first
 static moe_status forward_impl(const void* x, const void* router_w, const void* latent_down, const void* latent_up,
                                const uint8_t* expert_blob, int32_t k, const moe_config* cfg, const float* router_bias,
                                const uint8_t* shared_blob, void* out, moe_routing_out* routing, void* workspace,
-                               size_t workspace_bytes, const moe_stage_events* ev, moe_stream_t stream) {
+                               size_t workspace_bytes, const moe_stage_events* ev, moe_stream_t stream,
+                               uint8_t* expert_slots = nullptr, size_t slots_bytes = 0) {
   MOE_TRY(check_config(cfg, k));
   const moe_config& c = *cfg;
   if (c.num_shared > 0 && (!shared_blob || !aligned16(shared_blob))) return MOE_ERR_INVALID_ARG;
@@ -321,6 +330,13 @@ static moe_status forward_impl(const void* x, const void* router_w, const void* 
       !aligned16(expert_blob) || !aligned16(out))
     return MOE_ERR_INVALID_ARG;
   if (router_bias && (reinterpret_cast<uintptr_t>(router_bias) & 3u)) return MOE_ERR_INVALID_ARG;
+  const int64_t ebytes = c.expert_layout == MOE_LAYOUT_PACKED ? packed_expert_bytes(c.d_latent, c.d_ffn)
+                                                             : (int64_t)moe_expert_bytes(c.d_latent, c.d_ffn);
+  const int32_t nslots = max_tiles(c.num_tokens * k, c.num_experts);
+  if (expert_slots) {
+    if (!aligned16(expert_slots) || slots_bytes < (size_t)nslots * (size_t)ebytes) return MOE_ERR_INVALID_ARG;
+    if (c.num_experts > 1024) return MOE_ERR_UNSUPPORTED;
+  }
   const size_t xbytes = (size_t)c.num_tokens * c.d_model * 2;
   if (overlap(x, xbytes, out, xbytes)) return MOE_ERR_INVALID_ARG;
   const Layout l = layout(c, k);
@@ -366,14 +382,34 @@ static moe_status forward_impl(const void* x, const void* router_w, const void* 
     MOE_TRY(mark(MOE_STAGE_PERMUTE, true));
     MOE_TRY(dev(launch_permute(idx, c.num_tokens * k, c.num_experts, po, at<void>(ws, l.permws), st)));
   }
+  // the expert stage reads the blob, or the slots holding the routed experts' records
+  const uint8_t* eblob = expert_blob;
+  const int32_t* eidx = idx;
+  const int32_t* ecounts = counts;
+  const int32_t* eoffsets = offsets;
+  int32_t E_eff = c.num_experts;
+  int4* etiles = at<int4>(ws, l.tiles);
+  if (expert_slots) {
+    MOE_TRY(dev(launch_gather_experts(expert_blob, ebytes, etiles, at<int32_t>(ws, l.nact), nslots, expert_slots, st)));
+    MOE_TRY(dev(launch_remap_to_slots(etiles, at<int32_t>(ws, l.nact), nslots, counts, offsets, idx, c.num_tokens * k,
+                                      at<int4>(ws, l.tiles_s), at<int32_t>(ws, l.counts_s),
+                                      at<int32_t>(ws, l.offsets_s), at<int32_t>(ws, l.idx_s), st)));
+    eblob = expert_slots;
+    eidx = at<int32_t>(ws, l.idx_s);
+    ecounts = at<int32_t>(ws, l.counts_s);
+    eoffsets = at<int32_t>(ws, l.offsets_s);
+    E_eff = nslots;
+    etiles = at<int4>(ws, l.tiles_s);
+  }
   MOE_TRY(mark(MOE_STAGE_PERMUTE, false));
-  const MxArgs mx = mx_args(c, k, expert_blob, ws, l, perm, at<float>(ws, l.y));
+  MxArgs mx = mx_args(c, k, eblob, ws, l, perm, at<float>(ws, l.y));
+  mx.tiles = etiles;
   if (down_combine_fits(c.num_tokens, k)) {
     MOE_TRY(mark(MOE_STAGE_GATE_UP, true));
     MOE_TRY(dev(launch_gateup_mx(mx, st)));
     MOE_TRY(mark(MOE_STAGE_GATE_UP, false));
     MOE_TRY(mark(MOE_STAGE_DOWN, true));
-    MOE_TRY(dev(launch_down_combine_mx(mx, idx, w, at<uint16_t>(ws, l.z), st)));
+    MOE_TRY(dev(launch_down_combine_mx(mx, eidx, w, at<uint16_t>(ws, l.z), st)));
     MOE_TRY(mark(MOE_STAGE_DOWN, false));
     MOE_TRY(mark(MOE_STAGE_COMBINE, true));
     MOE_TRY(mark(MOE_STAGE_COMBINE, false));
@@ -384,7 +420,7 @@ static moe_status forward_impl(const void* x, const void* router_w, const void* 
     const bool gemm = use_gemm(rows, c.num_experts);
     MOE_TRY(mark(MOE_STAGE_GATE_UP, true));
     if (gemm) {
-      MOE_TRY(dev(launch_gemm_tiles(counts, offsets, c.num_experts, gt, mt, st)));
+      MOE_TRY(dev(launch_gemm_tiles(ecounts, eoffsets, E_eff, gt, mt, st)));
       MOE_TRY(dev(launch_gateup_gemm(mx, gt, mt, st)));
     } else {
       MOE_TRY(dev(launch_gateup_mx(mx, st)));
@@ -469,6 +505,40 @@ moe_status moe_layer_forward_profiled(const void* x, const void* router_w, const
                                       const moe_stage_events* events, moe_stream_t stream) {
   return forward_impl(x, router_w, latent_down, latent_up, expert_blob, k, cfg, router_bias, nullptr, out, routing,
                       workspace, workspace_bytes, events, stream);
+}
+
+moe_status moe_expert_slots_bytes(const moe_config* cfg, int32_t k, size_t* bytes) {
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  MOE_TRY(check_config(cfg, k));
+  const moe_config& c = *cfg;
+  const int64_t ebytes = c.expert_layout == MOE_LAYOUT_PACKED ? packed_expert_bytes(c.d_latent, c.d_ffn)
+                                                             : (int64_t)moe_expert_bytes(c.d_latent, c.d_ffn);
+  *bytes = (size_t)max_tiles(c.num_tokens * k, c.num_experts) * (size_t)ebytes;
+  return MOE_OK;
+}
+
+moe_status moe_layer_forward_streamed(const void* x, const void* router_w, const void* latent_down,
+                                      const void* latent_up, const uint8_t* expert_blob_host, int32_t k,
+                                      const moe_config* cfg, const float* router_bias, uint8_t* expert_slots,
+                                      size_t slots_bytes, void* out, moe_routing_out* routing, void* workspace,
+                                      size_t workspace_bytes, moe_stream_t stream) {
+  if (!expert_slots) return MOE_ERR_INVALID_ARG;
+  MOE_TRY(check_config(cfg, k));
+  if (cfg->num_shared > 0 || cfg->num_experts > 1024) return MOE_ERR_UNSUPPORTED;
+  if (cfg->num_tokens == 0) return MOE_OK;
+  size_t need = 0;
+  MOE_TRY(moe_expert_slots_bytes(cfg, k, &need));
+  if (!aligned16(expert_slots) || slots_bytes < need || !expert_blob_host) return MOE_ERR_INVALID_ARG;
+  // the device address of the pinned host records (host memory only: device memory and
+  // unregistered host memory are refused)
+  hipPointerAttribute_t attr{};
+  if (hipPointerGetAttributes(&attr, expert_blob_host) != hipSuccess || attr.type != hipMemoryTypeHost)
+    return MOE_ERR_INVALID_ARG;
+  void* dblob = nullptr;
+  if (hipHostGetDevicePointer(&dblob, const_cast<uint8_t*>(expert_blob_host), 0) != hipSuccess || !dblob)
+    return MOE_ERR_INVALID_ARG;
+  return forward_impl(x, router_w, latent_down, latent_up, static_cast<const uint8_t*>(dblob), k, cfg, router_bias,
+                      nullptr, out, routing, workspace, workspace_bytes, nullptr, stream, expert_slots, slots_bytes);
 }
 
 moe_status moe_dequant_mxfp4(const uint8_t* codes, const uint8_t* scales, int64_t rows, int32_t cols, float* out,

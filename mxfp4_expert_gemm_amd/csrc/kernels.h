@@ -128,6 +128,17 @@ hipError_t launch_gemm_tiles(const int32_t* counts, const int32_t* offsets, int3
 hipError_t launch_gateup_gemm(const MxArgs& p, const int4* gtiles, int64_t max_gtiles, hipStream_t st);
 hipError_t launch_down_gemm(const MxArgs& p, const int4* gtiles, int64_t max_gtiles, hipStream_t st);
 
+// ---- stream.hip: expert records fetched from host memory into HBM slots
+// copies the record of active expert j (tiles[j].x, j < *n_active) from src (device-
+// readable host memory, expert_bytes per record) into slot j of dst
+hipError_t launch_gather_experts(const uint8_t* src, int64_t expert_bytes, const int4* tiles, const int32_t* n_active,
+                                 int32_t max_slots, uint8_t* dst, hipStream_t st);
+// the grouping renumbered to slots (active expert j -> expert j): tiles_s [max_slots],
+// counts_s [max_slots], offsets_s [max_slots + 1], idx_s [rows]
+hipError_t launch_remap_to_slots(const int4* tiles, const int32_t* n_active, int32_t max_slots, const int32_t* counts,
+                                 const int32_t* offsets, const int32_t* idx, int64_t rows, int4* tiles_s,
+                                 int32_t* counts_s, int32_t* offsets_s, int32_t* idx_s, hipStream_t st);
+
 // ---- reap.hip: saliency[e] += sum over e's rows (perm order) of w[slot] ||y[slot]||_2
 hipError_t launch_reap_saliency(const float* y, const float* w, const int32_t* perm, const int32_t* offsets,
                                 int32_t E, int32_t L, double* saliency, hipStream_t st);

@@ -154,3 +154,29 @@ def test_config_struct_layout_matches_header(tmp_path):
     got = [int(v) for v in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()]
     assert got[0] == ctypes.sizeof(moe.MoEConfig)
     assert got[1:] == [getattr(moe.MoEConfig, f).offset for f in fields]
+
+
+def test_streamed_forward_slots_and_errors_before_any_launch():
+    L = moe.lib()
+    cfg = k3(T=1)
+    n = ctypes.c_size_t(0)
+    assert L.moe_expert_slots_bytes(ctypes.byref(cfg), 16, ctypes.byref(n)) == 0
+    assert n.value == 16 * 17_547_264                      # min(E, T*k) records
+    cfg64 = k3(T=64)
+    assert L.moe_expert_slots_bytes(ctypes.byref(cfg64), 16, ctypes.byref(n)) == 0
+    assert n.value == 896 * 17_547_264
+    assert L.moe_expert_slots_bytes(ctypes.byref(cfg), 0, ctypes.byref(n)) == -1
+
+    def sfwd(cfg, slots=FAKE + (4 << 30), slots_bytes=1 << 40, blob=FAKE + (8 << 30), k=16):
+        return L.moe_layer_forward_streamed(FAKE, FAKE + (1 << 30), FAKE + (2 << 30), FAKE + (3 << 30), blob, k,
+                                            ctypes.byref(cfg), None, slots, slots_bytes, FAKE + (5 << 30), None,
+                                            FAKE + (6 << 30), 1 << 40, None)
+    assert sfwd(k3(T=1), slots=None) == -1
+    assert sfwd(k3(T=0)) == 0
+    assert sfwd(k3(T=1), slots_bytes=16 * 17_547_264 - 1) == -1   # slot buffer too small
+    assert sfwd(k3(T=1), slots=FAKE + (4 << 30) + 8) == -1        # misaligned slots
+    assert sfwd(k3(T=1), blob=None) == -1
+    assert sfwd(k3(T=1), k=0) == -1
+    shared = k3(T=1)
+    shared.num_shared, shared.d_ffn_shared = 2, 3072
+    assert sfwd(shared) == -2
