@@ -8,10 +8,11 @@
 //
 // Block: 4 waves; wave w streams weight rows 16w..16w+15 of the block's 64 (gate and up
 // for gate/up, down for down) straight from HBM with GT_PF steps in flight, and runs
-// four 16x16x128 MFMA tiles (the 64 rows of the token tile) per matrix and per K step.
-// The activation tile (two-term e4m3, see quantize_quad8) moves through LDS two K steps
-// at a time, double-buffered: the loads of chunk c+1 are in registers while chunk c is
-// computed, and one barrier per chunk hands the buffers over.
+// one 16x16x128 MFMA tile per 16 routed rows of the tile, per matrix and per K step.
+// The activation tile (two-term e4m3, see quantize_quad8) moves through LDS in chunks of
+// 128 row-steps (two K steps of 64 rows, four of 32, eight of 16), double-buffered: the
+// loads of chunk c+1 are in registers while chunk c is computed, and one barrier per
+// chunk hands the buffers over.
 //
 // The grid is ordered so that each XCD (blocks b with the same b mod 8) works through a
 // contiguous range of tiles: the tiles of one expert, and the 48 (or 56) weight-row
@@ -25,22 +26,27 @@ namespace moe {
 
 constexpr int GT_TOK = 64;    // routed rows per tile
 constexpr int GT_ROWS = 64;   // weight rows per block (4 waves x 16)
-// K steps of weights in flight per wave and matrix: as deep as the registers allow (the
-// one-term kernels hold half the activation operands)
-template <int TERMS>
-constexpr int gt_pf_gateup() { return TERMS == 2 ? 2 : 4; }
-template <int TERMS>
-constexpr int gt_pf_down() { return TERMS == 2 ? 4 : 8; }
-constexpr int GT_CHUNK = 2;   // K steps per LDS activation chunk
 constexpr int GT_RS = 128;    // LDS row of a step's 128 code bytes, 16-byte chunk c at c ^ (row & 7)
-// one K step of the tile in LDS: hi codes [64][GT_RS], lo codes [64][GT_RS], hi scales
-// [64][4], lo scales [64][4].  The chunk swizzle keeps the MFMA-order reads of 16
-// consecutive rows and the row-order writes free of bank conflicts on gfx950.
-constexpr int GT_STEP_BYTES = 2 * GT_TOK * GT_RS + 2 * GT_TOK * 4;
-constexpr int GT_BUF_BYTES = GT_CHUNK * GT_STEP_BYTES;
-static_assert(16 % gt_pf_gateup<1>() == 0 && 16 % gt_pf_gateup<2>() == 0 && 16 % gt_pf_down<1>() == 0 &&
-                  16 % gt_pf_down<2>() == 0 && 16 % GT_CHUNK == 0,
-              "ring and chunks repeat every 16 steps");
+// The activation tile moves through LDS in chunks of GT_CHUNK_ROWSTEPS rows x steps: a
+// tile padded to R = 16, 32 or 64 rows stages 128 / R K steps per chunk, so a tile with
+// few rows (most experts at prefill hold a handful) waits for its activations once per
+// 8 steps rather than once per 2.  One step of R rows in LDS: hi codes [R][GT_RS], lo
+// codes [R][GT_RS], hi scales [R][4], lo scales [R][4].  The chunk swizzle keeps the
+// MFMA-order reads of 16 consecutive rows and the row-order writes free of bank
+// conflicts on gfx950.
+constexpr int GT_CHUNK_ROWSTEPS = 128;
+__host__ __device__ constexpr int gt_step_bytes(int R) { return 2 * R * GT_RS + 2 * R * 4; }
+constexpr int GT_BUF_BYTES = (GT_CHUNK_ROWSTEPS / GT_TOK) * gt_step_bytes(GT_TOK);
+static_assert((GT_CHUNK_ROWSTEPS / 16) * gt_step_bytes(16) == GT_BUF_BYTES &&
+                  (GT_CHUNK_ROWSTEPS / 32) * gt_step_bytes(32) == GT_BUF_BYTES,
+              "every chunk shape fills the same buffer");
+// K steps of weights in flight per wave and matrix, per tile height: as deep as the
+// registers allow (fewer token sub-tiles hold fewer accumulators; the one-term kernels
+// hold half the activation operands)
+template <int TERMS, int R>
+constexpr int gt_pf_gateup() { return R == 16 ? 8 : R == 32 ? 4 : TERMS == 2 ? 2 : 4; }
+template <int TERMS, int R>
+constexpr int gt_pf_down() { return R == 64 ? (TERMS == 2 ? 4 : 8) : 8; }
 
 // This thread's share of one chunk: 4 TERMS 16-byte code pieces and one scale dword.
 // TERMS = 2: the two exact e4m3 terms of bf16 activations; TERMS = 1: the MXFP8 mode,
@@ -51,65 +57,73 @@ struct GtRegs {
   uint32_t s;
 };
 
-// Loads chunk c (steps GT_CHUNK c ..) of the tile's rows: item j = tid + 256 u is
-// (step, term, row, 16-byte piece), so a wave moves 8 whole rows of one term.  Every
-// load is issued: rows past the tile read the row srow holds for them (a valid token)
-// and steps past the end re-read the last step, so the loads in flight are the same on
-// every path (see prime_stream); what they bring for such rows and steps is never used.
-// With one term, threads 128.. repeat the scale loads of threads 0..127 (and do not
-// store them), for the same reason.
-template <int TERMS>
+template <int R>
+constexpr int gt_log2() { return R == 16 ? 4 : R == 32 ? 5 : 6; }
+
+// Loads chunk c (steps CH c .. CH c + CH - 1, CH = 128 / R) of the tile's R rows: item
+// j = tid + 256 u is (step, term, row, 16-byte piece), so a wave moves whole rows of one
+// term.  Every load is issued: rows past the tile read the row srow holds for them (a
+// valid token) and steps past the end re-read the last step, so the loads in flight are
+// the same on every path (see prime_stream); what they bring for such rows and steps is
+// never used.  With one term, threads 128.. repeat the scale loads of threads 0..127
+// (and do not store them), for the same reason.
+template <int TERMS, int R>
 __device__ __forceinline__ void gt_load(GtRegs<TERMS>& r, const QRows& q, const int64_t* srow, int K, int nks,
                                         int c) {
+  constexpr int CH = GT_CHUNK_ROWSTEPS / R, LR = gt_log2<R>();
   const int tid = threadIdx.x;
   unroll_n<4 * TERMS>([&](auto uc) {
     constexpr int u = decltype(uc)::value;
-    const int j = tid + 256 * u;  // GT_CHUNK x TERMS x 64 rows x 8 pieces
-    const int s = j >> (8 + TERMS), term = TERMS == 2 ? (j >> 9) & 1 : 0, m = (j >> 3) & 63, part = j & 7;
-    const int ks = GT_CHUNK * c + s < nks ? GT_CHUNK * c + s : nks - 1;
+    const int j = tid + 256 * u;  // CH x TERMS x R rows x 8 pieces
+    const int rest = j >> (3 + LR);
+    const int s = TERMS == 2 ? rest >> 1 : rest, term = TERMS == 2 ? rest & 1 : 0, m = (j >> 3) & (R - 1),
+              part = j & 7;
+    const int ks = CH * c + s < nks ? CH * c + s : nks - 1;
     r.v[u] = *reinterpret_cast<const u32x4_t*>((term ? q.lo : q.hi) + srow[m] * K + 128 * ks + 16 * part);
   });
   {
-    const int it = TERMS == 2 ? tid : tid & 127;  // GT_CHUNK x 64 rows x TERMS
-    const int s = it >> (6 + TERMS - 1), m = (it >> (TERMS - 1)) & 63, term = TERMS == 2 ? it & 1 : 0;
-    const int ks = GT_CHUNK * c + s < nks ? GT_CHUNK * c + s : nks - 1;
+    const int it = TERMS == 2 ? tid : tid & 127;  // CH x R rows x TERMS
+    const int s = it >> (LR + TERMS - 1), m = (it >> (TERMS - 1)) & (R - 1), term = TERMS == 2 ? it & 1 : 0;
+    const int ks = CH * c + s < nks ? CH * c + s : nks - 1;
     r.s = *reinterpret_cast<const uint32_t*>((term ? q.slo : q.shi) + srow[m] * (K / 32) + 4 * ks);
   }
 }
 
-template <int TERMS>
+template <int TERMS, int R>
 __device__ __forceinline__ void gt_store(const GtRegs<TERMS>& r, uint8_t* buf) {
+  constexpr int LR = gt_log2<R>(), SB = gt_step_bytes(R);
   const int tid = threadIdx.x;
   unroll_n<4 * TERMS>([&](auto uc) {
     constexpr int u = decltype(uc)::value;
     const int j = tid + 256 * u;
-    const int s = j >> (8 + TERMS), term = TERMS == 2 ? (j >> 9) & 1 : 0, m = (j >> 3) & 63, part = j & 7;
-    *reinterpret_cast<u32x4_t*>(buf + s * GT_STEP_BYTES + term * GT_TOK * GT_RS + m * GT_RS + 16 * (part ^ (m & 7))) =
-        r.v[u];
+    const int rest = j >> (3 + LR);
+    const int s = TERMS == 2 ? rest >> 1 : rest, term = TERMS == 2 ? rest & 1 : 0, m = (j >> 3) & (R - 1),
+              part = j & 7;
+    *reinterpret_cast<u32x4_t*>(buf + s * SB + term * R * GT_RS + m * GT_RS + 16 * (part ^ (m & 7))) = r.v[u];
   });
   if (TERMS == 2 || tid < 128) {
     const int it = tid;
-    const int s = it >> (6 + TERMS - 1), m = (it >> (TERMS - 1)) & 63, term = TERMS == 2 ? it & 1 : 0;
-    *reinterpret_cast<uint32_t*>(buf + s * GT_STEP_BYTES + 2 * GT_TOK * GT_RS + term * GT_TOK * 4 + m * 4) = r.s;
+    const int s = it >> (LR + TERMS - 1), m = (it >> (TERMS - 1)) & (R - 1), term = TERMS == 2 ? it & 1 : 0;
+    *reinterpret_cast<uint32_t*>(buf + s * SB + 2 * R * GT_RS + term * R * 4 + m * 4) = r.s;
   }
 }
 
 // activation operand of step s of a chunk for tile row m (chunks g and 4 + g of the row)
-template <int TERMS>
+template <int TERMS, int R>
 __device__ __forceinline__ void gt_read(AStep& a, const uint8_t* buf, int s, int m, int g) {
-  const uint8_t* st = buf + s * GT_STEP_BYTES;
+  const uint8_t* st = buf + s * gt_step_bytes(R);
   const int c0 = 16 * (g ^ (m & 7)), c1 = 16 * ((4 + g) ^ (m & 7));
   const uint4 h0 = *reinterpret_cast<const uint4*>(st + m * GT_RS + c0);
   const uint4 h1 = *reinterpret_cast<const uint4*>(st + m * GT_RS + c1);
   a.hi[0] = (int)h0.x; a.hi[1] = (int)h0.y; a.hi[2] = (int)h0.z; a.hi[3] = (int)h0.w;
   a.hi[4] = (int)h1.x; a.hi[5] = (int)h1.y; a.hi[6] = (int)h1.z; a.hi[7] = (int)h1.w;
-  a.shi = st[2 * GT_TOK * GT_RS + m * 4 + g];
+  a.shi = st[2 * R * GT_RS + m * 4 + g];
   if constexpr (TERMS == 2) {
-    const uint4 l0 = *reinterpret_cast<const uint4*>(st + GT_TOK * GT_RS + m * GT_RS + c0);
-    const uint4 l1 = *reinterpret_cast<const uint4*>(st + GT_TOK * GT_RS + m * GT_RS + c1);
+    const uint4 l0 = *reinterpret_cast<const uint4*>(st + R * GT_RS + m * GT_RS + c0);
+    const uint4 l1 = *reinterpret_cast<const uint4*>(st + R * GT_RS + m * GT_RS + c1);
     a.lo[0] = (int)l0.x; a.lo[1] = (int)l0.y; a.lo[2] = (int)l0.z; a.lo[3] = (int)l0.w;
     a.lo[4] = (int)l1.x; a.lo[5] = (int)l1.y; a.lo[6] = (int)l1.z; a.lo[7] = (int)l1.w;
-    a.slo = st[2 * GT_TOK * GT_RS + GT_TOK * 4 + m * 4 + g];
+    a.slo = st[2 * R * GT_RS + R * 4 + m * 4 + g];
   }
 }
 
@@ -117,24 +131,26 @@ __device__ __forceinline__ void gt_read(AStep& a, const uint8_t* buf, int s, int
 // x * nb/8 .. (x+1) * nb/8 - 1 (nb a multiple of 8)
 __device__ __forceinline__ int gt_logical_block(int b, int nb) { return (b & 7) * (nb >> 3) + (b >> 3); }
 
-// The K loop of one tile: acc[q][tt] += A(token sub-tile tt) x W_q^T over all K steps.
-// The loop runs over whole 16-step blocks; steps past the end issue their (clamped)
-// loads, stores and barriers like the others and skip only the math, so every path
-// issues the same loads and the waits for them are exact.
-template <class W, int NMAT, int GT_PF, int TERMS>
+// The K loop of one tile padded to R rows: acc[q][tt] += A(token sub-tile tt) x W_q^T over
+// all K steps.  The loop runs over whole 16-step blocks; steps past the end issue their
+// (clamped) loads, stores and barriers like the others and skip only the math, so every
+// path issues the same loads and the waits for them are exact.
+template <class W, int NMAT, int GT_PF, int TERMS, int R>
 __device__ __forceinline__ void gt_mainloop(const W (&w)[NMAT], const QRows& q, const int64_t* srow, int n, int K,
                                             uint8_t* lds, f32x4 (&acc)[NMAT][4]) {
+  constexpr int CH = GT_CHUNK_ROWSTEPS / R;
+  static_assert(16 % GT_PF == 0 && 16 % CH == 0, "ring and chunks repeat every 16 steps");
   const int lane = lane_id(), g = lane >> 4, nl = lane & 15;
   const int nks = K / 128, nc = (nks + 15) / 16;
   const int ntt = (n + 15) / 16;  // token sub-tiles holding rows
   // chunk 0 into buffer 0, chunk 1 into registers, the first weight steps in flight
   GtRegs<TERMS> rg;
-  gt_load<TERMS>(rg, q, srow, K, nks, 0);
+  gt_load<TERMS, R>(rg, q, srow, K, nks, 0);
   SBlock sb[NMAT], sbn[NMAT];
   uint4 ring[NMAT][GT_PF];
   prime_stream<W, NMAT, GT_PF>(w, sb, ring, nks);
-  gt_store<TERMS>(rg, lds);
-  gt_load<TERMS>(rg, q, srow, K, nks, 1);
+  gt_store<TERMS, R>(rg, lds);
+  gt_load<TERMS, R>(rg, q, srow, K, nks, 1);
   lds_barrier();
   for (int cb = 0; cb < nc; ++cb) {
 #pragma unroll
@@ -142,7 +158,7 @@ __device__ __forceinline__ void gt_mainloop(const W (&w)[NMAT], const QRows& q, 
     unroll16([&](auto jc) {
       constexpr int J = decltype(jc)::value;
       const int ks = 16 * cb + J;
-      const int ch = ks / GT_CHUNK;
+      const int ch = ks / CH;
       const uint8_t* buf = lds + (ch & 1) * GT_BUF_BYTES;
       uint4 cw[NMAT];
 #pragma unroll
@@ -152,10 +168,10 @@ __device__ __forceinline__ void gt_mainloop(const W (&w)[NMAT], const QRows& q, 
       }
       if (ks < nks) {
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
+        for (int tt = 0; tt < R / 16; ++tt) {
           if (tt >= ntt) continue;  // token sub-tile past the tile's rows
           AStep a;
-          gt_read<TERMS>(a, buf, J % GT_CHUNK, 16 * tt + nl, g);
+          gt_read<TERMS, R>(a, buf, J % CH, 16 * tt + nl, g);
 #pragma unroll
           for (int mq = 0; mq < NMAT; ++mq) {
             const uint32_t sw = w[mq].template scale<J>(sb[mq]);
@@ -165,17 +181,32 @@ __device__ __forceinline__ void gt_mainloop(const W (&w)[NMAT], const QRows& q, 
           }
         }
       }
-      if constexpr (J % GT_CHUNK == GT_CHUNK - 1) {
+      if constexpr (J % CH == CH - 1) {
         // end of chunk ch: the registers hold chunk ch+1; every wave is past chunk ch-1,
         // so its buffer is free
-        gt_store<TERMS>(rg, lds + ((ch + 1) & 1) * GT_BUF_BYTES);
-        gt_load<TERMS>(rg, q, srow, K, nks, ch + 2);
+        gt_store<TERMS, R>(rg, lds + ((ch + 1) & 1) * GT_BUF_BYTES);
+        gt_load<TERMS, R>(rg, q, srow, K, nks, ch + 2);
         lds_barrier();
       }
     });
 #pragma unroll
     for (int mq = 0; mq < NMAT; ++mq) sb[mq] = sbn[mq];
   }
+}
+
+// the K loop for a tile of n rows, in the chunk shape of its height
+template <class W, int NMAT, int TERMS, bool GATEUP>
+__device__ __forceinline__ void gt_mainloop_any(const W (&w)[NMAT], const QRows& q, const int64_t* srow, int n,
+                                                int K, uint8_t* lds, f32x4 (&acc)[NMAT][4]) {
+  if (n <= 16)
+    gt_mainloop<W, NMAT, GATEUP ? gt_pf_gateup<TERMS, 16>() : gt_pf_down<TERMS, 16>(), TERMS, 16>(w, q, srow, n, K,
+                                                                                                  lds, acc);
+  else if (n <= 32)
+    gt_mainloop<W, NMAT, GATEUP ? gt_pf_gateup<TERMS, 32>() : gt_pf_down<TERMS, 32>(), TERMS, 32>(w, q, srow, n, K,
+                                                                                                  lds, acc);
+  else
+    gt_mainloop<W, NMAT, GATEUP ? gt_pf_gateup<TERMS, 64>() : gt_pf_down<TERMS, 64>(), TERMS, 64>(w, q, srow, n, K,
+                                                                                                  lds, acc);
 }
 
 // Gate/up with the GLU: a = bf16(silu(g) u) for the tile, re-quantised to two e4m3 terms
@@ -207,7 +238,7 @@ __global__ void __launch_bounds__(256, 2) gateup_gemm_kernel(MxArgs p, const int
   for (int mq = 0; mq < 2; ++mq)
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) acc[mq][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  gt_mainloop<W, 2, gt_pf_gateup<TERMS>(), TERMS>(w, p.hq, srow, n, L, lds, acc);
+  gt_mainloop_any<W, 2, TERMS, true>(w, p.hq, srow, n, L, lds, acc);
   // GLU into an LDS tile (the activation buffers are free now), then the requantisation
   float* at = reinterpret_cast<float*>(lds);  // [64 tokens][65]
   const int f = rt * GT_ROWS + 16 * wave + nl;
@@ -264,7 +295,7 @@ __global__ void __launch_bounds__(256, 2) down_gemm_kernel(MxArgs p, const int4*
   f32x4 acc[1][4];
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt) acc[0][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  gt_mainloop<W, 1, gt_pf_down<TERMS>(), TERMS>(w, p.aq, srow, n, F, lds, acc);
+  gt_mainloop_any<W, 1, TERMS, false>(w, p.aq, srow, n, F, lds, acc);
   const int l = rt * GT_ROWS + 16 * wave + nl;
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt)
