@@ -34,40 +34,53 @@ struct DenseParams {
   DenseSeg seg[2];
 };
 
+// The token rows are staged once per block in LDS (their loads issued first, then the
+// weight row's, so the wait for them leaves the weight loads in flight): the registers
+// then hold only the weight row, and more waves fit a SIMD, so the router + latent-down
+// grid (4480 rows at one token) and the latent-up grid (7168 rows) run in one round.
 template <int NCH, int G>
 __global__ void __launch_bounds__(256) dense_gemv_kernel(DenseParams p) {
+  constexpr int XN = G * NCH * 64;            // 16-byte pieces of the block's token rows
+  constexpr int XPT = (XN + 255) / 256;       // per thread
+  __shared__ uint4 xs[XN];
   const int lane = lane_id();
   const int wave = threadIdx.x / WAVE;
   int64_t row = (int64_t)blockIdx.x * 4 + wave;
   // the segment is chosen with scalar selects so every field stays in kernel-argument
   // registers (an indexed p.seg[si] would be read from memory after the loads)
   const bool second = row >= p.seg[0].rows;
-  if (second) {
-    row -= p.seg[0].rows;
-    if (p.nseg < 2 || row >= p.seg[1].rows) return;
-  }
+  if (second) row -= p.seg[0].rows;
   const DenseSeg s = second ? p.seg[1] : p.seg[0];
+  // a wave past the last row works on the segment's last row and writes nothing (no
+  // wave leaves before the block's barrier)
+  const bool valid = !second || (p.nseg >= 2 && row < p.seg[1].rows);
+  if (!valid) row = s.rows - 1;
   const int32_t K = p.K;
   const int64_t t0 = (int64_t)blockIdx.y * G;
 
+  uint4 xv[XPT];
+#pragma unroll
+  for (int u = 0; u < XPT; ++u) {
+    const int i = threadIdx.x + 256 * u < XN ? threadIdx.x + 256 * u : XN - 1;
+    const int g = i / (NCH * 64), rem = i - g * (NCH * 64);
+    const int col = 8 * rem;  // piece rem = 64 c + lane of token g
+    const int64_t t = t0 + g < p.T ? t0 + g : p.T - 1;
+    xv[u] = *reinterpret_cast<const uint4*>(p.x + t * K + (col < K ? col : 0));
+    if (col >= K || t0 + g >= p.T) xv[u] = make_uint4(0, 0, 0, 0);
+  }
   uint4 wr[NCH];
   const uint16_t* wrow = s.W + row * K;
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
-    int col = 8 * (64 * c + lane);
-    wr[c] = col < K ? load_nt16(wrow + col) : make_uint4(0, 0, 0, 0);
+    const int col = 8 * (64 * c + lane);
+    wr[c] = load_nt16(wrow + (col < K ? col : 0));
+    if (col >= K) wr[c] = make_uint4(0, 0, 0, 0);
   }
-  uint4 xr[G][NCH];
 #pragma unroll
-  for (int g = 0; g < G; ++g)
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      int col = 8 * (64 * c + lane);
-      if (col < K && t0 + g < p.T)
-        xr[g][c] = *reinterpret_cast<const uint4*>(p.x + (t0 + g) * K + col);
-      else
-        xr[g][c] = make_uint4(0, 0, 0, 0);
-    }
+  for (int u = 0; u < XPT; ++u)
+    if (threadIdx.x + 256 * u < XN) xs[threadIdx.x + 256 * u] = xv[u];
+  lds_barrier();  // the weight loads stay in flight
+  auto xr = [&](int g, int c) -> uint4 { return xs[g * (NCH * 64) + 64 * c + lane]; };
 
   if (!s.router) {
     // latent projections: fp32 chunk partials folded into fp64, rounded once to bf16
@@ -78,17 +91,18 @@ __global__ void __launch_bounds__(256) dense_gemv_kernel(DenseParams p) {
     for (int c = 0; c < NCH; ++c)
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        float pc = dot2(xr[g][c].x, wr[c].x, 0.f);
-        pc = dot2(xr[g][c].y, wr[c].y, pc);
-        pc = dot2(xr[g][c].z, wr[c].z, pc);
-        pc = dot2(xr[g][c].w, wr[c].w, pc);
+        const uint4 xc = xr(g, c);
+        float pc = dot2(xc.x, wr[c].x, 0.f);
+        pc = dot2(xc.y, wr[c].y, pc);
+        pc = dot2(xc.z, wr[c].z, pc);
+        pc = dot2(xc.w, wr[c].w, pc);
         acc[g] += (double)pc;
       }
     uint16_t* out = reinterpret_cast<uint16_t*>(s.out);
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       double v = wave_sum_dpp(acc[g]);
-      if (lane == 0 && t0 + g < p.T) {
+      if (valid && lane == 0 && t0 + g < p.T) {
         for (int a = 0; a < s.add_rows; ++a) v += (double)s.add[((t0 + g) * s.add_rows + a) * s.rows + row];
         out[(t0 + g) * s.rows + row] = f64_to_bf16(v);
       }
@@ -112,10 +126,11 @@ __global__ void __launch_bounds__(256) dense_gemv_kernel(DenseParams p) {
             bf16x2_subnormal(wr[c].w);
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      float pc = dot2(xr[g][c].x, wr[c].x, 0.f);
-      pc = dot2(xr[g][c].y, wr[c].y, pc);
-      pc = dot2(xr[g][c].z, wr[c].z, pc);
-      pc = dot2(xr[g][c].w, wr[c].w, pc);
+      const uint4 xc = xr(g, c);
+      float pc = dot2(xc.x, wr[c].x, 0.f);
+      pc = dot2(xc.y, wr[c].y, pc);
+      pc = dot2(xc.z, wr[c].z, pc);
+      pc = dot2(xc.w, wr[c].w, pc);
       acc[g] += (double)pc;
     }
   }
@@ -123,24 +138,25 @@ __global__ void __launch_bounds__(256) dense_gemv_kernel(DenseParams p) {
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     double v = wave_sum_dpp(acc[g]);
-    if (lane == 0 && t0 + g < p.T) out[(t0 + g) * s.rows + row] = (float)v;
+    if (valid && lane == 0 && t0 + g < p.T) out[(t0 + g) * s.rows + row] = (float)v;
   }
   wn = wave_sum_dpp(wn);
   const bool wany = __any(wsub != 0u);
-  if (lane == 0 && blockIdx.y == 0) s.wnorm[row] = wany ? __builtin_inff() : sqrtf(wn);
-  if (row == 0) {  // one wave per token group writes the token norms
+  if (valid && lane == 0 && blockIdx.y == 0) s.wnorm[row] = wany ? __builtin_inff() : sqrtf(wn);
+  if (valid && row == 0) {  // one wave per token group writes the token norms
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       float xn = 0.f;
       uint32_t xsub = 0;
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
-        xn = dot2(xr[g][c].x, xr[g][c].x, xn);
-        xn = dot2(xr[g][c].y, xr[g][c].y, xn);
-        xn = dot2(xr[g][c].z, xr[g][c].z, xn);
-        xn = dot2(xr[g][c].w, xr[g][c].w, xn);
-        xsub |= bf16x2_subnormal(xr[g][c].x) | bf16x2_subnormal(xr[g][c].y) | bf16x2_subnormal(xr[g][c].z) |
-                bf16x2_subnormal(xr[g][c].w);
+        const uint4 xc = xr(g, c);
+        xn = dot2(xc.x, xc.x, xn);
+        xn = dot2(xc.y, xc.y, xn);
+        xn = dot2(xc.z, xc.z, xn);
+        xn = dot2(xc.w, xc.w, xn);
+        xsub |= bf16x2_subnormal(xc.x) | bf16x2_subnormal(xc.y) | bf16x2_subnormal(xc.z) |
+                bf16x2_subnormal(xc.w);
       }
       xn = wave_sum_dpp(xn);
       const bool xany = __any(xsub != 0u);
