@@ -35,6 +35,7 @@ METRIC = "MoE-layer tokens/s on 1 MI355X; HBM GB/s (decode), FP4 MFMA util (pref
 HBM_PEAK_GBS = 8000.0
 FP4_PEAK_TFS = 10100.0  # dense MFMA, fp4
 FP8_PEAK_TFS = 5000.0   # dense MFMA, fp8
+HOST_LINK_PEAK_GBS = 64.0  # PCIe 5.0 x16, one direction
 
 
 def log(*a):
@@ -106,6 +107,9 @@ def main():
                     help="always-on shared experts of FFN width d_ffn (the routed layer alone by default)")
     ap.add_argument("--layout", default="packed", choices=["packed", "record"],
                     help="expert weights as packed once by moe_pack_experts (default) or as checkpoint records")
+    ap.add_argument("--experts-in", default="hbm", choices=["hbm", "host"],
+                    help="expert records resident in HBM (default) or in pinned host memory, the routed ones "
+                         "fetched over the host link every step (moe_layer_forward_streamed)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -146,6 +150,16 @@ def main():
         blob = moe.pack_experts(blob, c.E, c.L, c.F)
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
+    streamed = args.experts_in == "host"
+    if streamed:  # the experts move to pinned host memory; HBM keeps only the slots
+        if args.shared:
+            raise SystemExit("--experts-in host runs the routed layer only (no --shared)")
+        host_blob = torch.empty(blob.numel(), dtype=torch.uint8, pin_memory=True)
+        host_blob.copy_(blob)
+        del blob
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        blob = host_blob
     copies = [dict(router_w=up(dense["router_w"]), latent_down=up(dense["latent_down"]),
                    latent_up=up(dense["latent_up"])) for _ in range(max(1, args.dense_copies))]
     x_host = synth.make_tokens(c, T=c.T * nbatch).reshape(nbatch, c.T, c.d)
@@ -163,6 +177,7 @@ def main():
     cfg = moe.make_config(c.T, c.d, c.L, c.F, c.E, bias=bias, packed=packed, act_format=act_format,
                           num_shared=args.shared, d_ffn_shared=c.F if args.shared else 0)
     ws = moe.alloc_workspace(cfg, c.k, dev)
+    slots = moe.alloc_expert_slots(cfg, c.k, dev) if streamed else None
     out = torch.empty((c.T, c.d), dtype=torch.int16, device=dev)
     counts = torch.zeros((nbatch, c.E), dtype=torch.int32, device=dev)
     hip = HipEvents()
@@ -173,7 +188,11 @@ def main():
     def step(i, events=None):
         cp = copies[i % len(copies)]
         routing = {"expert_counts": counts[i]}
-        if events is None or args.shared:  # the stage events are not recorded with shared experts
+        if streamed:
+            moe.layer_forward_streamed(xs[i], cp["router_w"], cp["latent_down"], cp["latent_up"], blob, c.k,
+                                       d_ffn=c.F, expert_slots=slots, bias=bias, out=out, workspace=ws,
+                                       routing=routing, packed=packed, act_format=act_format)
+        elif events is None or args.shared:  # the stage events are not recorded with shared experts
             moe.layer_forward(xs[i], cp["router_w"], cp["latent_down"], cp["latent_up"], blob, c.k, d_ffn=c.F,
                               bias=bias, out=out, workspace=ws, routing=routing, packed=packed,
                               act_format=act_format, shared_blob=shared, num_shared=args.shared,
@@ -202,8 +221,8 @@ def main():
     hip.rt.hipEventRecord(ev_stop, stream)
     torch.cuda.synchronize()
     eager_ms = hip.elapsed_ms(ev_start, ev_stop)
-    dom_ms = ([hip.elapsed_ms(kev[2 * i], kev[2 * i + 1]) for i in range(W, W + K)] if not args.shared
-              else [float("nan")] * K)
+    dom_ms = ([hip.elapsed_ms(kev[2 * i], kev[2 * i + 1]) for i in range(W, W + K)]
+              if not (args.shared or streamed) else [float("nan")] * K)
 
     total_ms = eager_ms
     if args.graph:
@@ -245,7 +264,7 @@ def main():
     layer_gbs = float(np.mean(layer_bytes) / (ms_per_step * 1e-3) / 1e9)
 
     stages = None
-    if args.breakdown and not args.shared:
+    if args.breakdown and not (args.shared or streamed):
         evs = hip.create(2 * moe.NUM_STAGES)
         sums = np.zeros(moe.NUM_STAGES)
         n = min(K, 10)
@@ -279,7 +298,16 @@ def main():
                "sample": f"{n} tokens of the {c.name} workload, whole layer one token at a time "
                          f"(single-threaded C oracle, fp64 sums, exact router), {dt:.1f} s"}
 
-    if c.T * c.k >= 8 * c.E:
+    if streamed:
+        # the step is bound by the host link: the routed records cross it every step
+        link_bytes = active * 3 * mat_bytes
+        link_gbs = float(np.mean(link_bytes) / (ms_per_step * 1e-3) / 1e9)
+        roofline = {"bound": "host link", "kernel": "gather_experts_kernel (routed records, pinned host -> HBM)",
+                    "achieved": round(link_gbs, 1), "peak": HOST_LINK_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(link_gbs / HOST_LINK_PEAK_GBS, 4), "traffic": None,
+                    "note": "achieved = routed record bytes per step / whole step time (a lower bound on the link rate)",
+                    "bytes_per_step": int(np.mean(link_bytes))}
+    elif c.T * c.k >= 8 * c.E:
         # many routed rows per expert: the gate/up stage runs as grouped GEMMs on the matrix
         # cores; model flops 2 x rows x F x L per matrix against the dense FP4 peak (the
         # kernel issues e4m3 x e2m1 MFMAs, two per K step, at the fp8 rate)
@@ -319,7 +347,8 @@ def main():
                    "parallelism": "single GPU",
                    "dense_weight_copies": len(copies), "mean_active_experts": float(np.mean(active)),
                    "shared_experts": args.shared,
-                   "expert_layout": "packed by moe_pack_experts at load" if packed else "checkpoint records"},
+                   "expert_layout": "packed by moe_pack_experts at load" if packed else "checkpoint records",
+                   "experts_in": "pinned host memory, routed records fetched per step" if streamed else "HBM"},
         "roofline": roofline,
         "layer_hbm": {"achieved_GBs": round(layer_gbs, 1), "frac": round(layer_gbs / HBM_PEAK_GBS, 4),
                       "bytes_per_step": int(np.mean(layer_bytes))},
