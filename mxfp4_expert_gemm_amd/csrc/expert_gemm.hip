@@ -275,13 +275,18 @@ __global__ void __launch_bounds__(256, 2) gateup_gemm_kernel(MxArgs p, const int
   }
 }
 
-// Down: y[slot][l] fp32 for the tile's routed rows.
-template <class W, int TERMS>
+// Down: y[slot][l] fp32 for the tile's routed rows.  Each wave streams NG row groups of
+// 16 (groups 4 q + wave of the block's 4 NG, q < NG), so every activation operand read
+// from LDS feeds NG weight tiles: with NG = 2 (latent width a multiple of 128) a block
+// covers 128 latent rows, the LDS operand traffic per MFMA halves and each activation
+// chunk feeds twice the matrix-core work, the register profile of the gate/up kernel.
+template <class W, int TERMS, int NG>
 __global__ void __launch_bounds__(256, 2) down_gemm_kernel(MxArgs p, const int4* __restrict__ gtiles, int ntiles,
                                                             int nb) {
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ int64_t srow[GT_TOK];
-  const int F = p.F, L = p.L, nrt = L / GT_ROWS;
+  constexpr int ROWS = GT_ROWS * NG;
+  const int F = p.F, L = p.L, nrt = L / ROWS;
   const int lb = gt_logical_block(blockIdx.x, nb);
   if (lb / nrt >= ntiles) return;  // the grid is rounded up to a multiple of 8
   const int4 tile = gtiles[lb / nrt];
@@ -291,19 +296,26 @@ __global__ void __launch_bounds__(256, 2) down_gemm_kernel(MxArgs p, const int4*
   const int lane = lane_id(), wave = threadIdx.x / WAVE, g = lane >> 4, nl = lane & 15;
   for (int m = threadIdx.x; m < GT_TOK; m += blockDim.x) srow[m] = m < n ? p.perm[r0 + m] : 0;
   __syncthreads();
-  const W w[1] = {W::make(p.blob, e, L, F, MAT_DOWN, rt * 4 + wave, lane)};
-  f32x4 acc[1][4];
+  W w[NG];
 #pragma unroll
-  for (int tt = 0; tt < 4; ++tt) acc[0][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  gt_mainloop_any<W, 1, TERMS, false>(w, p.aq, srow, n, F, lds, acc);
-  const int l = rt * GT_ROWS + 16 * wave + nl;
+  for (int q = 0; q < NG; ++q) w[q] = W::make(p.blob, e, L, F, MAT_DOWN, rt * 4 * NG + 4 * q + wave, lane);
+  f32x4 acc[NG][4];
 #pragma unroll
-  for (int tt = 0; tt < 4; ++tt)
+  for (int q = 0; q < NG; ++q)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int m = 16 * tt + 4 * g + j;
-      if (m < n) p.y[srow[m] * L + l] = acc[0][tt][j];
-    }
+    for (int tt = 0; tt < 4; ++tt) acc[q][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  gt_mainloop_any<W, NG, TERMS, NG == 2>(w, p.aq, srow, n, F, lds, acc);
+#pragma unroll
+  for (int q = 0; q < NG; ++q) {
+    const int l = rt * ROWS + GT_ROWS * q + 16 * wave + nl;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int m = 16 * tt + 4 * g + j;
+        if (m < n) p.y[srow[m] * L + l] = acc[q][tt][j];
+      }
+  }
 }
 
 // Tiles of GT_TOK routed rows per active expert, in expert order: gtiles[0, ntiles) =
@@ -357,14 +369,25 @@ static hipError_t gateup_gemm_go(const MxArgs& p, const int4* gtiles, int64_t ma
   return hipGetLastError();
 }
 
-template <class W, int TERMS>
+template <class W, int TERMS, int NG>
 static hipError_t down_gemm_go(const MxArgs& p, const int4* gtiles, int64_t max_gtiles, int64_t nb, hipStream_t st) {
-  static const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&down_gemm_kernel<W, TERMS>),
+  static const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&down_gemm_kernel<W, TERMS, NG>),
                                                   hipFuncAttributeMaxDynamicSharedMemorySize, 2 * GT_BUF_BYTES);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((down_gemm_kernel<W, TERMS>), dim3((unsigned)nb), dim3(256), 2 * GT_BUF_BYTES, st, p, gtiles,
+  hipLaunchKernelGGL((down_gemm_kernel<W, TERMS, NG>), dim3((unsigned)nb), dim3(256), 2 * GT_BUF_BYTES, st, p, gtiles,
                      (int)max_gtiles, (int)nb);
   return hipGetLastError();
+}
+
+template <int NG>
+static hipError_t down_gemm_ng(const MxArgs& p, const int4* gtiles, int64_t max_gtiles, hipStream_t st) {
+  const int64_t nb = (max_gtiles * (p.L / (GT_ROWS * NG)) + 7) / 8 * 8;
+  if (nb > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (p.packed)
+    return p.mxfp8 ? down_gemm_go<PackedW, 1, NG>(p, gtiles, max_gtiles, nb, st)
+                   : down_gemm_go<PackedW, 2, NG>(p, gtiles, max_gtiles, nb, st);
+  return p.mxfp8 ? down_gemm_go<RecordW, 1, NG>(p, gtiles, max_gtiles, nb, st)
+                 : down_gemm_go<RecordW, 2, NG>(p, gtiles, max_gtiles, nb, st);
 }
 
 hipError_t launch_gateup_gemm(const MxArgs& p, const int4* gtiles, int64_t max_gtiles, hipStream_t st) {
@@ -382,13 +405,7 @@ hipError_t launch_gateup_gemm(const MxArgs& p, const int4* gtiles, int64_t max_g
 hipError_t launch_down_gemm(const MxArgs& p, const int4* gtiles, int64_t max_gtiles, hipStream_t st) {
   if (p.T == 0) return hipSuccess;
   if (p.L % GT_ROWS || p.F % 128) return hipErrorInvalidValue;
-  const int64_t nb = (max_gtiles * (p.L / GT_ROWS) + 7) / 8 * 8;
-  if (nb > 0x7FFFFFFF) return hipErrorInvalidValue;
-  if (p.packed)
-    return p.mxfp8 ? down_gemm_go<PackedW, 1>(p, gtiles, max_gtiles, nb, st)
-                   : down_gemm_go<PackedW, 2>(p, gtiles, max_gtiles, nb, st);
-  return p.mxfp8 ? down_gemm_go<RecordW, 1>(p, gtiles, max_gtiles, nb, st)
-                 : down_gemm_go<RecordW, 2>(p, gtiles, max_gtiles, nb, st);
+  return p.L % (2 * GT_ROWS) == 0 ? down_gemm_ng<2>(p, gtiles, max_gtiles, st) : down_gemm_ng<1>(p, gtiles, max_gtiles, st);
 }
 
 }  // namespace moe
