@@ -8,9 +8,9 @@
 // fp64 (fp32 partials of 8 exact products folded into fp64) at no cost in time; the
 // bf16 outputs are then the correctly rounded sums but for fp64-level ties.  One wave owns one
 // row; lane l reads 16 bytes (8 bf16) at column 8*(64c + l) for chunk c, so each
-// load instruction covers 1 KiB of the row contiguously and the token values the
-// lane needs stay in registers for the whole row.  Products of bf16 pairs are exact
-// in fp32 (v_dot2_f32_bf16).
+// load instruction covers 1 KiB of the row contiguously, and reads the matching token
+// values from the block's copy of the token rows in LDS.  Products of bf16 pairs are
+// exact in fp32 (v_dot2_f32_bf16).
 //
 // Router rows fold each 8-element chunk partial into an fp64 accumulator.  Error
 // bound: a chunk partial is 4 dot2 steps from zero, at most 8 fp32 roundings of
