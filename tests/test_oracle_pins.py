@@ -484,3 +484,30 @@ def test_shared_experts_with_zero_output_leave_the_layer():
     a = oracle.layer_forward(x, Wr, Wd, Wu, blob, k, L, F)
     b = oracle.layer_forward(x, Wr, Wd, Wu, blob, k, L, F, shared_blob=shared, num_shared=2, d_ffn_shared=F_s)
     assert np.array_equal(a["out"], b["out"])
+
+
+# ------------------------------------------------- expert layout (cosine check)
+
+def test_expert_cosine_detects_layout_mistakes():
+    """The per-expert cosine check of the GPU tests catches layout mistakes: with gate and
+    up swapped, the three matrices of a record mis-stacked by one, or the neighbouring
+    record read, the oracle's own expert output moves far from the correct one, while the
+    GPU tests require a cosine of at least 0.9999 (the layer's kimi-k3-mlx verification idea:
+    a mis-stacked or transposed expert drives the similarity towards zero)."""
+    from _util import cosine
+    c = synth.CONFIGS["tiny"]
+    lay = synth.make_layer(c)
+    hl = oracle.linear_bf16(lay["x"], lay["latent_down"])
+    rec = c.record_bytes
+    mb = rec // 3  # gate, up and down have the same size at the tiny shape (L == F)
+    for e in range(c.E):
+        r = lay["blob"][e * rec:(e + 1) * rec]
+        nxt = lay["blob"][((e + 1) % c.E) * rec:((e + 1) % c.E + 1) * rec]
+        swapped = np.concatenate([r[mb:2 * mb], r[:mb], r[2 * mb:]])
+        rotated = np.concatenate([r[mb:], r[:mb]])
+        for t in range(2):
+            _, y = oracle.expert(hl[t], r, c.L, c.F)
+            assert cosine(y, oracle.expert(hl[t], r, c.L, c.F)[1]) == pytest.approx(1.0, abs=1e-12)
+            assert cosine(y, oracle.expert(hl[t], swapped, c.L, c.F)[1]) < 0.95
+            assert abs(cosine(y, oracle.expert(hl[t], rotated, c.L, c.F)[1])) < 0.6
+            assert abs(cosine(y, oracle.expert(hl[t], nxt, c.L, c.F)[1])) < 0.6
