@@ -263,6 +263,16 @@ static hipError_t launch_dm(const DenseMfmaArgs& a0, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Tile of a batch below 256 tokens: the largest of 64 x 64, 64 x 32 and 32 x 32 (tokens x
+// rows) that still gives the grid about one block per CU, since a few dozen blocks (the
+// router at 64 tokens has 14 tiles of 64 x 64) leave most of the chip idle.  Every shape
+// runs the same K-tile arithmetic, so the results do not depend on the choice.
+static int small_tile(int64_t T, int32_t N) {
+  if (ceil_div(T, 64) * ceil_div(N, 64) >= 224) return 0;
+  if (ceil_div(T, 64) * ceil_div(N, 32) >= 200) return 1;
+  return 2;
+}
+
 hipError_t launch_dense_mfma(const uint16_t* x, int64_t T, int32_t K, const DenseSeg& s, hipStream_t st) {
   if (T == 0) return hipSuccess;
   if (!dense_uses_mfma(T, K) || s.rows <= 0) return hipErrorInvalidValue;
@@ -280,10 +290,18 @@ hipError_t launch_dense_mfma(const uint16_t* x, int64_t T, int32_t K, const Dens
                        (int64_t)s.rows, K, s.wnorm);
     hipLaunchKernelGGL(row_norms_kernel, dim3((unsigned)ceil_div(T, 4)), dim3(256), 0, st, x, T, K, s.xnorm);
     if (T >= 256) return launch_dm<4, 2, 2, true>(a, st);
-    return launch_dm<2, 2, 4, true>(a, st);
+    switch (small_tile(T, s.rows)) {
+      case 0: return launch_dm<2, 2, 4, true>(a, st);
+      case 1: return launch_dm<2, 1, 4, true>(a, st);
+      default: return launch_dm<1, 1, 4, true>(a, st);
+    }
   }
   if (T >= 256) return launch_dm<4, 4, 2, false>(a, st);
-  return launch_dm<2, 2, 4, false>(a, st);
+  switch (small_tile(T, s.rows)) {
+    case 0: return launch_dm<2, 2, 4, false>(a, st);
+    case 1: return launch_dm<2, 1, 4, false>(a, st);
+    default: return launch_dm<1, 1, 4, false>(a, st);
+  }
 }
 
 hipError_t launch_dense(const uint16_t* x, int64_t T, int32_t K, const DenseSeg* segs, int nseg, hipStream_t st) {
