@@ -138,20 +138,37 @@ __device__ __forceinline__ float exact_dot_wave(const uint16_t* __restrict__ x, 
   const int lane = lane_id();
   double s = 0.0, sa = 0.0;
   int nterm = 0;
-  for (int c = lane; c < d / 8; c += WAVE) {
-    uint4 xv = *reinterpret_cast<const uint4*>(x + 8 * c);
-    uint4 wv = *reinterpret_cast<const uint4*>(w + 8 * c);
-    uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w}, wsv[4] = {wv.x, wv.y, wv.z, wv.w};
+  // EXU chunks of 8 products per lane are loaded before any is used, so the row costs
+  // d / (8 WAVE EXU) memory round trips (two at d = 7168) rather than one per chunk
+  constexpr int EXU = 7;
+  const int nch = d / 8;
+  for (int c0 = lane; c0 < nch; c0 += WAVE * EXU) {
+    uint4 xv[EXU], wv[EXU];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      double p0 = (double)bf16lo(xs[q]) * (double)bf16lo(wsv[q]);
-      double p1 = (double)bf16hi(xs[q]) * (double)bf16hi(wsv[q]);
-      s += p0;
-      s += p1;
-      sa += fabs(p0);
-      sa += fabs(p1);
+    for (int u = 0; u < EXU; ++u) {
+      const int c = c0 + WAVE * u;
+      if (c < nch) {
+        xv[u] = *reinterpret_cast<const uint4*>(x + 8 * c);
+        wv[u] = *reinterpret_cast<const uint4*>(w + 8 * c);
+      } else {
+        xv[u] = wv[u] = make_uint4(0u, 0u, 0u, 0u);
+      }
     }
-    nterm += 8;
+#pragma unroll
+    for (int u = 0; u < EXU; ++u) {
+      if (c0 + WAVE * u >= nch) continue;
+      uint32_t xs[4] = {xv[u].x, xv[u].y, xv[u].z, xv[u].w}, wsv[4] = {wv[u].x, wv[u].y, wv[u].z, wv[u].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        double p0 = (double)bf16lo(xs[q]) * (double)bf16lo(wsv[q]);
+        double p1 = (double)bf16hi(xs[q]) * (double)bf16hi(wsv[q]);
+        s += p0;
+        s += p1;
+        sa += fabs(p0);
+        sa += fabs(p1);
+      }
+      nterm += 8;
+    }
   }
   s = wave_sum(s);
   sa = wave_sum(sa);
