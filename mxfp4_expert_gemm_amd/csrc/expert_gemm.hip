@@ -131,6 +131,27 @@ __device__ __forceinline__ void gt_read(AStep& a, const uint8_t* buf, int s, int
 // x * nb/8 .. (x+1) * nb/8 - 1 (nb a multiple of 8)
 __device__ __forceinline__ int gt_logical_block(int b, int nb) { return (b & 7) * (nb >> 3) + (b >> 3); }
 
+// (tile, row block) of logical block lb.  Tiles go in groups of GT_GROUP consecutive
+// tiles (the tiles of a popular expert are consecutive in the list), and within a group
+// row block by row block: the group's blocks for one row block run together on one XCD,
+// so a weight row block fetched for the first tile of an expert is served from that XCD's
+// L2 to the others, while the group's activations (GT_GROUP x 64 rows, about 1.8 MB of
+// two-term rows at K = 3584) stay in L2 across its row blocks.  Tiles past the last full
+// group go tile by tile.  A bijection of [0, ntiles x nrt).
+constexpr int GT_GROUP = 4;
+__device__ __forceinline__ void gt_tile_of(int lb, int ntiles, int nrt, int& ti, int& rt) {
+  const int full = ntiles / GT_GROUP * GT_GROUP * nrt;  // blocks in full groups
+  if (lb < full) {
+    const int g = lb / (GT_GROUP * nrt), w = lb - g * (GT_GROUP * nrt);
+    rt = w / GT_GROUP;
+    ti = g * GT_GROUP + (w - rt * GT_GROUP);
+  } else {
+    const int l2 = lb - full;
+    ti = ntiles / GT_GROUP * GT_GROUP + l2 / nrt;
+    rt = l2 - (l2 / nrt) * nrt;
+  }
+}
+
 // The K loop of one tile padded to R rows: acc[q][tt] += A(token sub-tile tt) x W_q^T over
 // all K steps.  The loop runs over whole 16-step blocks; steps past the end issue their
 // (clamped) loads, stores and barriers like the others and skip only the math, so every
@@ -219,10 +240,11 @@ __global__ void __launch_bounds__(256, 2) gateup_gemm_kernel(MxArgs p, const int
   __shared__ int sslot[GT_TOK];
   const int F = p.F, L = p.L, nrt = F / GT_ROWS;
   const int lb = gt_logical_block(blockIdx.x, nb);
-  if (lb / nrt >= ntiles) return;  // the grid is rounded up to a multiple of 8
-  const int4 tile = gtiles[lb / nrt];
+  int ti, rt;
+  gt_tile_of(lb, ntiles, nrt, ti, rt);
+  if (ti >= ntiles) return;  // the grid is rounded up to a multiple of 8
+  const int4 tile = gtiles[ti];
   if (tile.x < 0) return;
-  const int rt = lb - (lb / nrt) * nrt;
   const int e = tile.x, r0 = tile.y, n = tile.z;
   const int lane = lane_id(), wave = threadIdx.x / WAVE, g = lane >> 4, nl = lane & 15;
   for (int m = threadIdx.x; m < GT_TOK; m += blockDim.x) {
@@ -288,10 +310,11 @@ __global__ void __launch_bounds__(256, 2) down_gemm_kernel(MxArgs p, const int4*
   constexpr int ROWS = GT_ROWS * NG;
   const int F = p.F, L = p.L, nrt = L / ROWS;
   const int lb = gt_logical_block(blockIdx.x, nb);
-  if (lb / nrt >= ntiles) return;  // the grid is rounded up to a multiple of 8
-  const int4 tile = gtiles[lb / nrt];
+  int ti, rt;
+  gt_tile_of(lb, ntiles, nrt, ti, rt);
+  if (ti >= ntiles) return;  // the grid is rounded up to a multiple of 8
+  const int4 tile = gtiles[ti];
   if (tile.x < 0) return;
-  const int rt = lb - (lb / nrt) * nrt;
   const int e = tile.x, r0 = tile.y, n = tile.z;
   const int lane = lane_id(), wave = threadIdx.x / WAVE, g = lane >> 4, nl = lane & 15;
   for (int m = threadIdx.x; m < GT_TOK; m += blockDim.x) srow[m] = m < n ? p.perm[r0 + m] : 0;
