@@ -60,52 +60,90 @@ struct GtRegs {
 template <int R>
 constexpr int gt_log2() { return R == 16 ? 4 : R == 32 ? 5 : 6; }
 
-// Loads chunk c (steps CH c .. CH c + CH - 1, CH = 128 / R) of the tile's R rows: item
-// j = tid + 256 u is (step, term, row, 16-byte piece), so a wave moves whole rows of one
-// term.  Every load is issued: rows past the tile read the row srow holds for them (a
-// valid token) and steps past the end re-read the last step, so the loads in flight are
-// the same on every path (see prime_stream); what they bring for such rows and steps is
-// never used.  With one term, threads 128.. repeat the scale loads of threads 0..127
-// (and do not store them), for the same reason.
+// This thread's share of every chunk, fixed for the whole K loop.  Item j = tid + 256 u
+// of a chunk is (step, term, row, 16-byte piece); with tid < 256 its row and piece depend
+// on tid alone (row tid/8, or tid/8 + 32 for odd u at R = 64; piece tid mod 8) and its
+// step and term on u alone (plus bit tid/128 at R = 16), so the global row offsets and the
+// LDS offsets are computed once per tile rather than once per chunk.
 template <int TERMS, int R>
-__device__ __forceinline__ void gt_load(GtRegs<TERMS>& r, const QRows& q, const int64_t* srow, int K, int nks,
+struct GtThr {
+  static constexpr int NR = R == 64 ? 2 : 1;  // distinct rows of the thread's pieces
+  int64_t src[NR];   // srow[m] * K + 16 * piece
+  int32_t dst[NR];   // m * GT_RS + 16 * (piece ^ (m & 7)), plus the tid/128 part at R = 16
+  int tb;            // R = 16: tid / 128 (the term with two terms, else a step offset)
+  int64_t ssrc;      // scale dword: srow[m_s] * (K / 32)
+  int32_t sdst;      // its LDS offset
+  int ss, st;        // its step and term
+};
+
+template <int TERMS, int R>
+__device__ __forceinline__ GtThr<TERMS, R> gt_thread(const int64_t* srow, int K) {
+  constexpr int LR = gt_log2<R>(), SB = gt_step_bytes(R);
+  const int tid = threadIdx.x, part = tid & 7;
+  GtThr<TERMS, R> t;
+  t.tb = R == 16 ? tid >> 7 : 0;
+#pragma unroll
+  for (int i = 0; i < t.NR; ++i) {
+    const int m = R == 64 ? (tid >> 3) + 32 * i : (tid >> 3) & (R - 1);
+    t.src[i] = srow[m] * K + 16 * part;
+    t.dst[i] = m * GT_RS + 16 * (part ^ (m & 7));
+    if (R == 16) t.dst[i] += TERMS == 2 ? t.tb * R * GT_RS : t.tb * SB;
+  }
+  const int it = TERMS == 2 ? tid : tid & 127;  // CH x R rows x TERMS
+  const int ms = (it >> (TERMS - 1)) & (R - 1);
+  t.ss = it >> (LR + TERMS - 1);
+  t.st = TERMS == 2 ? it & 1 : 0;
+  t.ssrc = srow[ms] * (K / 32);
+  t.sdst = t.ss * SB + 2 * R * GT_RS + t.st * R * 4 + ms * 4;
+  return t;
+}
+
+// step and term of piece u (R = 16: plus the thread's tb, folded into src / dst)
+template <int TERMS, int R>
+__host__ __device__ constexpr int gt_piece_step(int u) {
+  return R == 64 ? (TERMS == 2 ? u >> 2 : u >> 1) : R == 32 ? (TERMS == 2 ? u >> 1 : u) : (TERMS == 2 ? u : 2 * u);
+}
+template <int TERMS, int R>
+__host__ __device__ constexpr int gt_piece_term(int u) {
+  return TERMS == 1 ? 0 : R == 64 ? (u >> 1) & 1 : R == 32 ? u & 1 : 0;
+}
+
+// Loads chunk c (steps CH c .. CH c + CH - 1, CH = 128 / R) of the tile's R rows.  Every
+// load is issued: rows past the tile read the row srow holds for them (a valid token)
+// and steps past the end re-read the last step, so the loads in flight are the same on
+// every path (see prime_stream); what they bring for such rows and steps is never used.
+// With one term, threads 128.. repeat the scale loads of threads 0..127 (and do not
+// store them), for the same reason.
+template <int TERMS, int R>
+__device__ __forceinline__ void gt_load(GtRegs<TERMS>& r, const QRows& q, const GtThr<TERMS, R>& t, int nks,
                                         int c) {
-  constexpr int CH = GT_CHUNK_ROWSTEPS / R, LR = gt_log2<R>();
-  const int tid = threadIdx.x;
+  constexpr int CH = 128 / R;
+  // R = 16 with two terms: the thread's term is tb; with one term, tb shifts the step
+  const uint8_t* hi16 = TERMS == 2 && R == 16 && t.tb ? q.lo : q.hi;
+  const int sofs = TERMS == 1 && R == 16 ? t.tb : 0;
   unroll_n<4 * TERMS>([&](auto uc) {
     constexpr int u = decltype(uc)::value;
-    const int j = tid + 256 * u;  // CH x TERMS x R rows x 8 pieces
-    const int rest = j >> (3 + LR);
-    const int s = TERMS == 2 ? rest >> 1 : rest, term = TERMS == 2 ? rest & 1 : 0, m = (j >> 3) & (R - 1),
-              part = j & 7;
-    const int ks = CH * c + s < nks ? CH * c + s : nks - 1;
-    r.v[u] = *reinterpret_cast<const u32x4_t*>((term ? q.lo : q.hi) + srow[m] * K + 128 * ks + 16 * part);
+    constexpr int s = gt_piece_step<TERMS, R>(u), term = gt_piece_term<TERMS, R>(u);
+    const int ks0 = CH * c + s + sofs;
+    const int ks = ks0 < nks ? ks0 : nks - 1;
+    const uint8_t* base = R == 16 ? hi16 : term ? q.lo : q.hi;
+    r.v[u] = *reinterpret_cast<const u32x4_t*>(base + t.src[R == 64 ? (u & 1) : 0] + 128 * ks);
   });
   {
-    const int it = TERMS == 2 ? tid : tid & 127;  // CH x R rows x TERMS
-    const int s = it >> (LR + TERMS - 1), m = (it >> (TERMS - 1)) & (R - 1), term = TERMS == 2 ? it & 1 : 0;
-    const int ks = CH * c + s < nks ? CH * c + s : nks - 1;
-    r.s = *reinterpret_cast<const uint32_t*>((term ? q.slo : q.shi) + srow[m] * (K / 32) + 4 * ks);
+    const int ks = CH * c + t.ss < nks ? CH * c + t.ss : nks - 1;
+    r.s = *reinterpret_cast<const uint32_t*>((t.st ? q.slo : q.shi) + t.ssrc + 4 * ks);
   }
 }
 
 template <int TERMS, int R>
-__device__ __forceinline__ void gt_store(const GtRegs<TERMS>& r, uint8_t* buf) {
-  constexpr int LR = gt_log2<R>(), SB = gt_step_bytes(R);
-  const int tid = threadIdx.x;
+__device__ __forceinline__ void gt_store(const GtRegs<TERMS>& r, const GtThr<TERMS, R>& t, uint8_t* buf) {
+  constexpr int SB = gt_step_bytes(R);
   unroll_n<4 * TERMS>([&](auto uc) {
     constexpr int u = decltype(uc)::value;
-    const int j = tid + 256 * u;
-    const int rest = j >> (3 + LR);
-    const int s = TERMS == 2 ? rest >> 1 : rest, term = TERMS == 2 ? rest & 1 : 0, m = (j >> 3) & (R - 1),
-              part = j & 7;
-    *reinterpret_cast<u32x4_t*>(buf + s * SB + term * R * GT_RS + m * GT_RS + 16 * (part ^ (m & 7))) = r.v[u];
+    constexpr int s = gt_piece_step<TERMS, R>(u), term = gt_piece_term<TERMS, R>(u);
+    *reinterpret_cast<u32x4_t*>(buf + s * SB + term * R * GT_RS + t.dst[R == 64 ? (u & 1) : 0]) = r.v[u];
   });
-  if (TERMS == 2 || tid < 128) {
-    const int it = tid;
-    const int s = it >> (LR + TERMS - 1), m = (it >> (TERMS - 1)) & (R - 1), term = TERMS == 2 ? it & 1 : 0;
-    *reinterpret_cast<uint32_t*>(buf + s * SB + 2 * R * GT_RS + term * R * 4 + m * 4) = r.s;
-  }
+  if (TERMS == 2 || threadIdx.x < 128) *reinterpret_cast<uint32_t*>(buf + t.sdst) = r.s;
 }
 
 // activation operand of step s of a chunk for tile row m (chunks g and 4 + g of the row)
@@ -165,13 +203,14 @@ __device__ __forceinline__ void gt_mainloop(const W (&w)[NMAT], const QRows& q, 
   const int nks = K / 128, nc = (nks + 15) / 16;
   const int ntt = (n + 15) / 16;  // token sub-tiles holding rows
   // chunk 0 into buffer 0, chunk 1 into registers, the first weight steps in flight
+  const GtThr<TERMS, R> thr = gt_thread<TERMS, R>(srow, K);
   GtRegs<TERMS> rg;
-  gt_load<TERMS, R>(rg, q, srow, K, nks, 0);
+  gt_load<TERMS, R>(rg, q, thr, nks, 0);
   SBlock sb[NMAT], sbn[NMAT];
   uint4 ring[NMAT][GT_PF];
   prime_stream<W, NMAT, GT_PF>(w, sb, ring, nks);
-  gt_store<TERMS, R>(rg, lds);
-  gt_load<TERMS, R>(rg, q, srow, K, nks, 1);
+  gt_store<TERMS, R>(rg, thr, lds);
+  gt_load<TERMS, R>(rg, q, thr, nks, 1);
   lds_barrier();
   for (int cb = 0; cb < nc; ++cb) {
 #pragma unroll
@@ -205,8 +244,8 @@ __device__ __forceinline__ void gt_mainloop(const W (&w)[NMAT], const QRows& q, 
       if constexpr (J % CH == CH - 1) {
         // end of chunk ch: the registers hold chunk ch+1; every wave is past chunk ch-1,
         // so its buffer is free
-        gt_store<TERMS, R>(rg, lds + ((ch + 1) & 1) * GT_BUF_BYTES);
-        gt_load<TERMS, R>(rg, q, srow, K, nks, ch + 2);
+        gt_store<TERMS, R>(rg, thr, lds + ((ch + 1) & 1) * GT_BUF_BYTES);
+        gt_load<TERMS, R>(rg, q, thr, nks, ch + 2);
         lds_barrier();
       }
     });
