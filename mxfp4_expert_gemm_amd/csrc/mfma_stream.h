@@ -176,14 +176,15 @@ __device__ __forceinline__ void read_a(AStep& a, const ALds& d, int m, int ntok,
   }
 }
 
-// a = bf16(silu(g) u) for the fp32 values g and u; the activation and the product are
-// evaluated in fp64 (the GLU is specified in fp32 or better), g e^g / (1 + e^g) for
-// g < 0 so a large |g| cannot overflow
+// a = bf16(silu(g) u) for the fp32 values g and u, evaluated in fp32 as the GLU is
+// specified (accurate expf, IEEE division, one rounding per operation), g e^g / (1 + e^g)
+// for g < 0 so a large |g| cannot overflow.  Against the exact value the fp32 result is
+// off by a few fp32 ulps, so its bf16 rounding differs from the correctly rounded one only
+// for values within that distance of a bf16 rounding boundary (about 1 in 10^4).
 __device__ __forceinline__ uint16_t glu_bf16(float g, float u) {
-  const double gd = (double)g;
-  const double e = exp(-fabs(gd));  // one exponential on either side
-  const double s = gd >= 0.0 ? gd / (1.0 + e) : gd * e / (1.0 + e);
-  return f64_to_bf16(s * (double)u);
+  const float e = expf(-fabsf(g));  // one exponential on either side
+  const float s = g >= 0.f ? g / (1.f + e) : (g * e) / (1.f + e);
+  return f32_to_bf16(s * u);
 }
 
 }  // namespace moe
