@@ -235,6 +235,39 @@ def test_expert_ffn_grouped_gemm_matches_streaming_kernels():
             assert rel_l2(ya[t * c.k + j], wy) < 1e-3
 
 
+@pytest.mark.parametrize("name,idx_rows", [
+    ("tiny", [[5, 5], [5, 1], [5, 5]]),       # expert 5 takes 5 rows, 3 of one token: two passes
+    ("decode1", [[7] * 16]),                  # one token, one expert in all 16 slots: four passes
+])
+def test_expert_ffn_repeated_experts(name, idx_rows):
+    """A caller may give an expert several slots of one token (the router never does): every
+    slot is still its own row, with the same bits as that (token, expert) pair computed
+    alone, and within the oracle's tolerance."""
+    h = host_layer(name, len(idx_rows))
+    c = h["cfg"]
+    dw = dev_weights(name)
+    hl = oracle.linear_bf16(h["x"], h["latent_down"])
+    idx = np.array(idx_rows, dtype=np.int32)
+    T, k = idx.shape
+    y, a = moe.expert_ffn(to_dev(hl), dw["blob"], to_dev(idx), d_model=c.d, d_ffn=c.F, num_experts=c.E,
+                          want_a=True)
+    y, a = from_dev(y), from_dev(a)
+    rec = c.record_bytes
+    for t in range(T):
+        for j in range(k):
+            e = int(idx[t, j])
+            # the pair alone: token t with e in slot 0 and distinct other experts
+            others = [x for x in range(c.E) if x != e][:k - 1]
+            one = np.array([[e] + others], dtype=np.int32)
+            y1, a1 = moe.expert_ffn(to_dev(hl[t:t + 1]), dw["blob"], to_dev(one), d_model=c.d, d_ffn=c.F,
+                                    num_experts=c.E, want_a=True)
+            r = t * k + j
+            assert np.array_equal(y[r], from_dev(y1)[0]) and np.array_equal(a[r], from_dev(a1)[0]), (t, j)
+            if j == 0 or idx[t, j] != idx[t, 0]:
+                _, wy = oracle.expert(hl[t], h["blob"][e * rec:(e + 1) * rec], c.L, c.F)
+                assert rel_l2(y[r], wy) < 1e-3
+
+
 def test_combine():
     rng = np.random.default_rng(1)
     T, k, L = 33, 16, 3584
