@@ -279,7 +279,9 @@ moe_status moe_permute(const int32_t* topk_idx, int64_t num_tokens, int32_t k, i
 /* Routed experts on latent rows: h bf16 [T][L] -> y fp32 [T*k][L] with row
  * t*k+j the output of expert topk_idx[t][j] on h[t]; a_out (nullable) bf16
  * [T*k][F] receives the GLU output in the same row order.  routing must hold
- * topk_idx, expert_counts, expert_offsets and perm (from moe_permute). */
+ * topk_idx, expert_counts, expert_offsets and perm (from moe_permute).  An id may
+ * repeat within a token (each slot is its own row); ids outside [0, E) are skipped:
+ * their rows of y and a_out are left as they were. */
 moe_status moe_expert_ffn(const void* h, const uint8_t* expert_blob, int32_t k, const moe_config* cfg,
                           const moe_routing_out* routing, float* y, void* a_out, void* workspace,
                           size_t workspace_bytes, moe_stream_t stream);

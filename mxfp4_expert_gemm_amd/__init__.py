@@ -307,13 +307,21 @@ def permute(idx: torch.Tensor, num_experts: int):
 
 def expert_ffn(h: torch.Tensor, expert_blob: torch.Tensor, idx: torch.Tensor, *, d_model: int, d_ffn: int,
                num_experts: int, want_a: bool = False, workspace=None, packed: bool = False,
-               act_format: int = ACT_FMT_BF16):
-    """Routed experts on latent rows h [T, L]: returns y fp32 [T*k, L] (and a bf16 [T*k, F])."""
+               act_format: int = ACT_FMT_BF16, y: Optional[torch.Tensor] = None, a: Optional[torch.Tensor] = None):
+    """Routed experts on latent rows h [T, L]: returns y fp32 [T*k, L] (and a bf16 [T*k, F]),
+    into the given y and a when passed."""
     T, L = h.shape
     k = idx.shape[1]
     cfg = make_config(T, d_model, L, d_ffn, num_experts, packed=packed, act_format=act_format)
-    y = torch.empty((T * k, L), dtype=torch.float32, device=h.device)
-    a = torch.empty((T * k, d_ffn), dtype=h.dtype, device=h.device) if want_a else None
+    if y is None:
+        y = torch.empty((T * k, L), dtype=torch.float32, device=h.device)
+    if a is None and want_a:
+        a = torch.empty((T * k, d_ffn), dtype=h.dtype, device=h.device)
+    want_a = a is not None
+    if tuple(y.shape) != (T * k, L) or y.dtype != torch.float32 or not y.is_contiguous():
+        raise ValueError(f"y must be a contiguous float32 [{T * k}, {L}] tensor")
+    if want_a and (tuple(a.shape) != (T * k, d_ffn) or a.element_size() != 2 or not a.is_contiguous()):
+        raise ValueError(f"a must be a contiguous 2-byte [{T * k}, {d_ffn}] tensor")
     if workspace is None:
         workspace = alloc_workspace(cfg, k, h.device)
     r = RoutingOut(idx.data_ptr(), None, None, None, None, None)

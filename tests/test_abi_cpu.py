@@ -180,3 +180,18 @@ def test_streamed_forward_slots_and_errors_before_any_launch():
     shared = k3(T=1)
     shared.num_shared, shared.d_ffn_shared = 2, 3072
     assert sfwd(shared) == -2
+
+
+def test_expert_ffn_binding_rejects_wrong_output_buffers():
+    # the shapes of caller-given outputs are checked before anything reaches the library
+    import torch
+    h = torch.zeros((3, 128), dtype=torch.int16)
+    idx = torch.zeros((3, 2), dtype=torch.int32)
+    kw = dict(d_model=256, d_ffn=128, num_experts=8)
+    with pytest.raises(ValueError):
+        moe.expert_ffn(h, h, idx, y=torch.zeros((5, 128), dtype=torch.float32), **kw)
+    with pytest.raises(ValueError):
+        moe.expert_ffn(h, h, idx, y=torch.zeros((6, 128), dtype=torch.float64), **kw)
+    with pytest.raises(ValueError):
+        moe.expert_ffn(h, h, idx, y=torch.zeros((6, 128), dtype=torch.float32),
+                       a=torch.zeros((6, 64), dtype=torch.int16), **kw)

@@ -268,6 +268,32 @@ def test_expert_ffn_repeated_experts(name, idx_rows):
                 assert rel_l2(y[r], wy) < 1e-3
 
 
+def test_expert_ffn_skips_ids_out_of_range():
+    """Slots whose expert id lies outside [0, E) are skipped: their rows of y and a keep
+    what the caller's buffers held; every other slot is its pair computed alone."""
+    name = "tiny"
+    idx = np.array([[2, -1], [8, 3], [1, 100]], dtype=np.int32)
+    h = host_layer(name, idx.shape[0])
+    c = h["cfg"]
+    dw = dev_weights(name)
+    hl = oracle.linear_bf16(h["x"], h["latent_down"])
+    T, k = idx.shape
+    y = torch.full((T * k, c.L), float("nan"), dtype=torch.float32, device="cuda")
+    a = torch.full((T * k, c.F), 0x7E5A, dtype=torch.int16, device="cuda")
+    moe.expert_ffn(to_dev(hl), dw["blob"], to_dev(idx), d_model=c.d, d_ffn=c.F, num_experts=c.E, y=y, a=a)
+    y, a = from_dev(y), from_dev(a)
+    for t in range(T):
+        for j in range(k):
+            e, r = int(idx[t, j]), t * k + j
+            if not 0 <= e < c.E:
+                assert np.isnan(y[r]).all() and (a[r] == 0x7E5A).all(), (t, j)
+                continue
+            one = np.array([[e] + [x for x in range(c.E) if x != e][:k - 1]], dtype=np.int32)
+            y1, a1 = moe.expert_ffn(to_dev(hl[t:t + 1]), dw["blob"], to_dev(one), d_model=c.d, d_ffn=c.F,
+                                    num_experts=c.E, want_a=True)
+            assert np.array_equal(y[r], from_dev(y1)[0]) and np.array_equal(a[r], from_dev(a1)[0]), (t, j)
+
+
 def test_combine():
     rng = np.random.default_rng(1)
     T, k, L = 33, 16, 3584
