@@ -300,8 +300,10 @@ moe_status moe_combine(const float* y, const float* topk_w, int64_t num_tokens, 
  * saliency: fp64 [num_experts] on the device, accumulated across calls (the caller
  * zeroes it, and divides by the number of calibration tokens at the end).  All device
  * pointers.  An expert pruned after scoring is a router bias of -inf on it in
- * moe_layer_forward / moe_route: it is never selected and the weights are renormalised
- * over the experts left (at least k must remain). */
+ * moe_layer_forward / moe_route: it is never selected while k or more experts remain and
+ * the weights are renormalised over the experts left.  With fewer than k left, every
+ * survivor is selected and the other slots take the lowest-numbered pruned experts at
+ * weight 0 (ties at -inf go to the lower index); that routing takes the exact path. */
 moe_status moe_reap_saliency(const float* y, const float* topk_w, const int32_t* perm,
                              const int32_t* expert_offsets, int64_t num_tokens, int32_t k,
                              int32_t d_latent, int32_t num_experts, double* saliency,

@@ -63,3 +63,36 @@ def test_pruned_layer_routes_exactly(name, T, n_keep):
     err = rel_l2(bf16_bits_to_f64(from_dev(out)[tokens]), bf16_bits_to_f64(ref["out"]))
     log(f"  {name} keep {n_keep}: rel-L2 {err:.3g}")
     assert err <= 2e-3
+
+
+@pytest.mark.parametrize("name,T,n_keep", [("tiny", 5, 1), ("decode1", None, 10)])
+def test_pruned_below_k_fills_with_zero_weight_experts(name, T, n_keep):
+    """Fewer survivors than k: every survivor is selected, the remaining slots take the
+    lowest-numbered pruned experts (ties at -inf go to the lower index) at weight 0, as
+    the oracle selects, and the layer output is the survivors' mixture."""
+    h = host_layer(name, T)
+    c = h["cfg"]
+    dw = dev_weights(name)
+    rng = np.random.default_rng(c.E * 7 + n_keep)
+    keep = np.sort(rng.choice(c.E, n_keep, replace=False))
+    bias = np.full(c.E, -np.inf, dtype=np.float32)
+    bias[keep] = 0.0
+    Tn = h["x"].shape[0]
+    idx = torch.empty((Tn, c.k), dtype=torch.int32, device="cuda")
+    wts = torch.empty((Tn, c.k), dtype=torch.float32, device="cuda")
+    out = moe.layer_forward(to_dev(h["x"]), dw["router_w"], dw["latent_down"], dw["latent_up"], dev_packed(name),
+                            c.k, d_ffn=c.F, bias=to_dev(bias), routing={"topk_idx": idx, "topk_w": wts},
+                            packed=True)
+    gi, gw = from_dev(idx), from_dev(wts)
+    lg = oracle.router_logits(h["x"], h["router_w"], bias)
+    want_idx, want_w = oracle.select(lg, c.k)
+    assert np.array_equal(gi, want_idx)
+    pruned = ~np.isin(gi, keep)
+    assert pruned.sum() == Tn * (c.k - n_keep) and (gw[pruned] == 0).all()
+    assert np.allclose(gw, want_w, rtol=1e-4, atol=1e-6)
+    tokens = [0] if Tn == 1 else [0, Tn - 1]
+    ref = oracle.layer_forward(h["x"], h["router_w"], h["latent_down"], h["latent_up"], h["blob"], c.k, c.L, c.F,
+                               bias=bias, tokens=tokens)
+    err = rel_l2(bf16_bits_to_f64(from_dev(out)[tokens]), bf16_bits_to_f64(ref["out"]))
+    log(f"  {name} keep {n_keep} < k: rel-L2 {err:.3g}")
+    assert err <= 2e-3

@@ -82,3 +82,17 @@ def test_prune_bias_keeps_the_most_salient_and_random_sets_overlap_27pct():
           for _ in range(400)]
     assert abs(np.mean(ov) - 242 / 896) < 0.01
     assert round(242 / 896, 2) == 0.27 and round(179 / 896, 2) == 0.20
+
+
+def test_fewer_survivors_than_k_fill_with_zero_weights():
+    """Pruned below k (outside the documented precondition): the selection still holds k
+    distinct experts, the survivors plus the lowest-index pruned ones (ties at -inf go to
+    the lower index), the pruned ones at weight 0 and the survivors' weights their softmax."""
+    E, k = 8, 4
+    lg = np.full((1, E), -np.inf, dtype=np.float32)
+    lg[0, 5], lg[0, 6] = 1.0, 3.0
+    idx, w = oracle.select(lg, k)
+    assert idx[0].tolist() == [0, 1, 5, 6]
+    e = np.exp(np.array([1.0 - 3.0, 0.0]))
+    assert w[0, 0] == 0.0 and w[0, 1] == 0.0
+    assert np.allclose(w[0, 2:], e / e.sum(), rtol=1e-6, atol=0)
