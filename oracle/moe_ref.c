@@ -198,16 +198,48 @@ float moe_ref_dot_bf16_exact(const uint16_t* a, const uint16_t* b, int64_t n) {
   return k_round(&K);
 }
 
+/*
+ * The same correctly rounded value, found faster when an fp64 sum decides it.
+ * Every product of two bf16 numbers is exact in fp64 (at most 16 significant
+ * bits, exponents within [-266, 256]).  Summed left to right in fp64, the
+ * computed s differs from the exact sum by at most (n-1)u * sum|p_i|, u = 2^-53
+ * (the textbook bound for recursive summation); B below is more than twice that,
+ * which also covers the rounding of S and of s -+ B.  Rounding to fp32 is
+ * monotone, so when s - B and s + B round to the same fp32 bit pattern the exact
+ * sum, which lies between them, rounds to it too.  Otherwise (an fp32 rounding
+ * boundary within B of s, a sign of zero undecided, or a non-finite input) the
+ * fixed-point accumulator above decides.
+ */
+static float router_dot(const uint16_t* a, const uint16_t* b, int64_t n) {
+  double s = 0.0, S = 0.0;
+  for (int64_t i = 0; i < n; ++i) {
+    double p = bf16_to_f64(a[i]) * bf16_to_f64(b[i]);
+    s += p;
+    S += fabs(p);
+  }
+  if (isfinite(s) && isfinite(S)) {
+    if (S == 0.0) return 0.0f;  /* every product is zero: the exact sum is +0 */
+    double B = (double)(n + 4) * ldexp(S, -52);
+    float lo = (float)(s - B), hi = (float)(s + B);
+    uint32_t ulo, uhi;
+    memcpy(&ulo, &lo, 4);
+    memcpy(&uhi, &hi, 4);
+    if (ulo == uhi) return lo;
+  }
+  return moe_ref_dot_bf16_exact(a, b, n);
+}
+
 /* ----------------------------------------------------------------- router */
 
 /* kimi-k3-mlx digest, architecture table (896 routed experts, router picks 16
- * per token); the router reads the 7168-wide token.  Bias is optional. */
+ * per token); the router reads the 7168-wide token.  Bias is optional.  Each
+ * logit is the correctly rounded fp32 of the exact dot product (router_dot). */
 int moe_ref_router_logits(const uint16_t* x, const uint16_t* router_w, const float* bias,
                           int64_t bias_stride, int64_t T, int32_t d, int32_t E, float* logits) {
   if (!x || !router_w || !logits || T < 0 || d <= 0 || E <= 0) return MOE_REF_ERR_ARG;
   for (int64_t t = 0; t < T; ++t)
     for (int32_t e = 0; e < E; ++e) {
-      float l = moe_ref_dot_bf16_exact(x + t * d, router_w + (int64_t)e * d, d);
+      float l = router_dot(x + t * d, router_w + (int64_t)e * d, d);
       if (bias) {
         volatile float s = l + bias[t * bias_stride + e]; /* one fp32 rounding */
         l = s;

@@ -85,7 +85,9 @@ uint16_t moe_ref_bf16_from_f64(double v);
 /* correctly rounded fp32 of the exact sum of a[i]*b[i] over bf16 vectors */
 float moe_ref_dot_bf16_exact(const uint16_t* a, const uint16_t* b, int64_t n);
 
-/* logits[t][e] = RN32(exact x_t . W_r[e]) (+ bias[t*bias_stride + e], one fp32 add) */
+/* logits[t][e] = RN32(exact x_t . W_r[e]) (+ bias[t*bias_stride + e], one fp32 add).
+ * Each logit equals moe_ref_dot_bf16_exact of the pair: an fp64 sum with a proven
+ * error bound settles the rounding when it can, the exact accumulator otherwise. */
 int moe_ref_router_logits(const uint16_t* x, const uint16_t* router_w, const float* bias,
                           int64_t bias_stride, int64_t T, int32_t d, int32_t E, float* logits);
 

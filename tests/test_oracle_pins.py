@@ -208,6 +208,80 @@ def test_exact_dot_ties_and_sticky_bits():
     assert math.isnan(oracle.dot_bf16_exact(np.array([inf, inf], np.uint16), np.array([one, 0xBF80], np.uint16)))
 
 
+def _router_one(a, b):
+    """The oracle's router logit of one token against one router row."""
+    return float(oracle.router_logits(np.ascontiguousarray(a, np.uint16)[None, :],
+                                      np.ascontiguousarray(b, np.uint16)[None, :])[0, 0])
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_router_logit_vs_fractions_wide_exponents(case):
+    """The router's logit (fp64 sum with an error bound, exact accumulator when the bound
+    cannot decide) is the correctly rounded exact dot, across the whole bf16 range."""
+    rng = np.random.default_rng(200 + case)
+    n = [1, 7, 64, 200, 33, 128][case]
+    lo, hi = [(1, 254), (100, 160), (0, 254), (110, 140), (1, 20), (235, 254)][case]
+    for _ in range(20):
+        a = _rand_bf16(rng, n, lo, hi)
+        b = _rand_bf16(rng, n, lo, hi)
+        want = fraction_to_f32(_exact_dot_frac(a, b))
+        assert _router_one(a, b) == want
+
+
+def test_router_logit_decided_exactly_near_rounding_boundaries():
+    """Sums within a few fp64 ulps of an fp32 rounding midpoint, where a plain fp64 sum
+    rounded to fp32 gives the wrong value: the bound must send them to the exact path."""
+    one, tiny, far, nfar = _bf(1.0), _bf(2.0 ** -12), _bf(2.0 ** -60), _bf(-(2.0 ** -60))
+    # 1 + 2^-24 + 2^-120: fp64 keeps 1 + 2^-24, a tie that rounds to 1; exactly it rounds up
+    assert _router_one([one, tiny, far], [one, tiny, far]) == 1.0 + 2.0 ** -23
+    assert _router_one([one, tiny, nfar], [one, tiny, far]) == 1.0
+    assert _router_one([one, tiny], [one, tiny]) == 1.0
+    # exact cancellation: +0, and a tiny survivor
+    z = _router_one([_bf(2.0), _bf(-2.0)], [_bf(1.0), _bf(1.0)])
+    assert z == 0.0 and math.copysign(1.0, z) == 1.0
+    assert _router_one([_bf(3.0), _bf(-3.0), _bf(2.0 ** -70)], [_bf(2.0 ** 60), _bf(2.0 ** 60), _bf(2.0 ** -70)]) \
+        == 2.0 ** -140
+    # a negative sum just below zero rounds to -0 in fp32; just above, to +0
+    s = _router_one([_bf(2.0 ** -80)], [_bf(-(2.0 ** -80))])
+    assert s == 0.0 and math.copysign(1.0, s) == -1.0
+    # all products zero (signed zeros included): +0
+    s = _router_one([0x8000, 0x0000], [0x3F80, 0xBF80])
+    assert s == 0.0 and math.copysign(1.0, s) == 1.0
+    # specials go to the exact path's IEEE rules
+    inf, nan = 0x7F80, 0x7FC0
+    assert _router_one([inf, one], [one, one]) == math.inf
+    assert math.isnan(_router_one([inf], [0]))
+    assert math.isnan(_router_one([nan], [one]))
+    assert _router_one([_bf(2.0 ** 127), _bf(2.0 ** 127)], [_bf(2.0), _bf(2.0)]) == math.inf
+    # random sums planted on fp32 midpoints, then nudged by one product far below
+    rng = np.random.default_rng(7)
+    for _ in range(200):
+        m = int(rng.integers(1 << 7, 1 << 8))
+        e = int(rng.integers(-20, 20))
+        # m * 2^e * (1 + 2^-8 + ...) : choose a, b so that the exact sum is v + half an fp32 ulp of v
+        v = Fraction(m) * Fraction(2) ** e
+        vf = float(v)
+        ulp_half = Fraction(2) ** (math.frexp(vf)[1] - 25)
+        hb = fraction_to_f32(ulp_half)
+        nudge = int(rng.integers(-1, 2))
+        a = [_bf(vf), _bf(hb), _bf(2.0 ** -70) if nudge else 0]
+        b = [one, one, _bf(float(nudge) * 2.0 ** -60) if nudge else 0]
+        want = fraction_to_f32(_exact_dot_frac(np.array(a, np.uint16), np.array(b, np.uint16)))
+        assert _router_one(a, b) == want
+
+
+def test_router_logits_equal_exact_dot_k3_router():
+    """Every logit of two K3-shaped tokens against the whole 896 x 7168 router equals the
+    exact accumulator's value bit for bit."""
+    c = synth.CONFIGS["decode1"]
+    x = synth.make_tokens(c, T=2)
+    W = synth.make_dense(c)["router_w"]
+    got = oracle.router_logits(x, W)
+    for t in range(2):
+        for e in range(c.E):
+            assert got[t, e] == oracle.dot_bf16_exact(x[t], W[e]), (t, e)
+
+
 def test_router_bias_is_one_fp32_add():
     c = synth.CONFIGS["tiny"]
     x = synth.make_tokens(c)
