@@ -48,16 +48,19 @@ float moe_ref_mxfp4_value(int32_t code, int32_t scale) {
 
 /* Low-nibble-first (kimi-k3-mlx digest, quantisation tiers): element 2j of a
  * row is the low nibble of byte j, element 2j+1 the high nibble.  The scale of
- * element c of row r is scales[r][c/32].  One row is dequantised at a time; the
- * block's 2^(s-127) is formed once and applied as an fp32 multiply, which is
- * exact (or overflows to inf) exactly as moe_ref_mxfp4_value. */
-static void mx_row(const uint8_t* codes, const uint8_t* scales, int64_t cols, int64_t r, float* out) {
-  float lut[16];
-  for (int c = 0; c < 16; ++c) lut[c] = moe_ref_e2m1(c);
+ * element c of row r is scales[r][c/32].  One row is dequantised at a time, to
+ * the weights' exact values: E2M1 * 2^(s-127) in fp64 (at most two significant
+ * bits, exponents from -128 to 129, so never rounded; NaN for s = 255).  The
+ * expert products use these values; dequantisation to fp32 rounds them once,
+ * which changes nothing except the weights of magnitude 2^128 and above (scales
+ * 253 and 254 with large codes), which become +-inf as in moe_ref_mxfp4_value. */
+static void mx_row(const uint8_t* codes, const uint8_t* scales, int64_t cols, int64_t r, double* out) {
+  double lut[16];
+  for (int c = 0; c < 16; ++c) lut[c] = (double)moe_ref_e2m1(c);
   const uint8_t* cr = codes + r * (cols / 2);
   const uint8_t* sr = scales + r * (cols / 32);
   for (int64_t b = 0; b < cols / 32; ++b) {
-    float sc = sr[b] == 255 ? nanf("") : ldexpf(1.0f, (int)sr[b] - 127);
+    double sc = sr[b] == 255 ? (double)nanf("") : ldexp(1.0, (int)sr[b] - 127);
     for (int64_t i = 0; i < 32; ++i) {
       int64_t c = b * 32 + i;
       uint8_t byte = cr[c / 2];
@@ -70,7 +73,13 @@ static void mx_row(const uint8_t* codes, const uint8_t* scales, int64_t cols, in
 int moe_ref_dequant_matrix(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
                            float* out) {
   if (!codes || !scales || !out || rows < 0 || cols <= 0 || cols % 32) return MOE_REF_ERR_ARG;
-  for (int64_t r = 0; r < rows; ++r) mx_row(codes, scales, cols, r, out + r * cols);
+  double* row = (double*)malloc(sizeof(double) * (size_t)cols);
+  if (!row) return MOE_REF_ERR_ARG;
+  for (int64_t r = 0; r < rows; ++r) {
+    mx_row(codes, scales, cols, r, row);
+    for (int64_t c = 0; c < cols; ++c) out[r * cols + c] = (float)row[c]; /* exact, or +-inf past fp32 */
+  }
+  free(row);
   return MOE_REF_OK;
 }
 
@@ -427,8 +436,8 @@ int moe_ref_expert_fmt(const uint16_t* h, const uint8_t* record, int32_t L, int3
   const uint8_t* down = record + 2 * mat;
   const int32_t wmax = L > F ? L : F;
   uint16_t* a = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)F);
-  float* wg = (float*)malloc(sizeof(float) * (size_t)wmax);
-  float* wu = (float*)malloc(sizeof(float) * (size_t)wmax);
+  double* wg = (double*)malloc(sizeof(double) * (size_t)wmax);
+  double* wu = (double*)malloc(sizeof(double) * (size_t)wmax);
   double* hv = (double*)malloc(sizeof(double) * (size_t)wmax);  /* the GEMM inputs as used */
   double* tmp = (double*)malloc(sizeof(double) * (size_t)wmax);
   if (!a || !wg || !wu || !hv || !tmp) { free(a); free(wg); free(wu); free(hv); free(tmp); return MOE_REF_ERR_ARG; }
@@ -443,8 +452,8 @@ int moe_ref_expert_fmt(const uint16_t* h, const uint8_t* record, int32_t L, int3
     mx_row(up, up + ncode, L, f, wu);
     double sg = 0.0, su = 0.0;
     for (int32_t l = 0; l < L; ++l) {
-      sg += hv[l] * (double)wg[l];
-      su += hv[l] * (double)wu[l];
+      sg += hv[l] * wg[l];
+      su += hv[l] * wu[l];
     }
     float g = (float)sg, u = (float)su;
     a[f] = moe_ref_bf16_from_f64(moe_ref_silu((double)g) * (double)u);
@@ -458,7 +467,7 @@ int moe_ref_expert_fmt(const uint16_t* h, const uint8_t* record, int32_t L, int3
   for (int32_t l = 0; l < L; ++l) {
     mx_row(down, down + ncode, F, l, wg);
     double s = 0.0;
-    for (int32_t f = 0; f < F; ++f) s += hv[f] * (double)wg[f];
+    for (int32_t f = 0; f < F; ++f) s += hv[f] * wg[f];
     y[l] = (float)s;
   }
   if (a_out) memcpy(a_out, a, sizeof(uint16_t) * (size_t)F);

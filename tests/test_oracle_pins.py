@@ -432,6 +432,82 @@ def _np_glu_expert(h_bits, record, L, F):
     return a, y
 
 
+def _np_dequant_exact(codes, scales, rows, cols):
+    """The weights' exact values in fp64 from the golden table: E2M1 * 2^(s-127), NaN for s = 255."""
+    lut = e2m1_table()
+    c = codes.reshape(rows, cols // 2)
+    nib = np.empty((rows, cols), dtype=np.int64)
+    nib[:, 0::2] = c & 15
+    nib[:, 1::2] = c >> 4
+    s = np.repeat(scales.reshape(rows, cols // 32).astype(np.int64), 32, axis=1)
+    w = np.ldexp(lut[nib], s - 127)
+    w[s == 255] = np.nan
+    return w
+
+
+def _np_glu_expert_exact(h_bits, record, L, F):
+    (gc, gs), (uc, us), (dc, ds) = split_record(record, L, F)
+    h = bf16_bits_to_f64(h_bits)
+    with np.errstate(all="ignore"):
+        g = (_np_dequant_exact(gc, gs, F, L) @ h).astype(np.float32).astype(np.float64)
+        u = (_np_dequant_exact(uc, us, F, L) @ h).astype(np.float32).astype(np.float64)
+        a = f64_to_bf16_bits(g / (1.0 + np.exp(-g)) * u)
+        y = (_np_dequant_exact(dc, ds, L, F) @ bf16_bits_to_f64(a)).astype(np.float32)
+    return a, y
+
+
+def _same_bits_or_nan(a, b):
+    a, b = np.asarray(a), np.asarray(b)
+    fa = a.astype(np.float64) if a.dtype != np.uint16 else bf16_bits_to_f64(a)
+    fb = b.astype(np.float64) if b.dtype != np.uint16 else bf16_bits_to_f64(b)
+    return bool(((fa == fb) & (np.signbit(fa) == np.signbit(fb)) | (np.isnan(fa) & np.isnan(fb))).all())
+
+
+def test_expert_extreme_scales_use_exact_weight_values():
+    """Records with e8m0 scales at both ends of the range (0 = 2^-127, 1-20, 235-254) and
+    NaN blocks (255): the oracle's expert equals an fp64 numpy GLU on the weights' exact
+    values, NaN included.  With h tiny enough, scales 253-254 give finite products although
+    their large weights lie past the fp32 range (no fp32 rounding of weights happens)."""
+    L, F = 64, 96
+    nc, ns = F * L // 2, F * L // 32
+    mat = nc + ns
+    cases = [  # (gate/up scale range, down scale range, h exponent, 255 blocks in (matrix, block index))
+        ((0, 0), (120, 130), 100, []),
+        ((1, 20), (1, 20), 100, []),
+        ((235, 254), (120, 130), -100, []),
+        ((60, 80), (235, 254), 0, []),
+        ((120, 130), (120, 130), 0, [(0, 5)]),
+        ((120, 130), (120, 130), 0, [(2, 7)]),
+        ((0, 254), (0, 254), 0, []),
+    ]
+    rng = np.random.default_rng(31)
+    saw_big = False
+    for n, (gu, dn, hexp, nan_blocks) in enumerate(cases):
+        rec = synth.expert_blob(500 + n, L, F, 1).copy()
+        for m, (lo, hi) in enumerate((gu, gu, dn)):
+            rec[m * mat + nc:(m + 1) * mat] = rng.integers(lo, hi + 1, ns)
+        for m, b in nan_blocks:
+            rec[m * mat + nc + b] = 255
+        h = f64_to_bf16_bits(rng.standard_normal(L) * 2.0 ** hexp)
+        a_o, y_o = oracle.expert(h, rec, L, F)
+        a_n, y_n = _np_glu_expert_exact(h, rec, L, F)
+        assert _same_bits_or_nan(a_o, a_n), n
+        assert _same_bits_or_nan(y_o, y_n), n
+        if gu[1] == 254 and hexp < 0:
+            saw_big = True
+            assert np.isfinite(y_o).all() and np.isfinite(bf16_bits_to_f64(a_o)).all()
+            # the fp32-rounded weights would have been infinite
+            assert np.isinf(np_dequant(*split_record(rec, L, F)[0], F, L)).any()
+        if nan_blocks:
+            m, b = nan_blocks[0]
+            if m == 0:  # a gate row holding NaN makes that a NaN and so every y NaN
+                assert np.isnan(y_o).all()
+            else:       # a down row holding NaN makes that y NaN only
+                row = b // (F // 32)
+                assert np.isnan(y_o[row]) and np.isfinite(np.delete(y_o, row)).all()
+    assert saw_big
+
+
 def _tiny_layer(E, seed=21, d=64, L=64, F=96, T=6):
     rng_seed = seed
     x = synth.normal_bf16(rng_seed, 1, 1.0, (T, d))
