@@ -191,11 +191,30 @@ typedef enum {
 /* A hipEvent_t (HIP declares it as struct ihipEvent_t*). */
 typedef struct ihipEvent_t* moe_event_t;
 
-/* Caller-created events recorded on the stream right before (begin) and right
- * after (end) the kernels of each stage; NULL entries are skipped. */
+/* Timing of the stages (every entry may be NULL; NULL entries are skipped):
+ *  begin/end: caller-created events recorded on the stream right before and right after
+ *    the kernels of each stage (hipEventRecord), so a stage's span includes its launch
+ *    gaps;
+ *  kernel_begin/kernel_end: caller-created events stamped by the dispatch of the stage's
+ *    main kernel itself (hipExtLaunchKernelGGL) at that kernel's start and end, so they
+ *    time the kernel alone (eager calls; not recorded into a graph);
+ *  kernel_clock: device pointers to 2 * MOE_CLOCK_SLOTS uint64 each, which the caller
+ *    sets to pairs {UINT64_MAX, 0} before the stage runs; block b of the stage's main
+ *    kernel lowers pair b % MOE_CLOCK_SLOTS's first word to the block's start and raises
+ *    its second word to the block's end, in ticks of the device's constant-rate wall
+ *    clock (hipDeviceAttributeWallClockRate kHz).  The kernel's span is the least first
+ *    word to the greatest second word.  The pointers are kernel arguments, so they also
+ *    work in a captured graph, on every replay.
+ *  The kernel_* entries are honoured for MOE_STAGE_GATE_UP (the gate/up kernel) and
+ *  MOE_STAGE_DOWN (the down kernel, fused with the combine for up to 64 routed rows) and
+ *  ignored for the other stages. */
+#define MOE_CLOCK_SLOTS 1024
 typedef struct {
   moe_event_t begin[MOE_NUM_STAGES];
   moe_event_t end[MOE_NUM_STAGES];
+  moe_event_t kernel_begin[MOE_NUM_STAGES];
+  moe_event_t kernel_end[MOE_NUM_STAGES];
+  uint64_t* kernel_clock[MOE_NUM_STAGES];
 } moe_stage_events;
 
 /* moe_layer_forward with hipEventRecord calls around its stages, for timing

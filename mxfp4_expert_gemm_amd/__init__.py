@@ -48,11 +48,18 @@ class MoEConfig(ctypes.Structure):
 
 
 NUM_STAGES = 7
+CLOCK_SLOTS = 1024  # MOE_CLOCK_SLOTS: {start, end} uint64 pairs behind each kernel_clock pointer
 STAGES = ["router_down", "route", "permute", "gate_up", "down", "combine", "up"]
 
 
 class StageEvents(ctypes.Structure):
-    _fields_ = [("begin", ctypes.c_void_p * NUM_STAGES), ("end", ctypes.c_void_p * NUM_STAGES)]
+    """moe_stage_events: events recorded around each stage (begin/end), events the dispatch
+    of a stage's main kernel stamps at its start and end (kernel_begin/kernel_end), and
+    device pointers to CLOCK_SLOTS {start, end} uint64 pairs the main kernel's blocks stamp
+    with the device wall clock (kernel_clock; gate/up and down stages)."""
+    _fields_ = [("begin", ctypes.c_void_p * NUM_STAGES), ("end", ctypes.c_void_p * NUM_STAGES),
+                ("kernel_begin", ctypes.c_void_p * NUM_STAGES), ("kernel_end", ctypes.c_void_p * NUM_STAGES),
+                ("kernel_clock", ctypes.c_void_p * NUM_STAGES)]
 
 
 class RoutingOut(ctypes.Structure):

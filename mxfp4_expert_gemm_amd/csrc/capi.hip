@@ -266,6 +266,7 @@ MxArgs mx_args(const moe_config& c, int k, const uint8_t* blob, void* ws, const 
   m.mxfp8 = c.act_format == MOE_ACT_FMT_MXFP8;
   m.a_bf16 = nullptr;
   m.y = y;
+  m.clock = nullptr;
   return m;
 }
 
@@ -350,6 +351,18 @@ static moe_status forward_impl(const void* x, const void* router_w, const void* 
     moe_event_t e = begin ? ev->begin[stage] : ev->end[stage];
     return e ? dev(hipEventRecord(reinterpret_cast<hipEvent_t>(e), st)) : MOE_OK;
   };
+  // events stamped by the dispatch of a stage's main kernel
+  auto kclock = [&](int stage) {
+    return ev ? reinterpret_cast<unsigned long long*>(ev->kernel_clock[stage]) : nullptr;
+  };
+  auto kev = [&](int stage) {
+    KernelEvents k;
+    if (ev) {
+      k.begin = reinterpret_cast<hipEvent_t>(ev->kernel_begin[stage]);
+      k.end = reinterpret_cast<hipEvent_t>(ev->kernel_end[stage]);
+    }
+    return k;
+  };
 
   int32_t* idx = routing && routing->topk_idx ? routing->topk_idx : at<int32_t>(ws, l.idx);
   float* w = routing && routing->topk_w ? routing->topk_w : at<float>(ws, l.w);
@@ -406,10 +419,12 @@ static moe_status forward_impl(const void* x, const void* router_w, const void* 
   mx.tiles = etiles;
   if (down_combine_fits(c.num_tokens, k)) {
     MOE_TRY(mark(MOE_STAGE_GATE_UP, true));
-    MOE_TRY(dev(launch_gateup_mx(mx, st)));
+    mx.clock = kclock(MOE_STAGE_GATE_UP);
+    MOE_TRY(dev(launch_gateup_mx(mx, st, kev(MOE_STAGE_GATE_UP))));
     MOE_TRY(mark(MOE_STAGE_GATE_UP, false));
     MOE_TRY(mark(MOE_STAGE_DOWN, true));
-    MOE_TRY(dev(launch_down_combine_mx(mx, eidx, w, at<uint16_t>(ws, l.z), st)));
+    mx.clock = kclock(MOE_STAGE_DOWN);
+    MOE_TRY(dev(launch_down_combine_mx(mx, eidx, w, at<uint16_t>(ws, l.z), st, kev(MOE_STAGE_DOWN))));
     MOE_TRY(mark(MOE_STAGE_DOWN, false));
     MOE_TRY(mark(MOE_STAGE_COMBINE, true));
     MOE_TRY(mark(MOE_STAGE_COMBINE, false));
@@ -419,15 +434,18 @@ static moe_status forward_impl(const void* x, const void* router_w, const void* 
     int4* gt = at<int4>(ws, l.gtiles);
     const bool gemm = use_gemm(rows, c.num_experts);
     MOE_TRY(mark(MOE_STAGE_GATE_UP, true));
+    mx.clock = kclock(MOE_STAGE_GATE_UP);
     if (gemm) {
       MOE_TRY(dev(launch_gemm_tiles(ecounts, eoffsets, E_eff, gt, mt, st)));
-      MOE_TRY(dev(launch_gateup_gemm(mx, gt, mt, st)));
+      MOE_TRY(dev(launch_gateup_gemm(mx, gt, mt, st, kev(MOE_STAGE_GATE_UP))));
     } else {
-      MOE_TRY(dev(launch_gateup_mx(mx, st)));
+      MOE_TRY(dev(launch_gateup_mx(mx, st, kev(MOE_STAGE_GATE_UP))));
     }
     MOE_TRY(mark(MOE_STAGE_GATE_UP, false));
     MOE_TRY(mark(MOE_STAGE_DOWN, true));
-    MOE_TRY(dev(gemm ? launch_down_gemm(mx, gt, mt, st) : launch_down_mx(mx, st)));
+    mx.clock = kclock(MOE_STAGE_DOWN);
+    MOE_TRY(dev(gemm ? launch_down_gemm(mx, gt, mt, st, kev(MOE_STAGE_DOWN))
+                     : launch_down_mx(mx, st, kev(MOE_STAGE_DOWN))));
     MOE_TRY(mark(MOE_STAGE_DOWN, false));
     MOE_TRY(mark(MOE_STAGE_COMBINE, true));
     MOE_TRY(dev(launch_combine(at<float>(ws, l.y), w, c.num_tokens, k, c.d_latent, at<uint16_t>(ws, l.z), st)));
@@ -473,6 +491,7 @@ static moe_status forward_impl(const void* x, const void* router_w, const void* 
     ms.mxfp8 = c.act_format == MOE_ACT_FMT_MXFP8;
     ms.a_bf16 = nullptr;
     ms.y = at<float>(ws, l.s_y);
+    ms.clock = nullptr;
     MOE_TRY(run_experts_on(ms, rows, S, ps.counts, ps.offsets, at<int4>(ws, l.s_gtiles), st));
     up.add = ms.y;
     up.add_rows = S;

@@ -227,6 +227,22 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (WAVE - 1); }
 
+// Optional stamps of a kernel's span on the device's constant-rate wall clock: block b
+// lowers clk[2 (b % MOE_CLOCK_SLOTS)] to its start and raises the next word to its end
+// (after a block barrier, so that is the end of its last wave).  The caller sets the
+// slots to {UINT64_MAX, 0}; the kernel's span is the minimum start to the maximum end.
+// Two global atomics without a return value per block, spread over the slots; nothing
+// at all when clk is null.  Every thread of the block must call clock_end.
+__device__ __forceinline__ void clock_begin(unsigned long long* clk) {
+  if (clk && threadIdx.x == 0) atomicMin(clk + 2 * (blockIdx.x % MOE_CLOCK_SLOTS), (unsigned long long)wall_clock64());
+}
+__device__ __forceinline__ void clock_end(unsigned long long* clk) {
+  if (clk) {
+    __syncthreads();
+    if (threadIdx.x == 0) atomicMax(clk + 2 * (blockIdx.x % MOE_CLOCK_SLOTS) + 1, (unsigned long long)wall_clock64());
+  }
+}
+
 __host__ __device__ constexpr inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 __host__ __device__ constexpr inline size_t align_up(size_t a, size_t b) { return (a + b - 1) / b * b; }
 
@@ -294,11 +310,20 @@ __device__ __forceinline__ float quad_max(float v) {
   v = fmaxf(v, dpp_f32<DPP_QUAD_1032>(v, 0.f));
   return fmaxf(v, dpp_f32<DPP_QUAD_2301>(v, 0.f));
 }
+// |v| for a finite v, 0 for NaN and +-inf: block maxima are taken over the finite values
+__device__ __forceinline__ float finite_abs(float v) {
+  const float a = fabsf(v);
+  return a <= 0x1.fffffep127f ? a : 0.f;
+}
+// E4M3 NaN (S.1111.111): a non-finite activation enters the matrix cores as NaN, so every
+// product that reads it is NaN (an infinity cannot be encoded in E4M3)
+constexpr uint32_t E4M3_NAN = 0x7Fu;
+
 __device__ __forceinline__ void quantize_quad8(const float (&v)[8], uint32_t (&hi)[2], uint32_t (&lo)[2], uint32_t& shi,
                                                uint32_t& slo) {
   float amax = 0.f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, finite_abs(v[i]));
   amax = quad_max(amax);
   float inv;
   shi = block_scale(amax, inv);
@@ -309,8 +334,10 @@ __device__ __forceinline__ void quantize_quad8(const float (&v)[8], uint32_t (&h
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     float q;
-    hi[i / 4] |= e4m3_rne(v[i] * inv, q) << (8 * (i % 4));
-    r[i] = v[i] - q * s_hi;
+    const bool fin = finite_abs(v[i]) == fabsf(v[i]);
+    const uint32_t code = e4m3_rne(fin ? v[i] * inv : 0.f, q);
+    hi[i / 4] |= (fin ? code : E4M3_NAN) << (8 * (i % 4));
+    r[i] = fin ? v[i] - q * s_hi : 0.f;
     rmax = fmaxf(rmax, fabsf(r[i]));
   }
   rmax = quad_max(rmax);
@@ -324,16 +351,17 @@ __device__ __forceinline__ void quantize_quad8(const float (&v)[8], uint32_t (&h
 }
 
 // MXFP8 of one 32-value block held by a quad (the activation format of the MXFP8 mode,
-// OCP Microscaling v1.0 convention): shared exponent X = floor(log2 max|v|) - 8, e8m0
-// byte X + 127 (clamped to the e8m0 range; 0 for a block of zeros), codes = v / 2^X
-// rounded to nearest-even E4M3 and saturated to +-448.  Written into the hi term; the lo
+// OCP Microscaling v1.0 convention): shared exponent X = floor(log2 max|v|) - 8 over the
+// finite values, e8m0 byte X + 127 (clamped to the e8m0 range; 0 for a block of zeros),
+// codes = v / 2^X rounded to nearest-even E4M3 and saturated to +-448, the E4M3 NaN code
+// for NaN and +-inf.  Written into the hi term; the lo
 // term is zero (codes 0, scale byte 127), so the two-term kernels compute the same
 // product and the grouped GEMMs skip it.
 __device__ __forceinline__ void quantize_quad8_mx(const float (&v)[8], uint32_t (&hi)[2], uint32_t (&lo)[2],
                                                   uint32_t& shi, uint32_t& slo) {
   float amax = 0.f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, finite_abs(v[i]));
   amax = quad_max(amax);
   int X = -127;
   if (amax > 0.f) {
@@ -346,8 +374,9 @@ __device__ __forceinline__ void quantize_quad8_mx(const float (&v)[8], uint32_t 
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     float q;
-    const float t = fminf(fmaxf(v[i] * inv, -448.f), 448.f);  // exact scaling, then saturation
-    hi[i / 4] |= e4m3_rne(t, q) << (8 * (i % 4));
+    const bool fin = finite_abs(v[i]) == fabsf(v[i]);
+    const float t = fminf(fmaxf(fin ? v[i] * inv : 0.f, -448.f), 448.f);  // exact scaling, then saturation
+    hi[i / 4] |= (fin ? e4m3_rne(t, q) : E4M3_NAN) << (8 * (i % 4));
   }
   lo[0] = lo[1] = 0u;
   slo = 127u;

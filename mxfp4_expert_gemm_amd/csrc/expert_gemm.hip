@@ -272,8 +272,8 @@ __device__ __forceinline__ void gt_mainloop_any(const W (&w)[NMAT], const QRows&
 // Gate/up with the GLU: a = bf16(silu(g) u) for the tile, re-quantised to two e4m3 terms
 // into aq (routed-row order), optionally also as bf16.
 template <class W, int TERMS>
-__global__ void __launch_bounds__(256, 2) gateup_gemm_kernel(MxArgs p, const int4* __restrict__ gtiles, int ntiles,
-                                                              int nb) {
+__device__ __forceinline__ void gateup_gemm_kernel_body(MxArgs p, const int4* __restrict__ gtiles, int ntiles,
+                                                        int nb) {
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ int64_t srow[GT_TOK];
   __shared__ int sslot[GT_TOK];
@@ -336,14 +336,22 @@ __global__ void __launch_bounds__(256, 2) gateup_gemm_kernel(MxArgs p, const int
   }
 }
 
+template <class W, int TERMS>
+__global__ void __launch_bounds__(256, 2) gateup_gemm_kernel(MxArgs p, const int4* __restrict__ gtiles, int ntiles,
+                                                              int nb) {
+  clock_begin(p.clock);
+  gateup_gemm_kernel_body<W, TERMS>(p, gtiles, ntiles, nb);
+  clock_end(p.clock);
+}
+
 // Down: y[slot][l] fp32 for the tile's routed rows.  Each wave streams NG row groups of
 // 16 (groups 4 q + wave of the block's 4 NG, q < NG), so every activation operand read
 // from LDS feeds NG weight tiles: with NG = 2 (latent width a multiple of 128) a block
 // covers 128 latent rows, the LDS operand traffic per MFMA halves and each activation
 // chunk feeds twice the matrix-core work, the register profile of the gate/up kernel.
 template <class W, int TERMS, int NG>
-__global__ void __launch_bounds__(256, 2) down_gemm_kernel(MxArgs p, const int4* __restrict__ gtiles, int ntiles,
-                                                            int nb) {
+__device__ __forceinline__ void down_gemm_kernel_body(MxArgs p, const int4* __restrict__ gtiles, int ntiles,
+                                                      int nb) {
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ int64_t srow[GT_TOK];
   constexpr int ROWS = GT_ROWS * NG;
@@ -378,6 +386,14 @@ __global__ void __launch_bounds__(256, 2) down_gemm_kernel(MxArgs p, const int4*
         if (m < n) p.y[srow[m] * L + l] = acc[q][tt][j];
       }
   }
+}
+
+template <class W, int TERMS, int NG>
+__global__ void __launch_bounds__(256, 2) down_gemm_kernel(MxArgs p, const int4* __restrict__ gtiles, int ntiles,
+                                                            int nb) {
+  clock_begin(p.clock);
+  down_gemm_kernel_body<W, TERMS, NG>(p, gtiles, ntiles, nb);
+  clock_end(p.clock);
 }
 
 // Tiles of GT_TOK routed rows per active expert, in expert order: gtiles[0, ntiles) =
@@ -422,52 +438,56 @@ hipError_t launch_gemm_tiles(const int32_t* counts, const int32_t* offsets, int3
 }
 
 template <class W, int TERMS>
-static hipError_t gateup_gemm_go(const MxArgs& p, const int4* gtiles, int64_t max_gtiles, int64_t nb, hipStream_t st) {
+static hipError_t gateup_gemm_go(const MxArgs& p, const int4* gtiles, int64_t max_gtiles, int64_t nb, hipStream_t st,
+                                 const KernelEvents& ev) {
   static const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gateup_gemm_kernel<W, TERMS>),
                                                   hipFuncAttributeMaxDynamicSharedMemorySize, 2 * GT_BUF_BYTES);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((gateup_gemm_kernel<W, TERMS>), dim3((unsigned)nb), dim3(256), 2 * GT_BUF_BYTES, st, p, gtiles,
-                     (int)max_gtiles, (int)nb);
-  return hipGetLastError();
+  return dispatch(ev, gateup_gemm_kernel<W, TERMS>, dim3((unsigned)nb), dim3(256), 2 * GT_BUF_BYTES, st, p, gtiles,
+                  (int)max_gtiles, (int)nb);
 }
 
 template <class W, int TERMS, int NG>
-static hipError_t down_gemm_go(const MxArgs& p, const int4* gtiles, int64_t max_gtiles, int64_t nb, hipStream_t st) {
+static hipError_t down_gemm_go(const MxArgs& p, const int4* gtiles, int64_t max_gtiles, int64_t nb, hipStream_t st,
+                               const KernelEvents& ev) {
   static const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&down_gemm_kernel<W, TERMS, NG>),
                                                   hipFuncAttributeMaxDynamicSharedMemorySize, 2 * GT_BUF_BYTES);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((down_gemm_kernel<W, TERMS, NG>), dim3((unsigned)nb), dim3(256), 2 * GT_BUF_BYTES, st, p, gtiles,
-                     (int)max_gtiles, (int)nb);
-  return hipGetLastError();
+  return dispatch(ev, down_gemm_kernel<W, TERMS, NG>, dim3((unsigned)nb), dim3(256), 2 * GT_BUF_BYTES, st, p, gtiles,
+                  (int)max_gtiles, (int)nb);
 }
 
 template <int NG>
-static hipError_t down_gemm_ng(const MxArgs& p, const int4* gtiles, int64_t max_gtiles, hipStream_t st) {
+static hipError_t down_gemm_ng(const MxArgs& p, const int4* gtiles, int64_t max_gtiles, hipStream_t st,
+                               const KernelEvents& ev) {
   const int64_t nb = (max_gtiles * (p.L / (GT_ROWS * NG)) + 7) / 8 * 8;
   if (nb > 0x7FFFFFFF) return hipErrorInvalidValue;
   if (p.packed)
-    return p.mxfp8 ? down_gemm_go<PackedW, 1, NG>(p, gtiles, max_gtiles, nb, st)
-                   : down_gemm_go<PackedW, 2, NG>(p, gtiles, max_gtiles, nb, st);
-  return p.mxfp8 ? down_gemm_go<RecordW, 1, NG>(p, gtiles, max_gtiles, nb, st)
-                 : down_gemm_go<RecordW, 2, NG>(p, gtiles, max_gtiles, nb, st);
+    return p.mxfp8 ? down_gemm_go<PackedW, 1, NG>(p, gtiles, max_gtiles, nb, st, ev)
+                   : down_gemm_go<PackedW, 2, NG>(p, gtiles, max_gtiles, nb, st, ev);
+  return p.mxfp8 ? down_gemm_go<RecordW, 1, NG>(p, gtiles, max_gtiles, nb, st, ev)
+                 : down_gemm_go<RecordW, 2, NG>(p, gtiles, max_gtiles, nb, st, ev);
 }
 
-hipError_t launch_gateup_gemm(const MxArgs& p, const int4* gtiles, int64_t max_gtiles, hipStream_t st) {
+hipError_t launch_gateup_gemm(const MxArgs& p, const int4* gtiles, int64_t max_gtiles, hipStream_t st,
+                              const KernelEvents& ev) {
   if (p.T == 0) return hipSuccess;
   if (p.F % GT_ROWS || p.L % 128) return hipErrorInvalidValue;
   const int64_t nb = (max_gtiles * (p.F / GT_ROWS) + 7) / 8 * 8;
   if (nb > 0x7FFFFFFF) return hipErrorInvalidValue;
   if (p.packed)
-    return p.mxfp8 ? gateup_gemm_go<PackedW, 1>(p, gtiles, max_gtiles, nb, st)
-                   : gateup_gemm_go<PackedW, 2>(p, gtiles, max_gtiles, nb, st);
-  return p.mxfp8 ? gateup_gemm_go<RecordW, 1>(p, gtiles, max_gtiles, nb, st)
-                 : gateup_gemm_go<RecordW, 2>(p, gtiles, max_gtiles, nb, st);
+    return p.mxfp8 ? gateup_gemm_go<PackedW, 1>(p, gtiles, max_gtiles, nb, st, ev)
+                   : gateup_gemm_go<PackedW, 2>(p, gtiles, max_gtiles, nb, st, ev);
+  return p.mxfp8 ? gateup_gemm_go<RecordW, 1>(p, gtiles, max_gtiles, nb, st, ev)
+                 : gateup_gemm_go<RecordW, 2>(p, gtiles, max_gtiles, nb, st, ev);
 }
 
-hipError_t launch_down_gemm(const MxArgs& p, const int4* gtiles, int64_t max_gtiles, hipStream_t st) {
+hipError_t launch_down_gemm(const MxArgs& p, const int4* gtiles, int64_t max_gtiles, hipStream_t st,
+                            const KernelEvents& ev) {
   if (p.T == 0) return hipSuccess;
   if (p.L % GT_ROWS || p.F % 128) return hipErrorInvalidValue;
-  return p.L % (2 * GT_ROWS) == 0 ? down_gemm_ng<2>(p, gtiles, max_gtiles, st) : down_gemm_ng<1>(p, gtiles, max_gtiles, st);
+  return p.L % (2 * GT_ROWS) == 0 ? down_gemm_ng<2>(p, gtiles, max_gtiles, st, ev)
+                                  : down_gemm_ng<1>(p, gtiles, max_gtiles, st, ev);
 }
 
 }  // namespace moe

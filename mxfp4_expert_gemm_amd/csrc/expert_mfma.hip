@@ -227,7 +227,7 @@ static_assert(16 % MX_PF == 0, "ring slots must repeat every 16 steps");
 // down projection (64 rows = two complete scale blocks per token).  Tokens go in
 // passes of MX_TOK with their latent rows staged in LDS.
 template <class W>
-__global__ void __launch_bounds__(256, 2) gateup_mx_kernel(MxArgs p) {
+__device__ __forceinline__ void gateup_mx_kernel_body(MxArgs p) {
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ float atile[MX_TOK][MX_ROWS + 1];
   __shared__ int64_t srows[MX_TOK];
@@ -304,11 +304,18 @@ __global__ void __launch_bounds__(256, 2) gateup_mx_kernel(MxArgs p) {
   }
 }
 
+template <class W>
+__global__ void __launch_bounds__(256, 2) gateup_mx_kernel(MxArgs p) {
+  clock_begin(p.clock);
+  gateup_mx_kernel_body<W>(p);
+  clock_end(p.clock);
+}
+
 // -------------------------------------------------------------------- down
 
 // Block: one active expert x 64 rows of down; y[slot][l] for every token of the expert.
 template <class W>
-__global__ void __launch_bounds__(256) down_mx_kernel(MxArgs p) {
+__device__ __forceinline__ void down_mx_kernel_body(MxArgs p) {
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ int64_t srows[MX_TOK];
   const int nrt = p.L / MX_ROWS;
@@ -352,6 +359,13 @@ __global__ void __launch_bounds__(256) down_mx_kernel(MxArgs p) {
   }
 }
 
+template <class W>
+__global__ void __launch_bounds__(256) down_mx_kernel(MxArgs p) {
+  clock_begin(p.clock);
+  down_mx_kernel_body<W>(p);
+  clock_end(p.clock);
+}
+
 // Small batches (T*k <= 64): the down projection of every routed row and the weighted
 // combine in one kernel.  Block b owns latent rows 16b..16b+15 for all T*k rows t*k+j,
 // one wave per routed row (DCM_WAVES waves); y stays in LDS and the block sums it per
@@ -368,9 +382,8 @@ __host__ __device__ constexpr size_t dcm_row_bytes(int F) { return ((size_t)2 * 
 constexpr size_t DCM_LDS_MAX = 160 * 1024 - DCM_SLOTS * 16 * sizeof(float);
 
 template <class W>
-__global__ void __launch_bounds__(DCM_WAVES * WAVE) down_combine_mx_kernel(MxArgs p, const int32_t* __restrict__ idx,
-                                                                         const float* __restrict__ w,
-                                                                         uint16_t* __restrict__ z) {
+__device__ __forceinline__ void down_combine_mx_kernel_body(MxArgs p, const int32_t* __restrict__ idx,
+                                                            const float* __restrict__ w, uint16_t* __restrict__ z) {
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ float ys[DCM_SLOTS][16];
   const int lane = lane_id(), wave = threadIdx.x / WAVE;
@@ -410,6 +423,15 @@ __global__ void __launch_bounds__(DCM_WAVES * WAVE) down_combine_mx_kernel(MxArg
     for (int j = 0; j < k; ++j) acc += (double)w[t * k + j] * (double)ys[t * k + j][nn];
     z[(int64_t)t * L + blockIdx.x * 16 + nn] = f64_to_bf16(acc);
   }
+}
+
+template <class W>
+__global__ void __launch_bounds__(DCM_WAVES * WAVE) down_combine_mx_kernel(MxArgs p, const int32_t* __restrict__ idx,
+                                                                         const float* __restrict__ w,
+                                                                         uint16_t* __restrict__ z) {
+  clock_begin(p.clock);
+  down_combine_mx_kernel_body<W>(p, idx, w, z);
+  clock_end(p.clock);
 }
 
 // ------------------------------------------------------------------ packing
@@ -464,28 +486,22 @@ hipError_t launch_pack_experts(const uint8_t* src, uint8_t* dst, int E, int L, i
 
 // ------------------------------------------------------------------ launchers
 
-hipError_t launch_gateup_mx(const MxArgs& p, hipStream_t st) {
+hipError_t launch_gateup_mx(const MxArgs& p, hipStream_t st, const KernelEvents& ev) {
   if (p.T == 0 || p.max_active == 0) return hipSuccess;
   if (p.F % MX_ROWS || p.L % 128) return hipErrorInvalidValue;
   if (mx_lds_bytes(p.L) > MX_LDS_MAX) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(p.max_active * (p.F / MX_ROWS)));
-  if (p.packed)
-    hipLaunchKernelGGL(gateup_mx_kernel<PackedW>, grid, dim3(256), mx_lds_bytes(p.L), st, p);
-  else
-    hipLaunchKernelGGL(gateup_mx_kernel<RecordW>, grid, dim3(256), mx_lds_bytes(p.L), st, p);
-  return hipGetLastError();
+  if (p.packed) return dispatch(ev, gateup_mx_kernel<PackedW>, grid, dim3(256), mx_lds_bytes(p.L), st, p);
+  return dispatch(ev, gateup_mx_kernel<RecordW>, grid, dim3(256), mx_lds_bytes(p.L), st, p);
 }
 
-hipError_t launch_down_mx(const MxArgs& p, hipStream_t st) {
+hipError_t launch_down_mx(const MxArgs& p, hipStream_t st, const KernelEvents& ev) {
   if (p.T == 0 || p.max_active == 0) return hipSuccess;
   if (p.L % MX_ROWS || p.F % 128) return hipErrorInvalidValue;
   if (mx_lds_bytes(p.F) > MX_LDS_MAX) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(p.max_active * (p.L / MX_ROWS)));
-  if (p.packed)
-    hipLaunchKernelGGL(down_mx_kernel<PackedW>, grid, dim3(256), mx_lds_bytes(p.F), st, p);
-  else
-    hipLaunchKernelGGL(down_mx_kernel<RecordW>, grid, dim3(256), mx_lds_bytes(p.F), st, p);
-  return hipGetLastError();
+  if (p.packed) return dispatch(ev, down_mx_kernel<PackedW>, grid, dim3(256), mx_lds_bytes(p.F), st, p);
+  return dispatch(ev, down_mx_kernel<RecordW>, grid, dim3(256), mx_lds_bytes(p.F), st, p);
 }
 
 bool down_combine_fits(int64_t T, int32_t k) { return T * k <= DCM_SLOTS; }
@@ -499,7 +515,7 @@ static hipError_t down_combine_lds_limit() {
 }
 
 hipError_t launch_down_combine_mx(const MxArgs& p, const int32_t* idx, const float* w, uint16_t* z,
-                                  hipStream_t st) {
+                                  hipStream_t st, const KernelEvents& ev) {
   if (p.T == 0) return hipSuccess;
   const int nslot = (int)(p.T * p.k);
   const int waves = nslot < DCM_WAVES ? nslot : DCM_WAVES;
@@ -509,13 +525,11 @@ hipError_t launch_down_combine_mx(const MxArgs& p, const int32_t* idx, const flo
   if (p.packed) {
     const hipError_t e = down_combine_lds_limit<PackedW>();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(down_combine_mx_kernel<PackedW>, grid, block, lds, st, p, idx, w, z);
-  } else {
-    const hipError_t e = down_combine_lds_limit<RecordW>();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(down_combine_mx_kernel<RecordW>, grid, block, lds, st, p, idx, w, z);
+    return dispatch(ev, down_combine_mx_kernel<PackedW>, grid, block, (uint32_t)lds, st, p, idx, w, z);
   }
-  return hipGetLastError();
+  const hipError_t e = down_combine_lds_limit<RecordW>();
+  if (e != hipSuccess) return e;
+  return dispatch(ev, down_combine_mx_kernel<RecordW>, grid, block, (uint32_t)lds, st, p, idx, w, z);
 }
 
 // ------------------------------------------------- activation quantisation

@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
 
 namespace moe {
@@ -99,6 +100,21 @@ __host__ __device__ constexpr int64_t packed_expert_bytes(int L, int F) {
 }
 hipError_t launch_pack_experts(const uint8_t* src, uint8_t* dst, int E, int L, int F, hipStream_t st);
 
+// Start and end events stamped by a kernel's own dispatch (hipExtLaunchKernelGGL): they
+// bracket that kernel alone, with no launch gap; both null for a plain launch.
+struct KernelEvents {
+  hipEvent_t begin = nullptr, end = nullptr;
+};
+template <typename... Args, typename F = void (*)(Args...)>
+inline hipError_t dispatch(const KernelEvents& ev, F kernel, dim3 grid, dim3 block, uint32_t lds, hipStream_t st,
+                           Args... args) {
+  if (ev.begin || ev.end)
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, st, ev.begin, ev.end, 0u, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, lds, st, args...);
+  return hipGetLastError();
+}
+
 struct MxArgs {
   const uint8_t* blob;
   int32_t packed;            // 1: blob in the packed layout, 0: checkpoint records
@@ -112,12 +128,13 @@ struct MxArgs {
   int32_t mxfp8;             // activation format of aq (and of hq): MXFP8, else two exact e4m3 terms
   uint16_t* a_bf16;          // nullable [T*k][F] GLU outputs by slot, bf16
   float* y;                  // [T*k][L] down outputs by slot
+  unsigned long long* clock; // nullable: MOE_CLOCK_SLOTS {start, end} pairs of the kernel's blocks (clock_begin/end)
 };
-hipError_t launch_gateup_mx(const MxArgs& p, hipStream_t st);
-hipError_t launch_down_mx(const MxArgs& p, hipStream_t st);
+hipError_t launch_gateup_mx(const MxArgs& p, hipStream_t st, const KernelEvents& ev = KernelEvents());
+hipError_t launch_down_mx(const MxArgs& p, hipStream_t st, const KernelEvents& ev = KernelEvents());
 bool down_combine_fits(int64_t T, int32_t k);
 hipError_t launch_down_combine_mx(const MxArgs& p, const int32_t* idx, const float* w, uint16_t* z,
-                                  hipStream_t st);
+                                  hipStream_t st, const KernelEvents& ev = KernelEvents());
 hipError_t launch_quantize_rows(const uint16_t* src, int64_t rows, int K, const QRows& q, bool mxfp8, hipStream_t st);
 
 // ---- expert_gemm.hip: grouped GEMMs for experts with many routed rows
@@ -125,8 +142,10 @@ hipError_t launch_quantize_rows(const uint16_t* src, int64_t rows, int K, const 
 int64_t gemm_max_tiles(int64_t rows, int32_t E);
 hipError_t launch_gemm_tiles(const int32_t* counts, const int32_t* offsets, int32_t E, int4* gtiles,
                              int64_t max_gtiles, hipStream_t st);
-hipError_t launch_gateup_gemm(const MxArgs& p, const int4* gtiles, int64_t max_gtiles, hipStream_t st);
-hipError_t launch_down_gemm(const MxArgs& p, const int4* gtiles, int64_t max_gtiles, hipStream_t st);
+hipError_t launch_gateup_gemm(const MxArgs& p, const int4* gtiles, int64_t max_gtiles, hipStream_t st,
+                              const KernelEvents& ev = KernelEvents());
+hipError_t launch_down_gemm(const MxArgs& p, const int4* gtiles, int64_t max_gtiles, hipStream_t st,
+                            const KernelEvents& ev = KernelEvents());
 
 // ---- stream.hip: expert records fetched from host memory into HBM slots
 // copies the record of active expert j (tiles[j].x, j < *n_active) from src (device-

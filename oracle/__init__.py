@@ -8,6 +8,7 @@ bf16 tensors travel as numpy uint16 bit patterns.
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
 import ctypes
 import os
 import subprocess
@@ -136,22 +137,50 @@ def dot_bf16_exact(a: np.ndarray, b: np.ndarray) -> float:
     return float(lib().moe_ref_dot_bf16_exact(_p(a), _p(b), a.size))
 
 
-def router_logits(x: np.ndarray, router_w: np.ndarray, bias: Optional[np.ndarray] = None) -> np.ndarray:
+def _spans(n: int, threads: int):
+    """[lo, hi) token ranges for up to `threads` shards of n tokens."""
+    parts = max(1, min(threads, n))
+    cuts = [n * i // parts for i in range(parts + 1)]
+    return [(cuts[i], cuts[i + 1]) for i in range(parts) if cuts[i + 1] > cuts[i]]
+
+
+def _run_shards(fn, spans):
+    """Run fn(lo, hi) for every span, in threads when there are several: the C library
+    keeps no state between calls and ctypes releases the GIL during each call, so the
+    shards run in parallel; each shard is the single-threaded oracle on its tokens."""
+    if len(spans) <= 1:
+        return [fn(lo, hi) for lo, hi in spans]
+    with cf.ThreadPoolExecutor(len(spans)) as ex:
+        return list(ex.map(lambda s: fn(*s), spans))
+
+
+def router_logits(x: np.ndarray, router_w: np.ndarray, bias: Optional[np.ndarray] = None,
+                  threads: int = 1) -> np.ndarray:
     T, d = x.shape
     E = router_w.shape[0]
     bias_stride = 0 if bias is None or bias.ndim == 1 else E
     out = np.empty((T, E), dtype=np.float32)
-    _check(lib().moe_ref_router_logits(_p(x), _p(router_w), _p(bias), bias_stride, T, d, E, _p(out)),
-           "router_logits")
+
+    def shard(lo, hi):
+        b = None if bias is None else (bias if bias_stride == 0 else bias[lo:hi])
+        _check(lib().moe_ref_router_logits(_p(x[lo:hi]), _p(router_w), _p(b), bias_stride, hi - lo, d, E,
+                                           _p(out[lo:hi])), "router_logits")
+
+    _run_shards(shard, _spans(T, threads))
     return out
 
 
-def select(logits: np.ndarray, k: int, renormalize: bool = True):
+def select(logits: np.ndarray, k: int, renormalize: bool = True, threads: int = 1):
     logits = np.ascontiguousarray(logits, dtype=np.float32)
     T, E = logits.shape
     idx = np.empty((T, k), dtype=np.int32)
     w = np.empty((T, k), dtype=np.float32)
-    _check(lib().moe_ref_select(_p(logits), T, E, k, int(renormalize), _p(idx), _p(w)), "select")
+
+    def shard(lo, hi):
+        _check(lib().moe_ref_select(_p(logits[lo:hi]), hi - lo, E, k, int(renormalize), _p(idx[lo:hi]),
+                                    _p(w[lo:hi])), "select")
+
+    _run_shards(shard, _spans(T, threads))
     return idx, w
 
 
@@ -225,13 +254,16 @@ def combine(y: np.ndarray, w: np.ndarray) -> np.ndarray:
 def layer_forward(x, router_w, latent_down, latent_up, blob, k: int, d_latent: int, d_ffn: int,
                   bias: Optional[np.ndarray] = None, tokens: Optional[Sequence[int]] = None,
                   act: int = ACT_SILU, renormalize: bool = True, act_format: int = ACT_BF16,
-                  shared_blob: Optional[np.ndarray] = None, num_shared: int = 0, d_ffn_shared: int = 0) -> dict:
-    """Whole layer for `tokens` (default: all).  Returns dict of out, idx, w, logits, h, z."""
+                  shared_blob: Optional[np.ndarray] = None, num_shared: int = 0, d_ffn_shared: int = 0,
+                  threads: int = 1) -> dict:
+    """Whole layer for `tokens` (default: all).  Returns dict of out, idx, w, logits, h, z.
+    threads > 1 splits the tokens into shards computed side by side (tokens are
+    independent in the layer, so the result is the same)."""
     T, d = x.shape
     E = router_w.shape[0]
     bias_stride = 0 if bias is None or bias.ndim == 1 else E
-    tok = None if tokens is None else np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
-    n = T if tok is None else tok.size
+    tok = np.arange(T, dtype=np.int32) if tokens is None else np.asarray(tokens, dtype=np.int32)
+    n = tok.size
     out = np.empty((n, d), dtype=np.uint16)
     idx = np.empty((n, k), dtype=np.int32)
     w = np.empty((n, k), dtype=np.float32)
@@ -239,9 +271,15 @@ def layer_forward(x, router_w, latent_down, latent_up, blob, k: int, d_latent: i
     h = np.empty((n, d_latent), dtype=np.uint16)
     z = np.empty((n, d_latent), dtype=np.uint16)
     sb = None if shared_blob is None else np.ascontiguousarray(shared_blob)
-    rc = lib().moe_ref_layer_forward_shared(d, d_latent, d_ffn, E, k, act, act_format, int(renormalize), _p(x),
-                                            _p(router_w), _p(bias), bias_stride, _p(latent_down), _p(latent_up),
-                                            _p(blob), _p(tok), n, _p(out), _p(idx), _p(w), _p(logits), _p(h), _p(z),
-                                            _p(sb), num_shared, d_ffn_shared)
-    _check(rc, "layer_forward")
+
+    def shard(lo, hi):
+        t = np.ascontiguousarray(tok[lo:hi])
+        rc = lib().moe_ref_layer_forward_shared(d, d_latent, d_ffn, E, k, act, act_format, int(renormalize), _p(x),
+                                                _p(router_w), _p(bias), bias_stride, _p(latent_down), _p(latent_up),
+                                                _p(blob), _p(t), hi - lo, _p(out[lo:hi]), _p(idx[lo:hi]),
+                                                _p(w[lo:hi]), _p(logits[lo:hi]), _p(h[lo:hi]), _p(z[lo:hi]),
+                                                _p(sb), num_shared, d_ffn_shared)
+        _check(rc, "layer_forward")
+
+    _run_shards(shard, _spans(n, threads))
     return dict(out=out, idx=idx, w=w, logits=logits, h=h, z=z)

@@ -395,14 +395,15 @@ static int32_t e4m3_code_of(double q) {
 
 /* One block of 32 values as MXFP8 (OCP Microscaling v1.0 convention, E4M3 elements):
  * shared exponent X = floor(log2(max |v|)) - 8 (8 = E4M3's largest normal exponent),
- * limited to the e8m0 range [-127, 127]; element codes = v / 2^X rounded to nearest
- * even E4M3, saturated to +-448; scale byte X + 127.  A block of zeros gets scale byte
- * 0 and zero codes (signs kept). */
+ * the maximum taken over the finite values and X limited to the e8m0 range [-127, 127];
+ * element codes = v / 2^X rounded to nearest even E4M3, saturated to +-448; scale byte
+ * X + 127.  A block of zeros gets scale byte 0 and zero codes (signs kept).  E4M3 has no
+ * infinity: NaN and +-inf elements get the NaN code 0x7F (the convention as read here). */
 int moe_ref_mxfp8_block(const double* v, uint8_t* codes, uint8_t* scale) {
   if (!v || !codes || !scale) return MOE_REF_ERR_ARG;
   double amax = 0.0;
   for (int i = 0; i < 32; ++i)
-    if (fabs(v[i]) > amax) amax = fabs(v[i]);
+    if (isfinite(v[i]) && fabs(v[i]) > amax) amax = fabs(v[i]);
   int X = -127;
   if (amax > 0.0) {
     int e;
@@ -411,7 +412,8 @@ int moe_ref_mxfp8_block(const double* v, uint8_t* codes, uint8_t* scale) {
     if (X < -127) X = -127;
     if (X > 127) X = 127;
   }
-  for (int i = 0; i < 32; ++i) codes[i] = (uint8_t)e4m3_code_of(ldexp(v[i], -X));
+  for (int i = 0; i < 32; ++i)
+    codes[i] = isfinite(v[i]) ? (uint8_t)e4m3_code_of(ldexp(v[i], -X)) : (uint8_t)0x7F;
   *scale = (uint8_t)(X + 127);
   return MOE_REF_OK;
 }

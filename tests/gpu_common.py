@@ -1,6 +1,7 @@
 """Shared fixtures for the GPU parity tests: seeded layers on host (for the oracle)
 and on the device (for the HIP library), built once per session."""
 import functools
+import os
 import sys
 
 import numpy as np
@@ -77,3 +78,20 @@ def dev_packed(name: str):
     t = moe.pack_experts(dev_weights(name)["blob"], c.E, c.L, c.F)
     torch.cuda.synchronize()
     return t
+
+
+# worker threads for the oracle's token shards: the host share of one GPU is 16 cores
+ORACLE_THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+@functools.lru_cache(maxsize=None)
+def oracle_routing(name: str):
+    """The oracle's routing of every token of a workload: (logits, idx, w), computed once
+    per session on token shards side by side."""
+    import oracle
+    h = host_layer(name)
+    c = h["cfg"]
+    log(f"oracle routing of all {h['x'].shape[0]} {name} tokens on {ORACLE_THREADS} threads ...")
+    logits = oracle.router_logits(h["x"], h["router_w"], h["bias"], threads=ORACLE_THREADS)
+    idx, w = oracle.select(logits, c.k, threads=ORACLE_THREADS)
+    return logits, idx, w

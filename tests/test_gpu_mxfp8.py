@@ -10,7 +10,7 @@ import mxfp4_expert_gemm_amd as moe
 import oracle
 import synth
 from _util import bf16_bits_to_f64, rel_l2
-from gpu_common import dev_packed, dev_weights, from_dev, host_layer, log, to_dev
+from gpu_common import ORACLE_THREADS, dev_packed, dev_weights, from_dev, host_layer, log, oracle_routing, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -30,12 +30,14 @@ def _run(name, T=None, tokens=None, packed=True):
     out = from_dev(out)
     tokens = list(range(Tn)) if tokens is None else tokens
     ref = oracle.layer_forward(h["x"], h["router_w"], h["latent_down"], h["latent_up"], h["blob"], c.k, c.L, c.F,
-                               bias=h["bias"], tokens=tokens, act_format=oracle.ACT_MXFP8)
+                               bias=h["bias"], tokens=tokens, act_format=oracle.ACT_MXFP8, threads=ORACLE_THREADS)
     assert np.array_equal(from_dev(idx)[tokens], ref["idx"])
+    if T is None and c.d == 7168:  # the routing does not depend on the activation format
+        assert np.array_equal(from_dev(idx), oracle_routing(name)[1])
     err = rel_l2(bf16_bits_to_f64(out[tokens]), bf16_bits_to_f64(ref["out"]))
     # the bf16-mode oracle, for scale: the mode really quantises
     ref_b = oracle.layer_forward(h["x"], h["router_w"], h["latent_down"], h["latent_up"], h["blob"], c.k, c.L,
-                                 c.F, bias=h["bias"], tokens=tokens)
+                                 c.F, bias=h["bias"], tokens=tokens, threads=ORACLE_THREADS)
     dev_b = rel_l2(bf16_bits_to_f64(out[tokens]), bf16_bits_to_f64(ref_b["out"]))
     log(f"  {name} T={Tn} MXFP8 rel-L2 = {err:.3g} (against the bf16 mode: {dev_b:.3g})")
     assert err <= TOL_OUT
@@ -57,8 +59,18 @@ def test_layer_mxfp8_decode1():
     _run("decode1")
 
 
+def test_layer_mxfp8_decode64_every_token():
+    _run("decode64")
+
+
 def test_layer_mxfp8_prefill4k_sampled():
     _run("prefill4k", tokens=[0, 2047, 4095])
+
+
+def test_layer_mxfp8_prefill32k_sampled():
+    """The prompt cap in the MXFP8 mode: every token's routing, outputs on a sample."""
+    rng = np.random.default_rng(0x8F8)
+    _run("prefill32k", tokens=sorted({0, 32767, *rng.choice(32768, 14, replace=False).tolist()}))
 
 
 def test_expert_ffn_mxfp8_rows():

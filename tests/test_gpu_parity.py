@@ -14,7 +14,7 @@ import mxfp4_expert_gemm_amd as moe
 import oracle
 import synth
 from _util import bf16_bits_to_f64, f64_to_bf16_bits, rel_l2
-from gpu_common import dev_weights, from_dev, host_layer, log, to_dev
+from gpu_common import ORACLE_THREADS, dev_weights, from_dev, host_layer, log, oracle_routing, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -109,18 +109,20 @@ def test_route_exact_path_decides_midpoints():
     assert np.array_equal(from_dev(idx), oracle.select(want, 3)[0])
 
 
-@pytest.mark.parametrize("name,T", [("tiny", None), ("decode1", None), ("decode64", None), ("prefill4k", 256),
-                                    ("prefill32k", 256)])
-def test_route_indices_bit_exact(name, T):
-    h = host_layer(name, T)
+@pytest.mark.parametrize("name", ["tiny", "decode1", "decode64", "prefill4k", "prefill32k"])
+def test_route_indices_bit_exact(name):
+    """Every token of every workload: the GPU's certified routing selects exactly the
+    oracle's experts (the correctly rounded logits' top-k, lowest index on ties)."""
+    h = host_layer(name)
     c = h["cfg"]
     dw = dev_weights(name)
     bias = None if h["bias"] is None else to_dev(h["bias"])
     log(f"route {name} T={h['x'].shape[0]}")
     logits, idx, w = moe.route(to_dev(h["x"]), dw["router_w"], c.k, bias=bias)
-    want_l = oracle.router_logits(h["x"], h["router_w"], h["bias"])
-    want_idx, want_w = oracle.select(want_l, c.k)
-    assert np.array_equal(from_dev(idx), want_idx)
+    want_l, want_idx, want_w = oracle_routing(name)
+    gidx = from_dev(idx)
+    bad = np.nonzero((gidx != want_idx).any(1))[0]
+    assert bad.size == 0, f"{bad.size} tokens routed differently, first {bad[:8].tolist()}"
     gl = from_dev(logits).astype(np.float64)
     dev_max = np.max(np.abs(gl - want_l))
     log(f"  max |logit - exact| = {dev_max:.3g}")
@@ -313,6 +315,9 @@ def test_combine():
 # ------------------------------------------------------------- whole layer
 
 def _layer_case(name, T=None, sample=None):
+    """The layer on a workload: routing, grouping and counts of every token against the
+    oracle's (bit-exact), outputs against the oracle's on `sample` (default: every token)
+    to the relative L2 tolerance.  Returns the outputs and routing outputs."""
     h = host_layer(name, T)
     c = h["cfg"]
     dw = dev_weights(name)
@@ -330,21 +335,27 @@ def _layer_case(name, T=None, sample=None):
                             bias=bias, routing=routing)
     torch.cuda.synchronize()
     out = from_dev(out)
-    gidx = from_dev(routing["topk_idx"])
+    got = {k: from_dev(v) for k, v in routing.items()}
+    gidx = got["topk_idx"]
     tokens = list(range(Tn)) if sample is None else sorted(set(sample))
     ref = oracle.layer_forward(h["x"], h["router_w"], h["latent_down"], h["latent_up"], h["blob"], c.k, c.L, c.F,
-                               bias=h["bias"], tokens=tokens)
+                               bias=h["bias"], tokens=tokens, threads=ORACLE_THREADS)
     assert np.array_equal(gidx[tokens], ref["idx"])
+    if T is None:
+        # every token's experts and weights, against the oracle's routing of the whole batch
+        _, want_idx, want_w = oracle_routing(name)
+        assert np.array_equal(gidx, want_idx)
+        assert np.allclose(got["topk_w"], want_w, rtol=1e-4, atol=1e-6)
     err = rel_l2(bf16_bits_to_f64(out[tokens]), bf16_bits_to_f64(ref["out"]))
-    log(f"  rel-L2 = {err:.3g}")
+    log(f"  rel-L2 over {len(tokens)} tokens = {err:.3g}")
     assert err <= TOL_OUT
-    # the permutation of the GPU's own routing equals the oracle's grouping of it
+    # the grouping: the oracle's grouping of the (oracle-equal) routing
     wc, wo, wp = oracle.permute(gidx, c.E)
-    assert np.array_equal(from_dev(routing["expert_counts"]), wc)
-    assert np.array_equal(from_dev(routing["expert_offsets"]), wo)
-    assert np.array_equal(from_dev(routing["perm"]), wp)
+    assert np.array_equal(got["expert_counts"], wc)
+    assert np.array_equal(got["expert_offsets"], wo)
+    assert np.array_equal(got["perm"], wp)
     assert (wc.sum() == Tn * c.k) and all(len(set(r)) == c.k for r in gidx.tolist())
-    return out
+    return out, got
 
 
 def test_layer_tiny():
@@ -355,21 +366,40 @@ def test_layer_decode1():
     _layer_case("decode1")
 
 
-def test_layer_decode64_sampled():
-    _layer_case("decode64", sample=[0, 17, 33, 63])
+def test_layer_decode64_every_token():
+    _layer_case("decode64")
 
 
-def test_layer_prefill4k_full_size_sampled():
-    """All 4096 tokens through the layer; routing, grouping and outputs checked on a seeded
-    sample of tokens (first, last, and spread), the grouping of every token against the
-    oracle's grouping of the GPU's routing."""
+def test_layer_prefill4k_full_size():
+    """All 4096 tokens through the layer: routing, weights and grouping of every token
+    against the oracle's; outputs on a seeded sample (first, last and spread)."""
     rng = np.random.default_rng(0x4096)
-    _layer_case("prefill4k", sample=[0, 4095] + rng.choice(4096, 10, replace=False).tolist())
+    _layer_case("prefill4k", sample=[0, 4095] + rng.choice(4096, 30, replace=False).tolist())
 
 
-def test_layer_prefill32k_full_size_sampled():
+def test_layer_prefill32k_full_size():
     rng = np.random.default_rng(0x32768)
-    _layer_case("prefill32k", sample=[0, 32767] + rng.choice(32768, 6, replace=False).tolist())
+    _layer_case("prefill32k", sample=[0, 32767] + rng.choice(32768, 30, replace=False).tolist())
+
+
+def test_layer_prefill4k_run_twice_bit_identical():
+    """The prefill path (integer atomics in the grouping, grouped GEMMs, the combine) gives
+    the same bits on a second run: outputs, routing, grouping."""
+    h = host_layer("prefill4k")
+    c = h["cfg"]
+    dw = dev_weights("prefill4k")
+    runs = []
+    for _ in range(2):
+        routing = dict(topk_idx=torch.empty((c.T, c.k), dtype=torch.int32, device="cuda"),
+                       topk_w=torch.empty((c.T, c.k), dtype=torch.float32, device="cuda"),
+                       expert_offsets=torch.empty(c.E + 1, dtype=torch.int32, device="cuda"),
+                       perm=torch.empty(c.T * c.k, dtype=torch.int32, device="cuda"))
+        out = moe.layer_forward(to_dev(h["x"]), dw["router_w"], dw["latent_down"], dw["latent_up"], dw["blob"], c.k,
+                                d_ffn=c.F, bias=to_dev(h["bias"]), routing=routing)
+        torch.cuda.synchronize()
+        runs.append([from_dev(out)] + [from_dev(v) for v in routing.values()])
+    for a, b in zip(*runs):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
 
 
 @pytest.mark.parametrize("T", [40, 600, 1100])
@@ -389,8 +419,8 @@ def test_layer_tiny_weights_every_dispatch_path(T):
 
 
 def test_layer_deterministic():
-    a = _layer_case("tiny")
-    b = _layer_case("tiny")
+    a, _ = _layer_case("tiny")
+    b, _ = _layer_case("tiny")
     assert np.array_equal(a, b)
 
 

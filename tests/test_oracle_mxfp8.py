@@ -103,6 +103,23 @@ def test_mxfp8_block_special_cases():
     assert s == 0 and oracle.e4m3_value(int(c[0])) * 2.0 ** -127 == 2.0 ** -130
 
 
+def test_mxfp8_block_non_finite_elements_are_nan():
+    """E4M3 has no infinity: NaN and +-inf elements get the NaN code 0x7F, and the block
+    scale and the other codes are those of the finite elements alone."""
+    rng = np.random.default_rng(77)
+    v = rng.standard_normal(32) * 5.0
+    w = v.copy()
+    w[[2, 9, 30]] = [np.nan, np.inf, -np.inf]
+    c, s = oracle.mxfp8_block(w)
+    assert (c[[2, 9, 30]] == 0x7F).all() and all(math.isnan(oracle.e4m3_value(int(x))) for x in c[[2, 9, 30]])
+    finite = np.delete(np.arange(32), [2, 9, 30])
+    bc, bs = _brute_block(np.where(np.isfinite(w), w, 0.0))
+    assert s == bs and np.array_equal(c[finite], bc[finite])
+    # a block of nothing but non-finite values: scale byte 0, every code NaN
+    c, s = oracle.mxfp8_block(np.full(32, np.inf))
+    assert s == 0 and (c == 0x7F).all()
+
+
 @pytest.mark.parametrize("seed", range(4))
 def test_mxfp8_quantisation_is_idempotent(seed):
     rng = np.random.default_rng(100 + seed)
