@@ -176,6 +176,25 @@ moe_status moe_layer_forward(const void* x, const void* router_w, const void* la
                              moe_routing_out* routing, void* workspace, size_t workspace_bytes,
                              moe_stream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): moe_layer_forward without the
+ * workspace argument.  Its scratch is one device array of MOE_NOALLOC_SCRATCH_BYTES that
+ * the library holds on every GPU it runs on until the process ends; the call allocates
+ * nothing (no hipMalloc, no allocating library routine).
+ *  - A batch whose moe_workspace_size(cfg, k) exceeds MOE_NOALLOC_SCRATCH_BYTES returns
+ *    MOE_ERR_WORKSPACE before anything is enqueued (at the Kimi K3 shapes, d 7168,
+ *    L 3584, F 3072, E 896, k 16: up to 188 tokens).
+ *  - Every call on one GPU uses that GPU's one array, which keeps the last call's
+ *    contents (the layer needs no part of it cleared): calls that overlap on one GPU
+ *    (other streams, other host threads) race, and the caller must serialise them.
+ *  - stream must belong to the current device (else MOE_ERR_INVALID_ARG).
+ *  - cfg->num_shared must be 0.  Other arguments and the result as moe_layer_forward. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+moe_status moe_layer_forward_noalloc(const void* x, const void* router_w, const void* latent_down,
+                                     const void* latent_up, const uint8_t* expert_blob, int32_t k,
+                                     const moe_config* cfg, const float* router_bias, void* out,
+                                     moe_routing_out* routing, moe_stream_t stream);
+
 /* Stages of moe_layer_forward, in launch order. */
 typedef enum {
   MOE_STAGE_ROUTER_DOWN = 0, /* router logits and latent down projection (one launch) */

@@ -30,7 +30,7 @@ EXPORTS = ["moe_expert_bytes", "moe_packed_expert_bytes", "moe_pack_experts", "m
            "moe_layer_forward_profiled",
            "moe_dequant_mxfp4", "moe_route", "moe_topk", "moe_permute", "moe_expert_ffn", "moe_combine",
            "moe_linear_bf16", "moe_reap_saliency", "moe_layer_forward_shared", "moe_expert_slots_bytes",
-           "moe_layer_forward_streamed"]
+           "moe_layer_forward_streamed", "moe_layer_forward_noalloc"]
 
 
 class MoEError(RuntimeError):
@@ -98,6 +98,7 @@ def lib():
             "moe_reap_saliency": (ctypes.c_int, [vp, vp, vp, vp, i64, i32, i32, i32, vp, vp]),
             "moe_layer_forward_shared": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, cfgp, vp, vp, vp, rp, vp, sz, vp]),
             "moe_expert_slots_bytes": (ctypes.c_int, [cfgp, i32, ctypes.POINTER(sz)]),
+            "moe_layer_forward_noalloc": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, cfgp, vp, vp, rp, vp]),
             "moe_layer_forward_streamed": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, cfgp, vp, vp, sz, vp, rp, vp, sz,
                                                           vp]),
         }
@@ -199,6 +200,26 @@ def layer_forward(x, router_w, latent_down, latent_up, expert_blob, k: int, *, d
         _check(lib().moe_layer_forward(_p(x), _p(router_w), _p(latent_down), _p(latent_up), _p(expert_blob), k,
                                        ctypes.byref(cfg), _p(bias), _p(out), ctypes.byref(r) if r else None,
                                        _p(workspace), workspace.numel(), _stream(stream)), "moe_layer_forward")
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # MOE_NOALLOC_SCRATCH_BYTES
+
+
+def layer_forward_noalloc(x, router_w, latent_down, latent_up, expert_blob, k: int, *, d_ffn: int, out: torch.Tensor,
+                          bias: Optional[torch.Tensor] = None, renormalize: bool = True, act: int = ACT_SILU,
+                          routing: Optional[dict] = None, stream=None, packed: bool = False,
+                          act_format: int = ACT_FMT_BF16) -> torch.Tensor:
+    """layer_forward without a workspace (moe_layer_forward_noalloc): the library's own device
+    scratch serves, and nothing is allocated here either, so `out` (and any routing tensors)
+    must be given.  Calls that overlap on one GPU race on that scratch."""
+    T, d = x.shape
+    cfg = make_config(T, d, latent_down.shape[0], d_ffn, router_w.shape[0], act=act, renormalize=renormalize,
+                      bias=bias, packed=packed, act_format=act_format)
+    r = _routing(routing)
+    _check(lib().moe_layer_forward_noalloc(_p(x), _p(router_w), _p(latent_down), _p(latent_up), _p(expert_blob), k,
+                                           ctypes.byref(cfg), _p(bias), _p(out), ctypes.byref(r) if r else None,
+                                           _stream(stream)), "moe_layer_forward_noalloc")
     return out
 
 
@@ -378,4 +399,5 @@ __all__ = ["lib", "MoEConfig", "RoutingOut", "MoEError", "make_config", "expert_
            "pack_experts", "LAYOUT_RECORD", "LAYOUT_PACKED", "ACT_FMT_BF16", "ACT_FMT_MXFP8", "workspace_size",
            "alloc_workspace", "layer_forward", "layer_forward_profiled", "StageEvents", "STAGES", "dequant_mxfp4", "route", "topk", "permute", "expert_ffn", "combine",
            "linear_bf16", "reap_saliency", "reap_prune_bias", "ACT_SILU", "ACT_SITU", "ROUTE_EXACT_ALL", "EXPORTS",
-           "LIB_PATH", "expert_slots_bytes", "alloc_expert_slots", "layer_forward_streamed"]
+           "LIB_PATH", "expert_slots_bytes", "alloc_expert_slots", "layer_forward_streamed", "layer_forward_noalloc",
+           "NOALLOC_SCRATCH_BYTES"]

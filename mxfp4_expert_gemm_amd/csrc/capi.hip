@@ -3,6 +3,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -270,6 +272,36 @@ MxArgs mx_args(const moe_config& c, int k, const uint8_t* blob, void* ws, const 
   return m;
 }
 
+// ---- scratch of the entry point without a workspace argument
+// One file-scope device array: each GPU the library runs on holds its own copy until the
+// process ends.  On the host its name is only a stand-in, not the device address: the
+// address comes from hipGetSymbolAddress, once per device with that device current, and
+// only that address is ever passed to kernels.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex scratch_mutex;
+void* scratch_addr[MAX_DEVICES];
+
+// the scratch's device address on the device that owns `stream`, which must be current
+moe_status scratch_for(hipStream_t stream, void** out) {
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess || cur < 0 || cur >= MAX_DEVICES) return MOE_ERR_DEVICE;
+  if (stream) {
+    hipDevice_t sd = -1;
+    if (hipStreamGetDevice(stream, &sd) != hipSuccess) return MOE_ERR_DEVICE;
+    if (sd != cur) return MOE_ERR_INVALID_ARG;
+  }
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (!scratch_addr[cur]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_DEVICE;
+    scratch_addr[cur] = p;
+  }
+  *out = scratch_addr[cur];
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -506,6 +538,21 @@ moe_status moe_layer_forward(const void* x, const void* router_w, const void* la
                              size_t workspace_bytes, moe_stream_t stream) {
   return forward_impl(x, router_w, latent_down, latent_up, expert_blob, k, cfg, router_bias, nullptr, out, routing,
                       workspace, workspace_bytes, nullptr, stream);
+}
+
+moe_status moe_layer_forward_noalloc(const void* x, const void* router_w, const void* latent_down,
+                                     const void* latent_up, const uint8_t* expert_blob, int32_t k,
+                                     const moe_config* cfg, const float* router_bias, void* out,
+                                     moe_routing_out* routing, moe_stream_t stream) {
+  MOE_TRY(check_config(cfg, k));
+  if (cfg->num_shared > 0) return MOE_ERR_INVALID_ARG;
+  if (cfg->num_tokens == 0) return MOE_OK;
+  // refuse a batch whose scratch would not fit before anything touches the device
+  if (layout(*cfg, k).total > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  MOE_TRY(scratch_for(reinterpret_cast<hipStream_t>(stream), &ws));
+  return forward_impl(x, router_w, latent_down, latent_up, expert_blob, k, cfg, router_bias, nullptr, out, routing,
+                      ws, (size_t)MOE_NOALLOC_SCRATCH_BYTES, nullptr, stream);
 }
 
 moe_status moe_layer_forward_shared(const void* x, const void* router_w, const void* latent_down,

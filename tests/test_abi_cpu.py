@@ -195,3 +195,17 @@ def test_expert_ffn_binding_rejects_wrong_output_buffers():
     with pytest.raises(ValueError):
         moe.expert_ffn(h, h, idx, y=torch.zeros((6, 128), dtype=torch.float32),
                        a=torch.zeros((6, 64), dtype=torch.int16), **kw)
+
+
+def test_noalloc_refuses_batches_past_its_scratch_before_any_launch():
+    """moe_layer_forward_noalloc: a batch whose workspace exceeds the library's scratch, or
+    one with shared experts, is refused before the device is touched."""
+    lib = moe.lib()
+    big = k3(T=4096)
+    n = ctypes.c_size_t(0)
+    assert lib.moe_workspace_size(ctypes.byref(big), 16, ctypes.byref(n)) == 0 and n.value > moe.NOALLOC_SCRATCH_BYTES
+    args = [FAKE] * 5
+    assert lib.moe_layer_forward_noalloc(*args, 16, ctypes.byref(big), None, FAKE, None, None) == -3
+    shared = k3(T=1, num_shared=2, d_ffn_shared=3072)
+    assert lib.moe_layer_forward_noalloc(*args, 16, ctypes.byref(shared), None, FAKE, None, None) == -1
+    assert lib.moe_layer_forward_noalloc(*args, 0, ctypes.byref(k3(T=1)), None, FAKE, None, None) == -1
