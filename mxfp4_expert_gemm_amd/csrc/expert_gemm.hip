@@ -396,6 +396,350 @@ __global__ void __launch_bounds__(256, 2) down_gemm_kernel(MxArgs p, const int4*
   clock_end(p.clock);
 }
 
+// ---------------------------------------------------- 32x32x64 grouped GEMMs
+//
+// The same tiles (up to 64 routed rows of one expert) on v_mfma_scale_f32_32x32x64_f8f6f4,
+// which does twice the work of the 16x16x128 form per operand byte: each activation
+// operand read from LDS and each weight operand loaded from memory feeds twice the
+// matrix-core work.  Operand layout (measured on gfx950 with exact small-integer
+// operands): lane l works on row/column l%32 and g = l/32; the FP8 operand holds
+// K = 16g..16g+15 in registers 0-3 and 32+16g..32+16g+15 in registers 4-7; the FP4
+// operand holds K = 32g..32g+31 (low nibble first); lane r + 32b supplies the scale of
+// row/column r for K block b; result register v of lane l is D[8(v/4) + 4g + v%4][l%32].
+//
+// A wave owns 32 weight rows of each of NMAT matrices (gate and up, or two 32-row groups
+// of down) and the tile's token sub-tiles of 32 rows; a K step of 128 is two half-steps
+// of 64.  Weight operands are loaded per wave from memory straight into registers, PF
+// steps ahead; the activation tile moves through LDS in the chunks of the kernels above.
+
+template <int N>
+using f32xN = float __attribute__((ext_vector_type(N)));
+typedef f32xN<16> f32x16;
+
+template <int OPSEL_B>
+__device__ __forceinline__ f32x16 mx_mfma32(const i32x8& a, const i32x8& b, f32x16 c, uint32_t sa, uint32_t sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0 /*A: fp8 e4m3*/, 4 /*B: fp4 e2m1*/, 0, (int)sa,
+                                                         OPSEL_B, (int)sb);
+}
+
+// One K step of one 32-row weight operand: the codes of the two half-steps and their
+// scale words (the scale byte is chosen by opsel(step) or already in the low byte).
+struct W32Step {
+  uint4 q[2];
+  uint32_t s[2];
+};
+
+// Packed layout: 32 weight rows are two 16-row groups; in group x, the 1024-byte code
+// tile of step s holds row r%16, K block kb at bytes 16 (r%16 + 16 kb).  Lane l takes
+// group (l%32)/16, row l%16, K block 2 hh + l/32 of the step: two 512-byte runs per load.
+// Scale tile t (256 bytes) holds, at byte 4 (r%16 + 16 kb) + j, step 4 t + j.
+struct W32Packed {
+  const uint8_t* c;
+  const uint8_t* s;
+  int nsc;
+  __device__ static W32Packed make(const uint8_t* blob, int e, int L, int F, int mat, int pair, int lane) {
+    const int K = mat == MAT_DOWN ? F : L;
+    const int64_t gu = (int64_t)(F / 16) * packed_group_bytes(L);
+    const uint8_t* m =
+        blob + (int64_t)e * packed_expert_bytes(L, F) + (mat == MAT_GATE ? 0 : mat == MAT_UP ? gu : 2 * gu);
+    const uint8_t* grp = m + (int64_t)(2 * pair + ((lane & 31) >> 4)) * packed_group_bytes(K);
+    const int pos = (lane & 15) + 16 * (lane >> 5);  // row in group + 16 x (K block within the half-step)
+    W32Packed w;
+    w.c = grp + 16 * pos;
+    w.s = grp + (int64_t)(K / 128) * 1024 + 4 * pos;
+    w.nsc = (K / 128 + 3) / 4;
+    return w;
+  }
+  __device__ __forceinline__ W32Step step(int ks) const {
+    W32Step r;
+    const uint8_t* cs = c + 1024 * ks;
+    r.q[0] = *reinterpret_cast<const uint4*>(cs);
+    r.q[1] = *reinterpret_cast<const uint4*>(cs + 512);
+    const uint8_t* ss = s + 256 * (ks >> 2);
+    r.s[0] = *reinterpret_cast<const uint32_t*>(ss);
+    r.s[1] = *reinterpret_cast<const uint32_t*>(ss + 128);
+    return r;
+  }
+  static constexpr int opsel(int j) { return j & 3; }
+};
+
+// Checkpoint record: row 32 pair + l%32, K block 4 s + 2 hh + l/32 of step s is bytes
+// 64 s + 32 hh + 16 (l/32) of the row's codes; its scale is byte 4 s + 2 hh + l/32 of
+// the row's scales, moved to the low byte.
+struct W32Record {
+  const uint8_t* c;
+  const uint8_t* s;
+  int sh;  // 8 x (l/32)
+  __device__ static W32Record make(const uint8_t* blob, int e, int L, int F, int mat, int pair, int lane) {
+    const int64_t mbytes = (int64_t)F * L / 2 + (int64_t)F * L / 32;
+    const int K = mat == MAT_DOWN ? F : L;
+    const uint8_t* m = blob + (int64_t)e * 3 * mbytes + mat * mbytes;
+    const int64_t row = 32 * pair + (lane & 31);
+    W32Record w;
+    w.c = m + row * (K / 2) + 16 * (lane >> 5);
+    w.s = m + (int64_t)(mat == MAT_DOWN ? L : F) * (K / 2) + row * (K / 32);
+    w.sh = 8 * (lane >> 5);
+    return w;
+  }
+  __device__ __forceinline__ W32Step step(int ks) const {
+    W32Step r;
+    const uint8_t* cs = c + 64 * ks;
+    r.q[0] = *reinterpret_cast<const uint4*>(cs);
+    r.q[1] = *reinterpret_cast<const uint4*>(cs + 32);
+    const uint32_t d = *reinterpret_cast<const uint32_t*>(s + 4 * ks);
+    r.s[0] = d >> sh;
+    r.s[1] = d >> (sh + 16);
+    return r;
+  }
+  static constexpr int opsel(int) { return 0; }
+};
+
+__device__ __forceinline__ i32x8 as_b32(const uint4& q) {
+  i32x8 b;
+  b[0] = (int)q.x; b[1] = (int)q.y; b[2] = (int)q.z; b[3] = (int)q.w;
+  b[4] = 0; b[5] = 0; b[6] = 0; b[7] = 0;
+  return b;
+}
+
+// activation operand of half-step hh of chunk step s, tile row m, for lane group g
+template <int TERMS, int R>
+__device__ __forceinline__ void gt32_read(i32x8& hi, i32x8& lo, uint32_t& shi, uint32_t& slo, const uint8_t* buf,
+                                          int s, int m, int g, int hh) {
+  const uint8_t* st = buf + s * gt_step_bytes(R);
+  const int c0 = 16 * ((4 * hh + g) ^ (m & 7)), c1 = 16 * ((4 * hh + 2 + g) ^ (m & 7));
+  const uint4 h0 = *reinterpret_cast<const uint4*>(st + m * GT_RS + c0);
+  const uint4 h1 = *reinterpret_cast<const uint4*>(st + m * GT_RS + c1);
+  hi[0] = (int)h0.x; hi[1] = (int)h0.y; hi[2] = (int)h0.z; hi[3] = (int)h0.w;
+  hi[4] = (int)h1.x; hi[5] = (int)h1.y; hi[6] = (int)h1.z; hi[7] = (int)h1.w;
+  shi = st[2 * R * GT_RS + m * 4 + 2 * hh + g];
+  if constexpr (TERMS == 2) {
+    const uint4 l0 = *reinterpret_cast<const uint4*>(st + R * GT_RS + m * GT_RS + c0);
+    const uint4 l1 = *reinterpret_cast<const uint4*>(st + R * GT_RS + m * GT_RS + c1);
+    lo[0] = (int)l0.x; lo[1] = (int)l0.y; lo[2] = (int)l0.z; lo[3] = (int)l0.w;
+    lo[4] = (int)l1.x; lo[5] = (int)l1.y; lo[6] = (int)l1.z; lo[7] = (int)l1.w;
+    slo = st[2 * R * GT_RS + R * 4 + m * 4 + 2 * hh + g];
+  }
+}
+
+// The K loop of one tile padded to R = 32 or 64 rows: acc[q][tt] += A(sub-tile tt) x W_q^T.
+// Every load is issued with clamped indices and only the math is guarded (see gt_mainloop).
+template <class W, int NMAT, int PF, int TERMS, int R>
+__device__ __forceinline__ void gt32_mainloop(const W (&w)[NMAT], const QRows& q, const int64_t* srow, int n, int K,
+                                              uint8_t* lds, f32x16 (&acc)[NMAT][R / 32]) {
+  constexpr int CH = GT_CHUNK_ROWSTEPS / R;
+  static_assert(16 % PF == 0 && 16 % CH == 0, "ring and chunks repeat every 16 steps");
+  const int lane = lane_id(), g = lane >> 5, nl = lane & 31;
+  const int nks = K / 128, nc = (nks + 15) / 16;
+  const int ntt = (n + 31) / 32;  // token sub-tiles holding rows
+  const GtThr<TERMS, R> thr = gt_thread<TERMS, R>(srow, K);
+  GtRegs<TERMS> rg;
+  gt_load<TERMS, R>(rg, q, thr, nks, 0);
+  W32Step ring[NMAT][PF];
+#pragma unroll
+  for (int d = 0; d < PF; ++d)
+#pragma unroll
+    for (int mq = 0; mq < NMAT; ++mq) ring[mq][d] = w[mq].step(d < nks ? d : nks - 1);
+  gt_store<TERMS, R>(rg, thr, lds);
+  gt_load<TERMS, R>(rg, q, thr, nks, 1);
+  lds_barrier();
+  for (int cb = 0; cb < nc; ++cb) {
+    unroll16([&](auto jc) {
+      constexpr int J = decltype(jc)::value;
+      const int ks = 16 * cb + J;
+      const int ch = ks / CH;
+      const uint8_t* buf = lds + (ch & 1) * GT_BUF_BYTES;
+      W32Step cw[NMAT];
+#pragma unroll
+      for (int mq = 0; mq < NMAT; ++mq) {
+        cw[mq] = ring[mq][J % PF];
+        ring[mq][J % PF] = w[mq].step(ks + PF < nks ? ks + PF : nks - 1);
+      }
+      if (ks < nks) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int tt = 0; tt < R / 32; ++tt) {
+            if (tt >= ntt) continue;  // token sub-tile past the tile's rows
+            i32x8 ahi, alo;
+            uint32_t shi, slo;
+            gt32_read<TERMS, R>(ahi, alo, shi, slo, buf, J % CH, 32 * tt + nl, g, hh);
+#pragma unroll
+            for (int mq = 0; mq < NMAT; ++mq) {
+              const i32x8 b = as_b32(cw[mq].q[hh]);
+              acc[mq][tt] = mx_mfma32<W::opsel(J)>(ahi, b, acc[mq][tt], shi, cw[mq].s[hh]);
+              if constexpr (TERMS == 2) acc[mq][tt] = mx_mfma32<W::opsel(J)>(alo, b, acc[mq][tt], slo, cw[mq].s[hh]);
+            }
+          }
+      }
+      if constexpr (J % CH == CH - 1) {
+        gt_store<TERMS, R>(rg, thr, lds + ((ch + 1) & 1) * GT_BUF_BYTES);
+        gt_load<TERMS, R>(rg, q, thr, nks, ch + 2);
+        lds_barrier();
+      }
+    });
+  }
+}
+
+// weight steps in flight per operand: deeper for 32-row tiles (half the accumulators)
+template <int TERMS, int R>
+constexpr int gt32_pf() { return R == 32 ? 4 : 2; }
+
+template <class W> struct W32Of;
+template <> struct W32Of<PackedW> { using type = W32Packed; };
+template <> struct W32Of<RecordW> { using type = W32Record; };
+
+constexpr int GT32_FROWS = 128;  // gate/up: F rows per block (4 waves x 32, gate and up)
+
+// Gate/up of one tile padded to R rows: the K loop, then a = bf16(silu(g) u) into an LDS
+// tile [64][GT32_FROWS + 1] (the activation buffers are free by then) and its two-term
+// requantisation into aq.
+template <class W, int TERMS, int R>
+__device__ __forceinline__ void gateup32_tile(const MxArgs& p, int e, int rt, int n, const int64_t* srow,
+                                              const int* sslot, uint8_t* lds) {
+  using WS = typename W32Of<W>::type;
+  const int F = p.F, L = p.L;
+  const int lane = lane_id(), wave = threadIdx.x / WAVE, g = lane >> 5, nl = lane & 31;
+  const int pair = rt * (GT32_FROWS / 32) + wave;
+  const WS w[2] = {WS::make(p.blob, e, L, F, MAT_GATE, pair, lane), WS::make(p.blob, e, L, F, MAT_UP, pair, lane)};
+  f32x16 acc[2][R / 32];
+#pragma unroll
+  for (int mq = 0; mq < 2; ++mq)
+#pragma unroll
+    for (int tt = 0; tt < R / 32; ++tt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[mq][tt][v] = 0.f;
+  gt32_mainloop<WS, 2, gt32_pf<TERMS, R>(), TERMS, R>(w, p.hq, srow, n, L, lds, acc);
+  __syncthreads();  // every wave is done with the activation buffers
+  float* at = reinterpret_cast<float*>(lds);  // [64 tokens][GT32_FROWS + 1]
+  constexpr int AS = GT32_FROWS + 1;
+  const int fl = 32 * wave + nl, f = rt * GT32_FROWS + fl;
+#pragma unroll
+  for (int tt = 0; tt < R / 32; ++tt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int m = 32 * tt + 8 * (v >> 2) + 4 * g + (v & 3);
+      if (m < n) {
+        const uint16_t ab = glu_bf16(acc[0][tt][v], acc[1][tt][v]);
+        at[m * AS + fl] = bf16f(ab);
+        if (p.a_bf16) p.a_bf16[(int64_t)sslot[m] * F + f] = ab;
+      }
+    }
+  __syncthreads();
+  for (int it = threadIdx.x; it < R * (GT32_FROWS / 8); it += blockDim.x) {
+    // a quad of lanes per (token, scale block): R tokens x 4 blocks x 4 lanes
+    const int m = it >> 4, blk = (it >> 2) & 3, sub = it & 3;
+    if (m < n) {
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = at[m * AS + 32 * blk + 8 * sub + i];
+      uint32_t hi[2], lo[2], shi, slo;
+      quantize_quad8_fmt(v, hi, lo, shi, slo, p.mxfp8 != 0);
+      const int64_t off = (int64_t)sslot[m] * F + rt * GT32_FROWS + 32 * blk + 8 * sub;
+      *reinterpret_cast<uint2*>(p.aq.hi + off) = make_uint2(hi[0], hi[1]);
+      *reinterpret_cast<uint2*>(p.aq.lo + off) = make_uint2(lo[0], lo[1]);
+      if (sub == 0) {
+        const int64_t soff = (int64_t)sslot[m] * (F / 32) + (rt * GT32_FROWS) / 32 + blk;
+        p.aq.shi[soff] = (uint8_t)shi;
+        p.aq.slo[soff] = (uint8_t)slo;
+      }
+    }
+  }
+}
+
+template <class W, int TERMS>
+__device__ __forceinline__ void gateup_gemm32_kernel_body(MxArgs p, const int4* __restrict__ gtiles, int ntiles,
+                                                          int nb) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  __shared__ int64_t srow[GT_TOK];
+  __shared__ int sslot[GT_TOK];
+  const int nrt = p.F / GT32_FROWS;
+  const int lb = gt_logical_block(blockIdx.x, nb);
+  int ti, rt;
+  gt_tile_of(lb, ntiles, nrt, ti, rt);
+  if (ti >= ntiles) return;  // the grid is rounded up to a multiple of 8
+  const int4 tile = gtiles[ti];
+  if (tile.x < 0) return;
+  const int e = tile.x, r0 = tile.y, n = tile.z;
+  for (int m = threadIdx.x; m < GT_TOK; m += blockDim.x) {
+    const int sl = m < n ? p.perm[r0 + m] : 0;
+    sslot[m] = sl;
+    srow[m] = sl / p.k;
+  }
+  __syncthreads();
+  if (n <= 32)
+    gateup32_tile<W, TERMS, 32>(p, e, rt, n, srow, sslot, lds);
+  else
+    gateup32_tile<W, TERMS, 64>(p, e, rt, n, srow, sslot, lds);
+}
+
+template <class W, int TERMS>
+__global__ void __launch_bounds__(256, 2) gateup_gemm32_kernel(MxArgs p, const int4* __restrict__ gtiles, int ntiles,
+                                                                int nb) {
+  clock_begin(p.clock);
+  gateup_gemm32_kernel_body<W, TERMS>(p, gtiles, ntiles, nb);
+  clock_end(p.clock);
+}
+
+// Down of one tile: y[slot][l] fp32.  Each wave holds NG 32-row groups of the down matrix
+// (groups 4 q + wave of the block's 4 NG), so a block covers 128 NG latent rows.
+template <class W, int TERMS, int NG, int R>
+__device__ __forceinline__ void down32_tile(const MxArgs& p, int e, int rt, int n, const int64_t* srow, uint8_t* lds) {
+  using WS = typename W32Of<W>::type;
+  const int F = p.F, L = p.L;
+  const int lane = lane_id(), wave = threadIdx.x / WAVE, g = lane >> 5, nl = lane & 31;
+  WS w[NG];
+#pragma unroll
+  for (int q = 0; q < NG; ++q) w[q] = WS::make(p.blob, e, L, F, MAT_DOWN, rt * 4 * NG + 4 * q + wave, lane);
+  f32x16 acc[NG][R / 32];
+#pragma unroll
+  for (int q = 0; q < NG; ++q)
+#pragma unroll
+    for (int tt = 0; tt < R / 32; ++tt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[q][tt][v] = 0.f;
+  gt32_mainloop<WS, NG, gt32_pf<TERMS, R>(), TERMS, R>(w, p.aq, srow, n, F, lds, acc);
+#pragma unroll
+  for (int q = 0; q < NG; ++q) {
+    const int l = (rt * 4 * NG + 4 * q + wave) * 32 + nl;
+#pragma unroll
+    for (int tt = 0; tt < R / 32; ++tt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = 32 * tt + 8 * (v >> 2) + 4 * g + (v & 3);
+        if (m < n) p.y[srow[m] * L + l] = acc[q][tt][v];
+      }
+  }
+}
+
+template <class W, int TERMS, int NG>
+__device__ __forceinline__ void down_gemm32_kernel_body(MxArgs p, const int4* __restrict__ gtiles, int ntiles,
+                                                        int nb) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  __shared__ int64_t srow[GT_TOK];
+  const int nrt = p.L / (128 * NG);
+  const int lb = gt_logical_block(blockIdx.x, nb);
+  int ti, rt;
+  gt_tile_of(lb, ntiles, nrt, ti, rt);
+  if (ti >= ntiles) return;  // the grid is rounded up to a multiple of 8
+  const int4 tile = gtiles[ti];
+  if (tile.x < 0) return;
+  const int e = tile.x, r0 = tile.y, n = tile.z;
+  for (int m = threadIdx.x; m < GT_TOK; m += blockDim.x) srow[m] = m < n ? p.perm[r0 + m] : 0;
+  __syncthreads();
+  if (n <= 32)
+    down32_tile<W, TERMS, NG, 32>(p, e, rt, n, srow, lds);
+  else
+    down32_tile<W, TERMS, NG, 64>(p, e, rt, n, srow, lds);
+}
+
+template <class W, int TERMS, int NG>
+__global__ void __launch_bounds__(256, 2) down_gemm32_kernel(MxArgs p, const int4* __restrict__ gtiles, int ntiles,
+                                                              int nb) {
+  clock_begin(p.clock);
+  down_gemm32_kernel_body<W, TERMS, NG>(p, gtiles, ntiles, nb);
+  clock_end(p.clock);
+}
+
 // Tiles of GT_TOK routed rows per active expert, in expert order: gtiles[0, ntiles) =
 // {expert, first row in perm, rows, 0}; gtiles[ntiles, max_gtiles) = {-1, 0, 0, 0}.
 __global__ void __launch_bounds__(1024) gemm_tiles_kernel(const int32_t* __restrict__ counts,
@@ -469,25 +813,57 @@ static hipError_t down_gemm_ng(const MxArgs& p, const int4* gtiles, int64_t max_
                  : down_gemm_go<RecordW, 2, NG>(p, gtiles, max_gtiles, nb, st, ev);
 }
 
+template <class W, int TERMS>
+static hipError_t gateup_gemm32_go(const MxArgs& p, const int4* gtiles, int64_t max_gtiles, int64_t nb,
+                                   hipStream_t st, const KernelEvents& ev) {
+  static const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gateup_gemm32_kernel<W, TERMS>),
+                                                  hipFuncAttributeMaxDynamicSharedMemorySize, 2 * GT_BUF_BYTES);
+  if (e != hipSuccess) return e;
+  return dispatch(ev, gateup_gemm32_kernel<W, TERMS>, dim3((unsigned)nb), dim3(256), 2 * GT_BUF_BYTES, st, p, gtiles,
+                  (int)max_gtiles, (int)nb);
+}
+
+template <class W, int TERMS, int NG>
+static hipError_t down_gemm32_go(const MxArgs& p, const int4* gtiles, int64_t max_gtiles, int64_t nb, hipStream_t st,
+                                 const KernelEvents& ev) {
+  static const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&down_gemm32_kernel<W, TERMS, NG>),
+                                                  hipFuncAttributeMaxDynamicSharedMemorySize, 2 * GT_BUF_BYTES);
+  if (e != hipSuccess) return e;
+  return dispatch(ev, down_gemm32_kernel<W, TERMS, NG>, dim3((unsigned)nb), dim3(256), 2 * GT_BUF_BYTES, st, p,
+                  gtiles, (int)max_gtiles, (int)nb);
+}
+
+template <int NG>
+static hipError_t down_gemm32_ng(const MxArgs& p, const int4* gtiles, int64_t max_gtiles, hipStream_t st,
+                                 const KernelEvents& ev) {
+  const int64_t nb = (max_gtiles * (p.L / (128 * NG)) + 7) / 8 * 8;
+  if (nb > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (p.packed)
+    return p.mxfp8 ? down_gemm32_go<PackedW, 1, NG>(p, gtiles, max_gtiles, nb, st, ev)
+                   : down_gemm32_go<PackedW, 2, NG>(p, gtiles, max_gtiles, nb, st, ev);
+  return p.mxfp8 ? down_gemm32_go<RecordW, 1, NG>(p, gtiles, max_gtiles, nb, st, ev)
+                 : down_gemm32_go<RecordW, 2, NG>(p, gtiles, max_gtiles, nb, st, ev);
+}
+
 hipError_t launch_gateup_gemm(const MxArgs& p, const int4* gtiles, int64_t max_gtiles, hipStream_t st,
                               const KernelEvents& ev) {
   if (p.T == 0) return hipSuccess;
-  if (p.F % GT_ROWS || p.L % 128) return hipErrorInvalidValue;
-  const int64_t nb = (max_gtiles * (p.F / GT_ROWS) + 7) / 8 * 8;
+  if (p.F % GT32_FROWS || p.L % 128) return hipErrorInvalidValue;
+  const int64_t nb = (max_gtiles * (p.F / GT32_FROWS) + 7) / 8 * 8;
   if (nb > 0x7FFFFFFF) return hipErrorInvalidValue;
   if (p.packed)
-    return p.mxfp8 ? gateup_gemm_go<PackedW, 1>(p, gtiles, max_gtiles, nb, st, ev)
-                   : gateup_gemm_go<PackedW, 2>(p, gtiles, max_gtiles, nb, st, ev);
-  return p.mxfp8 ? gateup_gemm_go<RecordW, 1>(p, gtiles, max_gtiles, nb, st, ev)
-                 : gateup_gemm_go<RecordW, 2>(p, gtiles, max_gtiles, nb, st, ev);
+    return p.mxfp8 ? gateup_gemm32_go<PackedW, 1>(p, gtiles, max_gtiles, nb, st, ev)
+                   : gateup_gemm32_go<PackedW, 2>(p, gtiles, max_gtiles, nb, st, ev);
+  return p.mxfp8 ? gateup_gemm32_go<RecordW, 1>(p, gtiles, max_gtiles, nb, st, ev)
+                 : gateup_gemm32_go<RecordW, 2>(p, gtiles, max_gtiles, nb, st, ev);
 }
 
 hipError_t launch_down_gemm(const MxArgs& p, const int4* gtiles, int64_t max_gtiles, hipStream_t st,
                             const KernelEvents& ev) {
   if (p.T == 0) return hipSuccess;
-  if (p.L % GT_ROWS || p.F % 128) return hipErrorInvalidValue;
-  return p.L % (2 * GT_ROWS) == 0 ? down_gemm_ng<2>(p, gtiles, max_gtiles, st, ev)
-                                  : down_gemm_ng<1>(p, gtiles, max_gtiles, st, ev);
+  if (p.L % 128 || p.F % 128) return hipErrorInvalidValue;
+  return p.L % 256 == 0 ? down_gemm32_ng<2>(p, gtiles, max_gtiles, st, ev)
+                        : down_gemm32_ng<1>(p, gtiles, max_gtiles, st, ev);
 }
 
 }  // namespace moe

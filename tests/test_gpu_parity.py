@@ -212,10 +212,11 @@ def test_expert_ffn(name, T):
     assert max(yerr) < 1e-3
 
 
-def test_expert_ffn_grouped_gemm_matches_streaming_kernels():
-    """The grouped GEMMs (8+ routed rows per expert on average) give the same bits as the
-    streaming kernels on the same rows: rows are independent and every K step feeds the
-    matrix cores the same operands in the same order."""
+def test_expert_ffn_grouped_gemm_and_streaming_kernels_against_the_oracle():
+    """The same routed rows through the streaming kernels (32 rows) and the grouped GEMMs
+    (96 rows: at least 8 per expert on average): the two run different matrix-core shapes
+    (16x16x128 against 32x32x64), so their fp32 sums differ in order; every row of both is
+    checked against the oracle, and the rows they share agree to the same tolerance."""
     c = synth.CONFIGS["tiny"]
     h = host_layer("tiny")
     dw = dev_weights("tiny")
@@ -226,15 +227,21 @@ def test_expert_ffn_grouped_gemm_matches_streaming_kernels():
                            want_a=True)   # 32 rows: streaming kernels
     big = moe.expert_ffn(to_dev(hl), dw["blob"], to_dev(idx), d_model=c.d, d_ffn=c.F, num_experts=c.E,
                          want_a=True)     # 96 rows: grouped GEMMs
-    assert np.array_equal(from_dev(small[0]), from_dev(big[0])[:32])
-    assert np.array_equal(from_dev(small[1]), from_dev(big[1])[:32])
+    ys, as_ = from_dev(small[0]), from_dev(small[1])
+    yb, ab = from_dev(big[0]), from_dev(big[1])
     rec = c.record_bytes
-    ya = from_dev(big[0])
-    for t in (0, 20, 47):
+    ulps = []
+    for t in range(48):
         for j in range(c.k):
-            e = int(idx[t, j])
-            _, wy = oracle.expert(hl[t], h["blob"][e * rec:(e + 1) * rec], c.L, c.F)
-            assert rel_l2(ya[t * c.k + j], wy) < 1e-3
+            e, r = int(idx[t, j]), t * c.k + j
+            wa, wy = oracle.expert(hl[t], h["blob"][e * rec:(e + 1) * rec], c.L, c.F)
+            assert rel_l2(yb[r], wy) < 1e-3, (t, j)
+            ulps.append(np.abs(ab[r].astype(np.int64) - wa.astype(np.int64)))
+            if t < 16:
+                assert rel_l2(ys[r], wy) < 1e-3, (t, j)
+                assert rel_l2(yb[r], ys[r]) < 1e-3, (t, j)
+    ulps = np.concatenate(ulps)
+    assert np.mean(ulps == 0) > 0.95 and np.mean(ulps <= 1) > 0.99
 
 
 @pytest.mark.parametrize("name,idx_rows", [
