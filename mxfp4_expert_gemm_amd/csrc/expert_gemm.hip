@@ -2,30 +2,36 @@
 //
 // When an expert holds many routed rows (prefill: about 73 per expert at 4096 tokens,
 // thousands on a popular expert), streaming its weights once per 4 rows as the decode
-// kernels do would read them dozens of times.  Here a block owns a tile of GT_TOK = 64
-// routed rows of one expert (the group's rows in perm order) times 64 weight rows, so
-// each weight byte is read once per 64 rows and every MFMA tile is full.
+// kernels do would read them dozens of times.  Here a block owns a tile of up to GT_TOK =
+// 64 routed rows of one expert (the group's rows in perm order) and a block of weight
+// rows, so each weight byte is read once per tile.
 //
-// Block: 4 waves; wave w streams weight rows 16w..16w+15 of the block's 64 (gate and up
-// for gate/up, down for down) straight from HBM with GT_PF steps in flight, and runs
-// one 16x16x128 MFMA tile per 16 routed rows of the tile, per matrix and per K step.
-// The activation tile (two-term e4m3, see quantize_quad8) moves through LDS in chunks of
-// 128 row-steps (two K steps of 64 rows, four of 32, eight of 16), double-buffered: the
-// loads of chunk c+1 are in registers while chunk c is computed, and one barrier per
-// chunk hands the buffers over.
+// The products run on v_mfma_scale_f32_32x32x64_f8f6f4: the FP8 operand is a 32-row token
+// sub-tile of the activations (two exact e4m3 terms, see quantize_quad8), the FP4 operand
+// 32 weight rows as stored, each with its e8m0 scales.  Operand layout, measured on gfx950
+// with exact small-integer operands: lane l works on row/column l%32 and g = l/32; the
+// FP8 operand holds K = 16g..16g+15 in registers 0-3 and 32+16g..32+16g+15 in registers
+// 4-7; the FP4 operand holds K = 32g..32g+31 (low nibble first); lane r + 32b supplies the
+// scale of row/column r for K block b; result register v of lane l is
+// D[8(v/4) + 4g + v%4][l%32].  One such product does twice the work of the 16x16x128 form
+// per operand byte read.
+//
+// Block: 4 waves.  A wave owns 32 weight rows of each of its two matrices (gate and up,
+// or two 32-row groups of down) and the tile's 32-row token sub-tiles; a K step of 128 is
+// two half-steps of 64.  Weight operands are loaded per wave straight from memory into
+// registers, PF steps ahead; the activation tile moves through LDS in chunks of 128
+// row-steps (two K steps of 64 rows, four of 32), double-buffered: the loads of chunk c+1
+// are in registers while chunk c is computed, and one barrier per chunk hands the buffers
+// over.  Two blocks share a CU.
 //
 // The grid is ordered so that each XCD (blocks b with the same b mod 8) works through a
-// contiguous range of tiles: the tiles of one expert, and the 48 (or 56) weight-row
-// blocks of one token tile, meet in the same L2.
-//
-// Numerics are those of the decode kernels: identical operands per K step and the same
-// fp32 accumulation order, so gate/up and down give bit-identical results to them.
+// contiguous range of tiles: the tiles of one expert, and the row blocks of one token
+// tile, meet in the same L2.
 #include "mfma_stream.h"
 
 namespace moe {
 
 constexpr int GT_TOK = 64;    // routed rows per tile
-constexpr int GT_ROWS = 64;   // weight rows per block (4 waves x 16)
 constexpr int GT_RS = 128;    // LDS row of a step's 128 code bytes, 16-byte chunk c at c ^ (row & 7)
 // The activation tile moves through LDS in chunks of GT_CHUNK_ROWSTEPS rows x steps: a
 // tile padded to R = 16, 32 or 64 rows stages 128 / R K steps per chunk, so a tile with
@@ -40,14 +46,6 @@ constexpr int GT_BUF_BYTES = (GT_CHUNK_ROWSTEPS / GT_TOK) * gt_step_bytes(GT_TOK
 static_assert((GT_CHUNK_ROWSTEPS / 16) * gt_step_bytes(16) == GT_BUF_BYTES &&
                   (GT_CHUNK_ROWSTEPS / 32) * gt_step_bytes(32) == GT_BUF_BYTES,
               "every chunk shape fills the same buffer");
-// K steps of weights in flight per wave and matrix, per tile height: as deep as the
-// registers allow (fewer token sub-tiles hold fewer accumulators; the one-term kernels
-// hold half the activation operands)
-template <int TERMS, int R>
-constexpr int gt_pf_gateup() { return R == 16 ? 8 : R == 32 ? 4 : TERMS == 2 ? 2 : 4; }
-template <int TERMS, int R>
-constexpr int gt_pf_down() { return R == 64 ? (TERMS == 2 ? 4 : 8) : 8; }
-
 // This thread's share of one chunk: 4 TERMS 16-byte code pieces and one scale dword.
 // TERMS = 2: the two exact e4m3 terms of bf16 activations; TERMS = 1: the MXFP8 mode,
 // whose second term is zero and is neither moved nor multiplied.
@@ -146,25 +144,6 @@ __device__ __forceinline__ void gt_store(const GtRegs<TERMS>& r, const GtThr<TER
   if (TERMS == 2 || threadIdx.x < 128) *reinterpret_cast<uint32_t*>(buf + t.sdst) = r.s;
 }
 
-// activation operand of step s of a chunk for tile row m (chunks g and 4 + g of the row)
-template <int TERMS, int R>
-__device__ __forceinline__ void gt_read(AStep& a, const uint8_t* buf, int s, int m, int g) {
-  const uint8_t* st = buf + s * gt_step_bytes(R);
-  const int c0 = 16 * (g ^ (m & 7)), c1 = 16 * ((4 + g) ^ (m & 7));
-  const uint4 h0 = *reinterpret_cast<const uint4*>(st + m * GT_RS + c0);
-  const uint4 h1 = *reinterpret_cast<const uint4*>(st + m * GT_RS + c1);
-  a.hi[0] = (int)h0.x; a.hi[1] = (int)h0.y; a.hi[2] = (int)h0.z; a.hi[3] = (int)h0.w;
-  a.hi[4] = (int)h1.x; a.hi[5] = (int)h1.y; a.hi[6] = (int)h1.z; a.hi[7] = (int)h1.w;
-  a.shi = st[2 * R * GT_RS + m * 4 + g];
-  if constexpr (TERMS == 2) {
-    const uint4 l0 = *reinterpret_cast<const uint4*>(st + R * GT_RS + m * GT_RS + c0);
-    const uint4 l1 = *reinterpret_cast<const uint4*>(st + R * GT_RS + m * GT_RS + c1);
-    a.lo[0] = (int)l0.x; a.lo[1] = (int)l0.y; a.lo[2] = (int)l0.z; a.lo[3] = (int)l0.w;
-    a.lo[4] = (int)l1.x; a.lo[5] = (int)l1.y; a.lo[6] = (int)l1.z; a.lo[7] = (int)l1.w;
-    a.slo = st[2 * R * GT_RS + R * 4 + m * 4 + g];
-  }
-}
-
 // logical block of physical block b: XCD x = b mod 8 runs logical blocks
 // x * nb/8 .. (x+1) * nb/8 - 1 (nb a multiple of 8)
 __device__ __forceinline__ int gt_logical_block(int b, int nb) { return (b & 7) * (nb >> 3) + (b >> 3); }
@@ -190,227 +169,7 @@ __device__ __forceinline__ void gt_tile_of(int lb, int ntiles, int nrt, int& ti,
   }
 }
 
-// The K loop of one tile padded to R rows: acc[q][tt] += A(token sub-tile tt) x W_q^T over
-// all K steps.  The loop runs over whole 16-step blocks; steps past the end issue their
-// (clamped) loads, stores and barriers like the others and skip only the math, so every
-// path issues the same loads and the waits for them are exact.
-template <class W, int NMAT, int GT_PF, int TERMS, int R>
-__device__ __forceinline__ void gt_mainloop(const W (&w)[NMAT], const QRows& q, const int64_t* srow, int n, int K,
-                                            uint8_t* lds, f32x4 (&acc)[NMAT][4]) {
-  constexpr int CH = GT_CHUNK_ROWSTEPS / R;
-  static_assert(16 % GT_PF == 0 && 16 % CH == 0, "ring and chunks repeat every 16 steps");
-  const int lane = lane_id(), g = lane >> 4, nl = lane & 15;
-  const int nks = K / 128, nc = (nks + 15) / 16;
-  const int ntt = (n + 15) / 16;  // token sub-tiles holding rows
-  // chunk 0 into buffer 0, chunk 1 into registers, the first weight steps in flight
-  const GtThr<TERMS, R> thr = gt_thread<TERMS, R>(srow, K);
-  GtRegs<TERMS> rg;
-  gt_load<TERMS, R>(rg, q, thr, nks, 0);
-  SBlock sb[NMAT], sbn[NMAT];
-  uint4 ring[NMAT][GT_PF];
-  prime_stream<W, NMAT, GT_PF>(w, sb, ring, nks);
-  gt_store<TERMS, R>(rg, thr, lds);
-  gt_load<TERMS, R>(rg, q, thr, nks, 1);
-  lds_barrier();
-  for (int cb = 0; cb < nc; ++cb) {
-#pragma unroll
-    for (int mq = 0; mq < NMAT; ++mq) w[mq].sblock(sbn[mq], cb + 1 < nc ? cb + 1 : cb);
-    unroll16([&](auto jc) {
-      constexpr int J = decltype(jc)::value;
-      const int ks = 16 * cb + J;
-      const int ch = ks / CH;
-      const uint8_t* buf = lds + (ch & 1) * GT_BUF_BYTES;
-      uint4 cw[NMAT];
-#pragma unroll
-      for (int mq = 0; mq < NMAT; ++mq) {
-        cw[mq] = ring[mq][J % GT_PF];
-        ring[mq][J % GT_PF] = w[mq].load(ks + GT_PF < nks ? ks + GT_PF : nks - 1);
-      }
-      if (ks < nks) {
-#pragma unroll
-        for (int tt = 0; tt < R / 16; ++tt) {
-          if (tt >= ntt) continue;  // token sub-tile past the tile's rows
-          AStep a;
-          gt_read<TERMS, R>(a, buf, J % CH, 16 * tt + nl, g);
-#pragma unroll
-          for (int mq = 0; mq < NMAT; ++mq) {
-            const uint32_t sw = w[mq].template scale<J>(sb[mq]);
-            const i32x8 b = as_b(cw[mq]);
-            acc[mq][tt] = mx_mfma<W::opsel(J)>(a.hi, b, acc[mq][tt], a.shi, sw);
-            if constexpr (TERMS == 2) acc[mq][tt] = mx_mfma<W::opsel(J)>(a.lo, b, acc[mq][tt], a.slo, sw);
-          }
-        }
-      }
-      if constexpr (J % CH == CH - 1) {
-        // end of chunk ch: the registers hold chunk ch+1; every wave is past chunk ch-1,
-        // so its buffer is free
-        gt_store<TERMS, R>(rg, thr, lds + ((ch + 1) & 1) * GT_BUF_BYTES);
-        gt_load<TERMS, R>(rg, q, thr, nks, ch + 2);
-        lds_barrier();
-      }
-    });
-#pragma unroll
-    for (int mq = 0; mq < NMAT; ++mq) sb[mq] = sbn[mq];
-  }
-}
-
-// the K loop for a tile of n rows, in the chunk shape of its height
-template <class W, int NMAT, int TERMS, bool GATEUP>
-__device__ __forceinline__ void gt_mainloop_any(const W (&w)[NMAT], const QRows& q, const int64_t* srow, int n,
-                                                int K, uint8_t* lds, f32x4 (&acc)[NMAT][4]) {
-  if (n <= 16)
-    gt_mainloop<W, NMAT, GATEUP ? gt_pf_gateup<TERMS, 16>() : gt_pf_down<TERMS, 16>(), TERMS, 16>(w, q, srow, n, K,
-                                                                                                  lds, acc);
-  else if (n <= 32)
-    gt_mainloop<W, NMAT, GATEUP ? gt_pf_gateup<TERMS, 32>() : gt_pf_down<TERMS, 32>(), TERMS, 32>(w, q, srow, n, K,
-                                                                                                  lds, acc);
-  else
-    gt_mainloop<W, NMAT, GATEUP ? gt_pf_gateup<TERMS, 64>() : gt_pf_down<TERMS, 64>(), TERMS, 64>(w, q, srow, n, K,
-                                                                                                  lds, acc);
-}
-
-// Gate/up with the GLU: a = bf16(silu(g) u) for the tile, re-quantised to two e4m3 terms
-// into aq (routed-row order), optionally also as bf16.
-template <class W, int TERMS>
-__device__ __forceinline__ void gateup_gemm_kernel_body(MxArgs p, const int4* __restrict__ gtiles, int ntiles,
-                                                        int nb) {
-  extern __shared__ __align__(16) uint8_t lds[];
-  __shared__ int64_t srow[GT_TOK];
-  __shared__ int sslot[GT_TOK];
-  const int F = p.F, L = p.L, nrt = F / GT_ROWS;
-  const int lb = gt_logical_block(blockIdx.x, nb);
-  int ti, rt;
-  gt_tile_of(lb, ntiles, nrt, ti, rt);
-  if (ti >= ntiles) return;  // the grid is rounded up to a multiple of 8
-  const int4 tile = gtiles[ti];
-  if (tile.x < 0) return;
-  const int e = tile.x, r0 = tile.y, n = tile.z;
-  const int lane = lane_id(), wave = threadIdx.x / WAVE, g = lane >> 4, nl = lane & 15;
-  for (int m = threadIdx.x; m < GT_TOK; m += blockDim.x) {
-    const int sl = m < n ? p.perm[r0 + m] : 0;
-    sslot[m] = sl;
-    srow[m] = sl / p.k;
-  }
-  __syncthreads();
-  const W w[2] = {W::make(p.blob, e, L, F, MAT_GATE, rt * 4 + wave, lane),
-                  W::make(p.blob, e, L, F, MAT_UP, rt * 4 + wave, lane)};
-  f32x4 acc[2][4];
-#pragma unroll
-  for (int mq = 0; mq < 2; ++mq)
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) acc[mq][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  gt_mainloop_any<W, 2, TERMS, true>(w, p.hq, srow, n, L, lds, acc);
-  // GLU into an LDS tile (the activation buffers are free now), then the requantisation
-  float* at = reinterpret_cast<float*>(lds);  // [64 tokens][65]
-  const int f = rt * GT_ROWS + 16 * wave + nl;
-#pragma unroll
-  for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int m = 16 * tt + 4 * g + j;
-      if (m < n) {
-        const uint16_t ab = glu_bf16(acc[0][tt][j], acc[1][tt][j]);
-        at[m * 65 + 16 * wave + nl] = bf16f(ab);
-        if (p.a_bf16) p.a_bf16[(int64_t)sslot[m] * F + f] = ab;
-      }
-    }
-  __syncthreads();
-  for (int it = threadIdx.x; it < GT_TOK * 8; it += blockDim.x) {
-    // a quad of lanes per (token, scale block): 64 tokens x 2 blocks x 4 lanes
-    const int m = it >> 3, blk = (it >> 2) & 1, sub = it & 3;
-    if (m < n) {
-      float v[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = at[m * 65 + 32 * blk + 8 * sub + i];
-      uint32_t hi[2], lo[2], shi, slo;
-      quantize_quad8_fmt(v, hi, lo, shi, slo, p.mxfp8 != 0);
-      const int64_t off = (int64_t)sslot[m] * F + rt * GT_ROWS + 32 * blk + 8 * sub;
-      *reinterpret_cast<uint2*>(p.aq.hi + off) = make_uint2(hi[0], hi[1]);
-      *reinterpret_cast<uint2*>(p.aq.lo + off) = make_uint2(lo[0], lo[1]);
-      if (sub == 0) {
-        const int64_t soff = (int64_t)sslot[m] * (F / 32) + (rt * GT_ROWS) / 32 + blk;
-        p.aq.shi[soff] = (uint8_t)shi;
-        p.aq.slo[soff] = (uint8_t)slo;
-      }
-    }
-  }
-}
-
-template <class W, int TERMS>
-__global__ void __launch_bounds__(256, 2) gateup_gemm_kernel(MxArgs p, const int4* __restrict__ gtiles, int ntiles,
-                                                              int nb) {
-  clock_begin(p.clock);
-  gateup_gemm_kernel_body<W, TERMS>(p, gtiles, ntiles, nb);
-  clock_end(p.clock);
-}
-
-// Down: y[slot][l] fp32 for the tile's routed rows.  Each wave streams NG row groups of
-// 16 (groups 4 q + wave of the block's 4 NG, q < NG), so every activation operand read
-// from LDS feeds NG weight tiles: with NG = 2 (latent width a multiple of 128) a block
-// covers 128 latent rows, the LDS operand traffic per MFMA halves and each activation
-// chunk feeds twice the matrix-core work, the register profile of the gate/up kernel.
-template <class W, int TERMS, int NG>
-__device__ __forceinline__ void down_gemm_kernel_body(MxArgs p, const int4* __restrict__ gtiles, int ntiles,
-                                                      int nb) {
-  extern __shared__ __align__(16) uint8_t lds[];
-  __shared__ int64_t srow[GT_TOK];
-  constexpr int ROWS = GT_ROWS * NG;
-  const int F = p.F, L = p.L, nrt = L / ROWS;
-  const int lb = gt_logical_block(blockIdx.x, nb);
-  int ti, rt;
-  gt_tile_of(lb, ntiles, nrt, ti, rt);
-  if (ti >= ntiles) return;  // the grid is rounded up to a multiple of 8
-  const int4 tile = gtiles[ti];
-  if (tile.x < 0) return;
-  const int e = tile.x, r0 = tile.y, n = tile.z;
-  const int lane = lane_id(), wave = threadIdx.x / WAVE, g = lane >> 4, nl = lane & 15;
-  for (int m = threadIdx.x; m < GT_TOK; m += blockDim.x) srow[m] = m < n ? p.perm[r0 + m] : 0;
-  __syncthreads();
-  W w[NG];
-#pragma unroll
-  for (int q = 0; q < NG; ++q) w[q] = W::make(p.blob, e, L, F, MAT_DOWN, rt * 4 * NG + 4 * q + wave, lane);
-  f32x4 acc[NG][4];
-#pragma unroll
-  for (int q = 0; q < NG; ++q)
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) acc[q][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  gt_mainloop_any<W, NG, TERMS, NG == 2>(w, p.aq, srow, n, F, lds, acc);
-#pragma unroll
-  for (int q = 0; q < NG; ++q) {
-    const int l = rt * ROWS + GT_ROWS * q + 16 * wave + nl;
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int m = 16 * tt + 4 * g + j;
-        if (m < n) p.y[srow[m] * L + l] = acc[q][tt][j];
-      }
-  }
-}
-
-template <class W, int TERMS, int NG>
-__global__ void __launch_bounds__(256, 2) down_gemm_kernel(MxArgs p, const int4* __restrict__ gtiles, int ntiles,
-                                                            int nb) {
-  clock_begin(p.clock);
-  down_gemm_kernel_body<W, TERMS, NG>(p, gtiles, ntiles, nb);
-  clock_end(p.clock);
-}
-
-// ---------------------------------------------------- 32x32x64 grouped GEMMs
-//
-// The same tiles (up to 64 routed rows of one expert) on v_mfma_scale_f32_32x32x64_f8f6f4,
-// which does twice the work of the 16x16x128 form per operand byte: each activation
-// operand read from LDS and each weight operand loaded from memory feeds twice the
-// matrix-core work.  Operand layout (measured on gfx950 with exact small-integer
-// operands): lane l works on row/column l%32 and g = l/32; the FP8 operand holds
-// K = 16g..16g+15 in registers 0-3 and 32+16g..32+16g+15 in registers 4-7; the FP4
-// operand holds K = 32g..32g+31 (low nibble first); lane r + 32b supplies the scale of
-// row/column r for K block b; result register v of lane l is D[8(v/4) + 4g + v%4][l%32].
-//
-// A wave owns 32 weight rows of each of NMAT matrices (gate and up, or two 32-row groups
-// of down) and the tile's token sub-tiles of 32 rows; a K step of 128 is two half-steps
-// of 64.  Weight operands are loaded per wave from memory straight into registers, PF
-// steps ahead; the activation tile moves through LDS in the chunks of the kernels above.
+// ------------------------------------------------------------ operands
 
 template <int N>
 using f32xN = float __attribute__((ext_vector_type(N)));
@@ -422,21 +181,23 @@ __device__ __forceinline__ f32x16 mx_mfma32(const i32x8& a, const i32x8& b, f32x
                                                          OPSEL_B, (int)sb);
 }
 
-// One K step of one 32-row weight operand: the codes of the two half-steps and their
-// scale words (the scale byte is chosen by opsel(step) or already in the low byte).
+// One K step of one 32-row weight operand: the codes of the two half-steps.
 struct W32Step {
   uint4 q[2];
-  uint32_t s[2];
 };
 
 // Packed layout: 32 weight rows are two 16-row groups; in group x, the 1024-byte code
 // tile of step s holds row r%16, K block kb at bytes 16 (r%16 + 16 kb).  Lane l takes
 // group (l%32)/16, row l%16, K block 2 hh + l/32 of the step: two 512-byte runs per load.
-// Scale tile t (256 bytes) holds, at byte 4 (r%16 + 16 kb) + j, step 4 t + j.
+// Scale tile t (256 bytes) holds, at byte 4 (r%16 + 16 kb) + j, step 4 t + j: one dword
+// per half-step serves four steps (the instruction's scale select picks the byte).
 struct W32Packed {
   const uint8_t* c;
   const uint8_t* s;
   int nsc;
+  struct Scales {
+    uint32_t d[2];  // half-steps 0 and 1 of steps 4 G .. 4 G + 3
+  };
   __device__ static W32Packed make(const uint8_t* blob, int e, int L, int F, int mat, int pair, int lane) {
     const int K = mat == MAT_DOWN ? F : L;
     const int64_t gu = (int64_t)(F / 16) * packed_group_bytes(L);
@@ -455,21 +216,28 @@ struct W32Packed {
     const uint8_t* cs = c + 1024 * ks;
     r.q[0] = *reinterpret_cast<const uint4*>(cs);
     r.q[1] = *reinterpret_cast<const uint4*>(cs + 512);
-    const uint8_t* ss = s + 256 * (ks >> 2);
-    r.s[0] = *reinterpret_cast<const uint32_t*>(ss);
-    r.s[1] = *reinterpret_cast<const uint32_t*>(ss + 128);
     return r;
   }
+  // the scales of steps 4 G .. 4 G + 3 (G < nsc)
+  __device__ __forceinline__ Scales group(int G) const {
+    const uint8_t* ss = s + 256 * G;
+    return Scales{{*reinterpret_cast<const uint32_t*>(ss), *reinterpret_cast<const uint32_t*>(ss + 128)}};
+  }
+  template <int J>
+  __device__ __forceinline__ static uint32_t scale(const Scales& sc, int hh) { return sc.d[hh]; }
   static constexpr int opsel(int j) { return j & 3; }
 };
 
 // Checkpoint record: row 32 pair + l%32, K block 4 s + 2 hh + l/32 of step s is bytes
-// 64 s + 32 hh + 16 (l/32) of the row's codes; its scale is byte 4 s + 2 hh + l/32 of
-// the row's scales, moved to the low byte.
+// 64 s + 32 hh + 16 (l/32) of the row's codes; its scale is byte 4 s + 2 hh + l/32 of the
+// row's scales, moved to the low byte (one dword per step).
 struct W32Record {
   const uint8_t* c;
   const uint8_t* s;
   int sh;  // 8 x (l/32)
+  struct Scales {
+    uint32_t d[4];  // steps 4 G .. 4 G + 3: the four K-block scales of each
+  };
   __device__ static W32Record make(const uint8_t* blob, int e, int L, int F, int mat, int pair, int lane) {
     const int64_t mbytes = (int64_t)F * L / 2 + (int64_t)F * L / 32;
     const int K = mat == MAT_DOWN ? F : L;
@@ -486,13 +254,35 @@ struct W32Record {
     const uint8_t* cs = c + 64 * ks;
     r.q[0] = *reinterpret_cast<const uint4*>(cs);
     r.q[1] = *reinterpret_cast<const uint4*>(cs + 32);
-    const uint32_t d = *reinterpret_cast<const uint32_t*>(s + 4 * ks);
-    r.s[0] = d >> sh;
-    r.s[1] = d >> (sh + 16);
     return r;
   }
+  // the scales of steps 4 G .. 4 G + 3; a step past the last (K / 128 not a multiple of 4)
+  // re-reads the last one and is never used
+  __device__ __forceinline__ Scales group(int G, int nks) const {
+    Scales r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ks = 4 * G + i < nks ? 4 * G + i : nks - 1;
+      r.d[i] = *reinterpret_cast<const uint32_t*>(s + 4 * ks);
+    }
+    return r;
+  }
+  template <int J>
+  __device__ __forceinline__ uint32_t scale(const Scales& sc, int hh) const { return sc.d[J & 3] >> (sh + 16 * hh); }
   static constexpr int opsel(int) { return 0; }
 };
+
+template <class W>
+__device__ __forceinline__ typename W::Scales w32_group(const W& w, int G, int nks);
+template <>
+__device__ __forceinline__ W32Packed::Scales w32_group(const W32Packed& w, int G, int nks) {
+  return w.group(G < w.nsc ? G : w.nsc - 1);
+}
+template <>
+__device__ __forceinline__ W32Record::Scales w32_group(const W32Record& w, int G, int nks) {
+  const int ng = (nks + 3) / 4;
+  return w.group(G < ng ? G : ng - 1, nks);
+}
 
 __device__ __forceinline__ i32x8 as_b32(const uint4& q) {
   i32x8 b;
@@ -522,7 +312,8 @@ __device__ __forceinline__ void gt32_read(i32x8& hi, i32x8& lo, uint32_t& shi, u
 }
 
 // The K loop of one tile padded to R = 32 or 64 rows: acc[q][tt] += A(sub-tile tt) x W_q^T.
-// Every load is issued with clamped indices and only the math is guarded (see gt_mainloop).
+// Every load is issued with clamped indices and only the math is guarded, so the loads in
+// flight are the same on every path and the compiler's waits for them are exact.
 template <class W, int NMAT, int PF, int TERMS, int R>
 __device__ __forceinline__ void gt32_mainloop(const W (&w)[NMAT], const QRows& q, const int64_t* srow, int n, int K,
                                               uint8_t* lds, f32x16 (&acc)[NMAT][R / 32]) {
@@ -539,15 +330,24 @@ __device__ __forceinline__ void gt32_mainloop(const W (&w)[NMAT], const QRows& q
   for (int d = 0; d < PF; ++d)
 #pragma unroll
     for (int mq = 0; mq < NMAT; ++mq) ring[mq][d] = w[mq].step(d < nks ? d : nks - 1);
+  // scales in groups of 4 steps, the next group loaded at the start of the current one
+  typename W::Scales sc[NMAT][2];
+#pragma unroll
+  for (int mq = 0; mq < NMAT; ++mq) sc[mq][0] = w32_group(w[mq], 0, nks);
   gt_store<TERMS, R>(rg, thr, lds);
   gt_load<TERMS, R>(rg, q, thr, nks, 1);
   lds_barrier();
   for (int cb = 0; cb < nc; ++cb) {
     unroll16([&](auto jc) {
       constexpr int J = decltype(jc)::value;
+      constexpr int SG = (J >> 2) & 1;  // parity of the step's scale group (4 groups per 16 steps)
       const int ks = 16 * cb + J;
       const int ch = ks / CH;
       const uint8_t* buf = lds + (ch & 1) * GT_BUF_BYTES;
+      if constexpr ((J & 3) == 0) {
+#pragma unroll
+        for (int mq = 0; mq < NMAT; ++mq) sc[mq][SG ^ 1] = w32_group(w[mq], (ks >> 2) + 1, nks);
+      }
       W32Step cw[NMAT];
 #pragma unroll
       for (int mq = 0; mq < NMAT; ++mq) {
@@ -566,8 +366,9 @@ __device__ __forceinline__ void gt32_mainloop(const W (&w)[NMAT], const QRows& q
 #pragma unroll
             for (int mq = 0; mq < NMAT; ++mq) {
               const i32x8 b = as_b32(cw[mq].q[hh]);
-              acc[mq][tt] = mx_mfma32<W::opsel(J)>(ahi, b, acc[mq][tt], shi, cw[mq].s[hh]);
-              if constexpr (TERMS == 2) acc[mq][tt] = mx_mfma32<W::opsel(J)>(alo, b, acc[mq][tt], slo, cw[mq].s[hh]);
+              const uint32_t sw = w[mq].template scale<J>(sc[mq][SG], hh);
+              acc[mq][tt] = mx_mfma32<W::opsel(J)>(ahi, b, acc[mq][tt], shi, sw);
+              if constexpr (TERMS == 2) acc[mq][tt] = mx_mfma32<W::opsel(J)>(alo, b, acc[mq][tt], slo, sw);
             }
           }
       }
@@ -609,9 +410,10 @@ __device__ __forceinline__ void gateup32_tile(const MxArgs& p, int e, int rt, in
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[mq][tt][v] = 0.f;
   gt32_mainloop<WS, 2, gt32_pf<TERMS, R>(), TERMS, R>(w, p.hq, srow, n, L, lds, acc);
-  __syncthreads();  // every wave is done with the activation buffers
+  lds_barrier();  // the activation buffers are free (the weight loads still in flight are not needed)
   float* at = reinterpret_cast<float*>(lds);  // [64 tokens][GT32_FROWS + 1]
   constexpr int AS = GT32_FROWS + 1;
+  uint8_t* sc = lds + 64 * AS * 4;           // scale bytes [term][64 tokens][4 blocks]
   const int fl = 32 * wave + nl, f = rt * GT32_FROWS + fl;
 #pragma unroll
   for (int tt = 0; tt < R / 32; ++tt)
@@ -624,7 +426,7 @@ __device__ __forceinline__ void gateup32_tile(const MxArgs& p, int e, int rt, in
         if (p.a_bf16) p.a_bf16[(int64_t)sslot[m] * F + f] = ab;
       }
     }
-  __syncthreads();
+  lds_barrier();
   for (int it = threadIdx.x; it < R * (GT32_FROWS / 8); it += blockDim.x) {
     // a quad of lanes per (token, scale block): R tokens x 4 blocks x 4 lanes
     const int m = it >> 4, blk = (it >> 2) & 3, sub = it & 3;
@@ -638,10 +440,19 @@ __device__ __forceinline__ void gateup32_tile(const MxArgs& p, int e, int rt, in
       *reinterpret_cast<uint2*>(p.aq.hi + off) = make_uint2(hi[0], hi[1]);
       *reinterpret_cast<uint2*>(p.aq.lo + off) = make_uint2(lo[0], lo[1]);
       if (sub == 0) {
-        const int64_t soff = (int64_t)sslot[m] * (F / 32) + (rt * GT32_FROWS) / 32 + blk;
-        p.aq.shi[soff] = (uint8_t)shi;
-        p.aq.slo[soff] = (uint8_t)slo;
+        sc[m * 4 + blk] = (uint8_t)shi;
+        sc[256 + m * 4 + blk] = (uint8_t)slo;
       }
+    }
+  }
+  lds_barrier();
+  // the 4 scale bytes of a token and term in one store
+  if (threadIdx.x < 2 * R) {
+    const int m = threadIdx.x >> 1, term = threadIdx.x & 1;
+    if (m < n) {
+      const int64_t soff = (int64_t)sslot[m] * (F / 32) + (rt * GT32_FROWS) / 32;
+      *reinterpret_cast<uint32_t*>((term ? p.aq.slo : p.aq.shi) + soff) =
+          *reinterpret_cast<const uint32_t*>(sc + 256 * term + 4 * m);
     }
   }
 }
@@ -779,38 +590,6 @@ hipError_t launch_gemm_tiles(const int32_t* counts, const int32_t* offsets, int3
   if (E > 16 * 1024) return hipErrorInvalidValue;
   hipLaunchKernelGGL(gemm_tiles_kernel, dim3(1), dim3(1024), 0, st, counts, offsets, E, gtiles, (int)max_gtiles);
   return hipGetLastError();
-}
-
-template <class W, int TERMS>
-static hipError_t gateup_gemm_go(const MxArgs& p, const int4* gtiles, int64_t max_gtiles, int64_t nb, hipStream_t st,
-                                 const KernelEvents& ev) {
-  static const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gateup_gemm_kernel<W, TERMS>),
-                                                  hipFuncAttributeMaxDynamicSharedMemorySize, 2 * GT_BUF_BYTES);
-  if (e != hipSuccess) return e;
-  return dispatch(ev, gateup_gemm_kernel<W, TERMS>, dim3((unsigned)nb), dim3(256), 2 * GT_BUF_BYTES, st, p, gtiles,
-                  (int)max_gtiles, (int)nb);
-}
-
-template <class W, int TERMS, int NG>
-static hipError_t down_gemm_go(const MxArgs& p, const int4* gtiles, int64_t max_gtiles, int64_t nb, hipStream_t st,
-                               const KernelEvents& ev) {
-  static const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&down_gemm_kernel<W, TERMS, NG>),
-                                                  hipFuncAttributeMaxDynamicSharedMemorySize, 2 * GT_BUF_BYTES);
-  if (e != hipSuccess) return e;
-  return dispatch(ev, down_gemm_kernel<W, TERMS, NG>, dim3((unsigned)nb), dim3(256), 2 * GT_BUF_BYTES, st, p, gtiles,
-                  (int)max_gtiles, (int)nb);
-}
-
-template <int NG>
-static hipError_t down_gemm_ng(const MxArgs& p, const int4* gtiles, int64_t max_gtiles, hipStream_t st,
-                               const KernelEvents& ev) {
-  const int64_t nb = (max_gtiles * (p.L / (GT_ROWS * NG)) + 7) / 8 * 8;
-  if (nb > 0x7FFFFFFF) return hipErrorInvalidValue;
-  if (p.packed)
-    return p.mxfp8 ? down_gemm_go<PackedW, 1, NG>(p, gtiles, max_gtiles, nb, st, ev)
-                   : down_gemm_go<PackedW, 2, NG>(p, gtiles, max_gtiles, nb, st, ev);
-  return p.mxfp8 ? down_gemm_go<RecordW, 1, NG>(p, gtiles, max_gtiles, nb, st, ev)
-                 : down_gemm_go<RecordW, 2, NG>(p, gtiles, max_gtiles, nb, st, ev);
 }
 
 template <class W, int TERMS>

@@ -176,14 +176,23 @@ __device__ __forceinline__ void read_a(AStep& a, const ALds& d, int m, int ntok,
   }
 }
 
-// a = bf16(silu(g) u) for the fp32 values g and u, evaluated in fp32 as the GLU is
-// specified (accurate expf, IEEE division, one rounding per operation), g e^g / (1 + e^g)
-// for g < 0 so a large |g| cannot overflow.  Against the exact value the fp32 result is
-// off by a few fp32 ulps, so its bf16 rounding differs from the correctly rounded one only
-// for values within that distance of a bf16 rounding boundary (about 1 in 10^4).
+// a = bf16(silu(g) u) for the fp32 values g and u, evaluated in fp32: silu(g) =
+// g / (1 + e^-g), as g e^g / (1 + e^g) for g < 0 so a large |g| cannot overflow.  The
+// exponential is the hardware 2^x of -|g| log2(e) and the division a hardware reciprocal:
+// each within a couple of fp32 ulps (the argument's rounding adds |g| 2^-24 relative), a
+// few fp32 ulps in all, so the bf16 rounding of a differs from that of the exact value
+// only for values within that distance of a bf16 rounding boundary (about 1 in 10^4).
+// The hardware 2^x flushes results below 2^-126, so for |g| above 83 it is taken of the
+// argument + 32 and the product g e^g scaled back by 2^-32 (an fp32 multiply, which keeps
+// subnormal results).  NaN and infinities behave as in the exact formula: g = +inf gives
+// +inf, g = -inf NaN.
 __device__ __forceinline__ uint16_t glu_bf16(float g, float u) {
-  const float e = expf(-fabsf(g));  // one exponential on either side
-  const float s = g >= 0.f ? g / (1.f + e) : (g * e) / (1.f + e);
+  const float x = -fabsf(g) * 1.44269504088896341f;  // log2 of e^-|g|
+  const bool tiny = x < -120.f;
+  const float e2 = __builtin_amdgcn_exp2f(tiny ? x + 32.f : x);  // e^-|g|, times 2^32 when tiny
+  const float sc = tiny ? 0x1p-32f : 1.f;
+  const float r = __builtin_amdgcn_rcpf(1.f + e2 * sc);
+  const float s = (g >= 0.f ? g : (g * e2) * sc) * r;
   return f32_to_bf16(s * u);
 }
 
