@@ -256,7 +256,15 @@ moe_status moe_layer_forward_profiled(const void* x, const void* router_w, const
  * x is split for the matrix cores in cfg->act_format like h.  The workspace grows by
  * the shared rows (moe_workspace_size accounts for them).  moe_layer_forward is this
  * call with num_shared = 0; with num_shared > 0 it returns MOE_ERR_INVALID_ARG.
- * shared_blob: device, 16-byte aligned. */
+ * shared_blob: device, 16-byte aligned.
+ * The shared experts depend on x alone, so they run beside the routed path on a second
+ * stream that the library creates once per device (default priority, non-blocking) at
+ * the first call whose stream is not being captured, and keeps until the process ends:
+ * `stream` records an event, the side stream waits on it, runs the shared experts and
+ * records a second event that `stream` waits on before the latent-up projection.  Stream
+ * capture records this fork and join as graph edges.  A first call made while `stream`
+ * is being captured runs the shared experts on `stream` itself (same result).  Calls on
+ * one device from several host threads take the side stream one at a time. */
 moe_status moe_layer_forward_shared(const void* x, const void* router_w, const void* latent_down,
                                     const void* latent_up, const uint8_t* expert_blob, int32_t k,
                                     const moe_config* cfg, const float* router_bias, const uint8_t* shared_blob,

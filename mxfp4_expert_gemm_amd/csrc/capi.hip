@@ -302,6 +302,63 @@ moe_status scratch_for(hipStream_t stream, void** out) {
   return MOE_OK;
 }
 
+// ---- the second stream the shared experts run on
+// One per device, created at the first call that needs it while the caller's stream is not
+// being captured, and kept until the process ends: default priority, no implicit
+// synchronisation with the null stream.  The caller's stream records `fork`, the side
+// stream waits on it, runs the shared experts and records `join`, and the caller's stream
+// waits on `join` before the latent-up projection: an event fork and join, which stream
+// capture records as graph edges.  `use` is held from the fork to the join's wait, so
+// calls on one device from several host threads take the side stream one at a time.
+struct SideStream {
+  hipStream_t side = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  std::mutex use;
+};
+std::mutex side_mutex;
+SideStream side_streams[MAX_DEVICES];
+
+// the side stream of the device that owns `st`; *out stays null when there is none and
+// none may be made now (the caller's stream is being captured): the shared experts then
+// run on the caller's stream
+moe_status side_for(hipStream_t st, SideStream** out) {
+  *out = nullptr;
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return MOE_ERR_DEVICE;
+  int device = cur;
+  if (st) {
+    hipDevice_t sd = -1;
+    if (hipStreamGetDevice(st, &sd) != hipSuccess) return MOE_ERR_DEVICE;
+    device = sd;
+  }
+  if (device < 0 || device >= MAX_DEVICES) return MOE_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(side_mutex);
+  SideStream& s = side_streams[device];
+  if (!s.side) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cs) != hipSuccess) return MOE_ERR_DEVICE;
+    if (cs != hipStreamCaptureStatusNone) return MOE_OK;
+    if (device != cur && hipSetDevice(device) != hipSuccess) return MOE_ERR_DEVICE;
+    hipStream_t side = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+    bool ok = hipStreamCreateWithFlags(&side, hipStreamNonBlocking) == hipSuccess &&
+              hipEventCreateWithFlags(&fork, hipEventDisableTiming) == hipSuccess &&
+              hipEventCreateWithFlags(&join, hipEventDisableTiming) == hipSuccess;
+    if (device != cur && hipSetDevice(cur) != hipSuccess) ok = false;
+    if (!ok) {
+      if (join) (void)hipEventDestroy(join);
+      if (fork) (void)hipEventDestroy(fork);
+      if (side) (void)hipStreamDestroy(side);
+      return MOE_ERR_DEVICE;
+    }
+    s.fork = fork;
+    s.join = join;
+    s.side = side;
+  }
+  *out = &s;
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -345,6 +402,43 @@ moe_status moe_workspace_size(const moe_config* cfg, int32_t k, size_t* bytes) {
   MOE_TRY(check_config(cfg, k));
   *bytes = layout(*cfg, k).total;
   return MOE_OK;
+}
+
+// the shared experts on x at the full width: every token's rows t*S + s, grouped by shared
+// expert, through the same expert kernels; their fp32 outputs (s_y) join the latent-up
+// product before its bf16 rounding
+static moe_status run_shared(const moe_config& c, const void* x, const uint8_t* shared_blob, void* ws,
+                             const Layout& l, hipStream_t st) {
+  const int32_t S = c.num_shared;
+  const int64_t rows = c.num_tokens * S;
+  const QRows xq{at<uint8_t>(ws, l.xq_hi), at<uint8_t>(ws, l.xq_lo), at<uint8_t>(ws, l.xq_shi),
+                 at<uint8_t>(ws, l.xq_slo)};
+  MOE_TRY(dev(launch_quantize_rows(static_cast<const uint16_t*>(x), c.num_tokens, c.d_model, xq,
+                                   c.act_format == MOE_ACT_FMT_MXFP8, st)));
+  PermOut ps{at<int32_t>(ws, l.s_counts), at<int32_t>(ws, l.s_offsets), at<int32_t>(ws, l.s_perm),
+             at<int4>(ws, l.s_tiles), at<int32_t>(ws, l.s_nact), S};
+  const int64_t gblocks = ceil_div(rows, 256) < 1024 ? ceil_div(rows, 256) : 1024;
+  hipLaunchKernelGGL(shared_group_kernel, dim3((unsigned)gblocks), dim3(256), 0, st, ps.counts, ps.offsets, ps.perm,
+                     ps.tiles, ps.n_active, c.num_tokens, S);
+  MOE_TRY(dev(hipGetLastError()));
+  MxArgs ms;
+  ms.blob = shared_blob;
+  ms.packed = c.expert_layout == MOE_LAYOUT_PACKED;
+  ms.L = c.d_model;
+  ms.F = c.d_ffn_shared;
+  ms.k = S;
+  ms.T = c.num_tokens;
+  ms.tiles = ps.tiles;
+  ms.max_active = S;
+  ms.perm = ps.perm;
+  ms.hq = xq;
+  ms.aq = QRows{at<uint8_t>(ws, l.sq_hi), at<uint8_t>(ws, l.sq_lo), at<uint8_t>(ws, l.sq_shi),
+                at<uint8_t>(ws, l.sq_slo)};
+  ms.mxfp8 = c.act_format == MOE_ACT_FMT_MXFP8;
+  ms.a_bf16 = nullptr;
+  ms.y = at<float>(ws, l.s_y);
+  ms.clock = nullptr;
+  return run_experts_on(ms, rows, S, ps.counts, ps.offsets, at<int4>(ws, l.s_gtiles), st);
 }
 
 // expert_slots non-null: expert_blob is device-readable host memory, and the experts
@@ -396,93 +490,119 @@ static moe_status forward_impl(const void* x, const void* router_w, const void* 
     return k;
   };
 
-  int32_t* idx = routing && routing->topk_idx ? routing->topk_idx : at<int32_t>(ws, l.idx);
-  float* w = routing && routing->topk_w ? routing->topk_w : at<float>(ws, l.w);
-  int32_t* counts = routing && routing->expert_counts ? routing->expert_counts : at<int32_t>(ws, l.counts);
-  int32_t* offsets = routing && routing->expert_offsets ? routing->expert_offsets : at<int32_t>(ws, l.offsets);
-  int32_t* perm = routing && routing->perm ? routing->perm : at<int32_t>(ws, l.perm);
-  float* logits_out = routing ? routing->logits : nullptr;
+  // the shared experts depend on x alone: they run beside the routed path, on a second
+  // stream, and join it before the latent-up projection
+  SideStream* side = nullptr;
+  std::unique_lock<std::mutex> side_lock;
+  if (c.num_shared > 0) MOE_TRY(side_for(st, &side));
+  if (side) side_lock = std::unique_lock<std::mutex>(side->use);
+  moe_status shared_status = MOE_OK;
+  if (side) {
+    MOE_TRY(dev(hipEventRecord(side->fork, st)));
+    MOE_TRY(dev(hipStreamWaitEvent(side->side, side->fork, 0)));
+    shared_status = run_shared(c, x, shared_blob, ws, l, side->side);
+    MOE_TRY(dev(hipEventRecord(side->join, side->side)));
+  }
+  auto routed = [&]() -> moe_status {
+    int32_t* idx = routing && routing->topk_idx ? routing->topk_idx : at<int32_t>(ws, l.idx);
+    float* w = routing && routing->topk_w ? routing->topk_w : at<float>(ws, l.w);
+    int32_t* counts = routing && routing->expert_counts ? routing->expert_counts : at<int32_t>(ws, l.counts);
+    int32_t* offsets = routing && routing->expert_offsets ? routing->expert_offsets : at<int32_t>(ws, l.offsets);
+    int32_t* perm = routing && routing->perm ? routing->perm : at<int32_t>(ws, l.perm);
+    float* logits_out = routing ? routing->logits : nullptr;
 
-  MOE_TRY(mark(MOE_STAGE_ROUTER_DOWN, true));
-  MOE_TRY(run_router_and_down(c, x, router_w, latent_down, ws, l, st));
-  MOE_TRY(mark(MOE_STAGE_ROUTER_DOWN, false));
-  RouteArgs ra = route_args(c, k, 0, x, router_w, router_bias, idx, w, logits_out, ws, l);
-  ra.h = at<uint16_t>(ws, l.h);
-  ra.hq = hq_rows(ws, l);
-  PermOut po{counts, offsets, perm, at<int4>(ws, l.tiles), at<int32_t>(ws, l.nact),
-             max_tiles(c.num_tokens * k, c.num_experts)};
-  MOE_TRY(mark(MOE_STAGE_ROUTE, true));
-  if (c.num_tokens <= ROUTE_FUSED_TOKENS) {
-    MOE_TRY(dev(launch_route_permute_small(ra, po, st)));
-    MOE_TRY(mark(MOE_STAGE_ROUTE, false));
-    MOE_TRY(mark(MOE_STAGE_PERMUTE, true));
-  } else if (c.num_tokens <= ROUTE_PLACE_TOKENS && c.num_tokens * k <= ROUTE_SMALL_ROWS) {
-    MOE_TRY(dev(launch_route(ra, st)));
-    MOE_TRY(mark(MOE_STAGE_ROUTE, false));
-    MOE_TRY(mark(MOE_STAGE_PERMUTE, true));
-    MOE_TRY(dev(launch_place_rows(idx, c.num_tokens, k, c.num_experts, po, st)));
-  } else {
-    MOE_TRY(dev(launch_route(ra, st)));
-    MOE_TRY(mark(MOE_STAGE_ROUTE, false));
-    MOE_TRY(mark(MOE_STAGE_PERMUTE, true));
-    MOE_TRY(dev(launch_permute(idx, c.num_tokens * k, c.num_experts, po, at<void>(ws, l.permws), st)));
-  }
-  // the expert stage reads the blob, or the slots holding the routed experts' records
-  const uint8_t* eblob = expert_blob;
-  const int32_t* eidx = idx;
-  const int32_t* ecounts = counts;
-  const int32_t* eoffsets = offsets;
-  int32_t E_eff = c.num_experts;
-  int4* etiles = at<int4>(ws, l.tiles);
-  if (expert_slots) {
-    MOE_TRY(dev(launch_gather_experts(expert_blob, ebytes, etiles, at<int32_t>(ws, l.nact), nslots, expert_slots, st)));
-    MOE_TRY(dev(launch_remap_to_slots(etiles, at<int32_t>(ws, l.nact), nslots, counts, offsets, idx, c.num_tokens * k,
-                                      at<int4>(ws, l.tiles_s), at<int32_t>(ws, l.counts_s),
-                                      at<int32_t>(ws, l.offsets_s), at<int32_t>(ws, l.idx_s), st)));
-    eblob = expert_slots;
-    eidx = at<int32_t>(ws, l.idx_s);
-    ecounts = at<int32_t>(ws, l.counts_s);
-    eoffsets = at<int32_t>(ws, l.offsets_s);
-    E_eff = nslots;
-    etiles = at<int4>(ws, l.tiles_s);
-  }
-  MOE_TRY(mark(MOE_STAGE_PERMUTE, false));
-  MxArgs mx = mx_args(c, k, eblob, ws, l, perm, at<float>(ws, l.y));
-  mx.tiles = etiles;
-  if (down_combine_fits(c.num_tokens, k)) {
-    MOE_TRY(mark(MOE_STAGE_GATE_UP, true));
-    mx.clock = kclock(MOE_STAGE_GATE_UP);
-    MOE_TRY(dev(launch_gateup_mx(mx, st, kev(MOE_STAGE_GATE_UP))));
-    MOE_TRY(mark(MOE_STAGE_GATE_UP, false));
-    MOE_TRY(mark(MOE_STAGE_DOWN, true));
-    mx.clock = kclock(MOE_STAGE_DOWN);
-    MOE_TRY(dev(launch_down_combine_mx(mx, eidx, w, at<uint16_t>(ws, l.z), st, kev(MOE_STAGE_DOWN))));
-    MOE_TRY(mark(MOE_STAGE_DOWN, false));
-    MOE_TRY(mark(MOE_STAGE_COMBINE, true));
-    MOE_TRY(mark(MOE_STAGE_COMBINE, false));
-  } else {
-    const int64_t rows = c.num_tokens * k;
-    const int64_t mt = gemm_max_tiles(rows, c.num_experts);
-    int4* gt = at<int4>(ws, l.gtiles);
-    const bool gemm = use_gemm(rows, c.num_experts);
-    MOE_TRY(mark(MOE_STAGE_GATE_UP, true));
-    mx.clock = kclock(MOE_STAGE_GATE_UP);
-    if (gemm) {
-      MOE_TRY(dev(launch_gemm_tiles(ecounts, eoffsets, E_eff, gt, mt, st)));
-      MOE_TRY(dev(launch_gateup_gemm(mx, gt, mt, st, kev(MOE_STAGE_GATE_UP))));
+    MOE_TRY(mark(MOE_STAGE_ROUTER_DOWN, true));
+    MOE_TRY(run_router_and_down(c, x, router_w, latent_down, ws, l, st));
+    MOE_TRY(mark(MOE_STAGE_ROUTER_DOWN, false));
+    RouteArgs ra = route_args(c, k, 0, x, router_w, router_bias, idx, w, logits_out, ws, l);
+    ra.h = at<uint16_t>(ws, l.h);
+    ra.hq = hq_rows(ws, l);
+    PermOut po{counts, offsets, perm, at<int4>(ws, l.tiles), at<int32_t>(ws, l.nact),
+               max_tiles(c.num_tokens * k, c.num_experts)};
+    MOE_TRY(mark(MOE_STAGE_ROUTE, true));
+    if (c.num_tokens <= ROUTE_FUSED_TOKENS) {
+      MOE_TRY(dev(launch_route_permute_small(ra, po, st)));
+      MOE_TRY(mark(MOE_STAGE_ROUTE, false));
+      MOE_TRY(mark(MOE_STAGE_PERMUTE, true));
+    } else if (c.num_tokens <= ROUTE_PLACE_TOKENS && c.num_tokens * k <= ROUTE_SMALL_ROWS) {
+      MOE_TRY(dev(launch_route(ra, st)));
+      MOE_TRY(mark(MOE_STAGE_ROUTE, false));
+      MOE_TRY(mark(MOE_STAGE_PERMUTE, true));
+      MOE_TRY(dev(launch_place_rows(idx, c.num_tokens, k, c.num_experts, po, st)));
     } else {
-      MOE_TRY(dev(launch_gateup_mx(mx, st, kev(MOE_STAGE_GATE_UP))));
+      MOE_TRY(dev(launch_route(ra, st)));
+      MOE_TRY(mark(MOE_STAGE_ROUTE, false));
+      MOE_TRY(mark(MOE_STAGE_PERMUTE, true));
+      MOE_TRY(dev(launch_permute(idx, c.num_tokens * k, c.num_experts, po, at<void>(ws, l.permws), st)));
     }
-    MOE_TRY(mark(MOE_STAGE_GATE_UP, false));
-    MOE_TRY(mark(MOE_STAGE_DOWN, true));
-    mx.clock = kclock(MOE_STAGE_DOWN);
-    MOE_TRY(dev(gemm ? launch_down_gemm(mx, gt, mt, st, kev(MOE_STAGE_DOWN))
-                     : launch_down_mx(mx, st, kev(MOE_STAGE_DOWN))));
-    MOE_TRY(mark(MOE_STAGE_DOWN, false));
-    MOE_TRY(mark(MOE_STAGE_COMBINE, true));
-    MOE_TRY(dev(launch_combine(at<float>(ws, l.y), w, c.num_tokens, k, c.d_latent, at<uint16_t>(ws, l.z), st)));
-    MOE_TRY(mark(MOE_STAGE_COMBINE, false));
+    // the expert stage reads the blob, or the slots holding the routed experts' records
+    const uint8_t* eblob = expert_blob;
+    const int32_t* eidx = idx;
+    const int32_t* ecounts = counts;
+    const int32_t* eoffsets = offsets;
+    int32_t E_eff = c.num_experts;
+    int4* etiles = at<int4>(ws, l.tiles);
+    if (expert_slots) {
+      MOE_TRY(dev(launch_gather_experts(expert_blob, ebytes, etiles, at<int32_t>(ws, l.nact), nslots, expert_slots, st)));
+      MOE_TRY(dev(launch_remap_to_slots(etiles, at<int32_t>(ws, l.nact), nslots, counts, offsets, idx, c.num_tokens * k,
+                                        at<int4>(ws, l.tiles_s), at<int32_t>(ws, l.counts_s),
+                                        at<int32_t>(ws, l.offsets_s), at<int32_t>(ws, l.idx_s), st)));
+      eblob = expert_slots;
+      eidx = at<int32_t>(ws, l.idx_s);
+      ecounts = at<int32_t>(ws, l.counts_s);
+      eoffsets = at<int32_t>(ws, l.offsets_s);
+      E_eff = nslots;
+      etiles = at<int4>(ws, l.tiles_s);
+    }
+    MOE_TRY(mark(MOE_STAGE_PERMUTE, false));
+    MxArgs mx = mx_args(c, k, eblob, ws, l, perm, at<float>(ws, l.y));
+    mx.tiles = etiles;
+    if (down_combine_fits(c.num_tokens, k)) {
+      MOE_TRY(mark(MOE_STAGE_GATE_UP, true));
+      mx.clock = kclock(MOE_STAGE_GATE_UP);
+      MOE_TRY(dev(launch_gateup_mx(mx, st, kev(MOE_STAGE_GATE_UP))));
+      MOE_TRY(mark(MOE_STAGE_GATE_UP, false));
+      MOE_TRY(mark(MOE_STAGE_DOWN, true));
+      mx.clock = kclock(MOE_STAGE_DOWN);
+      MOE_TRY(dev(launch_down_combine_mx(mx, eidx, w, at<uint16_t>(ws, l.z), st, kev(MOE_STAGE_DOWN))));
+      MOE_TRY(mark(MOE_STAGE_DOWN, false));
+      MOE_TRY(mark(MOE_STAGE_COMBINE, true));
+      MOE_TRY(mark(MOE_STAGE_COMBINE, false));
+    } else {
+      const int64_t rows = c.num_tokens * k;
+      const int64_t mt = gemm_max_tiles(rows, c.num_experts);
+      int4* gt = at<int4>(ws, l.gtiles);
+      const bool gemm = use_gemm(rows, c.num_experts);
+      MOE_TRY(mark(MOE_STAGE_GATE_UP, true));
+      mx.clock = kclock(MOE_STAGE_GATE_UP);
+      if (gemm) {
+        MOE_TRY(dev(launch_gemm_tiles(ecounts, eoffsets, E_eff, gt, mt, st)));
+        MOE_TRY(dev(launch_gateup_gemm(mx, gt, mt, st, kev(MOE_STAGE_GATE_UP))));
+      } else {
+        MOE_TRY(dev(launch_gateup_mx(mx, st, kev(MOE_STAGE_GATE_UP))));
+      }
+      MOE_TRY(mark(MOE_STAGE_GATE_UP, false));
+      MOE_TRY(mark(MOE_STAGE_DOWN, true));
+      mx.clock = kclock(MOE_STAGE_DOWN);
+      MOE_TRY(dev(gemm ? launch_down_gemm(mx, gt, mt, st, kev(MOE_STAGE_DOWN))
+                       : launch_down_mx(mx, st, kev(MOE_STAGE_DOWN))));
+      MOE_TRY(mark(MOE_STAGE_DOWN, false));
+      MOE_TRY(mark(MOE_STAGE_COMBINE, true));
+      MOE_TRY(dev(launch_combine(at<float>(ws, l.y), w, c.num_tokens, k, c.d_latent, at<uint16_t>(ws, l.z), st)));
+      MOE_TRY(mark(MOE_STAGE_COMBINE, false));
+    }
+    return MOE_OK;
+  };
+  moe_status routed_status = routed();
+  // joined whatever the routed path returned, so a capture never ends with the side
+  // stream still forked
+  if (side) {
+    const moe_status j = dev(hipStreamWaitEvent(st, side->join, 0));
+    if (routed_status == MOE_OK) routed_status = j;
   }
+  MOE_TRY(shared_status);
+  MOE_TRY(routed_status);
+  if (c.num_shared > 0 && !side) MOE_TRY(run_shared(c, x, shared_blob, ws, l, st));
   DenseSeg up;
   up.W = static_cast<const uint16_t*>(latent_up);
   up.rows = c.d_model;
@@ -492,41 +612,8 @@ static moe_status forward_impl(const void* x, const void* router_w, const void* 
   up.xnorm = nullptr;
   MOE_TRY(mark(MOE_STAGE_UP, true));
   if (c.num_shared > 0) {
-    // the shared experts on x at the full width: every token's rows t*S + s, grouped by
-    // shared expert, through the same expert kernels; their fp32 outputs join the
-    // latent-up product before its bf16 rounding
-    const int32_t S = c.num_shared;
-    const int64_t rows = c.num_tokens * S;
-    const QRows xq{at<uint8_t>(ws, l.xq_hi), at<uint8_t>(ws, l.xq_lo), at<uint8_t>(ws, l.xq_shi),
-                   at<uint8_t>(ws, l.xq_slo)};
-    MOE_TRY(dev(launch_quantize_rows(static_cast<const uint16_t*>(x), c.num_tokens, c.d_model, xq,
-                                     c.act_format == MOE_ACT_FMT_MXFP8, st)));
-    PermOut ps{at<int32_t>(ws, l.s_counts), at<int32_t>(ws, l.s_offsets), at<int32_t>(ws, l.s_perm),
-               at<int4>(ws, l.s_tiles), at<int32_t>(ws, l.s_nact), S};
-    const int64_t gblocks = ceil_div(rows, 256) < 1024 ? ceil_div(rows, 256) : 1024;
-    hipLaunchKernelGGL(shared_group_kernel, dim3((unsigned)gblocks), dim3(256), 0, st, ps.counts, ps.offsets, ps.perm,
-                       ps.tiles, ps.n_active, c.num_tokens, S);
-    MOE_TRY(dev(hipGetLastError()));
-    MxArgs ms;
-    ms.blob = shared_blob;
-    ms.packed = c.expert_layout == MOE_LAYOUT_PACKED;
-    ms.L = c.d_model;
-    ms.F = c.d_ffn_shared;
-    ms.k = S;
-    ms.T = c.num_tokens;
-    ms.tiles = ps.tiles;
-    ms.max_active = S;
-    ms.perm = ps.perm;
-    ms.hq = xq;
-    ms.aq = QRows{at<uint8_t>(ws, l.sq_hi), at<uint8_t>(ws, l.sq_lo), at<uint8_t>(ws, l.sq_shi),
-                  at<uint8_t>(ws, l.sq_slo)};
-    ms.mxfp8 = c.act_format == MOE_ACT_FMT_MXFP8;
-    ms.a_bf16 = nullptr;
-    ms.y = at<float>(ws, l.s_y);
-    ms.clock = nullptr;
-    MOE_TRY(run_experts_on(ms, rows, S, ps.counts, ps.offsets, at<int4>(ws, l.s_gtiles), st));
-    up.add = ms.y;
-    up.add_rows = S;
+    up.add = at<float>(ws, l.s_y);
+    up.add_rows = c.num_shared;
   }
   MOE_TRY(dev(launch_dense(at<uint16_t>(ws, l.z), c.num_tokens, c.d_latent, &up, 1, st)));
   return mark(MOE_STAGE_UP, false);

@@ -81,3 +81,49 @@ def test_shared_requires_the_blob():
                                      c.k, __import__("ctypes").byref(cfg), None, out.data_ptr(), None, ws.data_ptr(),
                                      ws.numel(), None)
     assert st == -1
+
+
+def test_layer_shared_prefill32k_sampled():
+    _run("prefill32k", tokens=[0, 16383, 32767])
+
+
+@pytest.mark.parametrize("name,T", [("decode1", None), ("tiny", 600)])
+def test_layer_shared_graph_replays_match_eager(name, T):
+    """The shared experts run on the library's second stream, forked from the caller's
+    stream and joined before the latent-up projection.  Captured into a graph (whose
+    capture stream differs from the eager call's), every replay, with other work on the
+    device between replays, gives the eager call's bits."""
+    h = host_layer(name, T)
+    c = h["cfg"]
+    dw = dev_weights(name)
+    dsh = moe.pack_experts(to_dev(_shared(c.d, c.F)), S, c.d, c.F)
+    blob = dev_packed(name)
+    Tn = h["x"].shape[0]
+    x = to_dev(h["x"])
+    bias = None if h["bias"] is None else to_dev(h["bias"])
+    cfg = moe.make_config(Tn, c.d, c.L, c.F, c.E, num_shared=S, d_ffn_shared=c.F, packed=True)
+    ws = moe.alloc_workspace(cfg, c.k, torch.device("cuda"))
+    out = torch.empty((Tn, c.d), dtype=torch.int16, device="cuda")
+
+    def call():
+        moe.layer_forward(x, dw["router_w"], dw["latent_down"], dw["latent_up"], blob, c.k, d_ffn=c.F, bias=bias,
+                          packed=True, shared_blob=dsh, num_shared=S, d_ffn_shared=c.F, out=out, workspace=ws)
+
+    call()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.zero_()
+        ws.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {rep} differs from the eager call"
+        call()  # eager work between replays, on the same buffers
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager)
+    log(f"  {name} T={Tn}: 3 graph replays bit-identical to the eager call")
