@@ -47,8 +47,9 @@
  *    before anything is enqueued and return synchronously; a failed launch
  *    returns MOE_ERR_DEVICE.
  *  - num_tokens == 0 is a no-op returning MOE_OK.
- *  - Calls on distinct workspaces are independent; the library has no global
- *    mutable state.
+ *  - Calls on distinct workspaces are independent.  The library's only global
+ *    state is the scratch array of moe_layer_forward_noalloc and the side stream
+ *    (with its two events) of moe_layer_forward_shared, one of each per device.
  */
 #ifndef MOE_LAYER_H
 #define MOE_LAYER_H
@@ -135,6 +136,10 @@ typedef struct {
   int32_t* expert_offsets; /* [E+1] exclusive prefix of expert_counts */
   int32_t* perm;           /* [T*k] row t*k+j of each routed (token, slot), grouped by
                               expert, tokens ascending inside a group */
+  double* saliency;        /* [E] fp64, 8-byte aligned: the layer adds the REAP sums of
+                              this batch, saliency[e] += sum over e's routed rows r of
+                              topk_w[r] * ||y[r]||_2 (as moe_reap_saliency), from partial
+                              sums the down kernels write; accumulated across calls */
 } moe_routing_out;
 
 /* Bytes of one expert record: 3 * L * F weights at 0.53125 B (kimi-k3-in-c
@@ -183,7 +188,7 @@ moe_status moe_layer_forward(const void* x, const void* router_w, const void* la
  * nothing (no hipMalloc, no allocating library routine).
  *  - A batch whose moe_workspace_size(cfg, k) exceeds MOE_NOALLOC_SCRATCH_BYTES returns
  *    MOE_ERR_WORKSPACE before anything is enqueued (at the Kimi K3 shapes, d 7168,
- *    L 3584, F 3072, E 896, k 16: up to 188 tokens).
+ *    L 3584, F 3072, E 896, k 16: up to 184 tokens).
  *  - Every call on one GPU uses that GPU's one array, which keeps the last call's
  *    contents (the layer needs no part of it cleared): calls that overlap on one GPU
  *    (other streams, other host threads) race, and the caller must serialise them.
@@ -354,6 +359,15 @@ moe_status moe_reap_saliency(const float* y, const float* topk_w, const int32_t*
                              const int32_t* expert_offsets, int64_t num_tokens, int32_t k,
                              int32_t d_latent, int32_t num_experts, double* saliency,
                              moe_stream_t stream);
+
+/* The router bias of a REAP-pruned layer (kimi-k3-mlx digest, REAP section: keep the
+ * experts of highest saliency, e.g. 242 or 179 of 896): bias[e] = 0 for the n_keep
+ * experts ranked first by saliency (higher first, ties to the lower index, NaN after
+ * every number), -inf for the others.  saliency: fp64 [num_experts]; bias: fp32
+ * [num_experts]; both device.  1 <= num_experts <= 1024 (else MOE_ERR_UNSUPPORTED),
+ * 0 <= n_keep <= num_experts. */
+moe_status moe_reap_keep_bias(const double* saliency, int32_t num_experts, int32_t n_keep, float* bias,
+                              moe_stream_t stream);
 
 /* Dense bf16 projection: out[t][o] = bf16(sum_i in[t][i] W[o][i]), fp32
  * accumulation (the latent down/up projections).  n_in multiple of 32. */

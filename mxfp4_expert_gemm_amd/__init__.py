@@ -30,7 +30,7 @@ EXPORTS = ["moe_expert_bytes", "moe_packed_expert_bytes", "moe_pack_experts", "m
            "moe_layer_forward_profiled",
            "moe_dequant_mxfp4", "moe_route", "moe_topk", "moe_permute", "moe_expert_ffn", "moe_combine",
            "moe_linear_bf16", "moe_reap_saliency", "moe_layer_forward_shared", "moe_expert_slots_bytes",
-           "moe_layer_forward_streamed", "moe_layer_forward_noalloc"]
+           "moe_layer_forward_streamed", "moe_layer_forward_noalloc", "moe_reap_keep_bias"]
 
 
 class MoEError(RuntimeError):
@@ -64,7 +64,8 @@ class StageEvents(ctypes.Structure):
 
 class RoutingOut(ctypes.Structure):
     _fields_ = [("topk_idx", ctypes.c_void_p), ("topk_w", ctypes.c_void_p), ("logits", ctypes.c_void_p),
-                ("expert_counts", ctypes.c_void_p), ("expert_offsets", ctypes.c_void_p), ("perm", ctypes.c_void_p)]
+                ("expert_counts", ctypes.c_void_p), ("expert_offsets", ctypes.c_void_p), ("perm", ctypes.c_void_p),
+                ("saliency", ctypes.c_void_p)]
 
 
 _lib = None
@@ -96,6 +97,7 @@ def lib():
             "moe_combine": (ctypes.c_int, [vp, vp, i64, i32, i32, vp, vp]),
             "moe_linear_bf16": (ctypes.c_int, [vp, vp, i64, i32, i32, vp, vp]),
             "moe_reap_saliency": (ctypes.c_int, [vp, vp, vp, vp, i64, i32, i32, i32, vp, vp]),
+            "moe_reap_keep_bias": (ctypes.c_int, [vp, i32, i32, vp, vp]),
             "moe_layer_forward_shared": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, cfgp, vp, vp, vp, rp, vp, sz, vp]),
             "moe_expert_slots_bytes": (ctypes.c_int, [cfgp, i32, ctypes.POINTER(sz)]),
             "moe_layer_forward_noalloc": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, cfgp, vp, vp, rp, vp]),
@@ -170,7 +172,7 @@ def _routing(r: Optional[dict]) -> Optional[RoutingOut]:
     if r is None:
         return None
     return RoutingOut(*[_p(r.get(n)) for n in ("topk_idx", "topk_w", "logits", "expert_counts", "expert_offsets",
-                                              "perm")])
+                                              "perm", "saliency")])
 
 
 def layer_forward(x, router_w, latent_down, latent_up, expert_blob, k: int, *, d_ffn: int,
@@ -386,12 +388,13 @@ def reap_saliency(y: torch.Tensor, topk_w: torch.Tensor, perm: torch.Tensor, exp
 
 
 def reap_prune_bias(saliency: torch.Tensor, n_keep: int) -> torch.Tensor:
-    """Router bias of a REAP-pruned layer: 0 on the n_keep experts of highest saliency
-    (ties to the lower index), -inf on the others (host logic: a top-n and a fill)."""
+    """Router bias of a REAP-pruned layer (moe_reap_keep_bias): 0 on the n_keep experts of
+    highest saliency (ties to the lower index, NaN last), -inf on the others."""
+    if saliency.dtype != torch.float64 or not saliency.is_contiguous():
+        raise ValueError("saliency must be a contiguous fp64 tensor")
     E = saliency.numel()
-    order = sorted(range(E), key=lambda e: (-float(saliency[e]), e))
-    bias = torch.full((E,), float("-inf"), dtype=torch.float32, device=saliency.device)
-    bias[torch.tensor(order[:n_keep], device=saliency.device)] = 0.0
+    bias = torch.empty((E,), dtype=torch.float32, device=saliency.device)
+    _check(lib().moe_reap_keep_bias(_p(saliency), E, n_keep, _p(bias), _stream()), "moe_reap_keep_bias")
     return bias
 
 

@@ -18,8 +18,19 @@ constexpr int MAX_DIM = 8192;  // columns a GEMV wave holds in registers
 constexpr int MAX_EXPERT_DIM = 7168;  // latent / FFN width whose staged activation rows fit LDS
 constexpr int MAX_SHARED = 8;
 
+// Experts run as grouped GEMMs over 64-row tiles once they hold 8 routed rows on
+// average; below that, the streaming kernels that read each expert once per 4 rows.
+bool use_gemm(int64_t rows, int32_t E) { return rows >= 8 * (int64_t)E; }
+
+// REAP partials per routed row: the latent-row blocks of the down kernel the batch runs
+int32_t sal_chunks(const moe_config& c, int k) {
+  if (down_combine_fits(c.num_tokens, k)) return down_combine_sal_chunks(c.d_latent);
+  if (use_gemm(c.num_tokens * k, c.num_experts)) return down_gemm_sal_chunks(c.d_latent);
+  return down_mx_sal_chunks(c.d_latent);
+}
+
 struct Layout {
-  size_t logits_fast, xnorm, wnorm, idx, w, counts, offsets, perm, tiles, nact, permws, h, y, z, gtiles;
+  size_t logits_fast, xnorm, wnorm, idx, w, counts, offsets, perm, tiles, nact, permws, h, y, z, gtiles, salp;
   // the grouping renumbered to HBM slots (experts fetched from host memory)
   size_t tiles_s, counts_s, offsets_s, idx_s;
   // shared experts: x split for the matrix cores, their grouping, GLU rows, outputs
@@ -62,6 +73,7 @@ Layout layout(const moe_config& c, int k) {
   l.y = take(T * K * L * 4);
   l.z = take(T * L * 2);
   l.gtiles = take((size_t)gemm_max_tiles((int64_t)(T * K), (int32_t)E) * 16);
+  l.salp = take(T * K * (size_t)sal_chunks(c, k) * 8);
   l.tiles_s = take(E * 16);
   l.counts_s = take(E * 4);
   l.offsets_s = take((E + 1) * 4);
@@ -131,9 +143,6 @@ moe_status check_config(const moe_config* c, int32_t k) {
 
 int32_t max_tiles(int64_t rows, int32_t E) { return (int32_t)(rows < E ? rows : E); }
 
-// Experts run as grouped GEMMs over 64-row tiles once they hold 8 routed rows on
-// average; below that, the streaming kernels that read each expert once per 4 rows.
-bool use_gemm(int64_t rows, int32_t E) { return rows >= 8 * (int64_t)E; }
 
 moe_status dev(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_DEVICE; }
 
@@ -269,6 +278,8 @@ MxArgs mx_args(const moe_config& c, int k, const uint8_t* blob, void* ws, const 
   m.a_bf16 = nullptr;
   m.y = y;
   m.clock = nullptr;
+  m.sal = nullptr;
+  m.sal_chunks = 0;
   return m;
 }
 
@@ -438,6 +449,8 @@ static moe_status run_shared(const moe_config& c, const void* x, const uint8_t* 
   ms.a_bf16 = nullptr;
   ms.y = at<float>(ws, l.s_y);
   ms.clock = nullptr;
+  ms.sal = nullptr;
+  ms.sal_chunks = 0;
   return run_experts_on(ms, rows, S, ps.counts, ps.offsets, at<int4>(ws, l.s_gtiles), st);
 }
 
@@ -457,6 +470,7 @@ static moe_status forward_impl(const void* x, const void* router_w, const void* 
       !aligned16(expert_blob) || !aligned16(out))
     return MOE_ERR_INVALID_ARG;
   if (router_bias && (reinterpret_cast<uintptr_t>(router_bias) & 3u)) return MOE_ERR_INVALID_ARG;
+  if (routing && routing->saliency && (reinterpret_cast<uintptr_t>(routing->saliency) & 7u)) return MOE_ERR_INVALID_ARG;
   const int64_t ebytes = c.expert_layout == MOE_LAYOUT_PACKED ? packed_expert_bytes(c.d_latent, c.d_ffn)
                                                              : (int64_t)moe_expert_bytes(c.d_latent, c.d_ffn);
   const int32_t nslots = max_tiles(c.num_tokens * k, c.num_experts);
@@ -557,6 +571,11 @@ static moe_status forward_impl(const void* x, const void* router_w, const void* 
     MOE_TRY(mark(MOE_STAGE_PERMUTE, false));
     MxArgs mx = mx_args(c, k, eblob, ws, l, perm, at<float>(ws, l.y));
     mx.tiles = etiles;
+    double* saliency = routing ? routing->saliency : nullptr;
+    if (saliency) {  // the down kernels write their REAP partials
+      mx.sal = at<double>(ws, l.salp);
+      mx.sal_chunks = sal_chunks(c, k);
+    }
     if (down_combine_fits(c.num_tokens, k)) {
       MOE_TRY(mark(MOE_STAGE_GATE_UP, true));
       mx.clock = kclock(MOE_STAGE_GATE_UP);
@@ -591,6 +610,8 @@ static moe_status forward_impl(const void* x, const void* router_w, const void* 
       MOE_TRY(dev(launch_combine(at<float>(ws, l.y), w, c.num_tokens, k, c.d_latent, at<uint16_t>(ws, l.z), st)));
       MOE_TRY(mark(MOE_STAGE_COMBINE, false));
     }
+    if (saliency)
+      MOE_TRY(dev(launch_reap_partials(mx.sal, mx.sal_chunks, w, perm, offsets, c.num_experts, saliency, st)));
     return MOE_OK;
   };
   moe_status routed_status = routed();
@@ -798,6 +819,15 @@ moe_status moe_reap_saliency(const float* y, const float* topk_w, const int32_t*
   if (num_tokens == 0) return MOE_OK;
   return dev(launch_reap_saliency(y, topk_w, perm, expert_offsets, num_experts, d_latent, saliency,
                                   reinterpret_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_reap_keep_bias(const double* saliency, int32_t num_experts, int32_t n_keep, float* bias,
+                              moe_stream_t stream) {
+  if (!saliency || !bias || num_experts < 1 || n_keep < 0 || n_keep > num_experts) return MOE_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(saliency) & 7u) || (reinterpret_cast<uintptr_t>(bias) & 3u))
+    return MOE_ERR_INVALID_ARG;
+  if (num_experts > MAX_E) return MOE_ERR_UNSUPPORTED;
+  return dev(launch_reap_keep_bias(saliency, num_experts, n_keep, bias, reinterpret_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_linear_bf16(const void* in, const void* W, int64_t num_tokens, int32_t n_in, int32_t n_out, void* out,

@@ -532,6 +532,35 @@ __device__ __forceinline__ void down32_tile(const MxArgs& p, int e, int rt, int 
         if (m < n) p.y[srow[m] * L + l] = acc[q][tt][v];
       }
   }
+  if (p.sal) {
+    // REAP partials: the block's y tile goes to LDS (the activation chunks are free once
+    // every wave is past the K loop); per routed row, four threads sum y^2 over a quarter
+    // of the block's latent rows each, in row order, and add the quarters in a fixed order
+    constexpr int YS = 128 * NG + 4;
+    static_assert(64 * YS * 4 <= 2 * GT_BUF_BYTES, "the y tile fits the chunk buffers");
+    float* yt = reinterpret_cast<float*>(lds);
+    lds_barrier();
+#pragma unroll
+    for (int q = 0; q < NG; ++q)
+#pragma unroll
+      for (int tt = 0; tt < R / 32; ++tt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int m = 32 * tt + 8 * (v >> 2) + 4 * g + (v & 3);
+          if (m < n) yt[m * YS + (4 * q + wave) * 32 + nl] = acc[q][tt][v];
+        }
+    lds_barrier();
+    const int m = threadIdx.x >> 2, part = threadIdx.x & 3;
+    double sq = 0.0;
+    if (m < n)
+      for (int i = part * 32 * NG; i < (part + 1) * 32 * NG; ++i) {
+        const double v = (double)yt[m * YS + i];
+        sq += v * v;
+      }
+    sq += __shfl_xor(sq, 1);  // (q0 + q1), (q2 + q3): the same sum on both lanes of a pair
+    sq += __shfl_xor(sq, 2);  // then their sum
+    if (part == 0 && m < n) p.sal[srow[m] * p.sal_chunks + rt] = sq;
+  }
 }
 
 template <class W, int TERMS, int NG>
@@ -649,10 +678,13 @@ hipError_t launch_gateup_gemm(const MxArgs& p, const int4* gtiles, int64_t max_g
                  : gateup_gemm32_go<RecordW, 2>(p, gtiles, max_gtiles, nb, st, ev);
 }
 
+int32_t down_gemm_sal_chunks(int32_t L) { return L / (L % 256 == 0 ? 256 : 128); }
+
 hipError_t launch_down_gemm(const MxArgs& p, const int4* gtiles, int64_t max_gtiles, hipStream_t st,
                             const KernelEvents& ev) {
   if (p.T == 0) return hipSuccess;
   if (p.L % 128 || p.F % 128) return hipErrorInvalidValue;
+  if (p.sal && p.sal_chunks != down_gemm_sal_chunks(p.L)) return hipErrorInvalidValue;
   return p.L % 256 == 0 ? down_gemm32_ng<2>(p, gtiles, max_gtiles, st, ev)
                         : down_gemm32_ng<1>(p, gtiles, max_gtiles, st, ev);
 }

@@ -318,6 +318,7 @@ template <class W>
 __device__ __forceinline__ void down_mx_kernel_body(MxArgs p) {
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ int64_t srows[MX_TOK];
+  __shared__ float ytile[MX_TOK][MX_ROWS];  // REAP partials: the pass's y rows
   const int nrt = p.L / MX_ROWS;
   const int slot = blockIdx.x / nrt;
   const int4 tile = p.tiles[slot];
@@ -354,6 +355,21 @@ __device__ __forceinline__ void down_mx_kernel_body(MxArgs p) {
     for (int j = 0; j < 4; ++j) {
       const int mm = 4 * g + j;
       if (mm < ntok) p.y[srows[mm] * L + l] = acc[0][j];
+    }
+    if (p.sal) {
+      // sum of y^2 over the block's 64 latent rows, per routed row, in row order
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (4 * g + j < ntok) ytile[4 * g + j][16 * wave + n] = acc[0][j];
+      __syncthreads();
+      if (threadIdx.x < ntok) {
+        double q = 0.0;
+        for (int i = 0; i < MX_ROWS; ++i) {
+          const double v = (double)ytile[threadIdx.x][i];
+          q += v * v;
+        }
+        p.sal[srows[threadIdx.x] * p.sal_chunks + rt] = q;
+      }
     }
     __syncthreads();
   }
@@ -417,6 +433,17 @@ __device__ __forceinline__ void down_combine_mx_kernel_body(MxArgs p, const int3
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
   __syncthreads();
+  if (p.sal) {
+    // REAP partials: sum of y^2 over the block's 16 latent rows, per routed row
+    for (int s = threadIdx.x; s < nslot; s += blockDim.x) {
+      double q = 0.0;
+      for (int nn = 0; nn < 16; ++nn) {
+        const double v = (double)ys[s][nn];
+        q += v * v;
+      }
+      p.sal[(int64_t)s * p.sal_chunks + blockIdx.x] = q;
+    }
+  }
   for (int q = threadIdx.x; q < (int)p.T * 16; q += blockDim.x) {
     const int t = q >> 4, nn = q & 15;
     double acc = 0.0;
@@ -499,12 +526,15 @@ hipError_t launch_down_mx(const MxArgs& p, hipStream_t st, const KernelEvents& e
   if (p.T == 0 || p.max_active == 0) return hipSuccess;
   if (p.L % MX_ROWS || p.F % 128) return hipErrorInvalidValue;
   if (mx_lds_bytes(p.F) > MX_LDS_MAX) return hipErrorInvalidValue;
+  if (p.sal && p.sal_chunks != down_mx_sal_chunks(p.L)) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(p.max_active * (p.L / MX_ROWS)));
   if (p.packed) return dispatch(ev, down_mx_kernel<PackedW>, grid, dim3(256), mx_lds_bytes(p.F), st, p);
   return dispatch(ev, down_mx_kernel<RecordW>, grid, dim3(256), mx_lds_bytes(p.F), st, p);
 }
 
 bool down_combine_fits(int64_t T, int32_t k) { return T * k <= DCM_SLOTS; }
+int32_t down_mx_sal_chunks(int32_t L) { return L / MX_ROWS; }
+int32_t down_combine_sal_chunks(int32_t L) { return L / 16; }
 
 template <class W>
 static hipError_t down_combine_lds_limit() {
@@ -521,6 +551,7 @@ hipError_t launch_down_combine_mx(const MxArgs& p, const int32_t* idx, const flo
   const int waves = nslot < DCM_WAVES ? nslot : DCM_WAVES;
   const size_t lds = (size_t)waves * dcm_row_bytes(p.F);
   if (!down_combine_fits(p.T, p.k) || p.L % 16 || p.F % 128 || lds > DCM_LDS_MAX) return hipErrorInvalidValue;
+  if (p.sal && p.sal_chunks != down_combine_sal_chunks(p.L)) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(p.L / 16)), block(DCM_WAVES * WAVE);
   if (p.packed) {
     const hipError_t e = down_combine_lds_limit<PackedW>();

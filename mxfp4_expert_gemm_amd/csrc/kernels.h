@@ -129,10 +129,15 @@ struct MxArgs {
   uint16_t* a_bf16;          // nullable [T*k][F] GLU outputs by slot, bf16
   float* y;                  // [T*k][L] down outputs by slot
   unsigned long long* clock; // nullable: MOE_CLOCK_SLOTS {start, end} pairs of the kernel's blocks (clock_begin/end)
+  double* sal;               // nullable [T*k][sal_chunks]: per slot, the sum of y^2 over each block of latent rows
+  int32_t sal_chunks;        // latent-row blocks of the down kernel that runs (down_*_sal_chunks)
 };
 hipError_t launch_gateup_mx(const MxArgs& p, hipStream_t st, const KernelEvents& ev = KernelEvents());
 hipError_t launch_down_mx(const MxArgs& p, hipStream_t st, const KernelEvents& ev = KernelEvents());
 bool down_combine_fits(int64_t T, int32_t k);
+// latent-row blocks per routed row of each down kernel: the REAP partials it writes
+int32_t down_mx_sal_chunks(int32_t L);
+int32_t down_combine_sal_chunks(int32_t L);
 hipError_t launch_down_combine_mx(const MxArgs& p, const int32_t* idx, const float* w, uint16_t* z,
                                   hipStream_t st, const KernelEvents& ev = KernelEvents());
 hipError_t launch_quantize_rows(const uint16_t* src, int64_t rows, int K, const QRows& q, bool mxfp8, hipStream_t st);
@@ -146,6 +151,7 @@ hipError_t launch_gateup_gemm(const MxArgs& p, const int4* gtiles, int64_t max_g
                               const KernelEvents& ev = KernelEvents());
 hipError_t launch_down_gemm(const MxArgs& p, const int4* gtiles, int64_t max_gtiles, hipStream_t st,
                             const KernelEvents& ev = KernelEvents());
+int32_t down_gemm_sal_chunks(int32_t L);
 
 // ---- stream.hip: expert records fetched from host memory into HBM slots
 // copies the record of active expert j (tiles[j].x, j < *n_active) from src (device-
@@ -161,6 +167,12 @@ hipError_t launch_remap_to_slots(const int4* tiles, const int32_t* n_active, int
 // ---- reap.hip: saliency[e] += sum over e's rows (perm order) of w[slot] ||y[slot]||_2
 hipError_t launch_reap_saliency(const float* y, const float* w, const int32_t* perm, const int32_t* offsets,
                                 int32_t E, int32_t L, double* saliency, hipStream_t st);
+// the same sums from the down kernels' partials: ||y[slot]||^2 = sum over c of sal[slot][c]
+hipError_t launch_reap_partials(const double* sal, int32_t nch, const float* w, const int32_t* perm,
+                                const int32_t* offsets, int32_t E, double* saliency, hipStream_t st);
+// bias[e] = 0 for the n_keep experts of highest saliency (ties to the lower index, NaN
+// lowest), -inf for the others
+hipError_t launch_reap_keep_bias(const double* saliency, int32_t E, int32_t n_keep, float* bias, hipStream_t st);
 
 // ---- combine.hip
 hipError_t launch_combine(const float* y, const float* w, int64_t T, int32_t k, int32_t L, uint16_t* z,

@@ -101,6 +101,10 @@ def test_forward_argument_errors_return_before_any_launch():
     assert fwd(k3(), ws_bytes=1024) == -3
     assert fwd(k3(), ws=FAKE + (2 << 30) + 8) == -1            # misaligned workspace
     assert fwd(k3(), bias=FAKE + 2) == -1                      # misaligned bias
+    r = moe.RoutingOut(saliency=FAKE + 4)                      # misaligned fp64 saliency
+    assert moe.lib().moe_layer_forward(FAKE, FAKE + (3 << 30), FAKE + (4 << 30), FAKE + (5 << 30), FAKE + (6 << 30),
+                                       16, ctypes.byref(k3()), None, FAKE + (1 << 30), ctypes.byref(r),
+                                       FAKE + (2 << 30), 1 << 40, None) == -1
 
 
 def test_stage_argument_errors():
@@ -140,20 +144,34 @@ def test_packed_layout_sizes_and_pack_errors():
     assert pack(FAKE, 4, 3584, 3072, FAKE + 4096, None) == -1            # overlapping buffers
 
 
-def test_config_struct_layout_matches_header(tmp_path):
-    """The ctypes mirror of moe_config has the header's size and field offsets."""
+@pytest.mark.parametrize("cname,pyname", [("moe_config", "MoEConfig"), ("moe_routing_out", "RoutingOut")])
+def test_struct_layout_matches_header(tmp_path, cname, pyname):
+    """The ctypes mirrors of the ABI's structs have the header's size and field offsets."""
     import subprocess
-    fields = [f[0] for f in moe.MoEConfig._fields_]
+    cls = getattr(moe, pyname)
+    fields = [f[0] for f in cls._fields_]
     src = tmp_path / "layout.c"
     src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "moe_layer.h"\nint main(void) {\n'
-                   '  printf("%zu\\n", sizeof(moe_config));\n' +
-                   "".join(f'  printf("%zu\\n", offsetof(moe_config, {f}));\n' for f in fields) + "  return 0;\n}\n")
+                   f'  printf("%zu\\n", sizeof({cname}));\n' +
+                   "".join(f'  printf("%zu\\n", offsetof({cname}, {f}));\n' for f in fields) + "  return 0;\n}\n")
     exe = tmp_path / "layout"
     inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
     subprocess.run(["gcc", "-std=c99", "-I", inc, str(src), "-o", str(exe)], check=True)
     got = [int(v) for v in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()]
-    assert got[0] == ctypes.sizeof(moe.MoEConfig)
-    assert got[1:] == [getattr(moe.MoEConfig, f).offset for f in fields]
+    assert got[0] == ctypes.sizeof(cls)
+    assert got[1:] == [getattr(cls, f).offset for f in fields]
+
+
+def test_reap_keep_bias_errors_before_any_launch():
+    L = moe.lib()
+    assert L.moe_reap_keep_bias(None, 896, 242, FAKE, None) == -1
+    assert L.moe_reap_keep_bias(FAKE, 896, 242, None, None) == -1
+    assert L.moe_reap_keep_bias(FAKE, 896, 897, FAKE, None) == -1       # more kept than experts
+    assert L.moe_reap_keep_bias(FAKE, 896, -1, FAKE, None) == -1
+    assert L.moe_reap_keep_bias(FAKE, 0, 0, FAKE, None) == -1
+    assert L.moe_reap_keep_bias(FAKE + 4, 896, 242, FAKE, None) == -1   # fp64 saliency misaligned
+    assert L.moe_reap_keep_bias(FAKE, 896, 242, FAKE + 2, None) == -1   # fp32 bias misaligned
+    assert L.moe_reap_keep_bias(FAKE, 2048, 242, FAKE, None) == -2      # more experts than one block ranks
 
 
 def test_streamed_forward_slots_and_errors_before_any_launch():

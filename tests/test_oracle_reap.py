@@ -3,9 +3,7 @@ S_j |C| = sum over tokens of g_j ||e_j||_2 and pruning as a router bias of -inf 
 weights renormalised over the experts left."""
 import numpy as np
 import pytest
-import torch
 
-import mxfp4_expert_gemm_amd as moe
 import oracle
 import synth
 from _util import bf16_bits_to_f64
@@ -71,17 +69,14 @@ def test_pruned_layer_equals_the_layer_of_the_survivors():
     assert np.array_equal(rs["w"], rp["w"]) and np.array_equal(rs["out"], rp["out"])
 
 
-def test_prune_bias_keeps_the_most_salient_and_random_sets_overlap_27pct():
-    s = torch.tensor([0.5, 3.0, 3.0, 0.1, 2.0, 0.0], dtype=torch.float64)
-    b = moe.reap_prune_bias(s, 3)
-    assert b.tolist() == [float("-inf"), 0.0, 0.0, float("-inf"), 0.0, float("-inf")]
-    # two random keep sets of 242 of 896 share 242/896 = 27% of their experts on average,
-    # the page's baseline for the domain-clustering comparison
-    rng = np.random.default_rng(9)
-    ov = [len(set(rng.choice(896, 242, replace=False)) & set(rng.choice(896, 242, replace=False))) / 242
-          for _ in range(400)]
-    assert abs(np.mean(ov) - 242 / 896) < 0.01
+def test_tier_fractions():
+    """The REAP tiers keep 242 and 179 of 896 experts (kimi-k3-mlx digest, REAP section):
+    27% and 20%, and 27% is also the expected overlap of two random 242-of-896 keep sets,
+    the baseline the domain-clustering section measures against (a hypergeometric mean:
+    242 x 242 / 896 shared experts).  The keep sets themselves come from GPU saliency in
+    the GPU tests (moe_reap_keep_bias, and the prefill32k domain keep sets)."""
     assert round(242 / 896, 2) == 0.27 and round(179 / 896, 2) == 0.20
+    assert abs((242 * 242 / 896) / 242 - 0.27) < 0.005
 
 
 def test_fewer_survivors_than_k_fill_with_zero_weights():
