@@ -354,7 +354,8 @@ moe_status moe_combine(const float* y, const float* topk_w, int64_t num_tokens, 
  * moe_layer_forward / moe_route: it is never selected while k or more experts remain and
  * the weights are renormalised over the experts left.  With fewer than k left, every
  * survivor is selected and the other slots take the lowest-numbered pruned experts at
- * weight 0 (ties at -inf go to the lower index); that routing takes the exact path. */
+ * weight 0 (ties at -inf go to the lower index); that routing takes the general path,
+ * where a pruned expert's logit is known to be exactly -inf and is not recomputed. */
 moe_status moe_reap_saliency(const float* y, const float* topk_w, const int32_t* perm,
                              const int32_t* expert_offsets, int64_t num_tokens, int32_t k,
                              int32_t d_latent, int32_t num_experts, double* saliency,

@@ -380,21 +380,26 @@ __device__ __forceinline__ void route_token_general(const RouteArgs& a, int64_t 
     const float M = wave_min_dpp(Mloc), m = wave_max_dpp(mloc);
     const bool all = (a.flags & MOE_ROUTE_EXACT_ALL) != 0;
     if (all || (k < E && !(M > m))) {
-      uint32_t amb = 0, cin = 0;
+      // amb: undecided experts, ranked below on exact values; known: those among them
+      // whose interval is a point (a pruned expert's exact -inf), already in val
+      uint32_t amb = 0, cin = 0, known = 0;
 #pragma unroll
       for (int i = 0; i < ROUTE_MAXI; ++i) {
         const int e = i * WAVE + lane;
         if (e < E) {
           if (all) amb |= 1u << i;
           else if (((sel >> i) & 1u) && lo[i] > m) cin |= 1u << i;
-          else if (lo[i] <= m && hi[i] >= M) amb |= 1u << i;
+          else if (lo[i] <= m && hi[i] >= M) {
+            amb |= 1u << i;
+            if (lo[i] == hi[i]) known |= 1u << i;
+          }
         }
       }
       int n_in = 0, n_amb = 0;
 #pragma unroll
       for (int i = 0; i < ROUTE_MAXI; ++i) {
         n_in += __popcll(__ballot((cin >> i) & 1u));
-        unsigned long long bal = __ballot((amb >> i) & 1u);
+        unsigned long long bal = __ballot(((amb & ~known) >> i) & 1u);
         n_amb += __popcll(bal);
         while (bal) {
           const int l = __ffsll((long long)bal) - 1;

@@ -319,6 +319,19 @@ def test_combine():
     assert np.mean(got == want) > 0.999
 
 
+def test_combine_past_65535_tokens():
+    """More tokens than the grid's second dimension holds (the kernel loops over tokens):
+    every token, the last ones included, as the oracle's fp64 combine."""
+    rng = np.random.default_rng(2)
+    T, k, L = 70001, 2, 128
+    y = rng.standard_normal((T * k, L)).astype(np.float32)
+    w = rng.random((T, k)).astype(np.float32)
+    got = from_dev(moe.combine(to_dev(y), to_dev(w), dtype=torch.int16))
+    want = oracle.combine(y, w)
+    assert np.array_equal(got[65530:], want[65530:])
+    assert np.mean(got == want) > 0.999
+
+
 # ------------------------------------------------------------- whole layer
 
 def _layer_case(name, T=None, sample=None):
@@ -367,6 +380,16 @@ def _layer_case(name, T=None, sample=None):
 
 def test_layer_tiny():
     _layer_case("tiny")
+
+
+def test_layer_tiny_past_65535_tokens():
+    """70001 tokens: more than a grid's second dimension holds; outputs of tokens on both
+    sides of 65535 against the oracle, routing and grouping of every token checked."""
+    out, got = _layer_case("tiny", T=70001, sample=[0, 65534, 65535, 65536, 70000])
+    h = host_layer("tiny", 70001)
+    assert h["bias"] is None
+    ridx = oracle.select(oracle.router_logits(h["x"], h["router_w"], None, threads=ORACLE_THREADS), h["cfg"].k)[0]
+    assert np.array_equal(got["topk_idx"], ridx)
 
 
 def test_layer_decode1():
