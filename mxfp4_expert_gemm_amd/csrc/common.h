@@ -319,6 +319,21 @@ __device__ __forceinline__ float finite_abs(float v) {
 // product that reads it is NaN (an infinity cannot be encoded in E4M3)
 constexpr uint32_t E4M3_NAN = 0x7Fu;
 
+// Four values (a scaled block element each, |a| < 256, or 0) to their e4m3 codes in one
+// dword (value j in byte j) and their rounded values, on the hardware conversion
+// (v_cvt_pk_fp8_f32 rounds to nearest even like e4m3_rne: checked equal on every bf16
+// value below 448, codes and rounded values, which covers every input here: bf16 values
+// and their exact residuals times powers of two).
+__device__ __forceinline__ uint32_t e4m3x4_hw(float a0, float a1, float a2, float a3, float (&q)[4]) {
+  int d = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false);
+  d = __builtin_amdgcn_cvt_pk_fp8_f32(a2, a3, d, true);
+  q[0] = __builtin_amdgcn_cvt_f32_fp8(d, 0);
+  q[1] = __builtin_amdgcn_cvt_f32_fp8(d, 1);
+  q[2] = __builtin_amdgcn_cvt_f32_fp8(d, 2);
+  q[3] = __builtin_amdgcn_cvt_f32_fp8(d, 3);
+  return (uint32_t)d;
+}
+
 __device__ __forceinline__ void quantize_quad8(const float (&v)[8], uint32_t (&hi)[2], uint32_t (&lo)[2], uint32_t& shi,
                                                uint32_t& slo) {
   float amax = 0.f;
@@ -330,23 +345,31 @@ __device__ __forceinline__ void quantize_quad8(const float (&v)[8], uint32_t (&h
   const float s_hi = 1.f / inv;
   float r[8];
   float rmax = 0.f;
-  hi[0] = hi[1] = 0u;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    float q;
-    const bool fin = finite_abs(v[i]) == fabsf(v[i]);
-    const uint32_t code = e4m3_rne(fin ? v[i] * inv : 0.f, q);
-    hi[i / 4] |= (fin ? code : E4M3_NAN) << (8 * (i % 4));
-    r[i] = fin ? v[i] - q * s_hi : 0.f;
-    rmax = fmaxf(rmax, fabsf(r[i]));
+  for (int h = 0; h < 2; ++h) {
+    bool fin[4];
+    float a[4], q[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float x = v[4 * h + j];
+      fin[j] = finite_abs(x) == fabsf(x);
+      a[j] = fin[j] ? x * inv : 0.f;
+    }
+    uint32_t d = e4m3x4_hw(a[0], a[1], a[2], a[3], q);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (!fin[j]) d = (d & ~(0xFFu << (8 * j))) | (E4M3_NAN << (8 * j));
+      r[4 * h + j] = fin[j] ? v[4 * h + j] - q[j] * s_hi : 0.f;
+      rmax = fmaxf(rmax, fabsf(r[4 * h + j]));
+    }
+    hi[h] = d;
   }
   rmax = quad_max(rmax);
   slo = block_scale(rmax, inv);
-  lo[0] = lo[1] = 0u;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    float q;
-    lo[i / 4] |= e4m3_rne(r[i] * inv, q) << (8 * (i % 4));
+  for (int h = 0; h < 2; ++h) {
+    float q[4];
+    lo[h] = e4m3x4_hw(r[4 * h] * inv, r[4 * h + 1] * inv, r[4 * h + 2] * inv, r[4 * h + 3] * inv, q);
   }
 }
 
