@@ -832,19 +832,20 @@ __global__ void __launch_bounds__(RB_THREADS) route_permute_one_kernel(RouteArgs
     }
     key = order_key(c);
   }
+  // the maximum of each 16-lane row (a group), by DPP within the row
+  static_assert(RB_GROUP == 16, "a group is one DPP row");
   uint32_t gm = key;
-#pragma unroll
-  for (int o = 1; o < RB_GROUP; o <<= 1) {
-    const uint32_t ov = (uint32_t)__shfl_xor((int)gm, o);
-    gm = ov > gm ? ov : gm;
-  }
+  gm = max(gm, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)gm, DPP_QUAD_1032, 0xF, 0xF, false));
+  gm = max(gm, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)gm, DPP_QUAD_2301, 0xF, 0xF, false));
+  gm = max(gm, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)gm, DPP_ROW_ROR4, 0xF, 0xF, false));
+  gm = max(gm, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)gm, DPP_ROW_ROR8, 0xF, 0xF, false));
   if ((lane & (RB_GROUP - 1)) == 0) S.gmax[tid / RB_GROUP] = gm;
-  __syncthreads();
+  lds_barrier();
   if (wave == 0) {
     const uint32_t t0 = kth_of_lanes(S.gmax[lane], k);
     if (lane == 0) S.tau = t0;
   }
-  __syncthreads();
+  lds_barrier();
   const uint32_t tau = S.tau;
   const bool cand = key != 0u && key >= tau;
   const unsigned long long cb = __ballot(cand);
@@ -855,7 +856,7 @@ __global__ void __launch_bounds__(RB_THREADS) route_permute_one_kernel(RouteArgs
     S.wcnt[wave] = __popcll(cb);
     S.wup[wave] = up;
   }
-  __syncthreads();
+  lds_barrier();
   int base = 0, n_c = 0;
 #pragma unroll
   for (int w = 0; w < RB_WAVES; ++w) {
@@ -872,7 +873,7 @@ __global__ void __launch_bounds__(RB_THREADS) route_permute_one_kernel(RouteArgs
     S.rl.cval[pos] = c;
     S.rl.crad[pos] = R;
   }
-  __syncthreads();
+  lds_barrier();
   if (fits) {
     // wave w ranks candidates 4w..4w+3 against all: rank = candidates ahead of it
     const unsigned long long pj = lane < n_c ? S.cpk[lane] : 0ull;
@@ -884,7 +885,7 @@ __global__ void __launch_bounds__(RB_THREADS) route_permute_one_kernel(RouteArgs
       if (lane == 0 && i < n_c) S.crank[i] = r;
     }
   }
-  __syncthreads();
+  lds_barrier();
   if (wave == 0) {
     bool fast = fits && a.renormalize && !(a.flags & MOE_ROUTE_EXACT_ALL);
     if (fast) {
@@ -919,7 +920,7 @@ __global__ void __launch_bounds__(RB_THREADS) route_permute_one_kernel(RouteArgs
     if (qg) quantize_group8(hraw, a.hq, jq, a.mxfp8 != 0);
     if (ng > RB_QT) quantize_quads(a.h, a.hq, a.L, jq + RB_QT, RB_QT, a.mxfp8 != 0);
   }
-  __syncthreads();  // the k selected experts, ascending, are in S.rl.oidx
+  lds_barrier();  // the k selected experts, ascending, are in S.rl.oidx
   const bool decided = S.decided;
   if (decided && a.logits_out && have) a.logits_out[e] = c;
   // one row per selected expert: offsets[e] = selected experts below e
