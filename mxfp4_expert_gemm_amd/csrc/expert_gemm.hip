@@ -20,9 +20,9 @@
 // or two 32-row groups of down) and the tile's 32-row token sub-tiles; a K step of 128 is
 // two half-steps of 64.  Weight operands are loaded per wave straight from memory into
 // registers, PF steps ahead; the activation tile moves through LDS in chunks of 128
-// row-steps (two K steps of 64 rows, four of 32), double-buffered: the loads of chunk c+1
-// are in registers while chunk c is computed, and one barrier per chunk hands the buffers
-// over.  Two blocks share a CU.
+// row-steps (two K steps of 64 rows, four of 32), double-buffered: chunk c+1 is loaded
+// straight into the other buffer while chunk c is computed, and one barrier per chunk
+// hands the buffers over.  Two blocks share a CU.
 //
 // The grid is ordered so that each XCD (blocks b with the same b mod 8) works through a
 // contiguous range of tiles: the tiles of one expert, and the row blocks of one token
@@ -53,106 +53,111 @@ constexpr int GT_BUF_BYTES = (GT_CHUNK_ROWSTEPS / GT_TOK) * gt_step_bytes(GT_TOK
 static_assert((GT_CHUNK_ROWSTEPS / 16) * gt_step_bytes(16) == GT_BUF_BYTES &&
                   (GT_CHUNK_ROWSTEPS / 32) * gt_step_bytes(32) == GT_BUF_BYTES,
               "every chunk shape fills the same buffer");
-// This thread's share of one chunk: gt_nu 16-byte code pieces and one scale dword.
-// TERMS = 2: the two exact e4m3 terms of bf16 activations; TERMS = 1: the MXFP8 mode,
-// whose second term is zero and is neither moved nor multiplied.
-template <int TERMS>
-constexpr int gt_nu() { return GT_CHUNK_ROWSTEPS * TERMS * 8 / 256; }  // 8 pieces per row-step and term
-template <int TERMS>
-constexpr int gt_ns() { return GT_CHUNK_ROWSTEPS * TERMS; }  // scale dwords per chunk
-template <int TERMS>
-struct GtRegs {
-  u32x4_t v[gt_nu<TERMS>()];
-  uint32_t s;
-};
-
-template <int R>
-constexpr int gt_log2() { return R == 16 ? 4 : R == 32 ? 5 : 6; }
-
-// This thread's share of every chunk, fixed for the whole K loop.  Item j = tid + 256 u
-// of a chunk is (step, term, row, 16-byte piece); with tid < 256 its row and piece depend
-// on tid alone (row tid/8, or tid/8 + 32 for odd u at R = 64; piece tid mod 8) and its
-// step and term on u alone (plus bit tid/128 at R = 16), so the global row offsets and the
-// LDS offsets are computed once per tile rather than once per chunk.
+// Each chunk goes from memory straight into LDS (global_load_lds_dwordx4 and _dword: lane
+// i of a wave writes what it loads to LDS at the instruction's base + 16 i, or + 4 i, so
+// the swizzle is applied on the source side), with no staging registers.  A chunk of a
+// tile padded to R rows holds CH = 128 / R K steps; per step, TERMS code planes of R rows
+// x 128 bytes and the scale dwords (TERMS = 2: the two exact e4m3 terms of bf16
+// activations; TERMS = 1: the MXFP8 mode, whose second term is zero and is neither moved
+// nor multiplied).  Its 16 TERMS code blocks of 1 KB (8 rows of one step and term) go four
+// to a wave, block j = 4 u + wave for the wave's u-th load, so a lane's rows are
+// 8 wave + lane / 8 plus 32 (u / (R / 32)) mod 2 at R = 64; its 128 TERMS scale bytes lie
+// in one step.  The loads are counted by vmcnt like any other: the chunk's last reader
+// waits for them before the barrier that hands the buffer over (gt_wait_barrier).
 template <int TERMS, int R>
-struct GtThr {
-  static constexpr int NR = R == 64 ? 2 : 1;  // distinct rows of the thread's pieces
-  int64_t src[NR];   // srow[m] * K + 16 * piece
-  int32_t dst[NR];   // m * GT_RS + 16 * (piece ^ gt_swz(m)), plus the tid/128 part at R = 16
-  int tb;            // R = 16: tid / 128 (the term with two terms, else a step offset)
-  int64_t ssrc;      // scale dword: srow[m_s] * (K / 32)
-  int32_t sdst;      // its LDS offset
-  int ss, st;        // its step and term
+struct GtDma {
+  static constexpr int CH = GT_CHUNK_ROWSTEPS / R;  // K steps per chunk
+  static constexpr int RB = R / 8;                   // code blocks per step and term
+  static constexpr int NA = RB / 4;                  // distinct rows of a lane's code loads
+  static constexpr int NU = 4 * TERMS;               // code loads per wave and chunk
+  static constexpr int WPS = R / 32;                 // waves sharing one step's scale bytes
+  int64_t src[NA];   // srow[m] * K + 16 * ((lane mod 8) ^ gt_swz(m)), m = 32 a + 8 wave + lane / 8
+  int64_t ssrc;      // srow[m_s] * (K / 32): the lane's scale dword (lanes < 32 TERMS)
+  const uint8_t* sbase;  // its scale plane (hi or lo)
+  int ss;            // step of the wave's scale bytes within the chunk
+  int soff;          // their LDS offset within the step
 };
 
 template <int TERMS, int R>
-__device__ __forceinline__ GtThr<TERMS, R> gt_thread(const int64_t* srow, int K) {
-  constexpr int LR = gt_log2<R>(), SB = gt_step_bytes(R);
-  const int tid = threadIdx.x, part = tid & 7;
-  GtThr<TERMS, R> t;
-  t.tb = R == 16 ? tid >> 7 : 0;
+__device__ __forceinline__ GtDma<TERMS, R> gt_dma_setup(const QRows& q, const int64_t* srow, int K, int wave,
+                                                       int lane) {
+  using D = GtDma<TERMS, R>;
+  D t;
 #pragma unroll
-  for (int i = 0; i < t.NR; ++i) {
-    const int m = R == 64 ? (tid >> 3) + 32 * i : (tid >> 3) & (R - 1);
-    t.src[i] = srow[m] * K + 16 * part;
-    t.dst[i] = m * GT_RS + 16 * (part ^ gt_swz(m));
-    if (R == 16) t.dst[i] += TERMS == 2 ? t.tb * R * GT_RS : t.tb * SB;
+  for (int a = 0; a < D::NA; ++a) {
+    const int m = 32 * a + 8 * wave + (lane >> 3);
+    t.src[a] = srow[m] * K + 16 * ((lane & 7) ^ gt_swz(m));
   }
-  const int it = tid & (gt_ns<TERMS>() - 1);  // CH x R rows x TERMS
-  const int ms = (it >> (TERMS - 1)) & (R - 1);
-  t.ss = it >> (LR + TERMS - 1);
-  t.st = TERMS == 2 ? it & 1 : 0;
+  // scale bytes of the wave: step wave / WPS, bytes 128 TERMS (wave mod WPS) + 4 lane of
+  // that step's [hi R x 4][lo R x 4]
+  t.ss = wave / D::WPS;
+  t.soff = 2 * R * GT_RS + 128 * TERMS * (wave % D::WPS);
+  const int o = 128 * TERMS * (wave % D::WPS) + 4 * (lane < 32 * TERMS ? lane : 0);
+  const int term = o / (4 * R), ms = (o % (4 * R)) / 4;
+  t.sbase = term ? q.slo : q.shi;
   t.ssrc = srow[ms] * (K / 32);
-  t.sdst = t.ss * SB + 2 * R * GT_RS + t.st * R * 4 + ms * 4;
   return t;
 }
 
-// step and term of piece u (R = 16: plus the thread's tb, folded into src / dst)
-template <int TERMS, int R>
-__host__ __device__ constexpr int gt_piece_step(int u) {
-  return R == 64 ? (TERMS == 2 ? u >> 2 : u >> 1) : R == 32 ? (TERMS == 2 ? u >> 1 : u) : (TERMS == 2 ? u : 2 * u);
+// One wave-wide load of 16 (or 4) bytes a lane from g into LDS at lds + 16 lane (4 lane);
+// lds is wave-uniform.  Written as asm so that the compiler, which cannot tell which LDS
+// bytes such a load writes, does not wait for every load in flight before each LDS read:
+// the kernel waits for these loads itself (gt_wait_barrier).  No register receives data,
+// and m0, which the instruction takes its LDS base from, is restored (a write of m0 needs
+// one wait state before an instruction that reads it).
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint8_t*)p;
 }
-template <int TERMS, int R>
-__host__ __device__ constexpr int gt_piece_term(int u) {
-  return TERMS == 1 ? 0 : R == 64 ? (u >> 1) & 1 : R == 32 ? u & 1 : 0;
+__device__ __forceinline__ void lds_dma16(const void* g, const uint8_t* lds) {
+  uint32_t save;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_nop 0\n\t"
+               "s_mov_b32 m0, %0"
+               : "=&s"(save)
+               : "v"(g), "s"(lds_addr(lds))
+               : "memory");
 }
-
-// Loads chunk c (steps CH c .. CH c + CH - 1, CH = 128 / R) of the tile's R rows.  Every
-// load is issued: rows past the tile read the row srow holds for them (a valid token)
-// and steps past the end re-read the last step, so the loads in flight are the same on
-// every path (see prime_stream); what they bring for such rows and steps is never used.
-// Threads past the chunk's gt_ns scale dwords repeat the loads of the threads below them
-// (and do not store them), for the same reason.
-template <int TERMS, int R>
-__device__ __forceinline__ void gt_load(GtRegs<TERMS>& r, const QRows& q, const GtThr<TERMS, R>& t, int nks,
-                                        int c) {
-  constexpr int CH = 128 / R;
-  // R = 16 with two terms: the thread's term is tb; with one term, tb shifts the step
-  const uint8_t* hi16 = TERMS == 2 && R == 16 && t.tb ? q.lo : q.hi;
-  const int sofs = TERMS == 1 && R == 16 ? t.tb : 0;
-  unroll_n<gt_nu<TERMS>()>([&](auto uc) {
-    constexpr int u = decltype(uc)::value;
-    constexpr int s = gt_piece_step<TERMS, R>(u), term = gt_piece_term<TERMS, R>(u);
-    const int ks0 = CH * c + s + sofs;
-    const int ks = ks0 < nks ? ks0 : nks - 1;
-    const uint8_t* base = R == 16 ? hi16 : term ? q.lo : q.hi;
-    r.v[u] = *reinterpret_cast<const u32x4_t*>(base + t.src[R == 64 ? (u & 1) : 0] + 128 * ks);
-  });
-  {
-    const int ks = CH * c + t.ss < nks ? CH * c + t.ss : nks - 1;
-    r.s = *reinterpret_cast<const uint32_t*>((t.st ? q.slo : q.shi) + t.ssrc + 4 * ks);
-  }
+__device__ __forceinline__ void lds_dma4(const void* g, const uint8_t* lds) {
+  uint32_t save;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %1, off\n\ts_nop 0\n\t"
+               "s_mov_b32 m0, %0"
+               : "=&s"(save)
+               : "v"(g), "s"(lds_addr(lds))
+               : "memory");
 }
 
+// Issues the loads of chunk c (steps CH c .. CH c + CH - 1) into buf: NU code loads and
+// one scale load per wave.  Steps past the end re-read the last step (never used).  buf
+// and wave are wave-uniform.  The empty asm keeps the compiler from moving later memory
+// operations above these loads, so the loads counted after them by gt_wait_barrier are
+// the ones issued after them.
 template <int TERMS, int R>
-__device__ __forceinline__ void gt_store(const GtRegs<TERMS>& r, const GtThr<TERMS, R>& t, uint8_t* buf) {
+__device__ __forceinline__ void gt_dma(const GtDma<TERMS, R>& t, const QRows& q, int nks, int c, uint8_t* buf,
+                                       int wave, int lane) {
+  using D = GtDma<TERMS, R>;
   constexpr int SB = gt_step_bytes(R);
-  unroll_n<gt_nu<TERMS>()>([&](auto uc) {
+  unroll_n<D::NU>([&](auto uc) {
     constexpr int u = decltype(uc)::value;
-    constexpr int s = gt_piece_step<TERMS, R>(u), term = gt_piece_term<TERMS, R>(u);
-    *reinterpret_cast<u32x4_t*>(buf + s * SB + term * R * GT_RS + t.dst[R == 64 ? (u & 1) : 0]) = r.v[u];
+    constexpr int s = u / (TERMS * D::RB / 4);
+    constexpr int term = TERMS == 2 ? (u / (D::RB / 4)) & 1 : 0;
+    constexpr int a = u % D::NA;
+    const int ks0 = D::CH * c + s;
+    const int ks = ks0 < nks ? ks0 : nks - 1;
+    lds_dma16((term ? q.lo : q.hi) + t.src[a] + 128 * ks, buf + s * SB + term * R * GT_RS + (4 * a + wave) * 1024);
   });
-  if (threadIdx.x < gt_ns<TERMS>()) *reinterpret_cast<uint32_t*>(buf + t.sdst) = r.s;
+  if (lane < 32 * TERMS) {
+    const int ks0 = D::CH * c + t.ss;
+    const int ks = ks0 < nks ? ks0 : nks - 1;
+    lds_dma4(t.sbase + t.ssrc + 4 * ks, buf + t.ss * SB + t.soff);
+  }
+  asm volatile("" ::: "memory");
+}
+
+// Waits until at most N of this wave's memory loads are outstanding (N: the loads it
+// issued after the chunk's gt_dma), then the block barrier that publishes the chunk.
+template <int N>
+__device__ __forceinline__ void gt_wait_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
 // logical block of physical block b: XCD x = b mod 8 runs logical blocks
@@ -328,14 +333,15 @@ __device__ __forceinline__ void gt32_read(i32x8& hi, i32x8& lo, uint32_t& shi, u
 template <class W, int NMAT, int PF, int TERMS, int R>
 __device__ __forceinline__ void gt32_mainloop(const W (&w)[NMAT], const QRows& q, const int64_t* srow, int n, int K,
                                               uint8_t* lds, f32x16 (&acc)[NMAT][R / 32]) {
-  constexpr int CH = GT_CHUNK_ROWSTEPS / R;
+  using D = GtDma<TERMS, R>;
+  constexpr int CH = D::CH;
   static_assert(16 % PF == 0 && 16 % CH == 0, "ring and chunks repeat every 16 steps");
   const int lane = lane_id(), g = lane >> 5, nl = lane & 31;
-  const int nks = K / 128, nc = (nks + 15) / 16;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / WAVE));
+  const int nks = K / 128, nc = (nks + 15) / 16, nch = (nks + CH - 1) / CH;
   const int ntt = (n + 31) / 32;  // token sub-tiles holding rows
-  const GtThr<TERMS, R> thr = gt_thread<TERMS, R>(srow, K);
-  GtRegs<TERMS> rg;
-  gt_load<TERMS, R>(rg, q, thr, nks, 0);
+  const D dt = gt_dma_setup<TERMS, R>(q, srow, K, wave, lane);
+  gt_dma<TERMS, R>(dt, q, nks, 0, lds, wave, lane);
   W32Step ring[NMAT][PF];
 #pragma unroll
   for (int d = 0; d < PF; ++d)
@@ -345,9 +351,7 @@ __device__ __forceinline__ void gt32_mainloop(const W (&w)[NMAT], const QRows& q
   typename W::Scales sc[NMAT][2];
 #pragma unroll
   for (int mq = 0; mq < NMAT; ++mq) sc[mq][0] = w32_group(w[mq], 0, nks);
-  gt_store<TERMS, R>(rg, thr, lds);
-  gt_load<TERMS, R>(rg, q, thr, nks, 1);
-  lds_barrier();
+  gt_wait_barrier<PF * NMAT * 2>();  // chunk 0: the weight ring's loads were issued after it
   for (int cb = 0; cb < nc; ++cb) {
     unroll16([&](auto jc) {
       constexpr int J = decltype(jc)::value;
@@ -367,7 +371,7 @@ __device__ __forceinline__ void gt32_mainloop(const W (&w)[NMAT], const QRows& q
       }
       if (ks < nks) {
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
+        for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
           for (int tt = 0; tt < R / 32; ++tt) {
             if (tt >= ntt) continue;  // token sub-tile past the tile's rows
@@ -382,11 +386,19 @@ __device__ __forceinline__ void gt32_mainloop(const W (&w)[NMAT], const QRows& q
               if constexpr (TERMS == 2) acc[mq][tt] = mx_mfma32<W::opsel(J)>(alo, b, acc[mq][tt], slo, sw);
             }
           }
+          // Chunk ch + 1 goes into the buffer chunk ch - 1 left (every wave passed the
+          // barrier after it), issued within the chunk's first step: the compiler's waits
+          // for the weight loads issued before it also wait for these loads, and the
+          // first such wait comes a step later.
+          if constexpr (J % CH == 0)
+            if (hh == 0 && ch + 1 < nch)
+              gt_dma<TERMS, R>(dt, q, nks, ch + 1, lds + ((ch + 1) & 1) * GT_BUF_BYTES, wave, lane);
+        }
       }
       if constexpr (J % CH == CH - 1) {
-        gt_store<TERMS, R>(rg, thr, lds + ((ch + 1) & 1) * GT_BUF_BYTES);
-        gt_load<TERMS, R>(rg, q, thr, nks, ch + 2);
-        lds_barrier();
+        // chunk ch + 1 is in LDS once the loads issued after it, the weight loads of the
+        // chunk's later CH - 1 steps, are all that may be outstanding
+        gt_wait_barrier<(CH - 1) * NMAT * 2>();
       }
     });
   }
