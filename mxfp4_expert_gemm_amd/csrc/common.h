@@ -21,12 +21,12 @@ __device__ __forceinline__ float bf16lo(uint32_t v) { return __uint_as_float(v <
 __device__ __forceinline__ float bf16hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
 __device__ __forceinline__ float bf16f(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
 
-// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.  Both results are
+// formed and one is kept by a mask, so no branch is taken per value.
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t nan = 0u - (uint32_t)(f != f);
+  return (uint16_t)((((u | 0x00400000u) & nan) | ((u + 0x7FFFu + ((u >> 16) & 1u)) & ~nan)) >> 16);
 }
 
 // fp64 -> bf16 bits, round to nearest even in one step (no detour through fp32):

@@ -433,23 +433,33 @@ __device__ __forceinline__ void gateup32_tile(const MxArgs& p, int e, int rt, in
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[mq][tt][v] = 0.f;
   gt32_mainloop<WS, 2, gt32_pf<TERMS, R>(), TERMS, R>(w, p.hq, srow, n, L, lds, acc);
-  lds_barrier();  // the activation buffers are free (the weight loads still in flight are not needed)
-  float* at = reinterpret_cast<float*>(lds);  // [64 tokens][GT32_FROWS + 1]
+  // the GLU of every accumulator row (rows past n are computed and never read), then the
+  // tile into LDS [64 tokens][GT32_FROWS + 1] once the activation buffers are free
+  float* at = reinterpret_cast<float*>(lds);
   constexpr int AS = GT32_FROWS + 1;
   static_assert(64 * AS * 4 + 2 * 64 * 4 <= 2 * GT_BUF_BYTES, "the GLU tile and its scale bytes fit the chunk buffers");
   uint8_t* sc = lds + 64 * AS * 4;           // scale bytes [term][64 tokens][4 blocks]
   const int fl = 32 * wave + nl, f = rt * GT32_FROWS + fl;
+  uint16_t ab[R / 32][16];
 #pragma unroll
   for (int tt = 0; tt < R / 32; ++tt)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int m = 32 * tt + 8 * (v >> 2) + 4 * g + (v & 3);
-      if (m < n) {
-        const uint16_t ab = glu_bf16(acc[0][tt][v], acc[1][tt][v]);
-        at[m * AS + fl] = bf16f(ab);
-        if (p.a_bf16) p.a_bf16[(int64_t)sslot[m] * F + f] = ab;
+    for (int v = 0; v < 16; ++v) ab[tt][v] = glu_bf16(acc[0][tt][v], acc[1][tt][v]);
+  if (p.a_bf16) {
+#pragma unroll
+    for (int tt = 0; tt < R / 32; ++tt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = 32 * tt + 8 * (v >> 2) + 4 * g + (v & 3);
+        if (m < n) p.a_bf16[(int64_t)sslot[m] * F + f] = ab[tt][v];
       }
-    }
+  }
+  lds_barrier();  // the activation buffers are free
+  float* atl = at + (4 * g) * AS + fl;
+#pragma unroll
+  for (int tt = 0; tt < R / 32; ++tt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) atl[(32 * tt + 8 * (v >> 2) + (v & 3)) * AS] = bf16f(ab[tt][v]);
   lds_barrier();
   for (int it = threadIdx.x; it < R * (GT32_FROWS / 8); it += blockDim.x) {
     // a quad of lanes per (token, scale block): R tokens x 4 blocks x 4 lanes
