@@ -72,7 +72,7 @@ Layout layout(const moe_config& c, int k) {
   l.aq_slo = take(T * K * F / 32);
   l.y = take(T * K * L * 4);
   l.z = take(T * L * 2);
-  l.gtiles = take((size_t)gemm_max_tiles((int64_t)(T * K), (int32_t)E) * 16);
+  l.gtiles = take(gemm_tiles_bytes((int64_t)(T * K), (int32_t)E));
   l.salp = take(T * K * (size_t)sal_chunks(c, k) * 8);
   l.tiles_s = take(E * 16);
   l.counts_s = take(E * 4);
@@ -96,7 +96,7 @@ Layout layout(const moe_config& c, int k) {
     l.sq_shi = take(T * S * FS / 32);
     l.sq_slo = take(T * S * FS / 32);
     l.s_y = take(T * S * D * 4);
-    l.s_gtiles = take((size_t)gemm_max_tiles((int64_t)(T * S), (int32_t)S) * 16);
+    l.s_gtiles = take(gemm_tiles_bytes((int64_t)(T * S), (int32_t)S));
   }
   l.total = off;
   return l;

@@ -24,9 +24,11 @@
 // straight into the other buffer while chunk c is computed, and one barrier per chunk
 // hands the buffers over.  Two blocks share a CU.
 //
-// The grid is ordered so that each XCD (blocks b with the same b mod 8) works through a
-// contiguous range of tiles: the tiles of one expert, and the row blocks of one token
-// tile, meet in the same L2.
+// The grid is persistent: two blocks per CU, each taking (tile, row block) items from a
+// queue until it runs dry, so no block waits for a dispatch slot and no block waits for
+// another.  Each XCD (blocks b with the same b mod 8) has its own queue over one eighth of
+// the active items, a contiguous range: the tiles of one expert, and the row blocks of one
+// token tile, meet in the same L2.
 #include "mfma_stream.h"
 
 namespace moe {
@@ -160,9 +162,38 @@ __device__ __forceinline__ void gt_wait_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-// logical block of physical block b: XCD x = b mod 8 runs logical blocks
-// x * nb/8 .. (x+1) * nb/8 - 1 (nb a multiple of 8)
-__device__ __forceinline__ int gt_logical_block(int b, int nb) { return (b & 7) * (nb >> 3) + (b >> 3); }
+// The work queues after the tile list (gtiles[max_gtiles]): GT_QUEUE_INTS ints, set by
+// gemm_tiles_kernel before the GEMMs run: next-item counters of the gate/up GEMM per XCD
+// [0, 8), of the down GEMM [8, 16), and the number of active tiles [16].
+constexpr int GT_QUEUE_GATEUP = 0, GT_QUEUE_DOWN = 8, GT_QUEUE_TILES = 16;
+static_assert((GT_QUEUE_TILES + 1) * 4 <= GEMM_QUEUE_BYTES, "the queues fit their bytes");
+__device__ __forceinline__ int* gt_queue(const int4* gtiles, int max_gtiles) {
+  return reinterpret_cast<int*>(const_cast<int4*>(gtiles) + max_gtiles);
+}
+
+// The item loop of a persistent block: fn(lb) for logical items lb of this block's XCD
+// range [x W / 8, (x + 1) W / 8), W = nitems, taken one at a time from the XCD's counter.
+// The next item's ticket is requested when an item starts and read when it ends, so its
+// round trip overlaps the item.  Every thread leaves the loop on the same ticket.
+template <class Fn>
+__device__ __forceinline__ void gt_items(int* counter, int64_t nitems, Fn&& fn) {
+  __shared__ int ticket;
+  const int x = blockIdx.x & 7;
+  const int lo = (int)(nitems * x / 8), hi = (int)(nitems * (x + 1) / 8);
+  if (threadIdx.x == 0) ticket = atomicAdd(counter, 1);
+  __syncthreads();
+  int tk = ticket;
+  for (;;) {
+    __syncthreads();  // every thread has read the ticket
+    if (lo + tk >= hi) break;
+    int next = 0;
+    if (threadIdx.x == 0) next = atomicAdd(counter, 1);
+    fn(lo + tk);
+    if (threadIdx.x == 0) ticket = next;
+    __syncthreads();
+    tk = ticket;
+  }
+}
 
 // (tile, row block) of logical block lb.  Tiles go in groups of GT_GROUP consecutive
 // tiles (the tiles of a popular expert are consecutive in the list), and within a group
@@ -492,36 +523,30 @@ __device__ __forceinline__ void gateup32_tile(const MxArgs& p, int e, int rt, in
 }
 
 template <class W, int TERMS>
-__device__ __forceinline__ void gateup_gemm32_kernel_body(MxArgs p, const int4* __restrict__ gtiles, int ntiles,
-                                                          int nb) {
+__global__ void __launch_bounds__(256, 2) gateup_gemm32_kernel(MxArgs p, const int4* __restrict__ gtiles,
+                                                                int max_gtiles) {
+  clock_begin(p.clock);
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ int64_t srow[GT_TOK];
   __shared__ int sslot[GT_TOK];
-  const int nrt = p.F / GT32_FROWS;
-  const int lb = gt_logical_block(blockIdx.x, nb);
-  int ti, rt;
-  gt_tile_of(lb, ntiles, nrt, ti, rt);
-  if (ti >= ntiles) return;  // the grid is rounded up to a multiple of 8
-  const int4 tile = gtiles[ti];
-  if (tile.x < 0) return;
-  const int e = tile.x, r0 = tile.y, n = tile.z;
-  for (int m = threadIdx.x; m < GT_TOK; m += blockDim.x) {
-    const int sl = m < n ? p.perm[r0 + m] : 0;
-    sslot[m] = sl;
-    srow[m] = sl / p.k;
-  }
-  __syncthreads();
-  if (n <= 32)
-    gateup32_tile<W, TERMS, 32>(p, e, rt, n, srow, sslot, lds);
-  else
-    gateup32_tile<W, TERMS, 64>(p, e, rt, n, srow, sslot, lds);
-}
-
-template <class W, int TERMS>
-__global__ void __launch_bounds__(256, 2) gateup_gemm32_kernel(MxArgs p, const int4* __restrict__ gtiles, int ntiles,
-                                                                int nb) {
-  clock_begin(p.clock);
-  gateup_gemm32_kernel_body<W, TERMS>(p, gtiles, ntiles, nb);
+  int* queue = gt_queue(gtiles, max_gtiles);
+  const int nrt = p.F / GT32_FROWS, ntiles = queue[GT_QUEUE_TILES];
+  gt_items(queue + GT_QUEUE_GATEUP + (blockIdx.x & 7), (int64_t)ntiles * nrt, [&](int lb) {
+    int ti, rt;
+    gt_tile_of(lb, ntiles, nrt, ti, rt);
+    const int4 tile = gtiles[ti];
+    const int e = tile.x, r0 = tile.y, n = tile.z;
+    for (int m = threadIdx.x; m < GT_TOK; m += blockDim.x) {
+      const int sl = m < n ? p.perm[r0 + m] : 0;
+      sslot[m] = sl;
+      srow[m] = sl / p.k;
+    }
+    __syncthreads();
+    if (n <= 32)
+      gateup32_tile<W, TERMS, 32>(p, e, rt, n, srow, sslot, lds);
+    else
+      gateup32_tile<W, TERMS, 64>(p, e, rt, n, srow, sslot, lds);
+  });
   clock_end(p.clock);
 }
 
@@ -586,36 +611,31 @@ __device__ __forceinline__ void down32_tile(const MxArgs& p, int e, int rt, int 
 }
 
 template <class W, int TERMS, int NG>
-__device__ __forceinline__ void down_gemm32_kernel_body(MxArgs p, const int4* __restrict__ gtiles, int ntiles,
-                                                        int nb) {
+__global__ void __launch_bounds__(256, 2) down_gemm32_kernel(MxArgs p, const int4* __restrict__ gtiles,
+                                                              int max_gtiles) {
+  clock_begin(p.clock);
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ int64_t srow[GT_TOK];
-  const int nrt = p.L / (128 * NG);
-  const int lb = gt_logical_block(blockIdx.x, nb);
-  int ti, rt;
-  gt_tile_of(lb, ntiles, nrt, ti, rt);
-  if (ti >= ntiles) return;  // the grid is rounded up to a multiple of 8
-  const int4 tile = gtiles[ti];
-  if (tile.x < 0) return;
-  const int e = tile.x, r0 = tile.y, n = tile.z;
-  for (int m = threadIdx.x; m < GT_TOK; m += blockDim.x) srow[m] = m < n ? p.perm[r0 + m] : 0;
-  __syncthreads();
-  if (n <= 32)
-    down32_tile<W, TERMS, NG, 32>(p, e, rt, n, srow, lds);
-  else
-    down32_tile<W, TERMS, NG, 64>(p, e, rt, n, srow, lds);
-}
-
-template <class W, int TERMS, int NG>
-__global__ void __launch_bounds__(256, 2) down_gemm32_kernel(MxArgs p, const int4* __restrict__ gtiles, int ntiles,
-                                                              int nb) {
-  clock_begin(p.clock);
-  down_gemm32_kernel_body<W, TERMS, NG>(p, gtiles, ntiles, nb);
+  int* queue = gt_queue(gtiles, max_gtiles);
+  const int nrt = p.L / (128 * NG), ntiles = queue[GT_QUEUE_TILES];
+  gt_items(queue + GT_QUEUE_DOWN + (blockIdx.x & 7), (int64_t)ntiles * nrt, [&](int lb) {
+    int ti, rt;
+    gt_tile_of(lb, ntiles, nrt, ti, rt);
+    const int4 tile = gtiles[ti];
+    const int e = tile.x, r0 = tile.y, n = tile.z;
+    for (int m = threadIdx.x; m < GT_TOK; m += blockDim.x) srow[m] = m < n ? p.perm[r0 + m] : 0;
+    __syncthreads();
+    if (n <= 32)
+      down32_tile<W, TERMS, NG, 32>(p, e, rt, n, srow, lds);
+    else
+      down32_tile<W, TERMS, NG, 64>(p, e, rt, n, srow, lds);
+  });
   clock_end(p.clock);
 }
 
 // Tiles of GT_TOK routed rows per active expert, in expert order: gtiles[0, ntiles) =
-// {expert, first row in perm, rows, 0}; gtiles[ntiles, max_gtiles) = {-1, 0, 0, 0}.
+// {expert, first row in perm, rows, 0}; gtiles[ntiles, max_gtiles) = {-1, 0, 0, 0}; the
+// work queues after them cleared and the tile count set.
 __global__ void __launch_bounds__(1024) gemm_tiles_kernel(const int32_t* __restrict__ counts,
                                                           const int32_t* __restrict__ offsets, int E,
                                                           int4* __restrict__ gtiles, int max_gtiles) {
@@ -644,9 +664,13 @@ __global__ void __launch_bounds__(1024) gemm_tiles_kernel(const int32_t* __restr
     }
   }
   for (int j = total + tid; j < max_gtiles; j += 1024) gtiles[j] = make_int4(-1, 0, 0, 0);
+  int* queue = gt_queue(gtiles, max_gtiles);
+  if (tid < GT_QUEUE_TILES) queue[tid] = 0;
+  if (tid == GT_QUEUE_TILES) queue[tid] = total;
 }
 
 int64_t gemm_max_tiles(int64_t rows, int32_t E) { return ceil_div(rows, GT_TOK) + (rows < E ? rows : E); }
+size_t gemm_tiles_bytes(int64_t rows, int32_t E) { return (size_t)gemm_max_tiles(rows, E) * 16 + GEMM_QUEUE_BYTES; }
 
 hipError_t launch_gemm_tiles(const int32_t* counts, const int32_t* offsets, int32_t E, int4* gtiles,
                              int64_t max_gtiles, hipStream_t st) {
@@ -655,49 +679,70 @@ hipError_t launch_gemm_tiles(const int32_t* counts, const int32_t* offsets, int3
   return hipGetLastError();
 }
 
+// The persistent grid: two blocks per CU (what the registers and LDS allow), no more
+// blocks than items, a multiple of 8 so that every XCD runs the same number.
+constexpr int GT_BLOCKS_PER_CU = 2;
+static hipError_t gt_grid(int64_t nitems, unsigned& grid) {
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const int64_t full = (int64_t)GT_BLOCKS_PER_CU * cus / 8 * 8, want = (nitems + 7) / 8 * 8;
+  const int64_t g = want < full ? want : full;
+  grid = (unsigned)(g > 8 ? g : 8);
+  return hipSuccess;
+}
+
 template <class W, int TERMS>
-static hipError_t gateup_gemm32_go(const MxArgs& p, const int4* gtiles, int64_t max_gtiles, int64_t nb,
+static hipError_t gateup_gemm32_go(const MxArgs& p, const int4* gtiles, int64_t max_gtiles, unsigned grid,
                                    hipStream_t st, const KernelEvents& ev) {
   static const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gateup_gemm32_kernel<W, TERMS>),
                                                   hipFuncAttributeMaxDynamicSharedMemorySize, 2 * GT_BUF_BYTES);
   if (e != hipSuccess) return e;
-  return dispatch(ev, gateup_gemm32_kernel<W, TERMS>, dim3((unsigned)nb), dim3(256), 2 * GT_BUF_BYTES, st, p, gtiles,
-                  (int)max_gtiles, (int)nb);
+  return dispatch(ev, gateup_gemm32_kernel<W, TERMS>, dim3(grid), dim3(256), 2 * GT_BUF_BYTES, st, p, gtiles,
+                  (int)max_gtiles);
 }
 
 template <class W, int TERMS, int NG>
-static hipError_t down_gemm32_go(const MxArgs& p, const int4* gtiles, int64_t max_gtiles, int64_t nb, hipStream_t st,
-                                 const KernelEvents& ev) {
+static hipError_t down_gemm32_go(const MxArgs& p, const int4* gtiles, int64_t max_gtiles, unsigned grid,
+                                 hipStream_t st, const KernelEvents& ev) {
   static const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&down_gemm32_kernel<W, TERMS, NG>),
                                                   hipFuncAttributeMaxDynamicSharedMemorySize, 2 * GT_BUF_BYTES);
   if (e != hipSuccess) return e;
-  return dispatch(ev, down_gemm32_kernel<W, TERMS, NG>, dim3((unsigned)nb), dim3(256), 2 * GT_BUF_BYTES, st, p,
-                  gtiles, (int)max_gtiles, (int)nb);
+  return dispatch(ev, down_gemm32_kernel<W, TERMS, NG>, dim3(grid), dim3(256), 2 * GT_BUF_BYTES, st, p, gtiles,
+                  (int)max_gtiles);
 }
 
 template <int NG>
 static hipError_t down_gemm32_ng(const MxArgs& p, const int4* gtiles, int64_t max_gtiles, hipStream_t st,
                                  const KernelEvents& ev) {
-  const int64_t nb = (max_gtiles * (p.L / (128 * NG)) + 7) / 8 * 8;
-  if (nb > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const int64_t items = max_gtiles * (p.L / (128 * NG));
+  if (items > 0x7FFFFFFF) return hipErrorInvalidValue;
+  unsigned grid = 0;
+  const hipError_t e = gt_grid(items, grid);
+  if (e != hipSuccess) return e;
   if (p.packed)
-    return p.mxfp8 ? down_gemm32_go<PackedW, 1, NG>(p, gtiles, max_gtiles, nb, st, ev)
-                   : down_gemm32_go<PackedW, 2, NG>(p, gtiles, max_gtiles, nb, st, ev);
-  return p.mxfp8 ? down_gemm32_go<RecordW, 1, NG>(p, gtiles, max_gtiles, nb, st, ev)
-                 : down_gemm32_go<RecordW, 2, NG>(p, gtiles, max_gtiles, nb, st, ev);
+    return p.mxfp8 ? down_gemm32_go<PackedW, 1, NG>(p, gtiles, max_gtiles, grid, st, ev)
+                   : down_gemm32_go<PackedW, 2, NG>(p, gtiles, max_gtiles, grid, st, ev);
+  return p.mxfp8 ? down_gemm32_go<RecordW, 1, NG>(p, gtiles, max_gtiles, grid, st, ev)
+                 : down_gemm32_go<RecordW, 2, NG>(p, gtiles, max_gtiles, grid, st, ev);
 }
 
 hipError_t launch_gateup_gemm(const MxArgs& p, const int4* gtiles, int64_t max_gtiles, hipStream_t st,
                               const KernelEvents& ev) {
   if (p.T == 0) return hipSuccess;
   if (p.F % GT32_FROWS || p.L % 128) return hipErrorInvalidValue;
-  const int64_t nb = (max_gtiles * (p.F / GT32_FROWS) + 7) / 8 * 8;
-  if (nb > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const int64_t items = max_gtiles * (p.F / GT32_FROWS);
+  if (items > 0x7FFFFFFF) return hipErrorInvalidValue;
+  unsigned grid = 0;
+  const hipError_t e = gt_grid(items, grid);
+  if (e != hipSuccess) return e;
   if (p.packed)
-    return p.mxfp8 ? gateup_gemm32_go<PackedW, 1>(p, gtiles, max_gtiles, nb, st, ev)
-                   : gateup_gemm32_go<PackedW, 2>(p, gtiles, max_gtiles, nb, st, ev);
-  return p.mxfp8 ? gateup_gemm32_go<RecordW, 1>(p, gtiles, max_gtiles, nb, st, ev)
-                 : gateup_gemm32_go<RecordW, 2>(p, gtiles, max_gtiles, nb, st, ev);
+    return p.mxfp8 ? gateup_gemm32_go<PackedW, 1>(p, gtiles, max_gtiles, grid, st, ev)
+                   : gateup_gemm32_go<PackedW, 2>(p, gtiles, max_gtiles, grid, st, ev);
+  return p.mxfp8 ? gateup_gemm32_go<RecordW, 1>(p, gtiles, max_gtiles, grid, st, ev)
+                 : gateup_gemm32_go<RecordW, 2>(p, gtiles, max_gtiles, grid, st, ev);
 }
 
 int32_t down_gemm_sal_chunks(int32_t L) { return L / (L % 256 == 0 ? 256 : 128); }
