@@ -24,11 +24,11 @@
 // straight into the other buffer while chunk c is computed, and one barrier per chunk
 // hands the buffers over.  Two blocks share a CU.
 //
-// The grid is persistent: two blocks per CU, each taking (tile, row block) items from a
-// queue until it runs dry, so no block waits for a dispatch slot and no block waits for
-// another.  Each XCD (blocks b with the same b mod 8) has its own queue over one eighth of
-// the active items, a contiguous range: the tiles of one expert, and the row blocks of one
-// token tile, meet in the same L2.
+// Block b of the grid runs on XCD b mod 8, and XCD x takes one eighth of the active
+// (tile, row block) items, a contiguous range in order: the tiles of one expert, and the
+// row blocks of one token tile, meet in the same L2.  The ranges are set from the active
+// tile count on the device, so the padding of the tile list past its last tile (the grid
+// is sized for the most tiles a batch can have) leaves every XCD the same share of work.
 #include "mfma_stream.h"
 
 namespace moe {
@@ -162,37 +162,18 @@ __device__ __forceinline__ void gt_wait_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-// The work queues after the tile list (gtiles[max_gtiles]): GT_QUEUE_INTS ints, set by
-// gemm_tiles_kernel before the GEMMs run: next-item counters of the gate/up GEMM per XCD
-// [0, 8), of the down GEMM [8, 16), and the number of active tiles [16].
-constexpr int GT_QUEUE_GATEUP = 0, GT_QUEUE_DOWN = 8, GT_QUEUE_TILES = 16;
-static_assert((GT_QUEUE_TILES + 1) * 4 <= GEMM_QUEUE_BYTES, "the queues fit their bytes");
-__device__ __forceinline__ int* gt_queue(const int4* gtiles, int max_gtiles) {
-  return reinterpret_cast<int*>(const_cast<int4*>(gtiles) + max_gtiles);
+// The active tile count follows the tile list (gtiles[max_gtiles]), set by gemm_tiles_kernel.
+__device__ __forceinline__ int gt_count(const int4* gtiles, int max_gtiles) {
+  return *reinterpret_cast<const int*>(gtiles + max_gtiles);
 }
 
-// The item loop of a persistent block: fn(lb) for logical items lb of this block's XCD
-// range [x W / 8, (x + 1) W / 8), W = nitems, taken one at a time from the XCD's counter.
-// The next item's ticket is requested when an item starts and read when it ends, so its
-// round trip overlaps the item.  Every thread leaves the loop on the same ticket.
-template <class Fn>
-__device__ __forceinline__ void gt_items(int* counter, int64_t nitems, Fn&& fn) {
-  __shared__ int ticket;
+// The item of block b: item lo + b / 8 of XCD x = b mod 8's range [x W / 8, (x + 1) W / 8)
+// of the W = nitems active items, if the range holds that many.
+__device__ __forceinline__ bool gt_block_item(int64_t nitems, int& lb) {
   const int x = blockIdx.x & 7;
   const int lo = (int)(nitems * x / 8), hi = (int)(nitems * (x + 1) / 8);
-  if (threadIdx.x == 0) ticket = atomicAdd(counter, 1);
-  __syncthreads();
-  int tk = ticket;
-  for (;;) {
-    __syncthreads();  // every thread has read the ticket
-    if (lo + tk >= hi) break;
-    int next = 0;
-    if (threadIdx.x == 0) next = atomicAdd(counter, 1);
-    fn(lo + tk);
-    if (threadIdx.x == 0) ticket = next;
-    __syncthreads();
-    tk = ticket;
-  }
+  lb = lo + (int)(blockIdx.x >> 3);
+  return lb < hi;
 }
 
 // (tile, row block) of logical block lb.  Tiles go in groups of GT_GROUP consecutive
@@ -529,9 +510,9 @@ __global__ void __launch_bounds__(256, 2) gateup_gemm32_kernel(MxArgs p, const i
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ int64_t srow[GT_TOK];
   __shared__ int sslot[GT_TOK];
-  int* queue = gt_queue(gtiles, max_gtiles);
-  const int nrt = p.F / GT32_FROWS, ntiles = queue[GT_QUEUE_TILES];
-  gt_items(queue + GT_QUEUE_GATEUP + (blockIdx.x & 7), (int64_t)ntiles * nrt, [&](int lb) {
+  const int nrt = p.F / GT32_FROWS, ntiles = gt_count(gtiles, max_gtiles);
+  int lb;
+  if (gt_block_item((int64_t)ntiles * nrt, lb)) {
     int ti, rt;
     gt_tile_of(lb, ntiles, nrt, ti, rt);
     const int4 tile = gtiles[ti];
@@ -546,7 +527,7 @@ __global__ void __launch_bounds__(256, 2) gateup_gemm32_kernel(MxArgs p, const i
       gateup32_tile<W, TERMS, 32>(p, e, rt, n, srow, sslot, lds);
     else
       gateup32_tile<W, TERMS, 64>(p, e, rt, n, srow, sslot, lds);
-  });
+  }
   clock_end(p.clock);
 }
 
@@ -616,9 +597,9 @@ __global__ void __launch_bounds__(256, 2) down_gemm32_kernel(MxArgs p, const int
   clock_begin(p.clock);
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ int64_t srow[GT_TOK];
-  int* queue = gt_queue(gtiles, max_gtiles);
-  const int nrt = p.L / (128 * NG), ntiles = queue[GT_QUEUE_TILES];
-  gt_items(queue + GT_QUEUE_DOWN + (blockIdx.x & 7), (int64_t)ntiles * nrt, [&](int lb) {
+  const int nrt = p.L / (128 * NG), ntiles = gt_count(gtiles, max_gtiles);
+  int lb;
+  if (gt_block_item((int64_t)ntiles * nrt, lb)) {
     int ti, rt;
     gt_tile_of(lb, ntiles, nrt, ti, rt);
     const int4 tile = gtiles[ti];
@@ -629,13 +610,13 @@ __global__ void __launch_bounds__(256, 2) down_gemm32_kernel(MxArgs p, const int
       down32_tile<W, TERMS, NG, 32>(p, e, rt, n, srow, lds);
     else
       down32_tile<W, TERMS, NG, 64>(p, e, rt, n, srow, lds);
-  });
+  }
   clock_end(p.clock);
 }
 
 // Tiles of GT_TOK routed rows per active expert, in expert order: gtiles[0, ntiles) =
-// {expert, first row in perm, rows, 0}; gtiles[ntiles, max_gtiles) = {-1, 0, 0, 0}; the
-// work queues after them cleared and the tile count set.
+// {expert, first row in perm, rows, 0}; gtiles[ntiles, max_gtiles) = {-1, 0, 0, 0}; then
+// the tile count.
 __global__ void __launch_bounds__(1024) gemm_tiles_kernel(const int32_t* __restrict__ counts,
                                                           const int32_t* __restrict__ offsets, int E,
                                                           int4* __restrict__ gtiles, int max_gtiles) {
@@ -664,34 +645,17 @@ __global__ void __launch_bounds__(1024) gemm_tiles_kernel(const int32_t* __restr
     }
   }
   for (int j = total + tid; j < max_gtiles; j += 1024) gtiles[j] = make_int4(-1, 0, 0, 0);
-  int* queue = gt_queue(gtiles, max_gtiles);
-  if (tid < GT_QUEUE_TILES) queue[tid] = 0;
-  if (tid == GT_QUEUE_TILES) queue[tid] = total;
+  if (tid == 0) *reinterpret_cast<int*>(gtiles + max_gtiles) = total;
 }
 
 int64_t gemm_max_tiles(int64_t rows, int32_t E) { return ceil_div(rows, GT_TOK) + (rows < E ? rows : E); }
-size_t gemm_tiles_bytes(int64_t rows, int32_t E) { return (size_t)gemm_max_tiles(rows, E) * 16 + GEMM_QUEUE_BYTES; }
+size_t gemm_tiles_bytes(int64_t rows, int32_t E) { return (size_t)gemm_max_tiles(rows, E) * 16 + GEMM_TILES_TAIL_BYTES; }
 
 hipError_t launch_gemm_tiles(const int32_t* counts, const int32_t* offsets, int32_t E, int4* gtiles,
                              int64_t max_gtiles, hipStream_t st) {
   if (E > 16 * 1024) return hipErrorInvalidValue;
   hipLaunchKernelGGL(gemm_tiles_kernel, dim3(1), dim3(1024), 0, st, counts, offsets, E, gtiles, (int)max_gtiles);
   return hipGetLastError();
-}
-
-// The persistent grid: two blocks per CU (what the registers and LDS allow), no more
-// blocks than items, a multiple of 8 so that every XCD runs the same number.
-constexpr int GT_BLOCKS_PER_CU = 2;
-static hipError_t gt_grid(int64_t nitems, unsigned& grid) {
-  int dev = 0, cus = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e != hipSuccess) return e;
-  const int64_t full = (int64_t)GT_BLOCKS_PER_CU * cus / 8 * 8, want = (nitems + 7) / 8 * 8;
-  const int64_t g = want < full ? want : full;
-  grid = (unsigned)(g > 8 ? g : 8);
-  return hipSuccess;
 }
 
 template <class W, int TERMS>
@@ -717,11 +681,9 @@ static hipError_t down_gemm32_go(const MxArgs& p, const int4* gtiles, int64_t ma
 template <int NG>
 static hipError_t down_gemm32_ng(const MxArgs& p, const int4* gtiles, int64_t max_gtiles, hipStream_t st,
                                  const KernelEvents& ev) {
-  const int64_t items = max_gtiles * (p.L / (128 * NG));
-  if (items > 0x7FFFFFFF) return hipErrorInvalidValue;
-  unsigned grid = 0;
-  const hipError_t e = gt_grid(items, grid);
-  if (e != hipSuccess) return e;
+  const int64_t grid64 = (max_gtiles * (p.L / (128 * NG)) + 7) / 8 * 8;  // the most items a batch can have
+  if (grid64 > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const unsigned grid = (unsigned)grid64;
   if (p.packed)
     return p.mxfp8 ? down_gemm32_go<PackedW, 1, NG>(p, gtiles, max_gtiles, grid, st, ev)
                    : down_gemm32_go<PackedW, 2, NG>(p, gtiles, max_gtiles, grid, st, ev);
@@ -733,11 +695,9 @@ hipError_t launch_gateup_gemm(const MxArgs& p, const int4* gtiles, int64_t max_g
                               const KernelEvents& ev) {
   if (p.T == 0) return hipSuccess;
   if (p.F % GT32_FROWS || p.L % 128) return hipErrorInvalidValue;
-  const int64_t items = max_gtiles * (p.F / GT32_FROWS);
-  if (items > 0x7FFFFFFF) return hipErrorInvalidValue;
-  unsigned grid = 0;
-  const hipError_t e = gt_grid(items, grid);
-  if (e != hipSuccess) return e;
+  const int64_t grid64 = (max_gtiles * (p.F / GT32_FROWS) + 7) / 8 * 8;  // the most items a batch can have
+  if (grid64 > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const unsigned grid = (unsigned)grid64;
   if (p.packed)
     return p.mxfp8 ? gateup_gemm32_go<PackedW, 1>(p, gtiles, max_gtiles, grid, st, ev)
                    : gateup_gemm32_go<PackedW, 2>(p, gtiles, max_gtiles, grid, st, ev);

@@ -144,8 +144,8 @@ hipError_t launch_quantize_rows(const uint16_t* src, int64_t rows, int K, const 
 
 // ---- expert_gemm.hip: grouped GEMMs for experts with many routed rows
 // tiles of up to 64 routed rows per active expert, built from counts/offsets, followed by
-// the GEMMs' work queues (GEMM_QUEUE_BYTES): gemm_tiles_bytes in all
-constexpr int GEMM_QUEUE_BYTES = 128;
+// their count (GEMM_TILES_TAIL_BYTES): gemm_tiles_bytes in all
+constexpr int GEMM_TILES_TAIL_BYTES = 16;
 int64_t gemm_max_tiles(int64_t rows, int32_t E);
 size_t gemm_tiles_bytes(int64_t rows, int32_t E);
 hipError_t launch_gemm_tiles(const int32_t* counts, const int32_t* offsets, int32_t E, int4* gtiles,
