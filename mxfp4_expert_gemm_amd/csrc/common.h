@@ -227,6 +227,34 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (WAVE - 1); }
 
+// One wave-wide load of 16 (or 4) bytes a lane from g into LDS at lds + 16 lane (4 lane);
+// lds is wave-uniform.  Written as asm so that the compiler, which cannot tell which LDS
+// bytes such a load writes, does not wait for every load in flight before each LDS read:
+// the kernel waits for these loads itself (an s_waitcnt vmcnt before the barrier that
+// hands the LDS over).  No register receives data,
+// and m0, which the instruction takes its LDS base from, is restored (a write of m0 needs
+// one wait state before an instruction that reads it).
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint8_t*)p;
+}
+__device__ __forceinline__ void lds_dma16(const void* g, const uint8_t* lds) {
+  uint32_t save;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_nop 0\n\t"
+               "s_mov_b32 m0, %0"
+               : "=&s"(save)
+               : "v"(g), "s"(lds_addr(lds))
+               : "memory");
+}
+__device__ __forceinline__ void lds_dma4(const void* g, const uint8_t* lds) {
+  uint32_t save;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %1, off\n\ts_nop 0\n\t"
+               "s_mov_b32 m0, %0"
+               : "=&s"(save)
+               : "v"(g), "s"(lds_addr(lds))
+               : "memory");
+}
+
+
 // Optional stamps of a kernel's span on the device's constant-rate wall clock: block b
 // lowers clk[2 (b % MOE_CLOCK_SLOTS)] to its start and raises the next word to its end
 // (after a block barrier, so that is the end of its last wave).  The caller sets the

@@ -206,6 +206,130 @@ __global__ void __launch_bounds__(256, 2) dense_mfma_kernel(DenseMfmaArgs p) {
     }
 }
 
+// The same GEMM with both operand tiles loaded straight into LDS (lds_dma16: lane i of a
+// wave writes its 16 bytes at the instruction's base + 16 i, so the chunk swizzle is
+// applied on the source side): no staging registers and no LDS store instructions.  Two
+// stages: K tile kt + 1 loads while tile kt is computed.  A K tile is (BM + BN) / 8
+// blocks of 8 rows x 128 bytes, block j = 4 u + wave going to the wave's u-th load.  The
+// K-tile arithmetic (and the router's fp64 folds) is the one of dense_mfma_kernel, so the
+// results are the same.  (Wave tiles of 128 x 64 in 256 x 128 blocks, which the free
+// registers allow at one block per CU, measured 2.69 ms against 1.67 ms at prefill32k.)
+template <int WM, int WN, bool ROUTER, int MINB>
+__global__ void __launch_bounds__(256, MINB) dense_mfma_dma_kernel(DenseMfmaArgs p) {
+  constexpr int BM = 32 * WM, BN = 32 * WN;
+  constexpr int NU = (BM + BN) / 32;  // 1 KB loads per wave and K tile
+  constexpr int A_BYTES = BM * DM_RS, STAGE = (BM + BN) * DM_RS;
+  extern __shared__ __align__(16) uint8_t lds[];
+
+  const int nbp = gridDim.x;
+  const int lb = (blockIdx.x & 7) * (nbp >> 3) + (blockIdx.x >> 3);
+  if (lb >= p.nblocks) return;
+  const int span = DM_GROUP * p.ntn;
+  const int grp = lb / span, first = grp * DM_GROUP;
+  const int gs = p.ntm - first < DM_GROUP ? p.ntm - first : DM_GROUP;
+  const int within = lb - grp * span;
+  const int tm = first + within % gs, tn = within / gs;
+  const int64_t t0 = (int64_t)tm * BM;
+  const int n0 = tn * BN;
+  const int K = p.K, nkt = K / DM_BK;
+  const int lane = lane_id(), wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / WAVE));
+  const int wm = wave >> 1, wn = wave & 1, nl = lane & 15, g = lane >> 4;
+
+  // the lane's rows: row 8 j + lane / 8 of the A tile then the B tile (clamped into the
+  // matrix, their results are not stored), chunk (lane mod 8) ^ (row mod 8)
+  const uint16_t* src[NU];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int r = 8 * (4 * u + wave) + (lane >> 3);
+    const int c = (lane & 7) ^ ((lane >> 3) & 7);
+    if (r < BM) {
+      const int64_t t = t0 + r < p.T ? t0 + r : p.T - 1;
+      src[u] = p.x + t * K + 8 * c;
+    } else {
+      const int n = n0 + (r - BM) < p.N ? n0 + (r - BM) : p.N - 1;
+      src[u] = p.W + (int64_t)n * K + 8 * c;
+    }
+  }
+  auto load_tile = [&](int kt, int buf) {
+#pragma unroll
+    for (int u = 0; u < NU; ++u) lds_dma16(src[u] + (int64_t)kt * DM_BK, lds + buf * STAGE + (4 * u + wave) * 1024);
+  };
+  auto wait_barrier = []() { asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+
+  f32x4_t acc[WM][WN];
+  double accd[ROUTER ? WM : 1][ROUTER ? WN : 1][4];
+#pragma unroll
+  for (int i = 0; i < WM; ++i)
+#pragma unroll
+    for (int jn = 0; jn < WN; ++jn) acc[i][jn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  if constexpr (ROUTER) {
+#pragma unroll
+    for (int i = 0; i < WM; ++i)
+#pragma unroll
+      for (int jn = 0; jn < WN; ++jn)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) accd[i][jn][r] = 0.0;
+  }
+
+  load_tile(0, 0);
+  wait_barrier();
+  const int arow = 16 * WM * wm + nl, brow = 16 * WN * wn + nl;
+  for (int kt = 0; kt < nkt; ++kt) {
+    // the other stage was last read in tile kt - 1, which every wave has finished
+    if (kt + 1 < nkt) load_tile(kt + 1, (kt + 1) & 1);
+    const uint8_t* s = lds + (kt & 1) * STAGE;
+#pragma unroll
+    for (int ks = 0; ks < DM_BK / 32; ++ks) {
+      bf16x8_t a[WM], b[WN];
+#pragma unroll
+      for (int i = 0; i < WM; ++i)  // rows arow + 16 i share arow & 7 = nl & 7
+        a[i] = *reinterpret_cast<const bf16x8_t*>(s + (arow + 16 * i) * DM_RS + 16 * ((4 * ks + g) ^ (nl & 7)));
+#pragma unroll
+      for (int jn = 0; jn < WN; ++jn)
+        b[jn] = *reinterpret_cast<const bf16x8_t*>(s + A_BYTES + (brow + 16 * jn) * DM_RS +
+                                                   16 * ((4 * ks + g) ^ (nl & 7)));
+#pragma unroll
+      for (int i = 0; i < WM; ++i)
+#pragma unroll
+        for (int jn = 0; jn < WN; ++jn)
+          acc[i][jn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[jn], acc[i][jn], 0, 0, 0);
+    }
+    if constexpr (ROUTER) {
+#pragma unroll
+      for (int i = 0; i < WM; ++i)
+#pragma unroll
+        for (int jn = 0; jn < WN; ++jn) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) accd[i][jn][r] += (double)acc[i][jn][r];
+          acc[i][jn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+    wait_barrier();  // tile kt + 1 is in LDS; every wave is past tile kt
+  }
+
+#pragma unroll
+  for (int i = 0; i < WM; ++i)
+#pragma unroll
+    for (int jn = 0; jn < WN; ++jn) {
+      const int n = n0 + 16 * WN * wn + 16 * jn + nl;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t t = t0 + 16 * WM * wm + 16 * i + 4 * g + r;
+        if (t < p.T && n < p.N) {
+          if constexpr (ROUTER)
+            static_cast<float*>(p.out)[t * p.N + n] = (float)accd[i][jn][r];
+          else if (p.add_rows == 0)
+            static_cast<uint16_t*>(p.out)[t * p.N + n] = f32_to_bf16(acc[i][jn][r]);
+          else {
+            double v = (double)acc[i][jn][r];
+            for (int a = 0; a < p.add_rows; ++a) v += (double)p.add[(t * p.add_rows + a) * p.N + n];
+            static_cast<uint16_t*>(p.out)[t * p.N + n] = f64_to_bf16(v);
+          }
+        }
+      }
+    }
+}
+
 // Euclidean norms of bf16 rows, as the GEMV router computes them: each lane sums the
 // squares of its 8-element chunks (exact products, fp32 sums), the wave adds the lanes,
 // the root is rounded once.  A row with a subnormal bf16 value gets +inf.
@@ -263,6 +387,34 @@ static hipError_t launch_dm(const DenseMfmaArgs& a0, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <int WM, int WN, bool ROUTER, int MINB>
+static hipError_t launch_dm_dma(const DenseMfmaArgs& a0, hipStream_t st) {
+  constexpr int BM = 32 * WM, BN = 32 * WN;
+  constexpr int LDS = 2 * (BM + BN) * DM_RS;
+  DenseMfmaArgs a = a0;
+  a.ntm = (int32_t)ceil_div(a.T, BM);
+  a.ntn = (int32_t)ceil_div(a.N, BN);
+  const int64_t nb = (int64_t)a.ntm * a.ntn;
+  if (ceil_div(a.T, BM) > 0x7FFFFFFF || nb > 0x7FFFFFF0) return hipErrorInvalidValue;
+  a.nblocks = (int32_t)nb;
+  const unsigned grid = (unsigned)((nb + 7) / 8 * 8);
+  if constexpr (LDS > 65536) {
+    static const hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&dense_mfma_dma_kernel<WM, WN, ROUTER, MINB>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((dense_mfma_dma_kernel<WM, WN, ROUTER, MINB>), dim3(grid), dim3(256), LDS, st, a);
+  return hipGetLastError();
+}
+
+// The LDS-direct kernel loads one K tile ahead, the register-staged one PF tiles: the
+// first is faster once the grid holds at least three blocks per CU slot pair (768
+// blocks), where the other resident block covers the load latency (prefill32k: latent
+// projections 1.90 -> 1.67 ms, router 0.68 -> 0.65 ms; prefill4k latent 0.31 -> 0.28 ms),
+// the second for smaller grids (prefill4k's router, 448 blocks: 0.12 against 0.14 ms).
+static bool dm_dma_pays(int64_t T, int32_t N, int BM, int BN) { return ceil_div(T, BM) * ceil_div(N, BN) >= 768; }
+
 // Tile of a batch below 256 tokens: the largest of 64 x 64, 64 x 32 and 32 x 32 (tokens x
 // rows) that still gives the grid about one block per CU, since a few dozen blocks (the
 // router at 64 tokens has 14 tiles of 64 x 64) leave most of the chip idle.  Every shape
@@ -289,14 +441,16 @@ hipError_t launch_dense_mfma(const uint16_t* x, int64_t T, int32_t K, const Dens
     hipLaunchKernelGGL(row_norms_kernel, dim3((unsigned)ceil_div(s.rows, 4)), dim3(256), 0, st, s.W,
                        (int64_t)s.rows, K, s.wnorm);
     hipLaunchKernelGGL(row_norms_kernel, dim3((unsigned)ceil_div(T, 4)), dim3(256), 0, st, x, T, K, s.xnorm);
-    if (T >= 256) return launch_dm<4, 2, 2, true>(a, st);
+    if (T >= 256)
+      return dm_dma_pays(T, s.rows, 128, 64) ? launch_dm_dma<4, 2, true, 2>(a, st) : launch_dm<4, 2, 2, true>(a, st);
     switch (small_tile(T, s.rows)) {
       case 0: return launch_dm<2, 2, 4, true>(a, st);
       case 1: return launch_dm<2, 1, 4, true>(a, st);
       default: return launch_dm<1, 1, 4, true>(a, st);
     }
   }
-  if (T >= 256) return launch_dm<4, 4, 2, false>(a, st);
+  if (T >= 256)
+    return dm_dma_pays(T, s.rows, 128, 128) ? launch_dm_dma<4, 4, false, 2>(a, st) : launch_dm<4, 4, 2, false>(a, st);
   switch (small_tile(T, s.rows)) {
     case 0: return launch_dm<2, 2, 4, false>(a, st);
     case 1: return launch_dm<2, 1, 4, false>(a, st);

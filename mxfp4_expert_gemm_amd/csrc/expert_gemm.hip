@@ -101,32 +101,6 @@ __device__ __forceinline__ GtDma<TERMS, R> gt_dma_setup(const QRows& q, const in
   return t;
 }
 
-// One wave-wide load of 16 (or 4) bytes a lane from g into LDS at lds + 16 lane (4 lane);
-// lds is wave-uniform.  Written as asm so that the compiler, which cannot tell which LDS
-// bytes such a load writes, does not wait for every load in flight before each LDS read:
-// the kernel waits for these loads itself (gt_wait_barrier).  No register receives data,
-// and m0, which the instruction takes its LDS base from, is restored (a write of m0 needs
-// one wait state before an instruction that reads it).
-__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
-  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint8_t*)p;
-}
-__device__ __forceinline__ void lds_dma16(const void* g, const uint8_t* lds) {
-  uint32_t save;
-  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_nop 0\n\t"
-               "s_mov_b32 m0, %0"
-               : "=&s"(save)
-               : "v"(g), "s"(lds_addr(lds))
-               : "memory");
-}
-__device__ __forceinline__ void lds_dma4(const void* g, const uint8_t* lds) {
-  uint32_t save;
-  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %1, off\n\ts_nop 0\n\t"
-               "s_mov_b32 m0, %0"
-               : "=&s"(save)
-               : "v"(g), "s"(lds_addr(lds))
-               : "memory");
-}
-
 // Issues the loads of chunk c (steps CH c .. CH c + CH - 1) into buf: NU code loads and
 // one scale load per wave.  Steps past the end re-read the last step (never used).  buf
 // and wave are wave-uniform.  The empty asm keeps the compiler from moving later memory
