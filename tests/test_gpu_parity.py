@@ -179,6 +179,22 @@ def test_linear_bf16(T, n_in, n_out):
     assert np.mean(got == want) > 0.99
 
 
+@pytest.mark.parametrize("n_in,n_out", [(7168, 3584), (3584, 7168)])
+def test_linear_bf16_kernel_choice(n_in, n_out):
+    """4133 tokens in 128 x 128 tiles make a grid of 924 or 1848 blocks, which runs the
+    LDS-direct matrix-core kernel; their first 256 tokens alone make 56 or 112 blocks, under
+    the 768 it needs, and run the register-staged one.  Both take the same K-tile arithmetic,
+    so the shared rows agree bit for bit; the ragged last tile matches the oracle."""
+    a = synth.normal_bf16(7, 1, 1.0, (4096 + 37, n_in))
+    W = synth.normal_bf16(7, 2, 0.02, (n_out, n_in))
+    dW = to_dev(W)
+    big = from_dev(moe.linear_bf16(to_dev(a), dW))
+    small = from_dev(moe.linear_bf16(to_dev(a[:256]), dW))
+    assert np.array_equal(big[:256], small)
+    want = oracle.linear_bf16(a[-37:], W)
+    assert rel_l2(bf16_bits_to_f64(big[-37:]), bf16_bits_to_f64(want)) < 1e-4
+
+
 @pytest.mark.parametrize("name,T", [("tiny", None), ("decode1", None), ("decode64", 8)])
 def test_expert_ffn(name, T):
     h = host_layer(name, T)
@@ -320,8 +336,9 @@ def test_combine():
 
 
 def test_combine_past_65535_tokens():
-    """More tokens than the grid's second dimension holds (the kernel loops over tokens):
-    every token, the last ones included, as the oracle's fp64 combine."""
+    """More tokens than a grid's second dimension could hold (the combine grid is flat
+    over tokens x latent quads): every token, the last ones included, as the oracle's
+    fp64 combine."""
     rng = np.random.default_rng(2)
     T, k, L = 70001, 2, 128
     y = rng.standard_normal((T * k, L)).astype(np.float32)
