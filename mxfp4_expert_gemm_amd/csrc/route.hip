@@ -476,20 +476,23 @@ __device__ __forceinline__ void route_token(const RouteArgs& a, int64_t t, Route
   const float xn = topk_mode ? 0.f : a.xnorm[t];
   const float gam = (float)a.gamma * (1.f + 0x1p-18f) * xn;
   const float pad = (float)a.d * 0x1p-124f;
-  // every load unconditional (lanes past E read the last expert and are masked after),
-  // so all of them are in flight together
+  // every load unconditional and from a pointer chosen once (lanes past E read the last
+  // expert and are masked after; a missing operand reads the logits and is not used), so
+  // no branch splits them and all are in flight together: one memory round trip
+  const float* pl = (topk_mode ? a.exact_logits : a.logits_fast) + t * E;
+  const bool has_bias = !topk_mode && a.bias != nullptr;
+  const float* pb = has_bias ? a.bias + t * a.bias_stride : pl;
+  const float* pw = topk_mode ? pl : a.wnorm;
   float lf[ROUTE_MAXI], bv[ROUTE_MAXI], wn[ROUTE_MAXI];
 #pragma unroll
   for (int i = 0; i < ROUTE_MAXI; ++i) {
     const int e = i * WAVE + lane < E ? i * WAVE + lane : E - 1;
-    if (topk_mode) {
-      lf[i] = a.exact_logits[t * E + e];
-    } else {
-      lf[i] = a.logits_fast[t * E + e];
-      bv[i] = a.bias ? a.bias[t * a.bias_stride + e] : 0.f;
-      wn[i] = a.wnorm[e];
-    }
+    lf[i] = pl[e];
+    bv[i] = pb[e];
+    wn[i] = pw[e];
   }
+#pragma unroll
+  for (int i = 0; i < ROUTE_MAXI; ++i) bv[i] = has_bias ? bv[i] : 0.f;
   uint32_t kmax = 0;
 #pragma unroll
   for (int i = 0; i < ROUTE_MAXI; ++i) {
@@ -589,14 +592,58 @@ __device__ __forceinline__ void route_token(const RouteArgs& a, int64_t t, Route
   emit_topk(a, t, L, mx_all, den_all);
 }
 
-// the token's latent row h as two e4m3 terms for the expert kernels (eight values per lane)
+// the 8 values of group j of a latent row, quantised (the quad of lanes holding the four
+// groups of a scale block is active together)
+__device__ __forceinline__ void quantize_group8(const uint4 raw, const QRows& q, int64_t j, bool mxfp8) {
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = bf16lo(w[i]);
+    v[2 * i + 1] = bf16hi(w[i]);
+  }
+  uint32_t hi[2], lo[2], shi, slo;
+  quantize_quad8_fmt(v, hi, lo, shi, slo, mxfp8);
+  *reinterpret_cast<uint2*>(q.hi + 8 * j) = make_uint2(hi[0], hi[1]);
+  *reinterpret_cast<uint2*>(q.lo + 8 * j) = make_uint2(lo[0], lo[1]);
+  if ((j & 3) == 0) {
+    q.shi[j >> 2] = (uint8_t)shi;
+    q.slo[j >> 2] = (uint8_t)slo;
+  }
+}
+
+// the token's latent row h as two e4m3 terms for the expert kernels, eight values per
+// lane and group: for L <= 8 * 64 * QH_GROUPS every group's load is issued before the
+// first is used (one memory round trip per row instead of one per two groups)
+constexpr int QH_GROUPS = 8;
 __device__ __forceinline__ void quantize_token_h(const RouteArgs& a, int64_t t) {
   if (!a.h) return;
   const QRows q{a.hq.hi + t * a.L, a.hq.lo + t * a.L, a.hq.shi + t * (a.L / 32), a.hq.slo + t * (a.L / 32)};
-  quantize_quads(a.h + t * a.L, q, a.L, lane_id(), WAVE, a.mxfp8 != 0);
+  const uint16_t* h = a.h + t * a.L;
+  const int ng = a.L / 8, lane = lane_id();
+  if (ng > QH_GROUPS * WAVE) {
+    quantize_quads(h, q, a.L, lane, WAVE, a.mxfp8 != 0);
+    return;
+  }
+  uint4 raw[QH_GROUPS];
+#pragma unroll
+  for (int u = 0; u < QH_GROUPS; ++u) {
+    const int j = lane + WAVE * u;
+    raw[u] = j < ng ? *reinterpret_cast<const uint4*>(h + 8 * j) : make_uint4(0u, 0u, 0u, 0u);
+  }
+#pragma unroll
+  for (int u = 0; u < QH_GROUPS; ++u)
+    if (lane + WAVE * u < ng) quantize_group8(raw[u], q, lane + WAVE * u, a.mxfp8 != 0);
 }
 
-__global__ void __launch_bounds__(256) route_kernel(RouteArgs a) {
+// MINB blocks per CU: 4 caps the kernel at 128 registers a lane, spilling in the general
+// path; for large batches the doubled occupancy over the 2 blocks of the uncapped build
+// (172 registers) pays (prefill32k: 0.49 -> 0.33 ms), while a few dozen tokens, whose
+// slowest token sets the kernel's length, run faster uncapped (decode64: 63 us against 71).
+constexpr int64_t ROUTE_WIDE_TOKENS = 2048;  // 512 blocks: two per CU at the uncapped occupancy
+
+template <int MINB>
+__global__ void __launch_bounds__(256, MINB) route_kernel(RouteArgs a) {
   __shared__ RouteLds scratch[4];
   const int wave = threadIdx.x / WAVE;
   const int64_t t = (int64_t)blockIdx.x * 4 + wave;
@@ -608,7 +655,11 @@ __global__ void __launch_bounds__(256) route_kernel(RouteArgs a) {
 hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
   if (a.T == 0) return hipSuccess;
   if (a.E > ROUTE_MAXI * WAVE) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(route_kernel, dim3((unsigned)ceil_div(a.T, 4)), dim3(256), 0, st, a);
+  const dim3 grid((unsigned)ceil_div(a.T, 4));
+  if (a.T >= ROUTE_WIDE_TOKENS)
+    hipLaunchKernelGGL(route_kernel<4>, grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(route_kernel<1>, grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
@@ -772,26 +823,6 @@ struct RouteBlockLds {
   uint32_t tau;
   int decided;
 };
-
-// the 8 values of group j of a latent row, quantised (the quad of lanes holding the four
-// groups of a scale block is active together)
-__device__ __forceinline__ void quantize_group8(const uint4 raw, const QRows& q, int64_t j, bool mxfp8) {
-  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-  float v[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    v[2 * i] = bf16lo(w[i]);
-    v[2 * i + 1] = bf16hi(w[i]);
-  }
-  uint32_t hi[2], lo[2], shi, slo;
-  quantize_quad8_fmt(v, hi, lo, shi, slo, mxfp8);
-  *reinterpret_cast<uint2*>(q.hi + 8 * j) = make_uint2(hi[0], hi[1]);
-  *reinterpret_cast<uint2*>(q.lo + 8 * j) = make_uint2(lo[0], lo[1]);
-  if ((j & 3) == 0) {
-    q.shi[j >> 2] = (uint8_t)shi;
-    q.slo[j >> 2] = (uint8_t)slo;
-  }
-}
 
 // route_token as a call: its registers are not reserved in the block kernel, where it
 // runs only when the block's selection cannot decide
