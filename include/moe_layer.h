@@ -321,11 +321,18 @@ moe_status moe_topk(const float* logits, int64_t num_tokens, int32_t num_experts
                     int32_t renormalize, int32_t* topk_idx, float* topk_w, moe_stream_t stream);
 
 /* Grouping of routed rows by expert: from idx [T][k] fill counts [E],
- * offsets [E+1], perm [T*k] (bit-exact, deterministic).  Uses the workspace
- * (size it with a cfg of the same T, E). */
+ * offsets [E+1], perm [T*k] (bit-exact, deterministic).  Uses a device
+ * workspace of at least moe_permute_workspace_size(T, k, E) bytes, 16-byte
+ * aligned (moe_workspace_size of a cfg with the same T and E is also enough);
+ * MOE_ERR_WORKSPACE if it is smaller. */
 moe_status moe_permute(const int32_t* topk_idx, int64_t num_tokens, int32_t k, int32_t num_experts,
                        int32_t* expert_counts, int32_t* expert_offsets, int32_t* perm,
                        void* workspace, size_t workspace_bytes, moe_stream_t stream);
+
+/* Bytes of device workspace moe_permute needs for T tokens of k rows over E
+ * experts, written to *bytes (host pointer; 0 for T = 0).  Host-only, no device
+ * call.  MOE_ERR_INVALID_ARG / MOE_ERR_UNSUPPORTED as moe_permute would return. */
+moe_status moe_permute_workspace_size(int64_t num_tokens, int32_t k, int32_t num_experts, size_t* bytes);
 
 /* Routed experts on latent rows: h bf16 [T][L] -> y fp32 [T*k][L] with row
  * t*k+j the output of expert topk_idx[t][j] on h[t]; a_out (nullable) bf16

@@ -30,7 +30,8 @@ EXPORTS = ["moe_expert_bytes", "moe_packed_expert_bytes", "moe_pack_experts", "m
            "moe_layer_forward_profiled",
            "moe_dequant_mxfp4", "moe_route", "moe_topk", "moe_permute", "moe_expert_ffn", "moe_combine",
            "moe_linear_bf16", "moe_reap_saliency", "moe_layer_forward_shared", "moe_expert_slots_bytes",
-           "moe_layer_forward_streamed", "moe_layer_forward_noalloc", "moe_reap_keep_bias"]
+           "moe_layer_forward_streamed", "moe_layer_forward_noalloc", "moe_reap_keep_bias",
+           "moe_permute_workspace_size"]
 
 
 class MoEError(RuntimeError):
@@ -93,6 +94,7 @@ def lib():
             "moe_route": (ctypes.c_int, [vp, vp, vp, cfgp, i32, i32, rp, vp, sz, vp]),
             "moe_topk": (ctypes.c_int, [vp, i64, i32, i32, i32, vp, vp, vp]),
             "moe_permute": (ctypes.c_int, [vp, i64, i32, i32, vp, vp, vp, vp, sz, vp]),
+            "moe_permute_workspace_size": (ctypes.c_int, [i64, i32, i32, ctypes.POINTER(sz)]),
             "moe_expert_ffn": (ctypes.c_int, [vp, vp, i32, cfgp, rp, vp, vp, vp, sz, vp]),
             "moe_combine": (ctypes.c_int, [vp, vp, i64, i32, i32, vp, vp]),
             "moe_linear_bf16": (ctypes.c_int, [vp, vp, i64, i32, i32, vp, vp]),
@@ -326,10 +328,9 @@ def permute(idx: torch.Tensor, num_experts: int):
     counts = torch.empty(num_experts, dtype=torch.int32, device=idx.device)
     offsets = torch.empty(num_experts + 1, dtype=torch.int32, device=idx.device)
     perm = torch.empty(T * k, dtype=torch.int32, device=idx.device)
-    align = lambda n: (n + 255) // 256 * 256
-    ws = torch.empty(align(((T * k + 2047) // 2048) * num_experts * 4) + align(num_experts * 4) +
-                     align(num_experts * 16) + 256,
-                     dtype=torch.uint8, device=idx.device)
+    n = ctypes.c_size_t(0)
+    _check(lib().moe_permute_workspace_size(T, k, num_experts, ctypes.byref(n)), "moe_permute_workspace_size")
+    ws = torch.empty(max(int(n.value), 256), dtype=torch.uint8, device=idx.device)
     _check(lib().moe_permute(_p(idx), T, k, num_experts, _p(counts), _p(offsets), _p(perm), _p(ws), ws.numel(),
                              _stream()), "moe_permute")
     return counts, offsets, perm

@@ -760,17 +760,36 @@ moe_status moe_topk(const float* logits, int64_t num_tokens, int32_t num_experts
   return dev(launch_route(a, reinterpret_cast<hipStream_t>(stream)));
 }
 
+// The standalone grouping's workspace: the permutation's scratch, then the tile list
+// and the active-expert count, each 256-byte aligned.
+static size_t permute_stage_bytes(int64_t rows, int32_t num_experts, size_t* pws) {
+  *pws = align_up(permute_ws_bytes(rows, num_experts), 256);
+  return *pws + align_up((size_t)num_experts * 16, 256) + 256;
+}
+
+static moe_status check_permute_args(int64_t num_tokens, int32_t k, int32_t num_experts) {
+  if (num_tokens < 0 || k < 1 || k > MAX_K || num_experts < 1 || k > num_experts) return MOE_ERR_INVALID_ARG;
+  if (num_experts > MAX_E) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status moe_permute_workspace_size(int64_t num_tokens, int32_t k, int32_t num_experts, size_t* bytes) {
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  MOE_TRY(check_permute_args(num_tokens, k, num_experts));
+  size_t pws = 0;
+  *bytes = num_tokens == 0 ? 0 : permute_stage_bytes(num_tokens * k, num_experts, &pws);
+  return MOE_OK;
+}
+
 moe_status moe_permute(const int32_t* topk_idx, int64_t num_tokens, int32_t k, int32_t num_experts,
                        int32_t* expert_counts, int32_t* expert_offsets, int32_t* perm, void* workspace,
                        size_t workspace_bytes, moe_stream_t stream) {
-  if (!topk_idx || !expert_counts || !expert_offsets || !perm || num_tokens < 0 || k < 1 || k > MAX_K ||
-      num_experts < 1 || k > num_experts)
-    return MOE_ERR_INVALID_ARG;
-  if (num_experts > MAX_E) return MOE_ERR_UNSUPPORTED;
+  if (!topk_idx || !expert_counts || !expert_offsets || !perm) return MOE_ERR_INVALID_ARG;
+  MOE_TRY(check_permute_args(num_tokens, k, num_experts));
   const int64_t rows = num_tokens * k;
   if (rows == 0) return MOE_OK;
-  const size_t pws = align_up(permute_ws_bytes(rows, num_experts), 256);
-  const size_t need = pws + align_up((size_t)num_experts * 16, 256) + 256;
+  size_t pws = 0;
+  const size_t need = permute_stage_bytes(rows, num_experts, &pws);
   if (!workspace || workspace_bytes < need) return MOE_ERR_WORKSPACE;
   PermOut po{expert_counts, expert_offsets, perm, at<int4>(workspace, pws),
              at<int32_t>(workspace, pws + align_up((size_t)num_experts * 16, 256)), max_tiles(rows, num_experts)};

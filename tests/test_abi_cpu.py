@@ -117,6 +117,17 @@ def test_stage_argument_errors():
     assert L.moe_topk(FAKE, 4, 2048, 2, 1, FAKE, FAKE, None) == -2
     assert L.moe_permute(FAKE, 4, 2, 8, FAKE, FAKE, FAKE, None, 0, None) == -3
     assert L.moe_permute(FAKE, 0, 2, 8, FAKE, FAKE, FAKE, None, 0, None) == 0
+    n = ctypes.c_size_t(7)
+    assert L.moe_permute_workspace_size(0, 2, 8, ctypes.byref(n)) == 0 and n.value == 0
+    for T, k, E in ((4, 2, 8), (4096, 16, 896), (70001, 2, 8)):
+        assert L.moe_permute_workspace_size(T, k, E, ctypes.byref(n)) == 0
+        assert n.value > 0 and n.value % 256 == 0
+        # one byte short of the size is refused before any device work
+        assert L.moe_permute(FAKE, T, k, E, FAKE, FAKE, FAKE, FAKE, n.value - 1, None) == -3
+    assert L.moe_permute_workspace_size(4, 9, 8, ctypes.byref(n)) == -1   # k > E
+    assert L.moe_permute_workspace_size(-1, 2, 8, ctypes.byref(n)) == -1
+    assert L.moe_permute_workspace_size(4, 2, 8, None) == -1
+    assert L.moe_permute_workspace_size(4, 2, 4096, ctypes.byref(n)) == -2  # E past the supported maximum
     assert L.moe_combine(FAKE, FAKE, 4, 2, 100, FAKE, None) == -1
     assert L.moe_linear_bf16(FAKE, FAKE, 4, 100, 8, FAKE, None) == -1
     assert L.moe_linear_bf16(FAKE, FAKE, 0, 64, 8, FAKE, None) == 0
