@@ -349,6 +349,21 @@ def test_combine_past_65535_tokens():
     assert np.mean(got == want) > 0.999
 
 
+def test_combine_grid_stride_pass():
+    """The flat combine grid is capped at 2^20 blocks of 256 threads (2^28 quads of latent
+    values); a batch past that takes a second grid-stride pass.  First tokens and the
+    tail (second pass) against the oracle's fp64 combine."""
+    T, k, L = (1 << 25) + 4099, 1, 32
+    g = torch.Generator(device="cuda").manual_seed(3)
+    y = torch.randn(T * k, L, device="cuda", generator=g)
+    w = torch.rand(T, k, device="cuda", generator=g)
+    z = moe.combine(y, w, dtype=torch.int16)
+    rows = torch.cat([torch.arange(0, 64), torch.arange(T - 8192, T)]).cuda()
+    got = from_dev(z[rows])
+    want = oracle.combine(from_dev(y[rows]), from_dev(w[rows]))
+    assert np.array_equal(got, want)
+
+
 # ------------------------------------------------------------- whole layer
 
 def _layer_case(name, T=None, sample=None):
