@@ -321,19 +321,33 @@ def summarise(r, layer, args, moe):
     in_graph = r["gu_graph_ms"] is not None
     gu_s = np.array(r["gu_graph_ms"] if in_graph else r["gu_ms"]) * 1e-3
     dn_s = np.array(r["dn_graph_ms"] if in_graph else r["dn_ms"]) * 1e-3
-    gu_eager_us = round(1e3 * float(np.mean(r["gu_ms"])), 2)
+    # with shared experts the layer call takes no kernel events or clocks: no kernel time
+    measured = bool(np.all(np.isfinite(gu_s)) and np.all(np.isfinite(dn_s)))
+
+    def us(v):  # a kernel time in microseconds, or None when not measured
+        return round(1e6 * float(v), 2) if measured else None
+
+    def rnd(v, n):
+        return round(float(v), n) if measured else None
+
+    gu_eager_us = round(1e3 * float(np.mean(r["gu_ms"])), 2) if measured else None
     timing = ("device wall-clock span (first block start to last wave end) in a graph of the timed steps"
               if in_graph else "events stamped by the kernel's dispatch in the timed eager pass")
+    if not measured:
+        timing = "not measured: the layer call with shared experts takes no kernel events"
     # whole-layer algorithmic bytes: weights read (dense + active experts) + x + out + bias
     dense_bytes = (c.E * c.d + 2 * c.L * c.d) * 2
     layer_bytes = dense_bytes + active * 3 * mat_bytes + 2 * c.T * c.d * 2
+    if args.shared:  # the shared experts' records (width d) are read every step too
+        layer_bytes = layer_bytes + args.shared * (moe.packed_expert_bytes(c.d, c.F) if layer.packed
+                                                   else moe.expert_bytes(c.d, c.F))
     if r["bias_host"] is not None:
         layer_bytes = layer_bytes + r["bias_host"].nbytes
     ms = r["ms_per_step"]
     layer_gbs = float(np.mean(layer_bytes) / (ms * 1e-3) / 1e9)
     # flops per step: bf16 router and latent projections, MXFP4 experts (model flops)
     f_bf16 = 2.0 * c.T * (c.d * c.E + 2 * c.d * c.L)
-    f_fp4 = 2.0 * 3 * c.T * c.k * c.L * c.F
+    f_fp4 = 2.0 * 3 * c.T * (c.k * c.L + args.shared * c.d) * c.F
     t_roof = max(float(np.mean(layer_bytes)) / (HBM_PEAK_GBS * 1e9),
                  f_fp4 / (FP4_PEAK_TFS * 1e12) + f_bf16 / (BF16_PEAK_TFS * 1e12))
     terms = 2 if args.act_format == "bf16" else 1
@@ -365,25 +379,25 @@ def summarise(r, layer, args, moe):
         flops = 2 * 2 * c.T * c.k * c.F * c.L
         tfs = flops / float(np.mean(gu_s)) / 1e12
         out["roofline"] = {"bound": "mfma", "kernel": "gate_up (grouped MXFP4 GEMM + fp32 GLU)",
-                           "achieved": round(tfs, 1), "peak": FP4_PEAK_TFS, "unit": "TFLOP/s",
-                           "frac": round(tfs / FP4_PEAK_TFS, 4), "traffic": None,
-                           "kernel_us": round(1e6 * float(np.mean(gu_s)), 2), "kernel_timing": timing,
+                           "achieved": rnd(tfs, 1), "peak": FP4_PEAK_TFS, "unit": "TFLOP/s",
+                           "frac": rnd(tfs / FP4_PEAK_TFS, 4), "traffic": None,
+                           "kernel_us": us(np.mean(gu_s)), "kernel_timing": timing,
                            "kernel_us_eager": gu_eager_us, "flops_per_launch": flops,
                            "mfma_terms_per_product": terms,
                            "issue_ceiling_TFs": FP8_PEAK_TFS / terms,
-                           "frac_of_issue_ceiling": round(tfs * terms / FP8_PEAK_TFS, 4),
-                           "down_kernel_us": round(1e6 * float(np.mean(dn_s)), 2)}
+                           "frac_of_issue_ceiling": rnd(tfs * terms / FP8_PEAK_TFS, 4),
+                           "down_kernel_us": us(np.mean(dn_s))}
     else:
         gbs = float(np.mean(gu_bytes / gu_s) / 1e9)
         dn_bytes = active * mat_bytes + c.T * c.k * c.F * 2 + c.T * c.L * 2
         out["roofline"] = {"bound": "hbm", "kernel": "gate_up (MXFP4 gate/up GEMV + fp32 GLU)",
-                           "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                           "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(c.name, layer.packed),
-                           "kernel_us": round(1e6 * float(np.mean(gu_s)), 2), "kernel_timing": timing,
+                           "achieved": rnd(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": rnd(gbs / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(c.name, layer.packed),
+                           "kernel_us": us(np.mean(gu_s)), "kernel_timing": timing,
                            "kernel_us_eager": gu_eager_us,
                            "bytes_per_launch": int(np.mean(gu_bytes)),
-                           "down_kernel_us": round(1e6 * float(np.mean(dn_s)), 2),
-                           "down_GBs": round(float(np.mean(dn_bytes / dn_s) / 1e9), 1)}
+                           "down_kernel_us": us(np.mean(dn_s)),
+                           "down_GBs": rnd(np.mean(dn_bytes / dn_s) / 1e9, 1)}
     return out
 
 
