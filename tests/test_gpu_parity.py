@@ -130,6 +130,26 @@ def test_route_indices_bit_exact(name):
     assert np.allclose(from_dev(w), want_w, rtol=1e-4, atol=1e-6)
 
 
+def test_route_batch_builds_agree():
+    """Batches of 2048 tokens and more route on a build capped at 128 registers a lane,
+    smaller ones on the uncapped build: 2048 and 2047 tokens of prefill4k route their
+    common tokens identically (indices, weights and logits bit for bit)."""
+    h = host_layer("prefill4k")
+    c = h["cfg"]
+    dw = dev_weights("prefill4k")
+    xs = h["x"][:2048]
+    bias = h["bias"]
+
+    def run(T):
+        b = None if bias is None else to_dev(bias[:T] if bias.ndim == 2 else bias)
+        return [from_dev(t) for t in moe.route(to_dev(xs[:T]), dw["router_w"], c.k, bias=b)]
+
+    big, small = run(2048), run(2047)
+    for a, b in zip(big, small):
+        assert np.array_equal(a[:2047].view(np.uint32) if a.dtype == np.float32 else a[:2047],
+                              b.view(np.uint32) if b.dtype == np.float32 else b)
+
+
 @pytest.mark.parametrize("T", [3, 40, 300])
 def test_route_subnormal_inputs_recomputed(T):
     """Tokens and router rows holding subnormal bf16 values (which the matrix cores or
