@@ -331,28 +331,43 @@ __global__ void __launch_bounds__(256, MINB) dense_mfma_dma_kernel(DenseMfmaArgs
 }
 
 // Euclidean norms of bf16 rows, as the GEMV router computes them: each lane sums the
-// squares of its 8-element chunks (exact products, fp32 sums), the wave adds the lanes,
-// the root is rounded once.  A row with a subnormal bf16 value gets +inf.
-__global__ void __launch_bounds__(256) row_norms_kernel(const uint16_t* __restrict__ rows, int64_t n, int32_t K,
-                                                        float* __restrict__ out) {
+// squares of its 8-element chunks (exact products, fp32 sums, chunks in column order),
+// the wave adds the lanes, the root is rounded once.  A row with a subnormal bf16 value
+// gets +inf.  One launch covers the router's rows (a, na of them) and the tokens (b, nb);
+// a lane's chunks are loaded RN_CH at a time, all before the first is used (K <= 8192: one
+// memory round trip per row).
+constexpr int RN_CH = 16;
+__global__ void __launch_bounds__(256) row_norms_kernel(const uint16_t* __restrict__ a, int64_t na,
+                                                        const uint16_t* __restrict__ b, int64_t nb, int32_t K,
+                                                        float* __restrict__ outa, float* __restrict__ outb) {
   const int lane = lane_id();
-  const int64_t row = (int64_t)blockIdx.x * 4 + threadIdx.x / WAVE;
-  if (row >= n) return;
-  const uint16_t* r = rows + row * K;
+  int64_t row = (int64_t)blockIdx.x * 4 + threadIdx.x / WAVE;
+  if (row >= na + nb) return;
+  const bool second = row >= na;
+  if (second) row -= na;
+  const uint16_t* r = (second ? b : a) + row * K;
   float s = 0.f;
   uint32_t sub = 0;
-  for (int col = 8 * lane; col < K; col += 8 * WAVE) {
-    const uint4 v = load_nt16(r + col);
-    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+  for (int c0 = 0; 8 * WAVE * c0 < K; c0 += RN_CH) {
+    uint4 v[RN_CH];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      s = dot2(d[i], d[i], s);
-      sub |= bf16x2_subnormal(d[i]);
+    for (int c = 0; c < RN_CH; ++c) {
+      const int col = 8 * (lane + WAVE * (c0 + c));
+      v[c] = col < K ? load_nt16(r + col) : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int c = 0; c < RN_CH; ++c) {
+      const uint32_t d[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s = dot2(d[i], d[i], s);
+        sub |= bf16x2_subnormal(d[i]);
+      }
     }
   }
   s = wave_sum_dpp(s);
   const bool any_sub = __any(sub != 0u);
-  if (lane == 0) out[row] = any_sub ? __builtin_inff() : sqrtf(s);
+  if (lane == 0) (second ? outb : outa)[row] = any_sub ? __builtin_inff() : sqrtf(s);
 }
 
 // ------------------------------------------------------------------------- host
@@ -438,9 +453,8 @@ hipError_t launch_dense_mfma(const uint16_t* x, int64_t T, int32_t K, const Dens
   a.add = s.add;
   a.add_rows = s.add ? s.add_rows : 0;
   if (s.router) {
-    hipLaunchKernelGGL(row_norms_kernel, dim3((unsigned)ceil_div(s.rows, 4)), dim3(256), 0, st, s.W,
-                       (int64_t)s.rows, K, s.wnorm);
-    hipLaunchKernelGGL(row_norms_kernel, dim3((unsigned)ceil_div(T, 4)), dim3(256), 0, st, x, T, K, s.xnorm);
+    hipLaunchKernelGGL(row_norms_kernel, dim3((unsigned)ceil_div(s.rows + T, 4)), dim3(256), 0, st, s.W,
+                       (int64_t)s.rows, x, T, K, s.wnorm, s.xnorm);
     if (T >= 256)
       return dm_dma_pays(T, s.rows, 128, 64) ? launch_dm_dma<4, 2, true, 2>(a, st) : launch_dm<4, 2, 2, true>(a, st);
     switch (small_tile(T, s.rows)) {
