@@ -69,7 +69,10 @@ __global__ void __launch_bounds__(PERM_THREADS) perm_count_kernel(const int32_t*
   for (int e = threadIdx.x; e < E; e += PERM_THREADS) cc[(int64_t)blockIdx.x * E + e] = hist[e];
 }
 
-// one block: chunk counts -> chunk bases (in place), counts, offsets, active list
+// one block: chunk counts -> each chunk's first row within its expert's group (in place),
+// counts, offsets, active list.  A thread runs down one expert's column of chunk counts,
+// PS_BATCH loads issued before the first is used.
+constexpr int PS_BATCH = 16;
 __global__ void __launch_bounds__(PERM_THREADS) perm_scan_kernel(int32_t* __restrict__ cc, int nchunks,
                                                                  int32_t E, int32_t* __restrict__ counts,
                                                                  int32_t* __restrict__ offsets,
@@ -82,10 +85,16 @@ __global__ void __launch_bounds__(PERM_THREADS) perm_scan_kernel(int32_t* __rest
   int* partial = sh + 2 * E;   // PERM_THREADS
   for (int e = threadIdx.x; e < E; e += PERM_THREADS) {
     int run = 0;
-    for (int c = 0; c < nchunks; ++c) {
-      int v = cc[(int64_t)c * E + e];
-      cc[(int64_t)c * E + e] = run;
-      run += v;
+    for (int c0 = 0; c0 < nchunks; c0 += PS_BATCH) {
+      int v[PS_BATCH];
+#pragma unroll
+      for (int u = 0; u < PS_BATCH; ++u) v[u] = c0 + u < nchunks ? cc[(int64_t)(c0 + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < PS_BATCH; ++u)
+        if (c0 + u < nchunks) {
+          cc[(int64_t)(c0 + u) * E + e] = run;
+          run += v[u];
+        }
     }
     tot[e] = run;
     counts[e] = run;
@@ -98,7 +107,6 @@ __global__ void __launch_bounds__(PERM_THREADS) perm_scan_kernel(int32_t* __rest
     offsets[e] = tot[e];
     if (counts[e] > 0) tiles[act[e]] = make_int4(e, tot[e], counts[e], -1);  // first row: scatter
     slot_of[e] = act[e];
-    for (int c = 0; c < nchunks; ++c) cc[(int64_t)c * E + e] += tot[e];
   }
   for (int sl = nact + threadIdx.x; sl < max_tiles; sl += PERM_THREADS) tiles[sl] = make_int4(-1, 0, 0, -1);
   if (threadIdx.x == 0) {
@@ -155,7 +163,7 @@ __global__ void __launch_bounds__(PERM_THREADS) perm_scatter_kernel(const int32_
     uint32_t key = keys[p];
     if (key != PAD_KEY) {
       uint32_t e = key >> 11, i = key & (PERM_CHUNK - 1);
-      const int pos = cbase[(int64_t)blockIdx.x * E + e] + (p - sstart[e]);
+      const int pos = offsets[e] + cbase[(int64_t)blockIdx.x * E + e] + (p - sstart[e]);
       perm[pos] = (int32_t)(base + i);
       if (pos == offsets[e]) tiles[slot_of[e]].w = (int32_t)(base + i);
     }
